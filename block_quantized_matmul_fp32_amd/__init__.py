@@ -1,0 +1,251 @@
+"""Python binding of the gfx950 block-quantized matmul library (include/vq.h).
+
+Argument marshalling only: every function passes device pointers, sizes and
+the current HIP stream to the C ABI of ``libvq.so`` and raises ``VQError``
+on a non-OK status.  PyTorch supplies device memory and streams; no step of
+the computation runs in Python or on the CPU.  If the library is not built
+(``python -m block_quantized_matmul_fp32_amd.build``) every call fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libvq.so")
+
+Q4_K, Q6_K, Q8_0, Q8_K, Q8_1 = 0, 1, 2, 3, 4
+TYPE_NAMES = {Q4_K: "Q4_K", Q6_K: "Q6_K", Q8_0: "Q8_0", Q8_K: "Q8_K", Q8_1: "Q8_1"}
+OP_GEMV, OP_GEMM, OP_GEMM_GROUPED = 0, 1, 2
+
+STATUS = {0: "VQ_OK", 1: "VQ_ERR_INVALID_ARG", 2: "VQ_ERR_UNSUPPORTED_TYPE", 3: "VQ_ERR_TYPE_PAIR",
+          4: "VQ_ERR_SHAPE", 5: "VQ_ERR_ALIAS", 6: "VQ_ERR_WORKSPACE", 7: "VQ_ERR_HIP"}
+
+EXPORTS = [
+    "vq_status_string", "vq_last_error", "vq_type_name", "vq_is_supported", "vq_block_values",
+    "vq_block_bytes", "vq_weight_bytes", "vq_act_bytes", "vq_act_d_offset", "vq_act_aux_offset",
+    "vq_quantize_act", "vq_quantize_weights", "vq_gemv", "vq_gemm", "vq_grouped_workspace_bytes",
+    "vq_gemm_grouped", "vq_weighted_sum", "vq_get_stats", "vq_reset_stats", "vq_version",
+]
+
+STAT_FIELDS = ["quantize_q8k", "quantize_q8_1", "quantize_weights", "gemv_q4k", "gemv_q6k", "gemv_q8_0",
+               "gemm_q4k", "gemm_q6k", "gemm_q8_0", "route", "gemm_grouped_q4k", "weighted_sum"]
+
+
+class VQStats(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_uint64) for f in STAT_FIELDS]
+
+
+class VQError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s: %s" % (STATUS.get(status, str(status)), message))
+        self.status = status
+        self.status_name = STATUS.get(status, str(status))
+        self.message = message
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libvq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libvq.so is not built (python -m block_quantized_matmul_fp32_amd.build); "
+                              "there is no fallback path")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I, Z = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+        L.vq_status_string.restype = ctypes.c_char_p
+        L.vq_status_string.argtypes = [I]
+        L.vq_last_error.restype = ctypes.c_char_p
+        L.vq_type_name.restype = ctypes.c_char_p
+        L.vq_type_name.argtypes = [I]
+        L.vq_is_supported.argtypes = [I, I, I]
+        L.vq_block_values.argtypes = [I]
+        L.vq_block_bytes.argtypes = [I]
+        L.vq_block_bytes.restype = Z
+        for f in ("vq_weight_bytes", "vq_act_bytes", "vq_act_d_offset", "vq_act_aux_offset"):
+            getattr(L, f).argtypes = [I, I64, I64]
+            getattr(L, f).restype = Z
+        L.vq_quantize_act.argtypes = [I, P, I64, I64, I64, P, P]
+        L.vq_quantize_weights.argtypes = [I, P, I64, I64, P, P]
+        L.vq_gemv.argtypes = [I, P, I64, I64, P, P, P, P]
+        L.vq_gemm.argtypes = [I, P, I64, I64, I, P, I64, P, I64, P]
+        L.vq_grouped_workspace_bytes.argtypes = [I64, I64, I64]
+        L.vq_grouped_workspace_bytes.restype = Z
+        L.vq_gemm_grouped.argtypes = [I, P, I64, I64, I64, I, P, I64, P, I64, P, P, P, P, Z, P]
+        L.vq_weighted_sum.argtypes = [P, P, I64, I64, I64, P, P]
+        L.vq_get_stats.argtypes = [ctypes.POINTER(VQStats)]
+        L.vq_version.restype = ctypes.c_char_p
+        for f in ("vq_quantize_act", "vq_quantize_weights", "vq_gemv", "vq_gemm", "vq_gemm_grouped",
+                  "vq_weighted_sum"):
+            getattr(L, f).restype = I
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise VQError(status, lib().vq_last_error().decode())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _torch():
+    import torch
+    return torch
+
+
+# ------------------------------------------------------------------- sizes
+def block_values(t: int) -> int:
+    return lib().vq_block_values(t)
+
+
+def block_bytes(t: int) -> int:
+    return lib().vq_block_bytes(t)
+
+
+def weight_bytes(w: int, N: int, K: int) -> int:
+    return lib().vq_weight_bytes(w, N, K)
+
+
+def act_bytes(act: int, M: int, K: int) -> int:
+    return lib().vq_act_bytes(act, M, K)
+
+
+def act_d_offset(act: int, M: int, K: int) -> int:
+    return lib().vq_act_d_offset(act, M, K)
+
+
+def act_aux_offset(act: int, M: int, K: int) -> int:
+    return lib().vq_act_aux_offset(act, M, K)
+
+
+def grouped_workspace_bytes(E: int, T: int, top_k: int) -> int:
+    return lib().vq_grouped_workspace_bytes(E, T, top_k)
+
+
+def is_supported(w: int, act: int, op: int) -> bool:
+    return bool(lib().vq_is_supported(w, act, op))
+
+
+def type_name(t: int) -> str:
+    return lib().vq_type_name(t).decode()
+
+
+def version() -> str:
+    return lib().vq_version().decode()
+
+
+def act_for(w: int) -> int:
+    """The activation type a weight type pairs with."""
+    return Q8_1 if w == Q8_0 else Q8_K
+
+
+# ------------------------------------------------------------------- calls
+def quantize_act(act: int, X, M: int = None, K: int = None, ldx: int = None, Xq=None, stream=None):
+    """vq_quantize_act: fp32 X [M, ldx] -> planar Q8_K / Q8_1 bytes (uint8 tensor)."""
+    if M is None:
+        M, K = (1, X.shape[0]) if X.dim() == 1 else (X.shape[0], X.shape[1])
+    if ldx is None:
+        ldx = K if X.dim() == 1 else X.stride(0)
+    if Xq is None:
+        Xq = _torch().empty(act_bytes(act, M, K), dtype=_torch().uint8, device=X.device)
+    _check(lib().vq_quantize_act(act, _ptr(X), M, K, ldx, _ptr(Xq), _stream(stream)))
+    return Xq
+
+
+def quantize_weights(w: int, W, N: int = None, K: int = None, Wq=None, stream=None):
+    """vq_quantize_weights: fp32 W [N, K] -> block bytes (uint8 tensor)."""
+    if N is None:
+        N, K = W.shape
+    if Wq is None:
+        Wq = _torch().empty(weight_bytes(w, N, K), dtype=_torch().uint8, device=W.device)
+    _check(lib().vq_quantize_weights(w, _ptr(W), N, K, _ptr(Wq), _stream(stream)))
+    return Wq
+
+
+def gemv(w: int, W, N: int, K: int, x, y=None, xq_out=None, stream=None):
+    """vq_gemv: y[N] = W . x with the activation quantizer fused in."""
+    if y is None:
+        y = _torch().empty(N, dtype=_torch().float32, device=x.device)
+    _check(lib().vq_gemv(w, _ptr(W), N, K, _ptr(x), _ptr(y), _ptr(xq_out), _stream(stream)))
+    return y
+
+
+def gemm(w: int, W, N: int, K: int, act: int, Xq, M: int, Y=None, ldy: int = None, stream=None):
+    """vq_gemm: Y[M, N] = deq(Xq) . deq(W)^T."""
+    if Y is None:
+        Y = _torch().empty((M, N), dtype=_torch().float32, device=Xq.device)
+    if ldy is None:
+        ldy = N if Y.dim() == 1 else Y.stride(0)
+    _check(lib().vq_gemm(w, _ptr(W), N, K, act, _ptr(Xq), M, _ptr(Y), ldy, _stream(stream)))
+    return Y
+
+
+def gemm_grouped(w: int, W, E: int, N: int, K: int, act: int, Xq, T: int, ids, top_k: int,
+                 route_w=None, Y=None, Ysum=None, ws=None, want_sum: bool = True, stream=None):
+    """vq_gemm_grouped: Y[T, top_k, N] and (optionally) Ysum[T, N]; returns (Y, Ysum, ws)."""
+    torch = _torch()
+    dev = Xq.device
+    if Y is None:
+        Y = torch.empty((T, top_k, N), dtype=torch.float32, device=dev)
+    if Ysum is None and want_sum and route_w is not None:
+        Ysum = torch.empty((T, N), dtype=torch.float32, device=dev)
+    need = grouped_workspace_bytes(E, T, top_k)
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check(lib().vq_gemm_grouped(w, _ptr(W), E, N, K, act, _ptr(Xq), T, _ptr(ids), top_k, _ptr(route_w),
+                                 _ptr(Y), _ptr(Ysum), _ptr(ws), ws.numel() if hasattr(ws, "numel") else need,
+                                 _stream(stream)))
+    return Y, Ysum, ws
+
+
+def weighted_sum(Y, route_w, T: int, top_k: int, N: int, Ysum=None, stream=None):
+    """vq_weighted_sum: Ysum[T, N] = sum_s w[t, s] * Y[t, s, :] (slot order, no FMA)."""
+    if Ysum is None:
+        Ysum = _torch().empty((T, N), dtype=_torch().float32, device=Y.device)
+    _check(lib().vq_weighted_sum(_ptr(Y), _ptr(route_w), T, top_k, N, _ptr(Ysum), _stream(stream)))
+    return Ysum
+
+
+def get_stats() -> dict:
+    s = VQStats()
+    lib().vq_get_stats(ctypes.byref(s))
+    return {f: int(getattr(s, f)) for f in STAT_FIELDS}
+
+
+def reset_stats():
+    lib().vq_reset_stats()
+
+
+def grouped_ws_views(ws, E: int, T: int, top_k: int):
+    """counts [E], offsets [E+1], list [T*top_k] views into a workspace after a
+    vq_gemm_grouped call (section layout of include/vq.h)."""
+    torch = _torch()
+
+    def a256(x):
+        return (x + 255) // 256 * 256
+
+    o_counts = 0
+    o_offsets = a256(4 * E)
+    o_list = o_offsets + a256(4 * (E + 1))
+    w32 = ws.view(torch.int32)
+    return (w32[o_counts // 4:o_counts // 4 + E], w32[o_offsets // 4:o_offsets // 4 + E + 1],
+            w32[o_list // 4:o_list // 4 + T * top_k])

@@ -1,0 +1,571 @@
+// gemm.hip -- prefill GEMM Y = X * W^T on int8 MFMA for gfx950, and its
+// routed-expert (MUL_MAT_ID) variant.
+//
+// Pages: vllm.cpp PR #3035 "scope a cooperative activation share for the WMMA
+// kernels" (each warp re-reading the same activation rows is the diagnosed
+// redundancy; one cooperatively loaded tile per block shared by all warps is
+// the fix), strix-llama.cpp PR #18 commits "MMQ register prefetch" (stage the
+// next 256-wide K iteration in registers while the current one is consumed)
+// and "routed-compact" (MUL_MAT_ID tiles sized to the rows of each expert).
+//
+// MI355X design (not the pages' RDNA WMMA tiles):
+//  * 256 threads, a 2x2 grid of waves; each wave owns 32 weight rows x BM/2
+//    activation rows as 16x16 MFMA tiles; the workgroup tile is 64 x BM.
+//  * Per 256-wide K step the workgroup stages ONE activation tile (int8 Q8_K
+//    or Q8_1 bytes plus scales) in LDS, shared by all four waves, and ONE
+//    unpacked weight tile, also shared; the next step's global bytes are
+//    already in flight in registers while the current step computes.
+//  * The per-sub-block integer scales are folded into the int8 MFMA operand
+//    so that a whole super-block is one int32 accumulation with no per-
+//    sub-block ALU work:
+//      Q4_K: sc (6 bit) = 8*sc_hi + sc_lo; planes q*sc_lo and q*sc_hi (each
+//            <= 105) -> S = 8*P_hi + P_lo.  The min term Mn = sum_j m_j*bs32_j
+//            runs on two 16x16x32 MFMAs with bs32 = 64*h + l.
+//      Q6_K: sc (int8) = 64*d2 + 8*d1 + d0 with digits in [-3,4]; planes
+//            (q-32)*d_i fit int8 -> S = 64*P2 + 8*P1 + P0.
+//      Q8_0: one 16x16x32 MFMA per 32-block, combined per block.
+//    The integer sums are exact, and the binary32 combine of each block and
+//    the ascending-block accumulation follow the fixed-order definition, so Y
+//    is bit-identical to it.
+#include "vq_device.h"
+#include "vq_internal.h"
+
+// Every binary32 expression in this file is evaluated as written: no
+// multiply-add contraction (the fixed-order definitions round each product
+// and each sum on their own).
+#pragma clang fp contract(off)
+
+namespace vqk {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+
+constexpr int kBN = 64;   // weight rows per workgroup
+constexpr int kKS = 256;  // K per step
+constexpr int kLD = 272;  // LDS row stride of the int8 tiles (256 + 16 against bank conflicts)
+
+// 16 bytes from a 2-byte aligned global address using 4-byte aligned loads;
+// never reads at or beyond `end`.
+__device__ __forceinline__ void gload16_a2(const uint8_t* p, const uint8_t* end, uint32_t out[4]) {
+    const uintptr_t a = (uintptr_t)p;
+    const uint32_t* q = (const uint32_t*)(a & ~(uintptr_t)3);
+    const uint32_t sh = (uint32_t)(a & 3);
+    uint32_t w0 = q[0], w1 = q[1], w2 = q[2], w3 = q[3];
+    if (sh == 0) {
+        out[0] = w0; out[1] = w1; out[2] = w2; out[3] = w3;
+        return;
+    }
+    uint32_t w4;
+    if ((const uint8_t*)(q + 5) <= end) w4 = q[4];
+    else w4 = (uint32_t)(*(const uint16_t*)(q + 4));
+    out[0] = __builtin_amdgcn_alignbyte(w1, w0, sh);
+    out[1] = __builtin_amdgcn_alignbyte(w2, w1, sh);
+    out[2] = __builtin_amdgcn_alignbyte(w3, w2, sh);
+    out[3] = __builtin_amdgcn_alignbyte(w4, w3, sh);
+}
+
+// Multiply the four int8 bytes of v by a small integer f (every true product
+// fits int8): even and odd bytes go through 16-bit lanes, so no carry crosses
+// a byte, and the low bytes are repacked with v_perm.
+__device__ __forceinline__ uint32_t bytes_mul(uint32_t v, int f) {
+    const us2 fe = (us2){(unsigned short)f, (unsigned short)f};
+    const us2 e = __builtin_bit_cast(us2, v & 0x00FF00FFu) * fe;
+    const us2 o = __builtin_bit_cast(us2, (v >> 8) & 0x00FF00FFu) * fe;
+    return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, o), __builtin_bit_cast(uint32_t, e),
+                                 0x06020400u);
+}
+
+// Unsigned 6-bit quants (bytes 0..63) -> signed (q - 32) bytes.
+__device__ __forceinline__ uint32_t bytes_sub32(uint32_t q) {
+    const us2 e = __builtin_bit_cast(us2, q & 0x00FF00FFu) - (us2){32, 32};
+    const us2 o = __builtin_bit_cast(us2, (q >> 8) & 0x00FF00FFu) - (us2){32, 32};
+    return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, o), __builtin_bit_cast(uint32_t, e),
+                                 0x06020400u);
+}
+
+template <int WT>
+struct GemmCfg;
+template <>
+struct GemmCfg<0> { static constexpr int P = 2; static constexpr int BB = kQ4KBytes; };
+template <>
+struct GemmCfg<1> { static constexpr int P = 3; static constexpr int BB = kQ6KBytes; };
+template <>
+struct GemmCfg<2> { static constexpr int P = 1; static constexpr int BB = kQ80Bytes; };
+
+// Row indirection of the grouped (MUL_MAT_ID) variant.
+struct GroupArgs {
+    const int32_t* tiles;   // [ntiles][4]: expert, first list slot, rows, 0
+    const int32_t* ntiles;  // device count of valid tiles
+    const int32_t* list;    // pair indices grouped per expert
+    int top_k;
+    int64_t expert_stride;  // bytes of one expert's [N][K/256] blocks
+};
+
+template <int WT, int BM, bool kGrouped>
+__global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ Wbase, int N, int K,
+                                                   int64_t wbytes, const int8_t* __restrict__ aqs,
+                                                   const void* __restrict__ ad,
+                                                   const int16_t* __restrict__ abs_, int M,
+                                                   float* __restrict__ Y, int64_t ldy,
+                                                   GroupArgs ga) {
+    constexpr int P = GemmCfg<WT>::P;
+    constexpr int BB = GemmCfg<WT>::BB;
+    constexpr int TM = BM / 32;            // 16-row activation tiles per wave
+    constexpr int ACH = BM * 16 / 256;     // 16-byte activation chunks per thread per step
+    __shared__ __attribute__((aligned(16))) int8_t sA[BM * kLD];
+    __shared__ __attribute__((aligned(16))) int8_t sW[P * kBN * kLD];
+    __shared__ __attribute__((aligned(16))) float sDa[BM * 8];
+    __shared__ __attribute__((aligned(16))) float sDw[kBN * 8];
+    __shared__ __attribute__((aligned(16))) int8_t sMw[kBN * 8];
+    __shared__ __attribute__((aligned(16))) int8_t sHl[BM * 16];
+    __shared__ int sRow[BM];    // activation row of each tile row (-1: none)
+    __shared__ int sOut[BM];    // output row of each tile row (-1: none)
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wn = wave & 1, wm = wave >> 1;
+    const int r16 = lane & 15, g = lane >> 4;
+    const int n0 = blockIdx.x * kBN;
+
+    const uint8_t* W = Wbase;
+    int rows_here = BM;
+    if (kGrouped) {
+        const int tix = blockIdx.y;
+        if (tix >= *ga.ntiles) return;
+        const int e = ga.tiles[4 * tix + 0];
+        const int first = ga.tiles[4 * tix + 1];
+        rows_here = ga.tiles[4 * tix + 2];
+        W = Wbase + (int64_t)e * ga.expert_stride;
+        if (tid < BM) {
+            if (tid < rows_here) {
+                const int p = ga.list[first + tid];
+                sRow[tid] = p / ga.top_k;
+                sOut[tid] = p;
+            } else {
+                sRow[tid] = -1;
+                sOut[tid] = -1;
+            }
+        }
+    } else {
+        const int m0 = blockIdx.y * BM;
+        if (tid < BM) {
+            const int m = m0 + tid;
+            sRow[tid] = (m < M) ? m : -1;
+            sOut[tid] = (m < M) ? m : -1;
+        }
+    }
+    __syncthreads();
+
+    const int nbw = (WT == 2) ? K / kQK8 : K / kQK;
+    const int64_t rb = (int64_t)nbw * BB;
+    const uint8_t* wend = Wbase + wbytes;
+    const int nsteps = (K + kKS - 1) / kKS;
+
+    // Per-thread load roles.
+    const int wrow = tid >> 2, wq = tid & 3;            // weight unpack: row, quarter
+    const bool wvalid = (n0 + wrow) < N;
+    const uint8_t* wrow_p = W + (int64_t)(n0 + wrow) * rb;
+
+    // Register-staged global data of one step.
+    uint4 regA[ACH];
+    uint32_t regW[24];
+    float regDa[2];
+    uint4 regBs[2];
+
+    auto load_step = [&](int s) {
+        // activation qs tile: BM rows x 256 bytes
+#pragma unroll
+        for (int i = 0; i < ACH; ++i) {
+            const int c = tid + 256 * i;
+            const int row = c >> 4, col = (c & 15) * 16;
+            const int ar = sRow[row];
+            const int kk = s * kKS + col;
+            if (ar >= 0 && kk < K)
+                regA[i] = *(const uint4*)(aqs + (int64_t)ar * K + kk);
+            else
+                regA[i] = make_uint4(0, 0, 0, 0);
+        }
+        // activation scales
+        if (WT == 2) {
+            // Q8_1: binary16 d of the step's 8 blocks; threads < BM, one row each
+            if (tid < BM) {
+                const int ar = sRow[tid];
+                const uint16_t* dp = (const uint16_t*)ad;
+                uint32_t h[8];
+#pragma unroll
+                for (int b = 0; b < 8; ++b) {
+                    const int blk = s * 8 + b;
+                    h[b] = (ar >= 0 && blk < nbw) ? dp[(int64_t)ar * nbw + blk] : 0u;
+                }
+                regBs[0] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                                      h[6] | (h[7] << 16));
+            }
+        } else {
+            if (tid < BM) {
+                const int ar = sRow[tid];
+                regDa[0] = (ar >= 0) ? ((const float*)ad)[(int64_t)ar * nbw + s] : 0.0f;
+                if (WT == 0) {
+                    if (ar >= 0) {
+                        const uint4* bp = (const uint4*)(abs_ + ((int64_t)ar * nbw + s) * 16);
+                        regBs[0] = bp[0];
+                        regBs[1] = bp[1];
+                    } else {
+                        regBs[0] = regBs[1] = make_uint4(0, 0, 0, 0);
+                    }
+                }
+            }
+        }
+        // weights
+        if (WT == 0) {
+            if (wvalid) {
+                const uint8_t* bp = wrow_p + (int64_t)s * kQ4KBytes;
+                const uint4 h = *(const uint4*)bp;
+                const uint4 q0 = *(const uint4*)(bp + 16 + 32 * wq);
+                const uint4 q1 = *(const uint4*)(bp + 32 + 32 * wq);
+                regW[0] = h.x; regW[1] = h.y; regW[2] = h.z; regW[3] = h.w;
+                regW[4] = q0.x; regW[5] = q0.y; regW[6] = q0.z; regW[7] = q0.w;
+                regW[8] = q1.x; regW[9] = q1.y; regW[10] = q1.z; regW[11] = q1.w;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 12; ++i) regW[i] = 0;
+            }
+        } else if (WT == 1) {
+            if (wvalid) {
+                const uint8_t* bp = wrow_p + (int64_t)s * kQ6KBytes;
+                gload16_a2(bp + 16 * wq, wend, regW + 0);             // ql, half 0
+                gload16_a2(bp + 64 + 16 * wq, wend, regW + 4);        // ql, half 1
+                gload16_a2(bp + 128 + 16 * (wq & 1), wend, regW + 8); // qh, half 0
+                gload16_a2(bp + 160 + 16 * (wq & 1), wend, regW + 12);// qh, half 1
+                const int8_t* sp = (const int8_t*)(bp + 192);
+                regW[16] = (uint32_t)(uint8_t)sp[wq] | ((uint32_t)(uint8_t)sp[4 + wq] << 8) |
+                           ((uint32_t)(uint8_t)sp[8 + wq] << 16) | ((uint32_t)(uint8_t)sp[12 + wq] << 24);
+                regW[17] = *(const uint16_t*)(bp + 208);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 18; ++i) regW[i] = 0;
+            }
+        } else {
+            // Q8_0: two 34-byte blocks (8s + 2wq, 8s + 2wq + 1) per thread
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int blk = s * 8 + 2 * wq + j;
+                if (wvalid && blk < nbw) {
+                    const uint8_t* bp = wrow_p + (int64_t)blk * kQ80Bytes;
+                    gload16_a2(bp + 2, wend, regW + 9 * j);
+                    gload16_a2(bp + 18, wend, regW + 9 * j + 4);
+                    regW[9 * j + 8] = *(const uint16_t*)bp;
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 9; ++i) regW[9 * j + i] = 0;
+                }
+            }
+        }
+    };
+
+    auto store_step = [&]() {
+#pragma unroll
+        for (int i = 0; i < ACH; ++i) {
+            const int c = tid + 256 * i;
+            const int row = c >> 4, col = (c & 15) * 16;
+            *(uint4*)(sA + row * kLD + col) = regA[i];
+        }
+        if (WT == 2) {
+            if (tid < BM) {
+                const uint32_t hw[4] = {regBs[0].x, regBs[0].y, regBs[0].z, regBs[0].w};
+#pragma unroll
+                for (int b = 0; b < 8; ++b)
+                    sDa[tid * 8 + b] = half_bits_to_float((hw[b >> 1] >> (16 * (b & 1))) & 0xFFFF);
+            }
+        } else if (tid < BM) {
+            sDa[tid] = regDa[0];
+            if (WT == 0) {
+                const uint32_t bw[8] = {regBs[0].x, regBs[0].y, regBs[0].z, regBs[0].w,
+                                        regBs[1].x, regBs[1].y, regBs[1].z, regBs[1].w};
+                uint32_t hh[2] = {0, 0}, ll[2] = {0, 0};
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int b0 = (int)(int16_t)(bw[j] & 0xFFFF);
+                    const int b1 = (int)(int16_t)(bw[j] >> 16);
+                    const int bs32 = b0 + b1;
+                    const int h = bs32 >> 6, l = bs32 & 63;
+                    hh[j >> 2] |= ((uint32_t)(h & 0xFF)) << (8 * (j & 3));
+                    ll[j >> 2] |= ((uint32_t)l) << (8 * (j & 3));
+                }
+                *(uint4*)(sHl + tid * 16) = make_uint4(hh[0], hh[1], ll[0], ll[1]);
+            }
+        }
+        if (WT == 0) {
+            const uint32_t sw = (wq < 2) ? regW[1] : regW[2];
+            const uint32_t s_lo = (sw >> (16 * (wq & 1))) & 0xFF;
+            const uint32_t s_hi = (sw >> (16 * (wq & 1) + 8)) & 0xFF;
+            const int sc0 = s_lo & 63, sc1 = s_hi & 63;
+            const int fa[2] = {sc0 & 7, sc0 >> 3};
+            const int fb[2] = {sc1 & 7, sc1 >> 3};
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                uint32_t lo[8], hi[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const uint32_t q = regW[4 + i];
+                    lo[i] = bytes_mul(q & 0x0F0F0F0Fu, fa[p]);
+                    hi[i] = bytes_mul((q >> 4) & 0x0F0F0F0Fu, fb[p]);
+                }
+                int8_t* dst = sW + (p * kBN + wrow) * kLD + 64 * wq;
+                *(uint4*)(dst + 0) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+                *(uint4*)(dst + 16) = make_uint4(lo[4], lo[5], lo[6], lo[7]);
+                *(uint4*)(dst + 32) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+                *(uint4*)(dst + 48) = make_uint4(hi[4], hi[5], hi[6], hi[7]);
+            }
+            if (wq == 0) {
+                sDw[wrow] = half_bits_to_float(regW[0] & 0xFFFF);
+                sDw[kBN + wrow] = half_bits_to_float(regW[0] >> 16);
+                // mins: m_j = (scales[j] >> 6) | (nibble j&1 of scales[8 + j/2]) << 2
+                uint32_t mw[2] = {0, 0};
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const uint32_t sj = ((j < 4 ? regW[1] : regW[2]) >> (8 * (j & 3))) & 0xFF;
+                    const uint32_t nb_ = (regW[3] >> (8 * (j >> 1) + 4 * (j & 1))) & 15;
+                    const uint32_t m = (sj >> 6) | (nb_ << 2);
+                    mw[j >> 2] |= m << (8 * (j & 3));
+                }
+                *(uint2*)(sMw + wrow * 8) = make_uint2(mw[0], mw[1]);
+            }
+        } else if (WT == 1) {
+            // runs: (h, lo/hi nibble) -> elements 128h + 64*hi + 16*wq, sub-block 8h + 4*hi + wq
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                for (int part = 0; part < 2; ++part) {
+                    const int sc = (int)(int8_t)((regW[16] >> (8 * (2 * h + part))) & 0xFF);
+                    const int d0 = ((sc + 3) & 7) - 3;
+                    const int t1 = (sc - d0) >> 3;
+                    const int d1 = ((t1 + 3) & 7) - 3;
+                    const int d2 = (t1 - d1) >> 3;
+                    const int sh = 2 * (2 * part + (wq >> 1));
+                    uint32_t qs[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t ql = regW[4 * h + i];
+                        const uint32_t qh = regW[8 + 4 * h + i];
+                        const uint32_t lo4 = part ? ((ql >> 4) & 0x0F0F0F0Fu) : (ql & 0x0F0F0F0Fu);
+                        qs[i] = bytes_sub32(lo4 | (((qh >> sh) & 0x03030303u) << 4));
+                    }
+                    const int dg[3] = {d0, d1, d2};
+#pragma unroll
+                    for (int p = 0; p < 3; ++p) {
+                        int8_t* dst = sW + (p * kBN + wrow) * kLD + 128 * h + 64 * part + 16 * wq;
+                        *(uint4*)dst = make_uint4(bytes_mul(qs[0], dg[p]), bytes_mul(qs[1], dg[p]),
+                                                  bytes_mul(qs[2], dg[p]), bytes_mul(qs[3], dg[p]));
+                    }
+                }
+            }
+            if (wq == 0) sDw[wrow] = half_bits_to_float(regW[17] & 0xFFFF);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int b = 2 * wq + j;
+                int8_t* dst = sW + wrow * kLD + 32 * b;
+                *(uint4*)dst = make_uint4(regW[9 * j + 0], regW[9 * j + 1], regW[9 * j + 2], regW[9 * j + 3]);
+                *(uint4*)(dst + 16) =
+                    make_uint4(regW[9 * j + 4], regW[9 * j + 5], regW[9 * j + 6], regW[9 * j + 7]);
+                sDw[wrow * 8 + b] = half_bits_to_float(regW[9 * j + 8] & 0xFFFF);
+            }
+        }
+    };
+
+    float acc[2][TM][4];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < TM; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[a][b][i] = 0.0f;
+
+    load_step(0);
+    for (int s = 0; s < nsteps; ++s) {
+        __syncthreads();
+        store_step();
+        __syncthreads();
+        if (s + 1 < nsteps) load_step(s + 1);
+
+        const int wn0 = 32 * wn, wm0 = (BM / 2) * wm;
+        if (WT == 2) {
+            const int nval = min(8, nbw - 8 * s);
+            for (int b = 0; b < nval; ++b) {
+                long av[2], bv[TM];
+#pragma unroll
+                for (int tn = 0; tn < 2; ++tn)
+                    av[tn] = *(const long*)(sW + (wn0 + 16 * tn + r16) * kLD + 32 * b + 8 * g);
+#pragma unroll
+                for (int tm = 0; tm < TM; ++tm)
+                    bv[tm] = *(const long*)(sA + (wm0 + 16 * tm + r16) * kLD + 32 * b + 8 * g);
+#pragma unroll
+                for (int tn = 0; tn < 2; ++tn) {
+                    float dwv[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) dwv[i] = sDw[(wn0 + 16 * tn + 4 * g + i) * 8 + b];
+#pragma unroll
+                    for (int tm = 0; tm < TM; ++tm) {
+                        v4i z = {0, 0, 0, 0};
+                        const v4i I = __builtin_amdgcn_mfma_i32_16x16x32_i8(av[tn], bv[tm], z, 0, 0, 0);
+                        const float da = sDa[(wm0 + 16 * tm + r16) * 8 + b];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float sc = dwv[i] * da;
+                            const float c = sc * (float)I[i];
+                            acc[tn][tm][i] = acc[tn][tm][i] + c;
+                        }
+                    }
+                }
+            }
+        } else {
+            v4i pacc[2][TM][P];
+#pragma unroll
+            for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+                for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+                    for (int p = 0; p < P; ++p) pacc[tn][tm][p] = (v4i){0, 0, 0, 0};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                v4i av[2][P], bv[TM];
+#pragma unroll
+                for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+                    for (int p = 0; p < P; ++p)
+                        av[tn][p] = *(const v4i*)(sW + (p * kBN + wn0 + 16 * tn + r16) * kLD + 64 * t + 16 * g);
+#pragma unroll
+                for (int tm = 0; tm < TM; ++tm)
+                    bv[tm] = *(const v4i*)(sA + (wm0 + 16 * tm + r16) * kLD + 64 * t + 16 * g);
+#pragma unroll
+                for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+                    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+                        for (int p = 0; p < P; ++p)
+                            pacc[tn][tm][p] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[tn][p], bv[tm],
+                                                                                    pacc[tn][tm][p], 0, 0, 0);
+            }
+            v4i mn[2][TM];
+            if (WT == 0) {
+                long am[2][2], bm[TM];
+#pragma unroll
+                for (int tn = 0; tn < 2; ++tn) {
+                    const long mv = *(const long*)(sMw + (wn0 + 16 * tn + r16) * 8);
+                    am[tn][0] = (g == 0) ? mv : 0;
+                    am[tn][1] = (g == 1) ? mv : 0;
+                }
+#pragma unroll
+                for (int tm = 0; tm < TM; ++tm) {
+                    const int8_t* hp = sHl + (wm0 + 16 * tm + r16) * 16;
+                    bm[tm] = (g == 0) ? *(const long*)hp : ((g == 1) ? *(const long*)(hp + 8) : 0);
+                }
+#pragma unroll
+                for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+                    for (int tm = 0; tm < TM; ++tm) {
+                        v4i z = {0, 0, 0, 0};
+                        const v4i dh = __builtin_amdgcn_mfma_i32_16x16x32_i8(am[tn][0], bm[tm], z, 0, 0, 0);
+                        const v4i dl = __builtin_amdgcn_mfma_i32_16x16x32_i8(am[tn][1], bm[tm], z, 0, 0, 0);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) mn[tn][tm][i] = (dh[i] << 6) + dl[i];
+                    }
+            }
+#pragma unroll
+            for (int tn = 0; tn < 2; ++tn) {
+                const int nb4 = wn0 + 16 * tn + 4 * g;
+                const float4 dv = *(const float4*)(sDw + nb4);
+                const float4 dmv = *(const float4*)(sDw + kBN + nb4);
+                const float dd[4] = {dv.x, dv.y, dv.z, dv.w};
+                const float dm[4] = {dmv.x, dmv.y, dmv.z, dmv.w};
+#pragma unroll
+                for (int tm = 0; tm < TM; ++tm) {
+                    const float da = sDa[wm0 + 16 * tm + r16];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        if (WT == 0) {
+                            const int S = (pacc[tn][tm][1][i] << 3) + pacc[tn][tm][0][i];
+                            const float t1 = dd[i] * (float)S;
+                            const float t2 = dm[i] * (float)mn[tn][tm][i];
+                            const float t3 = t1 - t2;
+                            const float c = da * t3;
+                            acc[tn][tm][i] = acc[tn][tm][i] + c;
+                        } else {
+                            const int S = (pacc[tn][tm][P - 1][i] << 6) + (pacc[tn][tm][1][i] << 3) +
+                                          pacc[tn][tm][0][i];
+                            const float t1 = dd[i] * (float)S;
+                            const float c = da * t1;
+                            acc[tn][tm][i] = acc[tn][tm][i] + c;
+                        }
+                    }
+                }
+            }
+        }
+    }
+
+    // Store: lane holds rows n = 4g + i of a 16x16 tile, column m = r16.
+    const int wn0 = 32 * wn, wm0 = (BM / 2) * wm;
+#pragma unroll
+    for (int tn = 0; tn < 2; ++tn) {
+        const int n = n0 + wn0 + 16 * tn + 4 * g;
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) {
+            const int orow = sOut[wm0 + 16 * tm + r16];
+            if (orow < 0) continue;
+            float* yp = Y + (int64_t)orow * ldy + n;
+            if (n + 3 < N && ((((uintptr_t)yp) & 15) == 0)) {
+                *(float4*)yp = make_float4(acc[tn][tm][0], acc[tn][tm][1], acc[tn][tm][2], acc[tn][tm][3]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (n + i < N) yp[i] = acc[tn][tm][i];
+            }
+        }
+    }
+}
+
+template <int WT>
+static hipError_t launch_gemm_t(const uint8_t* W, int64_t N, int64_t K, const void* aqs, const void* ad,
+                                const void* aux, int64_t M, float* Y, int64_t ldy, hipStream_t st) {
+    constexpr int BM = 128;
+    const int nbw = (WT == 2) ? (int)(K / kQK8) : (int)(K / kQK);
+    const int64_t wbytes = N * (int64_t)nbw * GemmCfg<WT>::BB;
+    dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + BM - 1) / BM));
+    GroupArgs ga = {};
+    gemm_kernel<WT, BM, false><<<grid, 256, 0, st>>>(W, (int)N, (int)K, wbytes, (const int8_t*)aqs, ad,
+                                                     (const int16_t*)aux, (int)M, Y, ldy, ga);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm(int wtype, const uint8_t* W, int64_t N, int64_t K, const void* act_qs,
+                       const void* act_d, const void* act_aux, int64_t M, float* Y, int64_t ldy,
+                       hipStream_t st) {
+    if (M == 0 || N == 0) return hipSuccess;
+    if (wtype == 0) return launch_gemm_t<0>(W, N, K, act_qs, act_d, act_aux, M, Y, ldy, st);
+    if (wtype == 1) return launch_gemm_t<1>(W, N, K, act_qs, act_d, act_aux, M, Y, ldy, st);
+    return launch_gemm_t<2>(W, N, K, act_qs, act_d, act_aux, M, Y, ldy, st);
+}
+
+// Grouped launch: one 64 x 64 tile per (weight-row block, routed tile).
+constexpr int kGroupBM = kGroupTileRows;
+
+hipError_t launch_gemm_grouped(const uint8_t* W, int64_t E, int64_t N, int64_t K, ActQ8K act,
+                               int64_t T, int64_t top_k, RouteWs ws, float* Y, hipStream_t st) {
+    const int nbw = (int)(K / kQK);
+    const int64_t estride = N * (int64_t)nbw * kQ4KBytes;
+    const int64_t max_tiles = (T * top_k + kGroupBM - 1) / kGroupBM + E;
+    if (max_tiles == 0) return hipSuccess;
+    dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)max_tiles);
+    GroupArgs ga;
+    ga.tiles = ws.tiles;
+    ga.ntiles = ws.ntiles;
+    ga.list = ws.list;
+    ga.top_k = (int)top_k;
+    ga.expert_stride = estride;
+    gemm_kernel<0, kGroupBM, true><<<grid, 256, 0, st>>>(W, (int)N, (int)K, E * estride, act.qs, act.d,
+                                                         act.bsums, (int)T, Y, N * 1, ga);
+    return hipGetLastError();
+}
+
+}  // namespace vqk

@@ -1,0 +1,63 @@
+// vq_internal.h -- launchers between the host API (vq_api.hip) and the kernel
+// files.  Every launcher assumes the host has already validated its
+// arguments (types, shapes, alignment, aliasing) and returns the
+// hipGetLastError() of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace vqk {
+
+// Rows of one routed-expert GEMM tile; the routing scan writes its tile table
+// in these units and the grouped GEMM consumes it.
+constexpr int kGroupTileRows = 64;
+
+// Planar activation buffers (include/vq.h).
+struct ActQ8K {
+    int8_t* qs;      // [M][K]
+    float* d;        // [M][K/256]
+    int16_t* bsums;  // [M][K/16]
+};
+struct ActQ81 {
+    int8_t* qs;      // [M][K]
+    uint16_t* d;     // [M][K/32] binary16
+    uint16_t* s;     // [M][K/32] binary16
+};
+
+hipError_t launch_quantize_q8k(const float* X, int64_t M, int64_t K, int64_t ldx, ActQ8K out,
+                               hipStream_t st);
+hipError_t launch_quantize_q8_1(const float* X, int64_t M, int64_t K, int64_t ldx, ActQ81 out,
+                                hipStream_t st);
+hipError_t launch_quantize_weights(int wtype, const float* W, int64_t N, int64_t K, uint8_t* out,
+                                   hipStream_t st);
+
+// Decode GEMV with the fused activation quantizer.  xq_out may be null.
+hipError_t launch_gemv(int wtype, const uint8_t* W, int64_t N, int64_t K, const float* x,
+                       float* y, uint8_t* xq_out, hipStream_t st);
+size_t gemv_lds_bytes(int wtype, int64_t N, int64_t K);
+
+// Prefill GEMM on pre-quantized activations.
+hipError_t launch_gemm(int wtype, const uint8_t* W, int64_t N, int64_t K, const void* act_qs,
+                       const void* act_d, const void* act_aux, int64_t M, float* Y, int64_t ldy,
+                       hipStream_t st);
+
+// Routed experts.
+struct RouteWs {
+    int32_t* counts;   // [E]
+    int32_t* offsets;  // [E+1]
+    int32_t* list;     // [T*top_k]
+    int32_t* chunk;    // [nchunks][E] per-chunk counts, then offsets
+    int32_t* tiles;    // tile table
+    int32_t* ntiles;   // [1]
+};
+size_t route_ws_layout(int64_t E, int64_t T, int64_t top_k, RouteWs* ws, uint8_t* base);
+hipError_t launch_route(const int32_t* ids, int64_t T, int64_t top_k, int64_t E, RouteWs ws,
+                        hipStream_t st);
+hipError_t launch_gemm_grouped(const uint8_t* W, int64_t E, int64_t N, int64_t K, ActQ8K act,
+                               int64_t T, int64_t top_k, RouteWs ws, float* Y, hipStream_t st);
+hipError_t launch_weighted_sum(const float* Y, const float* w, int64_t T, int64_t top_k, int64_t N,
+                               float* Ysum, hipStream_t st);
+
+}  // namespace vqk

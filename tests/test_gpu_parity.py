@@ -1,0 +1,352 @@
+"""GPU parity of the HIP path against the CPU oracle (needs an MI355X).
+
+Every call goes through the C ABI (libvq.so via the thin binding).  Bar:
+  * quantizer bytes, weight-encoder bytes, int32 sub-block sums (unit-scale
+    probes) and routing: bit-exact;
+  * GEMV, GEMM and grouped outputs: bit-identical to the oracle's fixed-order
+    binary32 definition (stronger than the NMSE <= 1e-6 gate, which is checked
+    too), and max relative error <= 5e-4 against the fp64 dequantized product;
+  * weighted expert sum: bit-identical to the oracle's sum of the GPU's Y.
+Sizes span several tiles with ragged tails; full workload sizes are checked on
+sampled outputs.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import ref_fp64
+import synth
+from tests import gpu_helpers as H
+from tests.conftest import gpu_available
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+import block_quantized_matmul_fp32_amd as vq  # noqa: E402
+
+NMSE_MAX = 1e-6
+REL_MAX = 5e-4
+
+WTYPES = [oracle.Q4_K, oracle.Q6_K, oracle.Q8_0]
+WNAME = {oracle.Q4_K: "Q4_K", oracle.Q6_K: "Q6_K", oracle.Q8_0: "Q8_0"}
+
+
+def oracle_act(wtype, X):
+    return oracle.quantize_q8_1(X) if wtype == oracle.Q8_0 else oracle.quantize_q8k(X)
+
+
+# ------------------------------------------------------------------ quantizers
+def special_rows_q8k():
+    rows = []
+    r = np.full(256, 0.0, np.float32); r[0] = -127; r[1:7] = [0.5, 1.5, 2.5, -0.5, -1.5, 3.5]; rows.append(r)
+    r = np.full(256, 1.0, np.float32); r[0] = 2.0; r[5] = -2.0; rows.append(r)
+    rows.append(np.zeros(256, np.float32))
+    rows.append(np.full(256, np.nan, np.float32))
+    r = np.full(256, 0.25, np.float32); r[3] = np.array([0x3EE48B35], np.uint32).view(np.float32)[0]; rows.append(r)
+    r = np.full(256, -3.0, np.float32); r[200] = 3.0; rows.append(r)  # ties at the end of the block
+    return np.concatenate(rows)
+
+
+def test_quantize_q8k_bitexact():
+    M, K = 37, 2048
+    X = synth.normal(1001, (M, K))
+    X[0, :1536] = special_rows_q8k()
+    X[1, 256:512] *= np.float32(1e-30)
+    X[2, :256] = np.float32(7.0)
+    for ldx, off in ((K, 0), (K + 4, 0), (K + 3, 1)):
+        H.say("quantize_q8k M=%d K=%d ldx=%d offset=%d" % (M, K, ldx, off))
+        Xp = np.zeros(M * ldx + off + 8, np.float32)
+        view = np.lib.stride_tricks.as_strided(Xp[off:], (M, K), (4 * ldx, 4))
+        view[:] = X
+        Xd = H.to_dev(Xp)
+        Xq = vq.quantize_act(vq.Q8_K, Xd[off:], M, K, ldx)
+        qs, d, bs = H.planes_q8k(H.host(Xq), M, K)
+        ref = oracle.quantize_q8k(X)
+        assert np.array_equal(qs, ref.qs)
+        assert np.array_equal(d.view(np.uint32), ref.d.view(np.uint32))
+        assert np.array_equal(bs, ref.bsums)
+
+
+def test_quantize_q8_1_bitexact():
+    M, K = 29, 2080
+    X = synth.normal(1002, (M, K))
+    X[0, :32] = 0.0
+    X[0, 32:64] = 0.0; X[0, 32] = 1.00048828125; X[0, 33] = X[0, 49] = 5.9604644775390625e-08
+    X[1, :32] = 0.0; X[1, 0] = 127.0; X[1, 1:7] = [0.5, 1.5, 2.5, -0.5, -1.5, -2.5]
+    X[2, 64:96] = np.nan
+    X[3] *= np.float32(2.0 ** -20)
+    for ldx, off in ((K, 0), (K + 1, 3)):
+        H.say("quantize_q8_1 M=%d K=%d ldx=%d offset=%d" % (M, K, ldx, off))
+        Xp = np.zeros(M * ldx + off + 8, np.float32)
+        view = np.lib.stride_tricks.as_strided(Xp[off:], (M, K), (4 * ldx, 4))
+        view[:] = X
+        Xq = vq.quantize_act(vq.Q8_1, H.to_dev(Xp)[off:], M, K, ldx)
+        qs, d, s = H.planes_q8_1(H.host(Xq), M, K)
+        ref = oracle.quantize_q8_1(X)
+        assert np.array_equal(qs, ref.qs)
+        assert np.array_equal(d, ref.d)
+        assert np.array_equal(s, ref.s)
+    assert s[0, 1] == 0x3C01  # butterfly-order case
+
+
+@pytest.mark.parametrize("wtype", WTYPES)
+def test_quantize_weights_bitexact(wtype):
+    N, K = 67, 1024
+    W = synth.normal(1003 + wtype, (N, K), 0.02)
+    W[0] = 0.0
+    W[1] = -0.01
+    W[2] = 0.03
+    W[3, :128] = 0.0
+    W[4, ::3] = 0.0
+    H.say("quantize_weights %s N=%d K=%d" % (WNAME[wtype], N, K))
+    got = H.host(vq.quantize_weights(wtype, H.to_dev(W)))
+    ref = oracle.quantize_weights(wtype, W).reshape(-1)
+    assert np.array_equal(got, ref)
+
+
+# ------------------------------------------------------------------ GEMV
+GEMV_SHAPES = {oracle.Q4_K: (300, 2560), oracle.Q6_K: (131, 1536), oracle.Q8_0: (300, 2080)}
+
+
+@pytest.mark.parametrize("wtype", WTYPES)
+def test_gemv_bitexact_and_fused_bytes(wtype):
+    N, K = GEMV_SHAPES[wtype]
+    W = synth.normal(1100 + wtype, (N, K), 0.02)
+    x = synth.normal(1110 + wtype, (K,))
+    Wq = oracle.quantize_weights(wtype, W)
+    act = oracle_act(wtype, x)
+    y_ref = oracle.gemm(wtype, Wq, N, K, act)[0]
+    H.say("gemv %s N=%d K=%d" % (WNAME[wtype], N, K))
+    xq = H.to_dev(np.zeros(vq.act_bytes(vq.act_for(wtype), 1, K), np.uint8))
+    y = H.to_dev(np.full(N, np.nan, np.float32))
+    vq.gemv(wtype, H.to_dev(Wq), N, K, H.to_dev(x), y=y, xq_out=xq)
+    H.assert_bitwise(H.host(y), y_ref, "gemv %s" % WNAME[wtype])
+    assert np.array_equal(H.host(xq), H.pack_act(act, wtype)), "fused quantizer bytes"
+    # the standalone quantizer writes the same bytes
+    sq = vq.quantize_act(vq.act_for(wtype), H.to_dev(np.ascontiguousarray(x)),
+                         Xq=H.to_dev(np.zeros(vq.act_bytes(vq.act_for(wtype), 1, K), np.uint8)))
+    assert np.array_equal(H.host(sq), H.host(xq))
+    r = ref_fp64.gemm_fp64(wtype, Wq, N, K, act)[0]
+    assert ref_fp64.nmse(H.host(y), r) <= NMSE_MAX
+    assert ref_fp64.max_rel_err(H.host(y), r)[0] <= REL_MAX
+
+
+@pytest.mark.parametrize("wtype", WTYPES)
+def test_gemv_edge_rows(wtype):
+    """N = 1, a single block per row, and N around the rows-per-workgroup split."""
+    qk = 32 if wtype == oracle.Q8_0 else 256
+    for N, K in ((1, qk), (257, qk), (513, 4 * qk)):
+        W = synth.normal((1200, N, K), (N, K), 0.02)
+        x = synth.normal((1201, K), (K,))
+        Wq = oracle.quantize_weights(wtype, W)
+        y_ref = oracle.gemm(wtype, Wq, N, K, oracle_act(wtype, x))[0]
+        H.say("gemv edge %s N=%d K=%d" % (WNAME[wtype], N, K))
+        y = vq.gemv(wtype, H.to_dev(Wq), N, K, H.to_dev(x))
+        H.assert_bitwise(H.host(y), y_ref, "gemv edge %s N=%d K=%d" % (WNAME[wtype], N, K))
+
+
+# ------------------------------------------------------------------ GEMM
+GEMM_SHAPES = {oracle.Q4_K: (150, 200, 1024), oracle.Q6_K: (150, 200, 1024), oracle.Q8_0: (150, 200, 2080)}
+
+
+@pytest.mark.parametrize("wtype", WTYPES)
+def test_gemm_bitexact(wtype):
+    M, N, K = GEMM_SHAPES[wtype]
+    W = synth.normal(1300 + wtype, (N, K), 0.02)
+    X = synth.normal(1310 + wtype, (M, K))
+    X[:, ::97] *= np.float32(20.0)
+    Wq = oracle.quantize_weights(wtype, W)
+    act = oracle_act(wtype, X)
+    Y_ref = oracle.gemm(wtype, Wq, N, K, act, nthreads=8)
+    H.say("gemm %s M=%d N=%d K=%d" % (WNAME[wtype], M, N, K))
+    ldy = N + 7
+    Yd = H.to_dev(np.full((M, ldy), np.nan, np.float32))
+    vq.gemm(wtype, H.to_dev(Wq), N, K, vq.act_for(wtype), H.to_dev(H.pack_act(act, wtype)), M, Y=Yd, ldy=ldy)
+    Yh = H.host(Yd)
+    H.assert_bitwise(Yh[:, :N], Y_ref, "gemm %s" % WNAME[wtype])
+    assert np.isnan(Yh[:, N:]).all(), "padding columns written"
+    r = ref_fp64.gemm_fp64(wtype, Wq, N, K, act)
+    assert ref_fp64.nmse(Yh[:, :N], r) <= NMSE_MAX
+    assert ref_fp64.max_rel_err(Yh[:, :N], r)[0] <= REL_MAX
+
+
+@pytest.mark.parametrize("wtype", WTYPES)
+def test_gemm_from_device_quantizer(wtype):
+    """GPU quantize_act feeding GPU GEMM, decode-through-prefill M values."""
+    N, K = 128, 512 if wtype != oracle.Q8_0 else 544
+    W = synth.normal(1400 + wtype, (N, K), 0.02)
+    Wq = oracle.quantize_weights(wtype, W)
+    Wd = H.to_dev(Wq)
+    for M in (1, 2, 7, 64, 129):
+        X = synth.normal((1401, M), (M, K))
+        H.say("gemm via device quantizer %s M=%d N=%d K=%d" % (WNAME[wtype], M, N, K))
+        Xq = vq.quantize_act(vq.act_for(wtype), H.to_dev(X))
+        Y = vq.gemm(wtype, Wd, N, K, vq.act_for(wtype), Xq, M)
+        H.assert_bitwise(H.host(Y), oracle.gemm(wtype, Wq, N, K, oracle_act(wtype, X)), "M=%d" % M)
+
+
+@pytest.mark.parametrize("wtype", WTYPES)
+def test_random_byte_blocks(wtype):
+    """Random block bytes (random scales, mins, quants incl. negative Q6_K scales),
+    binary16 d in [2^-10, 1]."""
+    rng = np.random.default_rng(1500 + wtype)
+    N, K, M = 96, 1024, 40
+    bb = oracle.BLOCK_BYTES[wtype]
+    nb = K // oracle.BLOCK_ELEMS[wtype]
+    Wq = rng.integers(0, 256, (N, nb, bb), dtype=np.uint8)
+    dv = (2.0 ** rng.uniform(-10, 0, (N, nb, 2))).astype(np.float16).view(np.uint8).reshape(N, nb, 4)
+    if wtype == oracle.Q4_K:
+        Wq[..., 0:4] = dv
+    elif wtype == oracle.Q6_K:
+        Wq[..., 208:210] = dv[..., 0:2]
+    else:
+        Wq[..., 0:2] = dv[..., 0:2]
+    Wq = Wq.reshape(N, -1)
+    X = synth.normal(1501 + wtype, (M, K))
+    act = oracle_act(wtype, X)
+    H.say("random bytes %s M=%d N=%d K=%d" % (WNAME[wtype], M, N, K))
+    Y = vq.gemm(wtype, H.to_dev(Wq), N, K, vq.act_for(wtype), H.to_dev(H.pack_act(act, wtype)), M)
+    H.assert_bitwise(H.host(Y), oracle.gemm(wtype, Wq, N, K, act), "gemm random bytes")
+    y = vq.gemv(wtype, H.to_dev(Wq), N, K, H.to_dev(X[0]))
+    H.assert_bitwise(H.host(y), oracle.gemm(wtype, Wq, N, K, oracle_act(wtype, X[:1]))[0], "gemv random bytes")
+
+
+def test_unit_scale_probes_exact_int32():
+    """d = 1, one sub-block scale 1, activations with iscale = 1: outputs are the
+    exact int32 sub-block sums (GEMV and GEMM)."""
+    a = ((np.arange(256) * 37) % 255 - 127).astype(np.float32)
+    rng = np.random.default_rng(1600)
+    q = rng.integers(0, 16, 256)
+    blocks = []
+    for j in range(8):
+        sc = np.zeros(8, np.int32); sc[j] = 1
+        blocks.append(oracle.q4k_build(0x3C00, 0, sc, np.zeros(8, np.int32), q))
+    Wq = np.stack(blocks)
+    want = np.array([sum(int(q[i]) * int(a[i]) for i in range(32 * j, 32 * j + 32)) for j in range(8)],
+                    np.float32)
+    H.say("unit-scale probes Q4_K")
+    y = vq.gemv(vq.Q4_K, H.to_dev(Wq), 8, 256, H.to_dev(a))
+    assert np.array_equal(H.host(y), want)
+    Xq = vq.quantize_act(vq.Q8_K, H.to_dev(np.stack([a] * 3)))
+    Y = vq.gemm(vq.Q4_K, H.to_dev(Wq), 8, 256, vq.Q8_K, Xq, 3)
+    assert np.array_equal(H.host(Y), np.stack([want] * 3))
+    q6 = rng.integers(0, 64, 256)
+    blocks = []
+    for j in range(16):
+        sc = np.zeros(16, np.int32); sc[j] = 1
+        blocks.append(oracle.q6k_build(0x3C00, sc, q6))
+    Wq = np.stack(blocks)
+    want = np.array([sum((int(q6[i]) - 32) * int(a[i]) for i in range(16 * j, 16 * j + 16)) for j in range(16)],
+                    np.float32)
+    H.say("unit-scale probes Q6_K")
+    y = vq.gemv(vq.Q6_K, H.to_dev(Wq), 16, 256, H.to_dev(a))
+    assert np.array_equal(H.host(y), want)
+    Y = vq.gemm(vq.Q6_K, H.to_dev(Wq), 16, 256, vq.Q8_K, Xq, 3)
+    assert np.array_equal(H.host(Y), np.stack([want] * 3))
+    # Q8_0: d = 1 weights, activations with amax 127 give d = 1
+    a32 = ((np.arange(64) * 29) % 255 - 127).astype(np.float32)
+    a32[0] = 127.0; a32[32] = -127.0
+    qw = rng.integers(-127, 128, (4, 64)).astype(np.int8)
+    Wq = np.zeros((4, 2, 34), np.uint8)
+    Wq[:, :, 0:2] = np.array([0x3C00], np.uint16).view(np.uint8)
+    Wq[:, :, 2:] = qw.reshape(4, 2, 32).view(np.uint8)
+    want = (qw.astype(np.int64) @ a32.astype(np.int64)).astype(np.float32)
+    H.say("unit-scale probes Q8_0")
+    y = vq.gemv(vq.Q8_0, H.to_dev(Wq.reshape(4, -1)), 4, 64, H.to_dev(a32))
+    assert np.array_equal(H.host(y), want)
+
+
+def test_determinism_and_witness():
+    N, K, M = 256, 2560, 130
+    W = synth.normal(1700, (N, K), 0.02)
+    Wq = H.to_dev(oracle.quantize_weights(oracle.Q4_K, W))
+    X = H.to_dev(synth.normal(1701, (M, K)))
+    vq.reset_stats()
+    H.say("determinism Q4_K")
+    Xq = vq.quantize_act(vq.Q8_K, X)
+    Y1 = H.host(vq.gemm(vq.Q4_K, Wq, N, K, vq.Q8_K, Xq, M))
+    Y2 = H.host(vq.gemm(vq.Q4_K, Wq, N, K, vq.Q8_K, Xq, M))
+    y1 = H.host(vq.gemv(vq.Q4_K, Wq, N, K, X[0]))
+    y2 = H.host(vq.gemv(vq.Q4_K, Wq, N, K, X[0]))
+    assert np.array_equal(Y1.view(np.uint32), Y2.view(np.uint32))
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+    st = vq.get_stats()
+    assert st["quantize_q8k"] == 1 and st["gemm_q4k"] == 2 and st["gemv_q4k"] == 2
+    assert st["gemm_q6k"] == 0 and st["gemv_q8_0"] == 0
+    # decode through prefill: the GEMM row 0 is the GEMV
+    H.assert_bitwise(y1, Y1[0], "gemv vs gemm row 0")
+
+
+# ------------------------------------------------------------------ grouped
+def run_grouped(E, N, K, T, top_k, ids, seed):
+    W = np.stack([synth.normal((seed, e), (N, K), 0.02) for e in range(E)])
+    Wq = np.stack([oracle.quantize_weights(oracle.Q4_K, W[e]) for e in range(E)]).reshape(E * N, -1)
+    X = synth.normal(seed + 1, (T, K))
+    logits = synth.normal(seed + 2, (T, top_k))
+    z = np.exp(logits - logits.max(1, keepdims=True))
+    rw = (z / z.sum(1, keepdims=True)).astype(np.float32)
+    act = oracle.quantize_q8k(X)
+    H.say("grouped E=%d N=%d K=%d T=%d top_k=%d" % (E, N, K, T, top_k))
+    Xq = vq.quantize_act(vq.Q8_K, H.to_dev(X))
+    Yd = H.to_dev(np.full((T, top_k, N), np.nan, np.float32))
+    Sd = H.to_dev(np.full((T, N), np.nan, np.float32))
+    Y, Ysum, ws = vq.gemm_grouped(vq.Q4_K, H.to_dev(Wq), E, N, K, vq.Q8_K, Xq, T, H.to_dev(ids), top_k,
+                                  route_w=H.to_dev(rw), Y=Yd, Ysum=Sd)
+    return Wq, act, rw, Y, Ysum, ws
+
+
+@pytest.mark.parametrize("case", ["uniform", "skewed"])
+def test_grouped_small(case):
+    E, N, K, top_k = 16, 80, 512, 4
+    if case == "uniform":
+        T = 50
+        ids = synth.random_ids(1800, T, E, top_k)
+    else:
+        # expert 0 empty, expert 1 in every token (rows > one tile), expert 2 once
+        T = 90
+        hint = np.ones(E); hint[0] = 0; hint[1] = 1e6; hint[2] = 0
+        ids = synth.skewed_ids(1801, T, E, top_k, hint)
+        ids[5, 3] = 2 if 2 not in ids[5] else ids[5, 3]
+    Wq, act, rw, Y, Ysum, ws = run_grouped(E, N, K, T, top_k, ids, 1810)
+    counts, offsets, lst = vq.grouped_ws_views(ws, E, T, top_k)
+    c_ref, o_ref, l_ref = oracle.route(ids, E)
+    assert np.array_equal(H.host(counts), c_ref)
+    assert np.array_equal(H.host(offsets), o_ref)
+    assert np.array_equal(H.host(lst), l_ref)
+    Y_ref = oracle.gemm_grouped(oracle.Q4_K, Wq, E, N, K, act, ids, nthreads=8)
+    Yh = H.host(Y)
+    H.assert_bitwise(Yh, Y_ref, "grouped Y")
+    H.assert_bitwise(H.host(Ysum), oracle.weighted_sum(Yh, rw), "weighted sum of the GPU's Y")
+    # each slot equals a dense GEMM of its expert
+    e = int(ids[0, 0])
+    dense = oracle.gemm(oracle.Q4_K, Wq[e * N:(e + 1) * N], N, K, act)
+    H.assert_bitwise(Yh[0, 0], dense[0], "slot vs dense")
+    # swapped ids must change the output
+    ids2 = ids.copy(); ids2[:, [0, 1]] = ids2[:, [1, 0]]
+    _, _, _, Y2, _, _ = run_grouped(E, N, K, T, top_k, ids2, 1810)
+    assert not np.array_equal(H.host(Y2), Yh)
+
+
+def test_grouped_expert_permutation():
+    """Permuting expert storage and remapping ids gives the same Y bitwise."""
+    E, N, K, T, top_k = 12, 64, 256, 40, 3
+    ids = synth.random_ids(1900, T, E, top_k)
+    Wq, act, rw, Y, Ysum, ws = run_grouped(E, N, K, T, top_k, ids, 1910)
+    perm = np.random.default_rng(1).permutation(E)
+    inv = np.argsort(perm)
+    Wp = Wq.reshape(E, N, -1)[perm].reshape(E * N, -1)
+    ids_p = inv[ids].astype(np.int32)
+    H.say("grouped permuted experts")
+    Xq = vq.quantize_act(vq.Q8_K, H.to_dev(synth.normal(1911, (T, K))))
+    Y2, _, _ = vq.gemm_grouped(vq.Q4_K, H.to_dev(Wp), E, N, K, vq.Q8_K, Xq, T, H.to_dev(ids_p), top_k,
+                               route_w=H.to_dev(rw))
+    H.assert_bitwise(H.host(Y2), H.host(Y), "permuted experts")
+
+
+def test_weighted_sum_standalone():
+    T, top_k, N = 33, 8, 512
+    Y = synth.normal(2000, (T, top_k, N))
+    w = synth.normal(2001, (T, top_k))
+    H.say("weighted sum T=%d top_k=%d N=%d" % (T, top_k, N))
+    S = vq.weighted_sum(H.to_dev(Y), H.to_dev(w), T, top_k, N)
+    H.assert_bitwise(H.host(S), oracle.weighted_sum(Y, w), "weighted sum")
