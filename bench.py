@@ -1,0 +1,383 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-quantized matmul hot path on one MI355X.
+
+Headline workload (one "step"): the batch-1 decode GEMVs of a Qwen-4B-like
+MLP -- Q4_K weights [9728, 2560] and Q6_K weights [2560, 9728], each with its
+fp32 activation quantized to Q8_K inside the GEMV (fused quantizer), seeded
+synthetic data.  value = algorithmic bytes of the step (compressed weights,
+fp32 x and y) / time, in GB/s, with the weights rotated through more buffer
+sets than the 256 MB Infinity Cache holds, so every step streams from HBM.
+
+The same line carries:
+  roofline     -- the dominant kernel (the Q6_K GEMV) against 8 TB/s HBM, its
+                  average launch duration from HIP events recorded around
+                  each of its launches in the timed region;
+  cpu_baseline -- the CPU oracle running the same decode step on the host's
+                  cores (a bounded number of repetitions);
+  prefill / q8_0 / grouped / quantizer -- the prefill GEMM (int8 TOPS), the
+                  Q8_0 x Q8_1 GEMM and GEMV, the routed-expert grouped GEMM with
+                  the weighted expert sum, and the standalone quantizer, timed
+                  with HIP events in the same run (secondary numbers).
+
+Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 20]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode GEMV GB/s + prefill GEMM int8 TOPS (% of MI355X roofline)"
+HBM_PEAK_GBS = 8000.0
+INT8_PEAK_TOPS = 5000.0
+MALL_BYTES = 256 << 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_sha(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+GEMV_SOURCES = ["block_quantized_matmul_fp32_amd/csrc/gemv.hip",
+                "block_quantized_matmul_fp32_amd/csrc/vq_device.h"]
+
+
+def traffic_from_profiles(kernel_key: str, sha: str, launches_bytes: float):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, or None if
+    the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = data.get(kernel_key)
+    if not ent or ent.get("source_sha") != sha:
+        return None
+    return ent.get("traffic_bytes_per_launch")
+
+
+def event_pair():
+    import torch
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def time_launches(fn, iters, warmup=3):
+    """Average per-launch duration (ms) from events around each launch."""
+    import torch
+    for _ in range(warmup):
+        fn(0)
+    torch.cuda.synchronize()
+    pairs = [event_pair() for _ in range(iters)]
+    for i in range(iters):
+        pairs[i][0].record()
+        fn(i)
+        pairs[i][1].record()
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in pairs) / iters
+
+
+def run_cpu_baseline(seconds: float):
+    """The CPU oracle on the same decode step (both GEMVs and their Q8_K
+    quantization), repeated until about `seconds` of work; GB/s on the same
+    algorithmic byte count as the GPU step."""
+    import numpy as np
+    import oracle
+    import synth
+    threads = min(16, len(os.sched_getaffinity(0)))
+    Wa = synth.tensor("decode_gemv", "Wa")
+    Wb = synth.tensor("decode_gemv", "Wb")
+    xa = synth.tensor("decode_gemv", "xa")
+    xb = synth.tensor("decode_gemv", "xb")
+    Qa = oracle.quantize_weights(oracle.Q4_K, Wa)
+    Qb = oracle.quantize_weights(oracle.Q6_K, Wb)
+    del Wa, Wb
+    step_bytes = decode_step_bytes()
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.gemm(oracle.Q4_K, Qa, 9728, 2560, oracle.quantize_q8k(xa), nthreads=threads)
+        oracle.gemm(oracle.Q6_K, Qb, 2560, 9728, oracle.quantize_q8k(xb), nthreads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 100000:
+            break
+    return {"value": round(step_bytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d repetitions of the full decode step (Q8_K quantization of x plus the Q4_K "
+                      "[9728,2560] and Q6_K [2560,9728] GEMVs) in %.1f s with %d threads" % (reps, el, threads),
+            "ms_per_step": round(1e3 * el / reps, 3)}
+
+
+def decode_step_bytes():
+    qa = 9728 * (2560 // 256) * 144
+    qb = 2560 * (9728 // 256) * 210
+    return qa + 4 * 2560 + 4 * 9728 + qb + 4 * 9728 + 4 * 2560
+
+
+def run_decode(args, torch, vq, synth):
+    dev = torch.device("cuda:0")
+    Wa = torch.from_numpy(synth.tensor("decode_gemv", "Wa")).to(dev)
+    Wb = torch.from_numpy(synth.tensor("decode_gemv", "Wb")).to(dev)
+    Qa0 = vq.quantize_weights(vq.Q4_K, Wa)
+    Qb0 = vq.quantize_weights(vq.Q6_K, Wb)
+    del Wa, Wb
+    xa = torch.from_numpy(synth.tensor("decode_gemv", "xa")).to(dev)
+    xb = torch.from_numpy(synth.tensor("decode_gemv", "xb")).to(dev)
+    set_bytes = Qa0.numel() + Qb0.numel()
+    R = max(2, math.ceil(args.rotate_mb * (1 << 20) / set_bytes))
+    Qa = [Qa0] + [Qa0.clone() for _ in range(R - 1)]
+    Qb = [Qb0] + [Qb0.clone() for _ in range(R - 1)]
+    ya = [torch.empty(9728, dtype=torch.float32, device=dev) for _ in range(R)]
+    yb = [torch.empty(2560, dtype=torch.float32, device=dev) for _ in range(R)]
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step(i):
+        s = i % R
+        vq.gemv(vq.Q4_K, Qa[s], 9728, 2560, xa, y=ya[s], stream=torch.cuda.current_stream().cuda_stream)
+        vq.gemv(vq.Q6_K, Qb[s], 2560, 9728, xb, y=yb[s], stream=torch.cuda.current_stream().cuda_stream)
+
+    # Eager warm-up (also sets the kernels' LDS attribute before any capture).
+    for i in range(max(args.warmup, 2)):
+        step(i)
+    torch.cuda.synchronize()
+
+    # The decode step is launch-bound from Python (a HIP launch costs several
+    # microseconds of host time, more than these kernels run), so the timed
+    # steps replay a HIP graph holding one step per rotation set.
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            for i in range(R):
+                step(i)
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    reps = max(1, math.ceil(args.steps / R))
+    for _ in range(max(1, args.warmup // R)):
+        g.replay()
+    torch.cuda.synchronize()
+    t0, t1 = event_pair()
+    t0.record()
+    for _ in range(reps):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / (reps * R)
+    steps_timed = reps * R
+
+    # Per-kernel launch durations: HIP events around each launch of one
+    # kernel, launched back to back on the current stream (rotated weights).
+    def one(wt, i):
+        s = i % R
+        if wt == vq.Q4_K:
+            vq.gemv(vq.Q4_K, Qa[s], 9728, 2560, xa, y=ya[s])
+        else:
+            vq.gemv(vq.Q6_K, Qb[s], 2560, 9728, xb, y=yb[s])
+
+    ka = time_launches(lambda i: one(vq.Q4_K, i), args.steps)
+    kb = time_launches(lambda i: one(vq.Q6_K, i), args.steps)
+    assert torch.isfinite(ya[0]).all() and torch.isfinite(yb[0]).all()
+    return {"ms_per_step": ms, "q4k_ms": ka, "q6k_ms": kb, "rotation_sets": R, "steps_timed": steps_timed,
+            "rotation_mb": round(R * set_bytes / (1 << 20), 1)}
+
+
+def run_prefill(torch, vq, synth, iters):
+    dev = torch.device("cuda:0")
+    out = {}
+    Wg = torch.from_numpy(synth.tensor("prefill_gemm", "Wgate")).to(dev)
+    Wd = torch.from_numpy(synth.tensor("prefill_gemm", "Wdown")).to(dev)
+    Qg = vq.quantize_weights(vq.Q4_K, Wg)
+    Qd = vq.quantize_weights(vq.Q6_K, Wd)
+    del Wg, Wd
+    for M in (512, 2048):
+        Xh = torch.from_numpy(synth.prefill_activations("Xh", M)).to(dev)
+        Xi = torch.from_numpy(synth.prefill_activations("Xi", M)).to(dev)
+        qh = vq.quantize_act(vq.Q8_K, Xh)
+        qi = vq.quantize_act(vq.Q8_K, Xi)
+        Yg = torch.empty((M, 9728), dtype=torch.float32, device=dev)
+        Yd = torch.empty((M, 2560), dtype=torch.float32, device=dev)
+        tg = time_launches(lambda i: vq.gemm(vq.Q4_K, Qg, 9728, 2560, vq.Q8_K, qh, M, Y=Yg), iters)
+        td = time_launches(lambda i: vq.gemm(vq.Q6_K, Qd, 2560, 9728, vq.Q8_K, qi, M, Y=Yd), iters)
+        tq = time_launches(lambda i: vq.quantize_act(vq.Q8_K, Xh, Xq=qh), iters)
+        ops = 2.0 * M * 9728 * 2560
+        out["M%d" % M] = {
+            "q4k_gate_us": round(tg * 1e3, 2), "q4k_tops": round(ops / (tg * 1e-3) / 1e12, 1),
+            "q4k_frac": round(ops / (tg * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
+            "q6k_down_us": round(td * 1e3, 2), "q6k_tops": round(ops / (td * 1e-3) / 1e12, 1),
+            "q6k_frac": round(ops / (td * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
+            "quantize_q8k_us": round(tq * 1e3, 2),
+            "quantize_q8k_gbs": round(M * 2560 * (4 + 1 + 4 / 256 + 2 / 16) / (tq * 1e-3) / 1e9, 1),
+        }
+    return out
+
+
+def run_q8_0(torch, vq, synth, iters):
+    dev = torch.device("cuda:0")
+    W = torch.from_numpy(synth.tensor("q8_0_gemm", "W")).to(dev)
+    Q = vq.quantize_weights(vq.Q8_0, W)
+    del W
+    X = torch.from_numpy(synth.tensor("q8_0_gemm", "X")).to(dev)
+    Xq = vq.quantize_act(vq.Q8_1, X)
+    Y = torch.empty((2048, 4096), dtype=torch.float32, device=dev)
+    t = time_launches(lambda i: vq.gemm(vq.Q8_0, Q, 4096, 2048, vq.Q8_1, Xq, 2048, Y=Y), iters)
+    R = max(2, math.ceil(640 * (1 << 20) / Q.numel()))
+    Qs = [Q] + [Q.clone() for _ in range(R - 1)]
+    y = torch.empty(4096, dtype=torch.float32, device=dev)
+    tv = time_launches(lambda i: vq.gemv(vq.Q8_0, Qs[i % R], 4096, 2048, X[0], y=y), 200)
+    ops = 2.0 * 2048 * 4096 * 2048
+    gbytes = Q.numel() + 4 * 2048 + 4 * 4096
+    return {"gemm_M2048_us": round(t * 1e3, 2), "gemm_tops": round(ops / (t * 1e-3) / 1e12, 1),
+            "gemm_frac": round(ops / (t * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
+            "gemv_us": round(tv * 1e3, 2), "gemv_gbs": round(gbytes / (tv * 1e-3) / 1e9, 1),
+            "gemv_frac": round(gbytes / (tv * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def run_grouped(torch, vq, synth, iters):
+    dev = torch.device("cuda:0")
+    cfg = synth.WORKLOADS["grouped_moe"]
+    E, N, K, T, top_k = cfg["E"], cfg["N"], cfg["K"], cfg["T"], cfg["top_k"]
+    ebytes = vq.weight_bytes(vq.Q4_K, N, K)
+    Q0 = torch.empty(E * ebytes, dtype=torch.uint8, device=dev)
+    for e in range(E):
+        We = torch.from_numpy(synth.expert_weights(e, N, K)).to(dev)
+        vq.quantize_weights(vq.Q4_K, We, Wq=Q0[e * ebytes:(e + 1) * ebytes])
+    torch.cuda.synchronize()
+    X = torch.from_numpy(synth.tensor("grouped_moe", "X")).to(dev)
+    ids_np, w_np = synth.routing(T, E, top_k)
+    ids = torch.from_numpy(ids_np).to(dev)
+    rw = torch.from_numpy(w_np).to(dev)
+    Xq = vq.quantize_act(vq.Q8_K, X)
+    Y = torch.empty((T, top_k, N), dtype=torch.float32, device=dev)
+    S = torch.empty((T, N), dtype=torch.float32, device=dev)
+    ws = torch.empty(vq.grouped_workspace_bytes(E, T, top_k), dtype=torch.uint8, device=dev)
+    R = max(2, math.ceil(640 * (1 << 20) / Q0.numel()))
+    Qs = [Q0] + [Q0.clone() for _ in range(R - 1)]
+
+    def call(i, sets):
+        vq.gemm_grouped(vq.Q4_K, sets[i % len(sets)], E, N, K, vq.Q8_K, Xq, T, ids, top_k, route_w=rw,
+                        Y=Y, Ysum=S, ws=ws)
+
+    t_cold = time_launches(lambda i: call(i, Qs), iters)
+    t_warm = time_launches(lambda i: call(i, [Q0]), iters)
+    ops = 2.0 * T * top_k * N * K
+    alg = Q0.numel() + Xq.numel() + Y.numel() * 4 + S.numel() * 4 + T * top_k * 8
+    return {"route_gemm_sum_us_cold": round(t_cold * 1e3, 2),
+            "tops_cold": round(ops / (t_cold * 1e-3) / 1e12, 1),
+            "mfma_frac_cold": round(ops / (t_cold * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
+            "hbm_frac_cold": round(alg / (t_cold * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "route_gemm_sum_us_warm": round(t_warm * 1e3, 2),
+            "tops_warm": round(ops / (t_warm * 1e-3) / 1e12, 1),
+            "mfma_frac_warm": round(ops / (t_warm * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
+            "rotation_sets_cold": R, "algorithmic_bytes": int(alg)}
+
+
+def calibrate_copy(torch, nbytes):
+    """A plain device copy of known size, for scaling rocprofv3 FETCH_SIZE and
+    WRITE_SIZE (run under rocprofv3 --pmc)."""
+    dev = torch.device("cuda:0")
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "launches": 5}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--rotate-mb", type=int, default=640,
+                    help="total size of the rotated weight sets (> the 256 MB Infinity Cache)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--secondary-iters", type=int, default=20)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes (rocprofv3 counter scaling)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path; run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X (no GPU visible)", file=sys.stderr)
+        sys.exit(1)
+    if args.calibrate_copy:
+        calibrate_copy(torch, args.calibrate_copy)
+        return
+
+    import block_quantized_matmul_fp32_amd as vq
+    import synth
+    vq.lib()  # fails loudly if the HIP library is missing
+
+    log("[bench] decode step: warmup %d, steps %d" % (args.warmup, args.steps))
+    dec = run_decode(args, torch, vq, synth)
+    step_bytes = decode_step_bytes()
+    value = step_bytes / (dec["ms_per_step"] * 1e-3) / 1e9
+    b6 = 2560 * (9728 // 256) * 210 + 4 * 9728 + 4 * 2560
+    ach6 = b6 / (dec["q6k_ms"] * 1e-3) / 1e9
+    b4 = 9728 * (2560 // 256) * 144 + 4 * 2560 + 4 * 9728
+    ach4 = b4 / (dec["q4k_ms"] * 1e-3) / 1e9
+    sha = source_sha(GEMV_SOURCES)
+    roofline = {"bound": "hbm", "kernel": "gemv_kernel<1> (Q6_K [2560,9728] x fused Q8_K)",
+                "achieved": round(ach6, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach6 / HBM_PEAK_GBS, 4),
+                "traffic": traffic_from_profiles("gemv_q6k_decode", sha, b6),
+                "algorithmic_bytes_per_launch": b6,
+                "avg_launch_us": round(dec["q6k_ms"] * 1e3, 3),
+                "source_sha": sha}
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": dec["steps_timed"], "warmup": args.warmup, "ms_per_step": round(dec["ms_per_step"], 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "decode GEMV, M=1: Q4_K [9728,2560] + Q6_K [2560,9728], "
+                               "Q8_K activation quantizer fused, seeded N(0,1) x and N(0,0.02) weights",
+                   "global_batch": 1, "parallelism": "none (1 GPU)",
+                   "launch": "timed steps replay a HIP graph (one step per rotation set)",
+                   "rotation_sets": dec["rotation_sets"], "rotation_mb": dec["rotation_mb"],
+                   "bytes_per_step": step_bytes},
+        "roofline": roofline,
+        "decode_kernels": {"q4k_us": round(dec["q4k_ms"] * 1e3, 3), "q4k_gbs": round(ach4, 1),
+                           "q4k_frac": round(ach4 / HBM_PEAK_GBS, 4),
+                           "q6k_us": round(dec["q6k_ms"] * 1e3, 3), "q6k_gbs": round(ach6, 1),
+                           "q6k_frac": round(ach6 / HBM_PEAK_GBS, 4)},
+    }
+    if not args.no_secondary:
+        log("[bench] prefill GEMM")
+        line["prefill"] = run_prefill(torch, vq, synth, args.secondary_iters)
+        log("[bench] Q8_0 GEMM and GEMV")
+        line["q8_0"] = run_q8_0(torch, vq, synth, args.secondary_iters)
+        log("[bench] grouped MUL_MAT_ID")
+        line["grouped"] = run_grouped(torch, vq, synth, max(5, args.secondary_iters // 2))
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline (%.0f s)" % args.cpu_seconds)
+        line["cpu_baseline"] = run_cpu_baseline(args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -47,9 +47,8 @@ constexpr int kLD = 272;  // LDS row stride of the int8 tiles (256 + 16 against 
 // 16 bytes from a 2-byte aligned global address using 4-byte aligned loads;
 // never reads at or beyond `end`.
 __device__ __forceinline__ void gload16_a2(const uint8_t* p, const uint8_t* end, uint32_t out[4]) {
-    const uintptr_t a = (uintptr_t)p;
-    const uint32_t* q = (const uint32_t*)(a & ~(uintptr_t)3);
-    const uint32_t sh = (uint32_t)(a & 3);
+    const uint32_t sh = (uint32_t)((uintptr_t)p & 3);
+    const uint32_t* q = (const uint32_t*)(p - sh);
     uint32_t w0 = q[0], w1 = q[1], w2 = q[2], w3 = q[3];
     if (sh == 0) {
         out[0] = w0; out[1] = w1; out[2] = w2; out[3] = w3;

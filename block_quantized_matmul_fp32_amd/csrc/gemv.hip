@@ -5,23 +5,30 @@
 // GEMV folds the activation quantizer into its prologue, bit-exact against
 // the CPU oracle); strix-llama.cpp PR #18, commit "mul_mat_vec_q_fq" (a
 // block quantizes the activation once into shared memory, with weight loads
-// issued before the quantization and its barrier) and commit "batch-one MMVQ
-// on one wave" (a fixed fp32 reduction order keeps decode deterministic).
+// issued before the quantization and its barrier), commit "warp reduce via
+// DPP" (lane exchange without LDS round trips) and commit "batch-one MMVQ on
+// one wave" (a fixed fp32 reduction order keeps decode deterministic).
 //
-// MI355X design.  The GEMV is HBM-bound: ~14-20 MB of weights, 1.8-2.6 us at
-// 8 TB/s, i.e. about one DRAM round trip's worth of bytes per CU.  So:
-//  * one 1024-thread workgroup per CU owns a contiguous run of rows; its
-//    weight bytes form one contiguous slab that is fetched with aligned
-//    16-byte loads, every load of the workgroup issued before anything is
-//    consumed (all bytes in flight at once);
-//  * while those loads are in flight the 16 waves quantize x into LDS with the
-//    shared quantizer body (one wave per Q8_K super-block);
-//  * the slab is parked in LDS (Q6_K and Q8_0 blocks are only 2-byte aligned;
-//    LDS reads at that alignment are rebuilt with v_alignbyte);
-//  * eight lanes own one (row, super-block): exact int32 sub-block sums with
-//    v_dot4_i32_i8, an exact int reduction over the eight lanes, then the
-//    block's binary32 combine; blocks of a row are summed in ascending order,
-//    so y is bit-identical to the fixed-order definition.
+// MI355X design.  The GEMV streams 9-20 MB of weights: a few microseconds of
+// HBM time, so everything else has to hide under the loads.
+//  * One 1024-thread workgroup per CU owns a contiguous run of rows.  Its
+//    (row, block) tasks are split into 16 contiguous ranges, one per wave; a
+//    wave's bytes are one contiguous span, fetched with aligned 16-byte
+//    loads into registers.
+//  * Order of issue: first the few x loads (L2 hits), then every weight load
+//    of the wave, so the quantizer only waits for x while the weights stream.
+//  * The 16 waves quantize x into LDS with the shared quantizer body (DPP
+//    reductions); one barrier publishes it.
+//  * Each wave then parks its own weight span in a private LDS region (the
+//    Q6_K / Q8_0 blocks are only 2-byte aligned; LDS reads at that alignment
+//    are rebuilt with v_alignbyte) and computes as soon as its own bytes are
+//    in: no workgroup barrier between a wave's loads and its compute.
+//  * Eight lanes own one (row, super-block) -- one lane per Q8_0 block: exact
+//    int32 sub-block sums with v_dot4_i32_i8, an exact DPP reduction over the
+//    eight lanes, then the block's binary32 combine into an LDS partial.
+//  * After one more barrier, one lane per row adds the row's partials in
+//    ascending block order from 0, so y is bit-identical to the fixed-order
+//    definition.
 #include "vq_device.h"
 #include "vq_internal.h"
 
@@ -33,8 +40,14 @@
 namespace vqk {
 
 constexpr int kGemvThreads = 1024;
-constexpr int kGemvChunks = 8;  // 16-byte chunks per thread: slab <= 128 KiB
+constexpr int kGemvWaves = kGemvThreads / 64;
+constexpr int kLMax = 8;            // 16-byte chunks per lane: a wave span <= 8 KiB
+constexpr int kXPre = 4;            // x rounds loaded before the weights
+constexpr int kStepLoads = kLMax;   // loads parked before computing (one step: measured fastest)
 constexpr size_t kMaxLds = 160 * 1024;
+// LDS bytes per quantized super-block of x: 256 + 16, so the 16 tasks of a
+// wave round (consecutive super-blocks) start on 16 different bank groups.
+constexpr int kActStride = kQK + 16;
 
 template <int WT>
 struct WFmt;
@@ -46,33 +59,70 @@ template <>
 struct WFmt<2> { static constexpr int kBlk = kQ80Bytes; static constexpr int kVals = kQK8; };
 
 struct GemvLayout {
-    int act_qs, act_d, act_bs, partial, slab, total;
+    int act_qs, act_d, act_bs, partial, regions, region_bytes, total;
 };
 
 __host__ __device__ inline int align16i(int x) { return (x + 15) & ~15; }
 
 // LDS layout of the GEMV workgroup; identical on host and device.
-__host__ __device__ inline GemvLayout gemv_layout(int wt, int K, int rows, int rb) {
+__host__ __device__ inline GemvLayout gemv_layout(int wt, int K, int rows, int region_bytes) {
     GemvLayout L;
     const int nbw = (wt == 2) ? K / kQK8 : K / kQK;
     L.act_qs = 0;
-    L.act_d = align16i(K);
-    const int nd = (wt == 2) ? K / kQK8 : K / kQK;
-    L.act_bs = L.act_d + align16i(nd * 4);
-    const int nbs = (wt == 2) ? 0 : K / 16;
-    L.partial = L.act_bs + align16i(nbs * 2);
-    L.slab = L.partial + align16i(rows * nbw * 4);
-    L.total = L.slab + rows * rb + 48;
+    L.act_d = (wt == 2) ? align16i(K) : (K / kQK) * kActStride;
+    L.act_bs = L.act_d + align16i(nbw * 4);
+    const int nbs_bytes = (wt == 2) ? (K / kQK8) * 4 : (K / 16) * 2;
+    L.partial = L.act_bs + align16i(nbs_bytes);
+    L.regions = L.partial + align16i(rows * nbw * 4);
+    L.region_bytes = region_bytes;
+    L.total = L.regions + kGemvWaves * region_bytes;
     return L;
+}
+
+// Byte span (relative to the workgroup's first row) of tasks [t0, t1).
+__host__ __device__ inline void task_span(int t0, int t1, int nb, int rb, int bb, int* b0, int* b1) {
+    if (t1 <= t0) { *b0 = 0; *b1 = 0; return; }
+    const int r0 = t0 / nb, k0 = t0 - r0 * nb;
+    const int r1 = (t1 - 1) / nb, k1 = (t1 - 1) - r1 * nb;
+    *b0 = r0 * rb + k0 * bb;
+    *b1 = r1 * rb + (k1 + 1) * bb;
+}
+
+// Barrier for LDS data only: wait for this wave's LDS operations, then
+// s_barrier (no wait on outstanding global loads, unlike __syncthreads).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+}
+
+// 32 bytes at a 2-byte aligned LDS address (9 aligned dword reads).
+__device__ __forceinline__ void lds_read32_a2(const uint8_t* p, uint32_t out[8]) {
+    const uint32_t sh = (uint32_t)((uintptr_t)p & 3);
+    const uint32_t* q = (const uint32_t*)(p - sh);
+    uint32_t w[9];
+#pragma unroll
+    for (int i = 0; i < 9; ++i) w[i] = q[i];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out[i] = __builtin_amdgcn_alignbyte(w[i + 1], w[i], sh);
+}
+
+// Number of whole tasks (row-major (row, block) order) inside the first E
+// bytes of the workgroup's rows.
+__device__ __forceinline__ int tasks_within(int E, int nb, int rb, int bb) {
+    const int r = E / rb;
+    const int k = (E - r * rb) / bb;
+    return r * nb + (k < nb ? k : nb);
 }
 
 template <int WT>
 __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
     const uint8_t* __restrict__ W, int N, int K, int64_t wbytes, const float* __restrict__ x,
-    float* __restrict__ y, uint8_t* __restrict__ xq_out, int rows_per_wg, int x_vec) {
+    float* __restrict__ y, uint8_t* __restrict__ xq_out, int rows_per_wg, int region_bytes, int x_vec) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     constexpr int BB = WFmt<WT>::kBlk;
     constexpr int QV = WFmt<WT>::kVals;
+    constexpr int LPT = (WT == 2) ? 1 : 2;    // lanes per task
+    constexpr int GPW = 64 / LPT;             // tasks per wave round
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -80,213 +130,294 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
     const int rb = nb * BB;
     const int n0 = blockIdx.x * rows_per_wg;
     const int rows = min(rows_per_wg, N - n0);
-    const GemvLayout L = gemv_layout(WT, K, rows_per_wg, rb);
-
-    // 1. Issue every weight load of this workgroup (aligned 16-byte chunks of
-    //    the contiguous row slab; the buffer's last partial chunk bytewise).
-    const int64_t s0 = (int64_t)n0 * rb, s1 = (int64_t)(n0 + rows) * rb;
-    const int64_t c0 = s0 >> 4, c1 = (s1 + 15) >> 4;
-    const int64_t full = wbytes >> 4;
-    uint4 buf[kGemvChunks];
-#pragma unroll
-    for (int i = 0; i < kGemvChunks; ++i) {
-        const int64_t c = c0 + tid + (int64_t)i * kGemvThreads;
-        buf[i] = make_uint4(0, 0, 0, 0);
-        if (c < c1) {
-            if (c < full) {
-                buf[i] = *(const uint4*)(W + 16 * c);
-            } else {
-                uint32_t wv[4] = {0, 0, 0, 0};
-                for (int bi = 0; bi < 16; ++bi) {
-                    const int64_t a = 16 * c + bi;
-                    if (a < wbytes) wv[bi >> 2] |= (uint32_t)W[a] << (8 * (bi & 3));
-                }
-                buf[i] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-            }
-        }
-    }
-
-    // 2. Quantize x into LDS while the weight loads are in flight.
+    const GemvLayout L = gemv_layout(WT, K, rows_per_wg, region_bytes);
     int8_t* act_qs = (int8_t*)(smem + L.act_qs);
     float* act_d = (float*)(smem + L.act_d);
     int16_t* act_bs = (int16_t*)(smem + L.act_bs);
-    const bool dump = (xq_out != nullptr) && blockIdx.x == 0;
+    uint32_t* act_ds = (uint32_t*)(smem + L.act_bs);  // Q8_1: binary16 d | s << 16 per block
+    float* partial = (float*)(smem + L.partial);
+    uint8_t* region = smem + L.regions + wave * region_bytes;
+
+    // ---- 1. x loads.  Loads are unconditional (addresses clamped into the
+    // buffers) so the code stays straight-line and each wait counts only the
+    // loads it needs.  The vector L1 returns data in order, so every wave's x
+    // loads are queued before any weight load of the workgroup: a bare
+    // s_barrier (no memory wait) separates the two.
+    const int xsteps = (K + kQK - 1) / kQK;  // 256 values per wave step
+    float4 xv[kXPre];
+#pragma unroll
+    for (int r = 0; r < kXPre; ++r) {
+        const int e = min((wave + kGemvWaves * r) * kQK + 4 * lane, K - 4);
+        const float* src = x + e;
+        xv[r] = x_vec ? *(const float4*)src : make_float4(src[0], src[1], src[2], src[3]);
+    }
+    __builtin_amdgcn_s_barrier();
+
+    // ---- 2. every weight load of this wave's span
+    const int ntask = rows * nb;
+    const int t0 = (int)((int64_t)ntask * wave / kGemvWaves);
+    const int t1 = (int)((int64_t)ntask * (wave + 1) / kGemvWaves);
+    int sb0, sb1;
+    task_span(t0, t1, nb, rb, BB, &sb0, &sb1);
+    const int64_t s0 = (int64_t)n0 * rb;
+    const int64_t wc0 = (s0 + sb0) >> 4;
+    const int64_t wc1 = (t1 > t0) ? ((s0 + sb1 + 15) >> 4) : wc0;
+    const int64_t full = wbytes >> 4;
+    uint4 buf[kLMax];
+#pragma unroll
+    for (int i = 0; i < kLMax; ++i) {
+        // past the span: the wave's last chunk again (one cache line, no new traffic)
+        const int64_t c = max(min(wc0 + lane + 64 * i, min(wc1, full) - 1), (int64_t)0);
+        buf[i] = *(const uint4*)(W + 16 * c);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- 3. quantize x into LDS
     if (WT != 2) {
         const int nsb = K / kQK;
-        int8_t* gq = (int8_t*)xq_out;
-        float* gd = (float*)(xq_out + align256((size_t)K));
-        int16_t* gb = (int16_t*)(xq_out + align256((size_t)K) + align256((size_t)nsb * 4));
-        for (int sb = wave; sb < nsb; sb += kGemvThreads / 64) {
-            const float* src = x + sb * kQK + 4 * lane;
-            float4 v = x_vec ? *(const float4*)src : make_float4(src[0], src[1], src[2], src[3]);
-            Q8KLane r = q8k_quant_lane(v, lane);
-            *(uint32_t*)(act_qs + sb * kQK + 4 * lane) = r.q4;
-            if (lane == 0) act_d[sb] = r.d;
-            if ((lane & 3) == 0) act_bs[sb * 16 + (lane >> 2)] = (int16_t)r.bsum;
-            if (dump) {
-                *(uint32_t*)(gq + sb * kQK + 4 * lane) = r.q4;
-                if (lane == 0) gd[sb] = r.d;
-                if ((lane & 3) == 0) gb[sb * 16 + (lane >> 2)] = (int16_t)r.bsum;
+#pragma unroll
+        for (int r = 0; r < kXPre; ++r) {
+            const int sb = wave + kGemvWaves * r;
+            if (sb < nsb) {
+                const Q8KLane q = q8k_quant_lane(xv[r], lane);
+                *(uint32_t*)(act_qs + sb * kActStride + 4 * lane) = q.q4;
+                if (lane == 0) act_d[sb] = q.d;
+                if ((lane & 3) == 0) act_bs[sb * 16 + (lane >> 2)] = (int16_t)q.bsum;
             }
         }
+        for (int sb = wave + kGemvWaves * kXPre; sb < nsb; sb += kGemvWaves) {
+            const float* src = x + sb * kQK + 4 * lane;
+            const Q8KLane q1 = q8k_quant_lane(x_vec ? *(const float4*)src
+                                                    : make_float4(src[0], src[1], src[2], src[3]), lane);
+            *(uint32_t*)(act_qs + sb * kActStride + 4 * lane) = q1.q4;
+            if (lane == 0) act_d[sb] = q1.d;
+            if ((lane & 3) == 0) act_bs[sb * 16 + (lane >> 2)] = (int16_t)q1.bsum;
+        }
     } else {
-        const int nblk = K / kQK8;
-        int8_t* gq = (int8_t*)xq_out;
-        uint16_t* gd = (uint16_t*)(xq_out + align256((size_t)K));
-        uint16_t* gs = (uint16_t*)(xq_out + align256((size_t)K) + align256((size_t)nblk * 2));
-        const int steps = (K + kQK - 1) / kQK;
-        for (int st = wave; st < steps; st += kGemvThreads / 64) {
-            const int e = st * kQK + 4 * lane;
+        auto quant_step = [&](int stp, float4 v) {
+            const int e = stp * kQK + 4 * lane;
             const bool valid = e < K;
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            const Q81Lane q = q81_quant_lane(v);
             if (valid) {
+                const int blk = e / kQK8;
+                *(uint32_t*)(act_qs + e) = q.q4;
+                const uint32_t d16 = float_to_half_bits(q.d);
+                if ((lane & 7) == 0) {
+                    act_d[blk] = half_bits_to_float(d16);
+                    act_ds[blk] = d16 | (float_to_half_bits(q.s) << 16);
+                }
+            }
+        };
+#pragma unroll
+        for (int r = 0; r < kXPre; ++r)
+            if (wave + kGemvWaves * r < xsteps) quant_step(wave + kGemvWaves * r, xv[r]);
+        for (int stp = wave + kGemvWaves * kXPre; stp < xsteps; stp += kGemvWaves) {
+            const int e = stp * kQK + 4 * lane;
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (e < K) {
                 const float* src = x + e;
                 v = x_vec ? *(const float4*)src : make_float4(src[0], src[1], src[2], src[3]);
             }
-            Q81Lane r = q81_quant_lane(v);
-            if (valid) {
-                const int blk = e / kQK8;
-                *(uint32_t*)(act_qs + e) = r.q4;
-                const uint32_t d16 = float_to_half_bits(r.d);
-                if ((lane & 7) == 0) act_d[blk] = half_bits_to_float(d16);
-                if (dump) {
-                    *(uint32_t*)(gq + e) = r.q4;
-                    if ((lane & 7) == 0) {
-                        gd[blk] = (uint16_t)d16;
-                        gs[blk] = (uint16_t)float_to_half_bits(r.s);
-                    }
-                }
-            }
+            quant_step(stp, v);
         }
     }
+    lds_barrier();  // quantized x visible to every wave; weights keep streaming
 
-    // 3. Park the weight slab in LDS.
-    uint8_t* slab = smem + L.slab;
-#pragma unroll
-    for (int i = 0; i < kGemvChunks; ++i) {
-        const int64_t c = c0 + tid + (int64_t)i * kGemvThreads;
-        if (c < c1) *(uint4*)(slab + 16 * (c - c0)) = buf[i];
-    }
-    __syncthreads();
-
-    // 4. Per (row, block) partials.
-    float* partial = (float*)(smem + L.partial);
-    const int soff = (int)(s0 - 16 * c0);
-    const int ntask = rows * nb;
-    if (WT == 0) {
-        const int g = tid & 7;
-        const int c = g >> 1, l0 = (g & 1) * 16;
-        for (int t = tid >> 3; t < ntask; t += kGemvThreads / 8) {
-            const int r = t / nb, blk = t - r * nb;
-            const uint8_t* bp = slab + soff + r * rb + blk * BB;
+    // ---- 4. park this wave's bytes in its region and compute its tasks
+    const int rbase = (int)(s0 - 16 * wc0);  // LDS byte of task byte o: region + rbase + o
+    const int grp = lane / LPT, sub = lane % LPT;
+    int next = t0;
+    int tr = (t0 + grp) / nb, tb = (t0 + grp) - ((t0 + grp) / nb) * nb;  // this lane's task (row, block)
+    auto advance = [&](int adv) {
+        next += adv;
+        tb += adv;
+        while (tb >= nb) { tb -= nb; ++tr; }
+    };
+    auto compute_task = [&](int r, int blk) {
+        const uint8_t* bp = region + rbase + __mul24(r, rb) + __mul24(blk, BB);
+        if (WT == 0) {
+            // lane half hf: sub-blocks 4hf..4hf+3 = qs bytes [64hf, 64hf+64)
+            const int hf = sub;
             const uint4 hdr = *(const uint4*)bp;
-            const uint4 qv = *(const uint4*)(bp + 16 + 16 * g);
-            const int8_t* ab = act_qs + blk * kQK + 64 * c + l0;
-            const uint4 alo = *(const uint4*)ab;
-            const uint4 ahi = *(const uint4*)(ab + 32);
-            const uint32_t sword = (c < 2) ? hdr.y : hdr.z;
-            const uint32_t s_lo = (sword >> (16 * (c & 1))) & 0xFF;
-            const uint32_t s_hi = (sword >> (16 * (c & 1) + 8)) & 0xFF;
-            const uint32_t mb = (hdr.w >> (8 * c)) & 0xFF;
-            const int sc0 = s_lo & 63, sc1 = s_hi & 63;
-            const int m0 = (int)((s_lo >> 6) | ((mb & 15) << 2));
-            const int m1 = (int)((s_hi >> 6) | ((mb >> 4) << 2));
-            int plo = 0, phi = 0;
-            plo = sdot4((int)(qv.x & 0x0F0F0F0Fu), (int)alo.x, plo);
-            plo = sdot4((int)(qv.y & 0x0F0F0F0Fu), (int)alo.y, plo);
-            plo = sdot4((int)(qv.z & 0x0F0F0F0Fu), (int)alo.z, plo);
-            plo = sdot4((int)(qv.w & 0x0F0F0F0Fu), (int)alo.w, plo);
-            phi = sdot4((int)((qv.x >> 4) & 0x0F0F0F0Fu), (int)ahi.x, phi);
-            phi = sdot4((int)((qv.y >> 4) & 0x0F0F0F0Fu), (int)ahi.y, phi);
-            phi = sdot4((int)((qv.z >> 4) & 0x0F0F0F0Fu), (int)ahi.z, phi);
-            phi = sdot4((int)((qv.w >> 4) & 0x0F0F0F0Fu), (int)ahi.w, phi);
-            int S = sc0 * plo + sc1 * phi;
-            int Mn = 0;
-            if ((g & 1) == 0) {
-                const int16_t* bs = act_bs + blk * 16 + 4 * c;
-                Mn = m0 * ((int)bs[0] + (int)bs[1]) + m1 * ((int)bs[2] + (int)bs[3]);
-            }
-            S += shfl_xor_i(S, 1); Mn += shfl_xor_i(Mn, 1);
-            S += shfl_xor_i(S, 2); Mn += shfl_xor_i(Mn, 2);
-            S += shfl_xor_i(S, 4); Mn += shfl_xor_i(Mn, 4);
-            if (g == 0) {
-                const float d = half_bits_to_float(hdr.x & 0xFFFF);
-                const float dmin = half_bits_to_float(hdr.x >> 16);
-                const float t1 = d * (float)S;
-                const float t2 = dmin * (float)Mn;
-                const float t3 = t1 - t2;
-                partial[r * nb + blk] = act_d[blk] * t3;
-            }
-        }
-    } else if (WT == 1) {
-        const int g = tid & 7;
-        const int h = g >> 2, k = g & 3;
-        const int sha = 2 * (k >> 1), shb = 2 * (2 + (k >> 1));
-        for (int t = tid >> 3; t < ntask; t += kGemvThreads / 8) {
-            const int r = t / nb, blk = t - r * nb;
-            const uint8_t* bp = slab + soff + r * rb + blk * BB;
-            uint32_t ql[4], qh[4];
-            lds_read16_a2(bp + 64 * h + 16 * k, ql);
-            lds_read16_a2(bp + 128 + 32 * h + 16 * (k & 1), qh);
-            const int sca = (int)(int8_t)bp[192 + 8 * h + k];
-            const int scb = (int)(int8_t)bp[192 + 8 * h + 4 + k];
-            const int8_t* ab = act_qs + blk * kQK + 128 * h + 16 * k;
-            const uint4 alo = *(const uint4*)ab;
-            const uint4 ahi = *(const uint4*)(ab + 64);
-            const uint32_t al[4] = {alo.x, alo.y, alo.z, alo.w};
-            const uint32_t ah[4] = {ahi.x, ahi.y, ahi.z, ahi.w};
-            int ia = 0, ib = 0;
+            uint32_t qw[16];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const uint32_t qa = (ql[i] & 0x0F0F0F0Fu) | (((qh[i] >> sha) & 0x03030303u) << 4);
-                const uint32_t qb = ((ql[i] >> 4) & 0x0F0F0F0Fu) | (((qh[i] >> shb) & 0x03030303u) << 4);
-                ia = sdot4((int)qa, (int)al[i], ia);
-                ib = sdot4((int)qb, (int)ah[i], ib);
+                const uint4 v = *(const uint4*)(bp + 16 + 64 * hf + 16 * i);
+                qw[4 * i] = v.x; qw[4 * i + 1] = v.y; qw[4 * i + 2] = v.z; qw[4 * i + 3] = v.w;
             }
-            const int16_t* bs = act_bs + blk * 16 + 8 * h + k;
-            ia -= 32 * (int)bs[0];
-            ib -= 32 * (int)bs[4];
-            int S = sca * ia + scb * ib;
-            S += shfl_xor_i(S, 1);
-            S += shfl_xor_i(S, 2);
-            S += shfl_xor_i(S, 4);
-            if (g == 0) {
+            const int8_t* ab = act_qs + __mul24(blk, kActStride) + 128 * hf;
+            uint32_t av[32];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint4 v = *(const uint4*)(ab + 16 * i);
+                av[4 * i] = v.x; av[4 * i + 1] = v.y; av[4 * i + 2] = v.z; av[4 * i + 3] = v.w;
+            }
+            int P[4] = {0, 0, 0, 0};  // sub-blocks 4hf + j
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const uint32_t w = qw[8 * c + i];
+                    P[2 * c] = sdot4((int)(w & 0x0F0F0F0Fu), (int)av[16 * c + i], P[2 * c]);
+                    P[2 * c + 1] = sdot4((int)((w >> 4) & 0x0F0F0F0Fu), (int)av[16 * c + 8 + i], P[2 * c + 1]);
+                }
+            const uint32_t sw = hf ? hdr.z : hdr.y;             // scales bytes 4hf..4hf+3
+            const uint32_t mw = hdr.w >> (16 * hf);             // min high nibbles, 2 bytes
+            const uint4 bsv = *(const uint4*)(act_bs + blk * 16 + 8 * hf);
+            const uint32_t bw[4] = {bsv.x, bsv.y, bsv.z, bsv.w};
+            int S = 0, Mn = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t sj = (sw >> (8 * j)) & 0xFF;
+                const uint32_t mh = (mw >> (4 * j)) & 15;
+                const int m = (int)((sj >> 6) | (mh << 2));
+                const int bs32 = (int)(int16_t)(bw[j] & 0xFFFF) + (int)(int16_t)(bw[j] >> 16);
+                S += __mul24((int)(sj & 63), P[j]);
+                Mn += __mul24(m, bs32);
+            }
+            S += dppi<0xB1>(S);
+            Mn += dppi<0xB1>(Mn);
+            if (hf == 0) {
+                const float d = half_bits_to_float(hdr.x & 0xFFFF);
+                const float dmin = half_bits_to_float(hdr.x >> 16);
+                const float t1f = d * (float)S;
+                const float t2f = dmin * (float)Mn;
+                const float t3f = t1f - t2f;
+                partial[__mul24(r, nb) + blk] = act_d[blk] * t3f;
+            }
+        } else if (WT == 1) {
+            // lane half h: values 128h..128h+127 (sub-blocks 8h..8h+7)
+            const int h = sub;
+            uint32_t ql[16], qh[8];
+            lds_read32_a2(bp + 64 * h, ql);
+            lds_read32_a2(bp + 64 * h + 32, ql + 8);
+            lds_read32_a2(bp + 128 + 32 * h, qh);
+            const uint16_t* scp = (const uint16_t*)(bp + 192 + 8 * h);
+            const uint32_t sc01 = scp[0], sc23 = scp[1], sc45 = scp[2], sc67 = scp[3];
+            const int8_t* ab = act_qs + __mul24(blk, kActStride) + 128 * h;
+            uint32_t av[32];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint4 v = *(const uint4*)(ab + 16 * i);
+                av[4 * i] = v.x; av[4 * i + 1] = v.y; av[4 * i + 2] = v.z; av[4 * i + 3] = v.w;
+            }
+            int I[8] = {0, 0, 0, 0, 0, 0, 0, 0};  // sub-blocks 8h + j
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t l = ql[4 * k + i];
+                    const uint32_t hq = qh[4 * (k & 1) + i];
+                    const int sa = 2 * (k >> 1), sb = 2 * (2 + (k >> 1));
+                    const uint32_t qa = (l & 0x0F0F0F0Fu) | (((hq >> sa) & 0x03030303u) << 4);
+                    const uint32_t qb = ((l >> 4) & 0x0F0F0F0Fu) | (((hq >> sb) & 0x03030303u) << 4);
+                    I[k] = sdot4((int)qa, (int)av[4 * k + i], I[k]);
+                    I[4 + k] = sdot4((int)qb, (int)av[16 + 4 * k + i], I[4 + k]);
+                }
+            const uint4 bsv = *(const uint4*)(act_bs + blk * 16 + 8 * h);
+            const uint32_t bw[4] = {bsv.x, bsv.y, bsv.z, bsv.w};
+            const uint32_t scw[4] = {sc01, sc23, sc45, sc67};
+            int S = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int bsj = (int)(int16_t)((bw[j >> 1] >> (16 * (j & 1))) & 0xFFFF);
+                const int scj = (int)(int8_t)((scw[j >> 1] >> (8 * (j & 1))) & 0xFF);
+                S += __mul24(scj, I[j] - 32 * bsj);
+            }
+            S += dppi<0xB1>(S);
+            if (h == 0) {
                 const float d = half_bits_to_float(*(const uint16_t*)(bp + 208));
-                const float t1 = d * (float)S;
-                partial[r * nb + blk] = act_d[blk] * t1;
+                const float t1f = d * (float)S;
+                partial[__mul24(r, nb) + blk] = act_d[blk] * t1f;
             }
-        }
-    } else {
-        for (int t = tid; t < ntask; t += kGemvThreads) {
-            const int r = t / nb, blk = t - r * nb;
-            const uint8_t* bp = slab + soff + r * rb + blk * BB;
-            uint32_t q0[4], q1[4];
-            lds_read16_a2(bp + 2, q0);
-            lds_read16_a2(bp + 18, q1);
+        } else {
+            uint32_t qw[8];
+            lds_read32_a2(bp + 2, qw);
             const uint4 a0 = *(const uint4*)(act_qs + blk * kQK8);
             const uint4 a1 = *(const uint4*)(act_qs + blk * kQK8 + 16);
+            const uint32_t av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
             int I = 0;
-            I = sdot4((int)q0[0], (int)a0.x, I);
-            I = sdot4((int)q0[1], (int)a0.y, I);
-            I = sdot4((int)q0[2], (int)a0.z, I);
-            I = sdot4((int)q0[3], (int)a0.w, I);
-            I = sdot4((int)q1[0], (int)a1.x, I);
-            I = sdot4((int)q1[1], (int)a1.y, I);
-            I = sdot4((int)q1[2], (int)a1.z, I);
-            I = sdot4((int)q1[3], (int)a1.w, I);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) I = sdot4((int)qw[i], (int)av[i], I);
             const float dw = half_bits_to_float(*(const uint16_t*)bp);
-            const float s = dw * act_d[blk];
-            partial[r * nb + blk] = s * (float)I;
+            const float sc = dw * act_d[blk];
+            partial[__mul24(r, nb) + blk] = sc * (float)I;
+        }
+    };
+
+#pragma unroll
+    for (int st = 0; st < kLMax / kStepLoads; ++st) {
+#pragma unroll
+        for (int j = 0; j < kStepLoads; ++j) {
+            const int i = kStepLoads * st + j;
+            const int64_t c = wc0 + lane + 64 * i;
+            if (c < wc1) {
+                uint4 v = buf[i];
+                if (c >= full) {  // the buffer's last partial chunk (last wave of the grid only)
+                    uint32_t wv[4] = {0, 0, 0, 0};
+                    for (int bi = 0; bi < 16; ++bi) {
+                        const int64_t a = 16 * c + bi;
+                        if (a < wbytes) wv[bi >> 2] |= (uint32_t)W[a] << (8 * (bi & 3));
+                    }
+                    v = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+                }
+                *(uint4*)(region + 16 * (int)(c - wc0)) = v;
+            }
+        }
+        // LDS operations of one wave complete in order: the parked bytes are
+        // visible to this wave's later reads without a barrier.
+        const int E = (int)(16 * (wc0 + 64 * kStepLoads * (st + 1)) - s0);
+        const int ready = min(t1, tasks_within(E, nb, rb, BB));
+        while (next < ready) {
+            const int cnt = min(GPW, ready - next);
+            if (grp < cnt) compute_task(tr, tb);
+            advance(cnt);
         }
     }
-    __syncthreads();
+    lds_barrier();
 
-    // 5. Rows: blocks summed in ascending order from 0.
+    // ---- 5. rows: blocks summed in ascending order from 0
     for (int r = tid; r < rows; r += kGemvThreads) {
-        float acc = 0.0f;
         const float* p = partial + r * nb;
-        for (int b = 0; b < nb; ++b) acc = acc + p[b];
+        float acc = 0.0f;
+        int b = 0;
+        if ((nb & 3) == 0) {
+            for (; b + 16 <= nb; b += 16) {
+                const float4 u0 = *(const float4*)(p + b);
+                const float4 u1 = *(const float4*)(p + b + 4);
+                const float4 u2 = *(const float4*)(p + b + 8);
+                const float4 u3 = *(const float4*)(p + b + 12);
+                acc = acc + u0.x; acc = acc + u0.y; acc = acc + u0.z; acc = acc + u0.w;
+                acc = acc + u1.x; acc = acc + u1.y; acc = acc + u1.z; acc = acc + u1.w;
+                acc = acc + u2.x; acc = acc + u2.y; acc = acc + u2.z; acc = acc + u2.w;
+                acc = acc + u3.x; acc = acc + u3.y; acc = acc + u3.z; acc = acc + u3.w;
+            }
+        }
+        for (; b < nb; ++b) acc = acc + p[b];
         y[n0 + r] = acc;
+    }
+
+    // ---- 6. the fused quantizer's bytes, for callers that want them
+    if (xq_out != nullptr && blockIdx.x == 0) {
+        const size_t od = align256((size_t)K);
+        const int stride = (WT == 2) ? kQK : kActStride;
+        for (int i = tid; i < K / 4; i += kGemvThreads)
+            ((uint32_t*)xq_out)[i] = *(const uint32_t*)(act_qs + (i / 64) * stride + 4 * (i % 64));
+        if (WT != 2) {
+            const int nsb = K / kQK;
+            float* gd = (float*)(xq_out + od);
+            int16_t* gb = (int16_t*)(xq_out + od + align256((size_t)nsb * 4));
+            for (int i = tid; i < nsb; i += kGemvThreads) gd[i] = act_d[i];
+            for (int i = tid; i < K / 16; i += kGemvThreads) gb[i] = act_bs[i];
+        } else {
+            const int nblk = K / kQK8;
+            uint16_t* gd = (uint16_t*)(xq_out + od);
+            uint16_t* gs = (uint16_t*)(xq_out + od + align256((size_t)nblk * 2));
+            for (int i = tid; i < nblk; i += kGemvThreads) {
+                gd[i] = (uint16_t)(act_ds[i] & 0xFFFF);
+                gs[i] = (uint16_t)(act_ds[i] >> 16);
+            }
+        }
     }
 }
 
@@ -307,43 +438,75 @@ static int num_cus() {
 static int block_bytes_of(int wt) { return wt == 0 ? kQ4KBytes : (wt == 1 ? kQ6KBytes : kQ80Bytes); }
 static int block_vals_of(int wt) { return wt == 2 ? kQK8 : kQK; }
 
-// Rows per workgroup: about one workgroup per CU, fewer rows when the slab
-// would not fit the per-thread chunk budget or LDS.
-static int gemv_rows_per_wg(int wt, int64_t N, int64_t K) {
-    const int rb = (int)(K / block_vals_of(wt)) * block_bytes_of(wt);
+struct GemvPlan {
+    int rows;          // rows per workgroup
+    int region_bytes;  // LDS bytes per wave region
+    int lds;           // dynamic LDS bytes
+    bool ok;
+};
+
+// Largest per-wave span (bytes, incl. 16-byte alignment slack) for a given
+// rows-per-workgroup, by walking the task split the kernel uses.
+static int max_wave_span(int rows, int nb, int rb, int bb) {
+    const int ntask = rows * nb;
+    int best = 0;
+    for (int w = 0; w < kGemvWaves; ++w) {
+        const int t0 = (int)((int64_t)ntask * w / kGemvWaves);
+        const int t1 = (int)((int64_t)ntask * (w + 1) / kGemvWaves);
+        int b0, b1;
+        task_span(t0, t1, nb, rb, bb, &b0, &b1);
+        best = b1 - b0 > best ? b1 - b0 : best;
+    }
+    return best;
+}
+
+// About one workgroup per CU; fewer rows per workgroup when a wave's span
+// would not fit its chunk budget or the workgroup would not fit LDS.
+static GemvPlan gemv_plan(int wt, int64_t N, int64_t K) {
+    GemvPlan p;
+    const int bb = block_bytes_of(wt);
+    const int nb = (int)(K / block_vals_of(wt));
+    const int rb = nb * bb;
     int rows = (int)((N + num_cus() - 1) / num_cus());
     if (rows < 1) rows = 1;
-    const int max_slab = kGemvChunks * kGemvThreads * 16 - 48;
-    while (rows > 1 && (rows * rb > max_slab ||
-                        (size_t)gemv_layout(wt, (int)K, rows, rb).total > kMaxLds))
+    for (;;) {
+        const int span = max_wave_span(rows, nb, rb, bb);
+        const int region = align16i(span + 32) + 32;  // alignment slack + over-read slack
+        const GemvLayout L = gemv_layout(wt, (int)K, rows, region);
+        const bool fits = span + 32 <= kLMax * 64 * 16 && (size_t)L.total <= kMaxLds;
+        if (fits || rows == 1) {
+            p.rows = rows;
+            p.region_bytes = region;
+            p.lds = L.total;
+            p.ok = fits;
+            return p;
+        }
         --rows;
-    return rows;
+    }
 }
 
 size_t gemv_lds_bytes(int wtype, int64_t N, int64_t K) {
-    const int rb = (int)(K / block_vals_of(wtype)) * block_bytes_of(wtype);
-    const int rows = gemv_rows_per_wg(wtype, N, K);
-    if ((int64_t)rb > (int64_t)kGemvChunks * kGemvThreads * 16 - 48) return (size_t)-1;
-    return (size_t)gemv_layout(wtype, (int)K, rows, rb).total;
+    const GemvPlan p = gemv_plan(wtype, N, K);
+    return p.ok ? (size_t)p.lds : (size_t)-1;
 }
 
 template <int WT>
 static hipError_t launch_gemv_t(const uint8_t* W, int64_t N, int64_t K, const float* x, float* y,
                                 uint8_t* xq_out, hipStream_t st) {
     static bool attr_set = false;
-    const int rb = (int)(K / WFmt<WT>::kVals) * WFmt<WT>::kBlk;
-    const int rows = gemv_rows_per_wg(WT, N, K);
-    const int lds = gemv_layout(WT, (int)K, rows, rb).total;
+    const GemvPlan p = gemv_plan(WT, N, K);
+    if (!p.ok) return hipErrorInvalidValue;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void*)gemv_kernel<WT>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    const int grid = (int)((N + rows - 1) / rows);
+    const int rb = (int)(K / WFmt<WT>::kVals) * WFmt<WT>::kBlk;
+    const int grid = (int)((N + p.rows - 1) / p.rows);
     const int x_vec = (((uintptr_t)x) & 15) == 0;
-    gemv_kernel<WT><<<grid, kGemvThreads, lds, st>>>(W, (int)N, (int)K, (int64_t)N * rb, x, y,
-                                                     xq_out, rows, x_vec);
+    gemv_kernel<WT><<<grid, kGemvThreads, p.lds, st>>>(W, (int)N, (int)K, (int64_t)N * rb, x, y, xq_out,
+                                                        p.rows, p.region_bytes, x_vec);
     return hipGetLastError();
 }
 

@@ -44,32 +44,58 @@ __device__ __forceinline__ int sdot4(int a, int b, int c) {
 
 // 16 bytes at a 2-byte aligned LDS address, as four dwords, using only
 // 4-byte aligned reads.
+// The aligned pointer is formed by pointer arithmetic (not an integer round
+// trip) so the compiler keeps the LDS address space and emits ds_read.  The
+// fifth dword is always read (callers keep 4 bytes of slack after the data);
+// v_alignbyte with a zero shift returns its low operand.
 __device__ __forceinline__ void lds_read16_a2(const uint8_t* p, uint32_t out[4]) {
-    uintptr_t a = (uintptr_t)p;
-    const uint32_t* q = (const uint32_t*)(a & ~(uintptr_t)3);
-    uint32_t sh = (uint32_t)(a & 3);
-    uint32_t w0 = q[0], w1 = q[1], w2 = q[2], w3 = q[3];
-    if (sh == 0) {
-        out[0] = w0; out[1] = w1; out[2] = w2; out[3] = w3;
-    } else {
-        uint32_t w4 = q[4];
-        out[0] = __builtin_amdgcn_alignbyte(w1, w0, sh);
-        out[1] = __builtin_amdgcn_alignbyte(w2, w1, sh);
-        out[2] = __builtin_amdgcn_alignbyte(w3, w2, sh);
-        out[3] = __builtin_amdgcn_alignbyte(w4, w3, sh);
-    }
+    const uint32_t sh = (uint32_t)((uintptr_t)p & 3);
+    const uint32_t* q = (const uint32_t*)(p - sh);
+    const uint32_t w0 = q[0], w1 = q[1], w2 = q[2], w3 = q[3], w4 = q[4];
+    out[0] = __builtin_amdgcn_alignbyte(w1, w0, sh);
+    out[1] = __builtin_amdgcn_alignbyte(w2, w1, sh);
+    out[2] = __builtin_amdgcn_alignbyte(w3, w2, sh);
+    out[3] = __builtin_amdgcn_alignbyte(w4, w3, sh);
+}
+
+// ---------------------------------------------------------------------------
+// Lane exchange through DPP (VALU, no LDS round trip).  Control codes:
+//   0xB1 quad_perm [1,0,3,2] (lane ^ 1)     0x4E quad_perm [2,3,0,1] (lane ^ 2)
+//   0x141 row_half_mirror (lane i <-> 7-i in each 8)   0x140 row_mirror (16)
+//   0x10n row_shl:n (lane i reads lane i+n inside its row of 16)
+// bound_ctrl zero-fills lanes whose source is outside the row.
+// ---------------------------------------------------------------------------
+template <int C>
+__device__ __forceinline__ int dppi(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, C, 0xF, 0xF, true);
+}
+template <int C>
+__device__ __forceinline__ float dppf(float v) {
+    return __builtin_bit_cast(float, dppi<C>(__builtin_bit_cast(int, v)));
+}
+// Sum over each group of 8 lanes, left on all 8 lanes (exact for ints).
+__device__ __forceinline__ int sum8(int v) {
+    v += dppi<0xB1>(v);
+    v += dppi<0x4E>(v);
+    v += dppi<0x141>(v);
+    return v;
+}
+__device__ __forceinline__ int readlane_i(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+__device__ __forceinline__ float readlane_f(float v, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
 }
 
 // ---------------------------------------------------------------------------
 // Q8_K quantizer body (vllm.cpp PR #2890, commit "QuantizeQ8KKWarpCoop", and
 // commit "gamma predicate + amax-seed fix").  One wave quantizes one
 // super-block of 256 values; lane l holds values 4l..4l+3.
-//   - each lane scans its 4 values ascending with a strict compare from
-//     amax = 0 (first occurrence, a NaN never wins);
-//   - the wave reduction keeps the larger magnitude and, on a tie, the lower
-//     element index, which equals the sequential first occurrence;
+//   - amax: each lane scans its 4 values with a strict compare from 0 (a NaN
+//     never wins), then the wave maximum;
+//   - mx is the value at the lowest index whose magnitude equals amax (lowest
+//     lane by ballot, then lowest component), which is exactly the first
+//     occurrence an ascending strict-compare scan keeps;
 //   - iscale = -127/mx (IEEE division), q = min(127, rint(iscale*x)), d =
-//     1/iscale; amax == 0 gives the zero block;
+//     1/iscale; amax == 0 (all zero or all NaN) gives the zero block;
 //   - bsum_j (16 values = lanes 4j..4j+3) is left on every lane of the quad.
 // ---------------------------------------------------------------------------
 struct Q8KLane {
@@ -78,47 +104,78 @@ struct Q8KLane {
     int bsum;      // sum of the 16 quants of this lane's quad
 };
 
+// N independent super-blocks per wave, processed in lockstep so that their
+// dependency chains (reductions, divisions) overlap.
+template <int N>
+__device__ __forceinline__ void q8k_quant_lanes(const float4 (&v)[N], Q8KLane (&out)[N]) {
+    float a[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        const float xs[4] = {v[n].x, v[n].y, v[n].z, v[n].w};
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float ax = fabsf(xs[i]);
+            if (ax > m) m = ax;
+        }
+        a[n] = m;
+    }
+#pragma unroll
+    for (int n = 0; n < N; ++n) a[n] = fmaxf(a[n], dppf<0xB1>(a[n]));
+#pragma unroll
+    for (int n = 0; n < N; ++n) a[n] = fmaxf(a[n], dppf<0x4E>(a[n]));
+#pragma unroll
+    for (int n = 0; n < N; ++n) a[n] = fmaxf(a[n], dppf<0x141>(a[n]));
+#pragma unroll
+    for (int n = 0; n < N; ++n) a[n] = fmaxf(a[n], dppf<0x140>(a[n]));
+    float amax[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n)
+        amax[n] = fmaxf(fmaxf(readlane_f(a[n], 0), readlane_f(a[n], 16)),
+                        fmaxf(readlane_f(a[n], 32), readlane_f(a[n], 48)));
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        const float xs[4] = {v[n].x, v[n].y, v[n].z, v[n].w};
+        // first occurrence of the largest magnitude: the lowest lane holding one,
+        // and inside that lane the lowest component
+        const bool hit = fabsf(xs[0]) == amax[n] || fabsf(xs[1]) == amax[n] ||
+                         fabsf(xs[2]) == amax[n] || fabsf(xs[3]) == amax[n];
+        const unsigned long long mask = __ballot(hit);
+        const float sel = fabsf(xs[0]) == amax[n] ? xs[0]
+                        : (fabsf(xs[1]) == amax[n] ? xs[1] : (fabsf(xs[2]) == amax[n] ? xs[2] : xs[3]));
+        const int first = mask ? __builtin_ctzll(mask) : 0;
+        const float mx = readlane_f(sel, first);
+        if (amax[n] == 0.0f) {
+            out[n].q4 = 0u;
+            out[n].d = 0.0f;
+            out[n].bsum = 0;
+            continue;
+        }
+        const float iscale = -127.0f / mx;
+        uint32_t packed = 0;
+        int sum = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float t = iscale * xs[i];
+            int q = (int)__builtin_rintf(t);
+            q = q > 127 ? 127 : q;
+            sum += q;
+            packed |= ((uint32_t)(q & 0xFF)) << (8 * i);
+        }
+        sum += dppi<0xB1>(sum);
+        sum += dppi<0x4E>(sum);
+        out[n].q4 = packed;
+        out[n].d = 1.0f / iscale;
+        out[n].bsum = sum;
+    }
+}
+
 __device__ __forceinline__ Q8KLane q8k_quant_lane(float4 v, int lane) {
-    float amax = 0.0f, mx = 0.0f;
-    int idx = 0x7FFFFFFF;
-    const float xs[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        float ax = fabsf(xs[i]);
-        if (ax > amax) { amax = ax; mx = xs[i]; idx = 4 * lane + i; }
-    }
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        float oa = shfl_xor_f(amax, o);
-        float om = shfl_xor_f(mx, o);
-        int oi = shfl_xor_i(idx, o);
-        bool take = (oa > amax) || (oa == amax && oi < idx);
-        if (take) { amax = oa; mx = om; idx = oi; }
-    }
-    Q8KLane r;
-    if (amax == 0.0f) {
-        r.q4 = 0u;
-        r.d = 0.0f;
-        r.bsum = 0;
-        return r;
-    }
-    const float iscale = -127.0f / mx;
-    uint32_t packed = 0;
-    int s = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        float t = iscale * xs[i];
-        int q = (int)__builtin_rintf(t);
-        q = q > 127 ? 127 : q;
-        s += q;
-        packed |= ((uint32_t)(q & 0xFF)) << (8 * i);
-    }
-    s += shfl_xor_i(s, 1);
-    s += shfl_xor_i(s, 2);
-    r.q4 = packed;
-    r.d = 1.0f / iscale;
-    r.bsum = s;
-    return r;
+    (void)lane;
+    const float4 vv[1] = {v};
+    Q8KLane r[1];
+    q8k_quant_lanes<1>(vv, r);
+    return r[0];
 }
 
 // ---------------------------------------------------------------------------
@@ -126,8 +183,9 @@ __device__ __forceinline__ Q8KLane q8k_quant_lane(float4 v, int lane) {
 // "mul_mat_vec_q_fq generic").  Eight lanes hold one 32-block (lane l holds
 // values 4l..4l+3 of the wave's 256).  amax over the block; d = amax/127;
 // q = roundf(x/d) (0 when amax == 0); s = binary32 butterfly sum: element i
-// first meets i^16 (lane ^4), then i^8 (lane ^2), i^4 (lane ^1), i^2 and i^1
-// (inside the lane).  Returns the 4 quants, d (binary32) and s (binary32).
+// first meets i^16 (lane +4), then i^8 (lane +2), i^4 (lane +1), i^2 and i^1
+// (inside the lane).  s is exact on the first lane of each group of 8 (the
+// other lanes' s is not the block sum).
 // ---------------------------------------------------------------------------
 struct Q81Lane {
     uint32_t q4;
@@ -140,14 +198,12 @@ __device__ __forceinline__ Q81Lane q81_quant_lane(float4 v) {
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        float ax = fabsf(xs[i]);
+        const float ax = fabsf(xs[i]);
         if (ax > amax) amax = ax;
     }
-#pragma unroll
-    for (int o = 1; o < 8; o <<= 1) {
-        float oa = shfl_xor_f(amax, o);
-        if (oa > amax) amax = oa;
-    }
+    amax = fmaxf(amax, dppf<0xB1>(amax));
+    amax = fmaxf(amax, dppf<0x4E>(amax));
+    amax = fmaxf(amax, dppf<0x141>(amax));
     const float d = amax / 127.0f;
     uint32_t packed = 0;
 #pragma unroll
@@ -157,14 +213,14 @@ __device__ __forceinline__ Q81Lane q81_quant_lane(float4 v) {
         packed |= ((uint32_t)(q & 0xFF)) << (8 * i);
     }
     float b0 = xs[0], b1 = xs[1], b2 = xs[2], b3 = xs[3];
-    b0 = b0 + shfl_xor_f(b0, 4); b1 = b1 + shfl_xor_f(b1, 4);
-    b2 = b2 + shfl_xor_f(b2, 4); b3 = b3 + shfl_xor_f(b3, 4);
-    b0 = b0 + shfl_xor_f(b0, 2); b1 = b1 + shfl_xor_f(b1, 2);
-    b2 = b2 + shfl_xor_f(b2, 2); b3 = b3 + shfl_xor_f(b3, 2);
-    b0 = b0 + shfl_xor_f(b0, 1); b1 = b1 + shfl_xor_f(b1, 1);
-    b2 = b2 + shfl_xor_f(b2, 1); b3 = b3 + shfl_xor_f(b3, 1);
-    float t0 = b0 + b2;
-    float t1 = b1 + b3;
+    b0 = b0 + dppf<0x104>(b0); b1 = b1 + dppf<0x104>(b1);
+    b2 = b2 + dppf<0x104>(b2); b3 = b3 + dppf<0x104>(b3);
+    b0 = b0 + dppf<0x102>(b0); b1 = b1 + dppf<0x102>(b1);
+    b2 = b2 + dppf<0x102>(b2); b3 = b3 + dppf<0x102>(b3);
+    b0 = b0 + dppf<0x101>(b0); b1 = b1 + dppf<0x101>(b1);
+    b2 = b2 + dppf<0x101>(b2); b3 = b3 + dppf<0x101>(b3);
+    const float t0 = b0 + b2;
+    const float t1 = b1 + b3;
     Q81Lane r;
     r.q4 = packed;
     r.d = d;
