@@ -77,7 +77,8 @@ def event_pair():
 
 
 def time_launches(fn, iters, warmup=3):
-    """Average per-launch duration (ms) from events around each launch."""
+    """Average per-launch duration (ms) from HIP events around each launch
+    (eager launches; only for kernels much longer than a launch's host cost)."""
     import torch
     for _ in range(warmup):
         fn(0)
@@ -89,6 +90,38 @@ def time_launches(fn, iters, warmup=3):
         pairs[i][1].record()
     torch.cuda.synchronize()
     return sum(a.elapsed_time(b) for a, b in pairs) / iters
+
+
+def time_graph(fn, per_graph, min_calls, warmup=2):
+    """Average duration (ms) of one call of fn, from HIP events around replays
+    of a HIP graph that holds `per_graph` back-to-back calls fn(0..per_graph-1),
+    recorded on the stream the graph replays on.  A host launch costs several
+    microseconds, more than the decode kernels run, so eager back-to-back
+    launches would time the host; the graph times the GPU."""
+    import torch
+    for i in range(max(warmup, 1)):
+        fn(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            for i in range(per_graph):
+                fn(i)
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    reps = max(1, math.ceil(min_calls / per_graph))
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0, t1 = event_pair()
+    t0.record()
+    for _ in range(reps):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / (reps * per_graph), reps * per_graph
 
 
 def run_cpu_baseline(seconds: float):
@@ -144,54 +177,16 @@ def run_decode(args, torch, vq, synth):
     Qb = [Qb0] + [Qb0.clone() for _ in range(R - 1)]
     ya = [torch.empty(9728, dtype=torch.float32, device=dev) for _ in range(R)]
     yb = [torch.empty(2560, dtype=torch.float32, device=dev) for _ in range(R)]
-    stream = torch.cuda.current_stream().cuda_stream
-
     def step(i):
         s = i % R
-        vq.gemv(vq.Q4_K, Qa[s], 9728, 2560, xa, y=ya[s], stream=torch.cuda.current_stream().cuda_stream)
-        vq.gemv(vq.Q6_K, Qb[s], 2560, 9728, xb, y=yb[s], stream=torch.cuda.current_stream().cuda_stream)
+        vq.gemv(vq.Q4_K, Qa[s], 9728, 2560, xa, y=ya[s])
+        vq.gemv(vq.Q6_K, Qb[s], 2560, 9728, xb, y=yb[s])
 
-    # Eager warm-up (also sets the kernels' LDS attribute before any capture).
-    for i in range(max(args.warmup, 2)):
-        step(i)
-    torch.cuda.synchronize()
-
-    # The decode step is launch-bound from Python (a HIP launch costs several
-    # microseconds of host time, more than these kernels run), so the timed
-    # steps replay a HIP graph holding one step per rotation set.
-    g = torch.cuda.CUDAGraph()
-    cap = torch.cuda.Stream()
-    cap.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(cap):
-        with torch.cuda.graph(g, stream=cap):
-            for i in range(R):
-                step(i)
-    torch.cuda.current_stream().wait_stream(cap)
-    torch.cuda.synchronize()
-    reps = max(1, math.ceil(args.steps / R))
-    for _ in range(max(1, args.warmup // R)):
-        g.replay()
-    torch.cuda.synchronize()
-    t0, t1 = event_pair()
-    t0.record()
-    for _ in range(reps):
-        g.replay()
-    t1.record()
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / (reps * R)
-    steps_timed = reps * R
-
-    # Per-kernel launch durations: HIP events around each launch of one
-    # kernel, launched back to back on the current stream (rotated weights).
-    def one(wt, i):
-        s = i % R
-        if wt == vq.Q4_K:
-            vq.gemv(vq.Q4_K, Qa[s], 9728, 2560, xa, y=ya[s])
-        else:
-            vq.gemv(vq.Q6_K, Qb[s], 2560, 9728, xb, y=yb[s])
-
-    ka = time_launches(lambda i: one(vq.Q4_K, i), args.steps)
-    kb = time_launches(lambda i: one(vq.Q6_K, i), args.steps)
+    # The timed steps replay a HIP graph holding one step per rotation set.
+    ms, steps_timed = time_graph(step, R, args.steps, warmup=max(2, args.warmup // R))
+    # Per-kernel average launch duration: the same, with one kernel per node.
+    ka, _ = time_graph(lambda i: vq.gemv(vq.Q4_K, Qa[i % R], 9728, 2560, xa, y=ya[i % R]), R, args.steps)
+    kb, _ = time_graph(lambda i: vq.gemv(vq.Q6_K, Qb[i % R], 2560, 9728, xb, y=yb[i % R]), R, args.steps)
     assert torch.isfinite(ya[0]).all() and torch.isfinite(yb[0]).all()
     return {"ms_per_step": ms, "q4k_ms": ka, "q6k_ms": kb, "rotation_sets": R, "steps_timed": steps_timed,
             "rotation_mb": round(R * set_bytes / (1 << 20), 1)}
@@ -212,9 +207,9 @@ def run_prefill(torch, vq, synth, iters):
         qi = vq.quantize_act(vq.Q8_K, Xi)
         Yg = torch.empty((M, 9728), dtype=torch.float32, device=dev)
         Yd = torch.empty((M, 2560), dtype=torch.float32, device=dev)
-        tg = time_launches(lambda i: vq.gemm(vq.Q4_K, Qg, 9728, 2560, vq.Q8_K, qh, M, Y=Yg), iters)
-        td = time_launches(lambda i: vq.gemm(vq.Q6_K, Qd, 2560, 9728, vq.Q8_K, qi, M, Y=Yd), iters)
-        tq = time_launches(lambda i: vq.quantize_act(vq.Q8_K, Xh, Xq=qh), iters)
+        tg, _ = time_graph(lambda i: vq.gemm(vq.Q4_K, Qg, 9728, 2560, vq.Q8_K, qh, M, Y=Yg), 4, iters)
+        td, _ = time_graph(lambda i: vq.gemm(vq.Q6_K, Qd, 2560, 9728, vq.Q8_K, qi, M, Y=Yd), 4, iters)
+        tq, _ = time_graph(lambda i: vq.quantize_act(vq.Q8_K, Xh, Xq=qh), 8, iters)
         ops = 2.0 * M * 9728 * 2560
         out["M%d" % M] = {
             "q4k_gate_us": round(tg * 1e3, 2), "q4k_tops": round(ops / (tg * 1e-3) / 1e12, 1),
@@ -235,11 +230,11 @@ def run_q8_0(torch, vq, synth, iters):
     X = torch.from_numpy(synth.tensor("q8_0_gemm", "X")).to(dev)
     Xq = vq.quantize_act(vq.Q8_1, X)
     Y = torch.empty((2048, 4096), dtype=torch.float32, device=dev)
-    t = time_launches(lambda i: vq.gemm(vq.Q8_0, Q, 4096, 2048, vq.Q8_1, Xq, 2048, Y=Y), iters)
+    t, _ = time_graph(lambda i: vq.gemm(vq.Q8_0, Q, 4096, 2048, vq.Q8_1, Xq, 2048, Y=Y), 4, iters)
     R = max(2, math.ceil(640 * (1 << 20) / Q.numel()))
     Qs = [Q] + [Q.clone() for _ in range(R - 1)]
     y = torch.empty(4096, dtype=torch.float32, device=dev)
-    tv = time_launches(lambda i: vq.gemv(vq.Q8_0, Qs[i % R], 4096, 2048, X[0], y=y), 200)
+    tv, _ = time_graph(lambda i: vq.gemv(vq.Q8_0, Qs[i % R], 4096, 2048, X[0], y=y), R, 200)
     ops = 2.0 * 2048 * 4096 * 2048
     gbytes = Q.numel() + 4 * 2048 + 4 * 4096
     return {"gemm_M2048_us": round(t * 1e3, 2), "gemm_tops": round(ops / (t * 1e-3) / 1e12, 1),
@@ -273,8 +268,8 @@ def run_grouped(torch, vq, synth, iters):
         vq.gemm_grouped(vq.Q4_K, sets[i % len(sets)], E, N, K, vq.Q8_K, Xq, T, ids, top_k, route_w=rw,
                         Y=Y, Ysum=S, ws=ws)
 
-    t_cold = time_launches(lambda i: call(i, Qs), iters)
-    t_warm = time_launches(lambda i: call(i, [Q0]), iters)
+    t_cold, _ = time_graph(lambda i: call(i, Qs), R, iters)
+    t_warm, _ = time_graph(lambda i: call(i, [Q0]), 4, iters)
     ops = 2.0 * T * top_k * N * K
     alg = Q0.numel() + Xq.numel() + Y.numel() * 4 + S.numel() * 4 + T * top_k * 8
     return {"route_gemm_sum_us_cold": round(t_cold * 1e3, 2),

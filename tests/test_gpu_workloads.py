@@ -1,0 +1,184 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times (needs an MI355X).
+
+Weights are encoded on the host by the oracle and uploaded (the GPU encoder's
+bytes are checked equal to them separately), activations are quantized on the
+GPU and checked byte for byte against the oracle's, and the outputs are
+compared bit for bit with the oracle's fixed-order binary32 definition: in
+full where the oracle finishes in seconds (the decode GEMVs, routing, the
+weighted sum), otherwise on sampled outputs (whole first and last rows and
+columns plus random positions).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import ref_fp64
+import synth
+from tests import gpu_helpers as H
+from tests.conftest import gpu_available
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+import block_quantized_matmul_fp32_amd as vq  # noqa: E402
+
+THREADS = min(16, oracle.default_threads())
+
+
+def sample_positions(M, N, n_random, seed):
+    """(ms, ns): row 0, row M-1, column 0, column N-1 in full, and random cells."""
+    rng = np.random.default_rng(seed)
+    ms = [np.zeros(N, np.int64), np.full(N, M - 1, np.int64), np.arange(M), np.arange(M),
+          rng.integers(0, M, n_random)]
+    ns = [np.arange(N), np.arange(N), np.zeros(M, np.int64), np.full(M, N - 1, np.int64),
+          rng.integers(0, N, n_random)]
+    return np.concatenate(ms).astype(np.int64), np.concatenate(ns).astype(np.int64)
+
+
+def check_act_bytes(wtype, Xq_dev, X):
+    M, K = X.shape
+    buf = H.host(Xq_dev)
+    if wtype == oracle.Q8_0:
+        ref = oracle.quantize_q8_1(X)
+        qs, d, s = H.planes_q8_1(buf, M, K)
+        assert np.array_equal(qs, ref.qs) and np.array_equal(d, ref.d) and np.array_equal(s, ref.s)
+    else:
+        ref = oracle.quantize_q8k(X)
+        qs, d, bs = H.planes_q8k(buf, M, K)
+        assert np.array_equal(qs, ref.qs)
+        assert np.array_equal(d.view(np.uint32), ref.d.view(np.uint32))
+        assert np.array_equal(bs, ref.bsums)
+    return ref
+
+
+def test_tiny_q4k_gemm_full():
+    """8 x 1024 activations against a [256, 1024] Q4_K matrix, every output."""
+    W = synth.tensor("tiny_q4k_gemm", "W")
+    X = synth.tensor("tiny_q4k_gemm", "X")
+    N, K = W.shape
+    M = X.shape[0]
+    Wq = oracle.quantize_weights(oracle.Q4_K, W)
+    H.say("tiny Q4_K GEMM M=%d N=%d K=%d" % (M, N, K))
+    Wd = H.to_dev(W)
+    assert np.array_equal(H.host(vq.quantize_weights(vq.Q4_K, Wd)), Wq.reshape(-1))
+    Xq = vq.quantize_act(vq.Q8_K, H.to_dev(X))
+    act = check_act_bytes(oracle.Q4_K, Xq, X)
+    Y = vq.gemm(vq.Q4_K, H.to_dev(Wq), N, K, vq.Q8_K, Xq, M,
+                Y=H.to_dev(np.full((M, N), np.nan, np.float32)))
+    H.assert_bitwise(H.host(Y), oracle.gemm(oracle.Q4_K, Wq, N, K, act), "tiny GEMM")
+
+
+@pytest.mark.parametrize("which", ["Q4_K", "Q6_K"])
+def test_decode_gemv_full(which):
+    """The decode step's GEMVs at [9728, 2560] (Q4_K) and [2560, 9728] (Q6_K),
+    fused Q8_K quantizer, every output."""
+    wtype = oracle.Q4_K if which == "Q4_K" else oracle.Q6_K
+    wn, xn = ("Wa", "xa") if which == "Q4_K" else ("Wb", "xb")
+    W = synth.tensor("decode_gemv", wn)
+    x = synth.tensor("decode_gemv", xn)
+    N, K = W.shape
+    Wq = oracle.quantize_weights(wtype, W)
+    H.say("decode GEMV %s N=%d K=%d" % (which, N, K))
+    Wd = H.to_dev(W)
+    assert np.array_equal(H.host(vq.quantize_weights(wtype, Wd)), Wq.reshape(-1)), "encoder bytes"
+    del Wd
+    xq = H.to_dev(np.zeros(vq.act_bytes(vq.Q8_K, 1, K), np.uint8))
+    y = vq.gemv(wtype, H.to_dev(Wq), N, K, H.to_dev(x), y=H.to_dev(np.full(N, np.nan, np.float32)),
+                xq_out=xq)
+    act = check_act_bytes(wtype, xq, x[None, :])
+    ref = oracle.gemm(wtype, Wq, N, K, act, nthreads=THREADS)[0]
+    yh = H.host(y)
+    H.assert_bitwise(yh, ref, "decode GEMV " + which)
+    r64 = ref_fp64.gemm_fp64(wtype, Wq, N, K, act)[0]
+    assert ref_fp64.max_rel_err(yh, r64)[0] <= 5e-4
+    assert ref_fp64.nmse(yh, ref) <= 1e-6
+
+
+def test_q8_0_gemv_full():
+    """Q8_0 [4096, 2048] against row 0 of the Q8_0 workload's X, fused Q8_1."""
+    W = synth.tensor("q8_0_gemm", "W")
+    x = synth.tensor("q8_0_gemm", "X")[0]
+    N, K = W.shape
+    Wq = oracle.quantize_weights(oracle.Q8_0, W)
+    H.say("Q8_0 GEMV N=%d K=%d" % (N, K))
+    xq = H.to_dev(np.zeros(vq.act_bytes(vq.Q8_1, 1, K), np.uint8))
+    y = vq.gemv(vq.Q8_0, H.to_dev(Wq), N, K, H.to_dev(x), xq_out=xq)
+    act = check_act_bytes(oracle.Q8_0, xq, x[None, :])
+    H.assert_bitwise(H.host(y), oracle.gemm(oracle.Q8_0, Wq, N, K, act, nthreads=THREADS)[0], "Q8_0 GEMV")
+
+
+@pytest.mark.parametrize("M", [512, 2048])
+@pytest.mark.parametrize("which", ["gate_Q4_K", "down_Q6_K"])
+def test_prefill_gemm_sampled(which, M):
+    """The prefill GEMMs at M in {512, 2048}: activation bytes in full, outputs
+    on whole edge rows/columns and random cells."""
+    if which == "gate_Q4_K":
+        wtype, W, X = oracle.Q4_K, synth.tensor("prefill_gemm", "Wgate"), synth.prefill_activations("Xh", M)
+    else:
+        wtype, W, X = oracle.Q6_K, synth.tensor("prefill_gemm", "Wdown"), synth.prefill_activations("Xi", M)
+    N, K = W.shape
+    Wq = oracle.quantize_weights(wtype, W)
+    del W
+    H.say("prefill GEMM %s M=%d N=%d K=%d" % (which, M, N, K))
+    Xq = vq.quantize_act(vq.Q8_K, H.to_dev(X))
+    act = check_act_bytes(wtype, Xq, X)
+    Y = vq.gemm(wtype, H.to_dev(Wq), N, K, vq.Q8_K, Xq, M,
+                Y=H.to_dev(np.full((M, N), np.nan, np.float32)))
+    Yh = H.host(Y)
+    assert np.isfinite(Yh).all(), "every output written"
+    ms, ns = sample_positions(M, N, 20000, 7000 + M)
+    ref = oracle.gemm_sampled(wtype, Wq, N, K, act, ms, ns, nthreads=THREADS)
+    H.assert_bitwise(Yh[ms, ns], ref, "prefill %s M=%d" % (which, M))
+
+
+def test_q8_0_gemm_sampled():
+    """Q8_0 [4096, 2048] x Q8_1 activations at M = 2048."""
+    W = synth.tensor("q8_0_gemm", "W")
+    X = synth.tensor("q8_0_gemm", "X")
+    N, K = W.shape
+    M = X.shape[0]
+    Wq = oracle.quantize_weights(oracle.Q8_0, W)
+    H.say("Q8_0 GEMM M=%d N=%d K=%d" % (M, N, K))
+    Xq = vq.quantize_act(vq.Q8_1, H.to_dev(X))
+    act = check_act_bytes(oracle.Q8_0, Xq, X)
+    Y = vq.gemm(vq.Q8_0, H.to_dev(Wq), N, K, vq.Q8_1, Xq, M,
+                Y=H.to_dev(np.full((M, N), np.nan, np.float32)))
+    Yh = H.host(Y)
+    assert np.isfinite(Yh).all()
+    ms, ns = sample_positions(M, N, 20000, 7100)
+    ref = oracle.gemm_sampled(oracle.Q8_0, Wq, N, K, act, ms, ns, nthreads=THREADS)
+    H.assert_bitwise(Yh[ms, ns], ref, "Q8_0 GEMM")
+
+
+def test_grouped_moe_full_size():
+    """256 experts of Q4_K [512, 2048], 2048 tokens, top-8 routing: routing
+    bitwise in full, Y on sampled tokens, Ysum bitwise in full against the
+    oracle's weighted sum of the GPU's Y."""
+    cfg = synth.WORKLOADS["grouped_moe"]
+    E, N, K, T, top_k = cfg["E"], cfg["N"], cfg["K"], cfg["T"], cfg["top_k"]
+    Wq = np.concatenate([oracle.quantize_weights(oracle.Q4_K, synth.expert_weights(e, N, K))
+                         for e in range(E)])
+    X = synth.tensor("grouped_moe", "X")
+    ids, rw = synth.routing(T, E, top_k)
+    H.say("grouped MoE E=%d N=%d K=%d T=%d top_k=%d" % (E, N, K, T, top_k))
+    for e in (0, E - 1):
+        We = H.to_dev(synth.expert_weights(e, N, K))
+        assert np.array_equal(H.host(vq.quantize_weights(vq.Q4_K, We)), Wq[e * N:(e + 1) * N].reshape(-1))
+    Xq = vq.quantize_act(vq.Q8_K, H.to_dev(X))
+    Y, S, ws = vq.gemm_grouped(vq.Q4_K, H.to_dev(Wq), E, N, K, vq.Q8_K, Xq, T, H.to_dev(ids), top_k,
+                               route_w=H.to_dev(rw),
+                               Y=H.to_dev(np.full((T, top_k, N), np.nan, np.float32)),
+                               Ysum=H.to_dev(np.full((T, N), np.nan, np.float32)))
+    counts, offsets, lst = vq.grouped_ws_views(ws, E, T, top_k)
+    c_ref, o_ref, l_ref = oracle.route(ids, E)
+    assert np.array_equal(H.host(counts), c_ref)
+    assert np.array_equal(H.host(offsets), o_ref)
+    assert np.array_equal(H.host(lst), l_ref)
+    Yh = H.host(Y)
+    assert np.isfinite(Yh).all(), "every (t, s) row written"
+    toks = np.unique(np.concatenate([[0, 1, T - 1], np.random.default_rng(7200).integers(0, T, 29)]))
+    act_s = oracle.quantize_q8k(X[toks])
+    Y_ref = oracle.gemm_grouped(oracle.Q4_K, Wq, E, N, K, act_s, ids[toks], nthreads=THREADS)
+    H.assert_bitwise(Yh[toks], Y_ref, "grouped Y (sampled tokens)")
+    H.assert_bitwise(H.host(S), oracle.weighted_sum(Yh, rw), "Ysum")
