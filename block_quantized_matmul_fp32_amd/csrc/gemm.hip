@@ -39,6 +39,7 @@ namespace vqk {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u4v __attribute__((ext_vector_type(4)));  // native vector: plain loads and stores
 
 constexpr int kBN = 64;   // weight rows per workgroup
 constexpr int kKS = 256;  // K per step
@@ -100,21 +101,29 @@ struct GroupArgs {
     int64_t expert_stride;  // bytes of one expert's [N][K/256] blocks
 };
 
-template <int WT, int BM, bool kGrouped>
-__global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ Wbase, int N, int K,
-                                                   int64_t wbytes, const int8_t* __restrict__ aqs,
-                                                   const void* __restrict__ ad,
-                                                   const int16_t* __restrict__ abs_, int M,
-                                                   float* __restrict__ Y, int64_t ldy,
-                                                   GroupArgs ga) {
+// Workgroup of 2 x WM waves (128 * WM threads) computing a 64 x (16 * TM * WM)
+// output tile; each wave owns 32 weight rows x 16 * TM activation rows
+// (2 x TM MFMA tiles of 16 x 16).  A weight row's step (one super-block, or eight
+// Q8_0 blocks) is unpacked by 2 * WM threads, each taking 8 / (2 * WM) of
+// its eight 16-byte pieces, so the unpack cost per output falls as WM grows.
+template <int WT, int WM, int TM, bool kGrouped>
+__global__ __launch_bounds__(128 * WM, 2) void gemm_kernel(const uint8_t* __restrict__ Wbase, int N, int K,
+                                                           int64_t wbytes, const int8_t* __restrict__ aqs,
+                                                           const void* __restrict__ ad,
+                                                           const int16_t* __restrict__ abs_, int M,
+                                                           float* __restrict__ Y, int64_t ldy,
+                                                           GroupArgs ga) {
     constexpr int P = GemmCfg<WT>::P;
     constexpr int BB = GemmCfg<WT>::BB;
-    constexpr int TM = BM / 32;            // 16-row activation tiles per wave
-    constexpr int ACH = BM * 16 / 256;     // 16-byte activation chunks per thread per step
+    constexpr int NT = 128 * WM;           // threads
+    constexpr int BM = 16 * TM * WM;       // activation rows per workgroup
+    constexpr int ACH = BM * 16 / NT;      // 16-byte activation chunks per thread per step
+    constexpr int UPR = NT / kBN;          // threads per weight row
+    constexpr int PPT = 8 / UPR;           // 16-byte pieces per thread
     __shared__ __attribute__((aligned(16))) int8_t sA[BM * kLD];
     __shared__ __attribute__((aligned(16))) int8_t sW[P * kBN * kLD];
-    __shared__ __attribute__((aligned(16))) float sDa[BM * 8];
-    __shared__ __attribute__((aligned(16))) float sDw[kBN * 8];
+    __shared__ __attribute__((aligned(16))) float sDa[(WT == 2) ? BM * 8 : BM];
+    __shared__ __attribute__((aligned(16))) float sDw[(WT == 2) ? kBN * 8 : 2 * kBN];
     __shared__ __attribute__((aligned(16))) int8_t sMw[kBN * 8];
     __shared__ __attribute__((aligned(16))) int8_t sHl[BM * 16];
     __shared__ int sRow[BM];    // activation row of each tile row (-1: none)
@@ -122,19 +131,18 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ W
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wn = wave & 1, wm = wave >> 1;
     const int r16 = lane & 15, g = lane >> 4;
     const int n0 = blockIdx.x * kBN;
 
     const uint8_t* W = Wbase;
-    int rows_here = BM;
     if (kGrouped) {
         const int tix = blockIdx.y;
         if (tix >= *ga.ntiles) return;
         const int e = ga.tiles[4 * tix + 0];
         const int first = ga.tiles[4 * tix + 1];
-        rows_here = ga.tiles[4 * tix + 2];
+        const int rows_here = ga.tiles[4 * tix + 2];
         W = Wbase + (int64_t)e * ga.expert_stride;
         if (tid < BM) {
             if (tid < rows_here) {
@@ -161,95 +169,96 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ W
     const uint8_t* wend = Wbase + wbytes;
     const int nsteps = (K + kKS - 1) / kKS;
 
-    // Per-thread load roles.
-    const int wrow = tid >> 2, wq = tid & 3;            // weight unpack: row, quarter
-    const bool wvalid = (n0 + wrow) < N;
-    const uint8_t* wrow_p = W + (int64_t)(n0 + wrow) * rb;
+    // Activation chunks of this thread: row (tid >> 4) + (NT / 16) * i, bytes
+    // 16 * (tid & 15) of each step.  Rows past the tile read activation row 0
+    // (their outputs are never stored).
+    const int acol = 16 * (tid & 15);
+    const int8_t* ap[ACH];
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) {
+        const int ar = sRow[(tid >> 4) + (NT / 16) * i];
+        ap[i] = aqs + (int64_t)(ar >= 0 ? ar : 0) * K + acol;
+    }
+    const int my_ar = (tid < BM) ? sRow[tid] : -1;  // scale row of threads < BM
+
+    // Weight unpack role: row wr, pieces [PPT * wu, PPT * wu + PPT).
+    const int wr = tid / UPR, wu = tid % UPR;
+    const bool wvalid = (n0 + wr) < N;
+    const uint8_t* wrow_p = W + (int64_t)(wvalid ? n0 + wr : 0) * rb;
 
     // Register-staged global data of one step.
-    uint4 regA[ACH];
-    uint32_t regW[24];
-    float regDa[2];
+    u4v regA[ACH];
+    constexpr int SCW = (PPT + 1) / 2;     // Q6_K: words of per-piece scale byte pairs
+    uint32_t regW[(WT == 0) ? 4 + 4 * PPT : ((WT == 1) ? 8 * PPT + SCW + 1 : 9 * PPT)];
+    float regDa;
     uint4 regBs[2];
 
-    auto load_step = [&](int s) {
-        // activation qs tile: BM rows x 256 bytes
+    // part < 0: every load of step s; part 0..3: a quarter of the activation
+    // chunks, plus the scales (part 0) or the weights (part 1), so that the
+    // next step's loads can be spread between the current step's MFMAs.
+    auto load_step = [&](int s, int part) __attribute__((always_inline)) {
+        const int kk = s * kKS;
 #pragma unroll
         for (int i = 0; i < ACH; ++i) {
-            const int c = tid + 256 * i;
-            const int row = c >> 4, col = (c & 15) * 16;
-            const int ar = sRow[row];
-            const int kk = s * kKS + col;
-            if (ar >= 0 && kk < K)
-                regA[i] = *(const uint4*)(aqs + (int64_t)ar * K + kk);
+            if (part >= 0 && (i * 4 / ACH) != part) continue;
+            if (WT != 2 || kk + acol < K)
+                regA[i] = *(const u4v*)(ap[i] + kk);
             else
-                regA[i] = make_uint4(0, 0, 0, 0);
+                regA[i] = (u4v){0u, 0u, 0u, 0u};
         }
-        // activation scales
-        if (WT == 2) {
-            // Q8_1: binary16 d of the step's 8 blocks; threads < BM, one row each
-            if (tid < BM) {
-                const int ar = sRow[tid];
-                const uint16_t* dp = (const uint16_t*)ad;
+        if (part > 1) return;
+        if (part <= 0 && tid < BM) {
+            const int ar = my_ar >= 0 ? my_ar : 0;
+            if (WT == 2) {
+                const uint16_t* dp = (const uint16_t*)ad + (int64_t)ar * nbw;
                 uint32_t h[8];
 #pragma unroll
                 for (int b = 0; b < 8; ++b) {
                     const int blk = s * 8 + b;
-                    h[b] = (ar >= 0 && blk < nbw) ? dp[(int64_t)ar * nbw + blk] : 0u;
+                    h[b] = (blk < nbw) ? dp[blk] : 0u;
                 }
                 regBs[0] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
                                       h[6] | (h[7] << 16));
-            }
-        } else {
-            if (tid < BM) {
-                const int ar = sRow[tid];
-                regDa[0] = (ar >= 0) ? ((const float*)ad)[(int64_t)ar * nbw + s] : 0.0f;
+            } else {
+                regDa = ((const float*)ad)[(int64_t)ar * nbw + s];
                 if (WT == 0) {
-                    if (ar >= 0) {
-                        const uint4* bp = (const uint4*)(abs_ + ((int64_t)ar * nbw + s) * 16);
-                        regBs[0] = bp[0];
-                        regBs[1] = bp[1];
-                    } else {
-                        regBs[0] = regBs[1] = make_uint4(0, 0, 0, 0);
-                    }
+                    const uint4* bp = (const uint4*)(abs_ + ((int64_t)ar * nbw + s) * 16);
+                    regBs[0] = bp[0];
+                    regBs[1] = bp[1];
                 }
             }
         }
-        // weights
+        if (part == 0) return;
         if (WT == 0) {
-            if (wvalid) {
-                const uint8_t* bp = wrow_p + (int64_t)s * kQ4KBytes;
-                const uint4 h = *(const uint4*)bp;
-                const uint4 q0 = *(const uint4*)(bp + 16 + 32 * wq);
-                const uint4 q1 = *(const uint4*)(bp + 32 + 32 * wq);
-                regW[0] = h.x; regW[1] = h.y; regW[2] = h.z; regW[3] = h.w;
-                regW[4] = q0.x; regW[5] = q0.y; regW[6] = q0.z; regW[7] = q0.w;
-                regW[8] = q1.x; regW[9] = q1.y; regW[10] = q1.z; regW[11] = q1.w;
-            } else {
+            const uint8_t* bp = wrow_p + (int64_t)s * kQ4KBytes;
+            const uint4 h = *(const uint4*)bp;
+            regW[0] = h.x; regW[1] = h.y; regW[2] = h.z; regW[3] = h.w;
 #pragma unroll
-                for (int i = 0; i < 12; ++i) regW[i] = 0;
+            for (int j = 0; j < PPT; ++j) {
+                const uint4 q = *(const uint4*)(bp + 16 + 16 * (PPT * wu + j));
+                regW[4 + 4 * j] = q.x; regW[5 + 4 * j] = q.y; regW[6 + 4 * j] = q.z; regW[7 + 4 * j] = q.w;
             }
         } else if (WT == 1) {
-            if (wvalid) {
-                const uint8_t* bp = wrow_p + (int64_t)s * kQ6KBytes;
-                gload16_a2(bp + 16 * wq, wend, regW + 0);             // ql, half 0
-                gload16_a2(bp + 64 + 16 * wq, wend, regW + 4);        // ql, half 1
-                gload16_a2(bp + 128 + 16 * (wq & 1), wend, regW + 8); // qh, half 0
-                gload16_a2(bp + 160 + 16 * (wq & 1), wend, regW + 12);// qh, half 1
-                const int8_t* sp = (const int8_t*)(bp + 192);
-                regW[16] = (uint32_t)(uint8_t)sp[wq] | ((uint32_t)(uint8_t)sp[4 + wq] << 8) |
-                           ((uint32_t)(uint8_t)sp[8 + wq] << 16) | ((uint32_t)(uint8_t)sp[12 + wq] << 24);
-                regW[17] = *(const uint16_t*)(bp + 208);
-            } else {
+            const uint8_t* bp = wrow_p + (int64_t)s * kQ6KBytes;
+            uint32_t scw[SCW];
 #pragma unroll
-                for (int i = 0; i < 18; ++i) regW[i] = 0;
+            for (int k = 0; k < SCW; ++k) scw[k] = 0;
+#pragma unroll
+            for (int j = 0; j < PPT; ++j) {
+                const int pc = PPT * wu + j, h = pc >> 2, v = pc & 3;
+                gload16_a2(bp + 64 * h + 16 * v, wend, regW + 8 * j);                  // ql
+                gload16_a2(bp + 128 + 32 * h + 16 * (v & 1), wend, regW + 8 * j + 4);  // qh
+                const uint32_t sa = bp[192 + 8 * h + v], sb = bp[196 + 8 * h + v];
+                scw[j >> 1] |= (sa | (sb << 8)) << (16 * (j & 1));
             }
-        } else {
-            // Q8_0: two 34-byte blocks (8s + 2wq, 8s + 2wq + 1) per thread
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int blk = s * 8 + 2 * wq + j;
-                if (wvalid && blk < nbw) {
+            for (int k = 0; k < SCW; ++k) regW[8 * PPT + k] = scw[k];
+            regW[8 * PPT + SCW] = *(const uint16_t*)(bp + 208);
+        } else {
+#pragma unroll
+            for (int j = 0; j < PPT; ++j) {
+                const int blk = s * 8 + PPT * wu + j;
+                if (blk < nbw) {
                     const uint8_t* bp = wrow_p + (int64_t)blk * kQ80Bytes;
                     gload16_a2(bp + 2, wend, regW + 9 * j);
                     gload16_a2(bp + 18, wend, regW + 9 * j + 4);
@@ -262,113 +271,120 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ W
         }
     };
 
-    auto store_step = [&]() {
+    auto store_step = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < ACH; ++i) {
-            const int c = tid + 256 * i;
-            const int row = c >> 4, col = (c & 15) * 16;
-            *(uint4*)(sA + row * kLD + col) = regA[i];
-        }
-        if (WT == 2) {
-            if (tid < BM) {
+        for (int i = 0; i < ACH; ++i)
+            *(u4v*)(sA + ((tid >> 4) + (NT / 16) * i) * kLD + acol) = regA[i];
+        if (tid < BM) {
+            if (WT == 2) {
                 const uint32_t hw[4] = {regBs[0].x, regBs[0].y, regBs[0].z, regBs[0].w};
 #pragma unroll
                 for (int b = 0; b < 8; ++b)
                     sDa[tid * 8 + b] = half_bits_to_float((hw[b >> 1] >> (16 * (b & 1))) & 0xFFFF);
-            }
-        } else if (tid < BM) {
-            sDa[tid] = regDa[0];
-            if (WT == 0) {
-                const uint32_t bw[8] = {regBs[0].x, regBs[0].y, regBs[0].z, regBs[0].w,
-                                        regBs[1].x, regBs[1].y, regBs[1].z, regBs[1].w};
-                uint32_t hh[2] = {0, 0}, ll[2] = {0, 0};
+            } else {
+                sDa[tid] = regDa;
+                if (WT == 0) {
+                    // bs32_j = bsums[2j] + bsums[2j+1] = 64 * h + l, 0 <= l < 64 (int8 operands)
+                    const uint32_t bw[8] = {regBs[0].x, regBs[0].y, regBs[0].z, regBs[0].w,
+                                            regBs[1].x, regBs[1].y, regBs[1].z, regBs[1].w};
+                    uint32_t hh[2] = {0, 0}, ll[2] = {0, 0};
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int b0 = (int)(int16_t)(bw[j] & 0xFFFF);
-                    const int b1 = (int)(int16_t)(bw[j] >> 16);
-                    const int bs32 = b0 + b1;
-                    const int h = bs32 >> 6, l = bs32 & 63;
-                    hh[j >> 2] |= ((uint32_t)(h & 0xFF)) << (8 * (j & 3));
-                    ll[j >> 2] |= ((uint32_t)l) << (8 * (j & 3));
+                    for (int j = 0; j < 8; ++j) {
+                        const int bs32 = (int)(int16_t)(bw[j] & 0xFFFF) + (int)(int16_t)(bw[j] >> 16);
+                        hh[j >> 2] |= ((uint32_t)((bs32 >> 6) & 0xFF)) << (8 * (j & 3));
+                        ll[j >> 2] |= ((uint32_t)(bs32 & 63)) << (8 * (j & 3));
+                    }
+                    *(uint4*)(sHl + tid * 16) = make_uint4(hh[0], hh[1], ll[0], ll[1]);
                 }
-                *(uint4*)(sHl + tid * 16) = make_uint4(hh[0], hh[1], ll[0], ll[1]);
             }
         }
+        int8_t* wdst = sW + wr * kLD;
         if (WT == 0) {
-            const uint32_t sw = (wq < 2) ? regW[1] : regW[2];
-            const uint32_t s_lo = (sw >> (16 * (wq & 1))) & 0xFF;
-            const uint32_t s_hi = (sw >> (16 * (wq & 1) + 8)) & 0xFF;
-            const int sc0 = s_lo & 63, sc1 = s_hi & 63;
-            const int fa[2] = {sc0 & 7, sc0 >> 3};
-            const int fb[2] = {sc1 & 7, sc1 >> 3};
+            // piece pc = 16 qs bytes at 16 * pc: low nibbles are values
+            // 64c + 16hf + i (sub-block 2c), high nibbles 64c + 32 + 16hf + i
+            // (sub-block 2c + 1), c = pc / 2, hf = pc % 2.  Plane 0 holds
+            // q * (sc & 7), plane 1 q * (sc >> 3).
 #pragma unroll
-            for (int p = 0; p < 2; ++p) {
-                uint32_t lo[8], hi[8];
+            for (int j = 0; j < PPT; ++j) {
+                const int pc = PPT * wu + j, c = pc >> 1, hf = pc & 1;
+                const uint32_t sw = (c < 2) ? regW[1] : regW[2];
+                const int sh = 16 * (c & 1);
+                const int scl = (int)((sw >> sh) & 63), sch = (int)((sw >> (sh + 8)) & 63);
+                const int fl[2] = {scl & 7, scl >> 3};
+                const int fh[2] = {sch & 7, sch >> 3};
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const uint32_t q = regW[4 + i];
-                    lo[i] = bytes_mul(q & 0x0F0F0F0Fu, fa[p]);
-                    hi[i] = bytes_mul((q >> 4) & 0x0F0F0F0Fu, fb[p]);
+                for (int p = 0; p < 2; ++p) {
+                    uint32_t lo[4], hi[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t q = regW[4 + 4 * j + i];
+                        lo[i] = bytes_mul(q & 0x0F0F0F0Fu, fl[p]);
+                        hi[i] = bytes_mul((q >> 4) & 0x0F0F0F0Fu, fh[p]);
+                    }
+                    int8_t* dst = wdst + p * kBN * kLD + 64 * c + 16 * hf;
+                    *(uint4*)dst = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+                    *(uint4*)(dst + 32) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
                 }
-                int8_t* dst = sW + (p * kBN + wrow) * kLD + 64 * wq;
-                *(uint4*)(dst + 0) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-                *(uint4*)(dst + 16) = make_uint4(lo[4], lo[5], lo[6], lo[7]);
-                *(uint4*)(dst + 32) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-                *(uint4*)(dst + 48) = make_uint4(hi[4], hi[5], hi[6], hi[7]);
             }
-            if (wq == 0) {
-                sDw[wrow] = half_bits_to_float(regW[0] & 0xFFFF);
-                sDw[kBN + wrow] = half_bits_to_float(regW[0] >> 16);
+            if (wu == 0) {
+                sDw[wr] = half_bits_to_float(regW[0] & 0xFFFF);
+                sDw[kBN + wr] = half_bits_to_float(regW[0] >> 16);
                 // mins: m_j = (scales[j] >> 6) | (nibble j&1 of scales[8 + j/2]) << 2
                 uint32_t mw[2] = {0, 0};
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const uint32_t sj = ((j < 4 ? regW[1] : regW[2]) >> (8 * (j & 3))) & 0xFF;
-                    const uint32_t nb_ = (regW[3] >> (8 * (j >> 1) + 4 * (j & 1))) & 15;
-                    const uint32_t m = (sj >> 6) | (nb_ << 2);
-                    mw[j >> 2] |= m << (8 * (j & 3));
+                    const uint32_t nb_ = (regW[3] >> (4 * j)) & 15;
+                    mw[j >> 2] |= ((sj >> 6) | (nb_ << 2)) << (8 * (j & 3));
                 }
-                *(uint2*)(sMw + wrow * 8) = make_uint2(mw[0], mw[1]);
+                *(uint2*)(sMw + wr * 8) = make_uint2(mw[0], mw[1]);
             }
         } else if (WT == 1) {
-            // runs: (h, lo/hi nibble) -> elements 128h + 64*hi + 16*wq, sub-block 8h + 4*hi + wq
+            // piece pc = (h, v): ql bytes 64h + 16v.. hold values 128h + 16v + i
+            // (low nibbles, sub-block 8h + v) and 128h + 64 + 16v + i (high,
+            // sub-block 8h + 4 + v); their top bits are pairs v/2 and 2 + v/2
+            // of qh bytes 32h + 16(v % 2) + i.  Planes: the base-8 digits
+            // (each in [-3, 4]) of the int8 scale times (q - 32).
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
+            for (int j = 0; j < PPT; ++j) {
+                const int pc = PPT * wu + j, h = pc >> 2, v = pc & 3;
+                const int sa = 2 * (v >> 1);
+                const uint32_t scp = (regW[8 * PPT + (j >> 1)] >> (16 * (j & 1))) & 0xFFFF;
 #pragma unroll
                 for (int part = 0; part < 2; ++part) {
-                    const int sc = (int)(int8_t)((regW[16] >> (8 * (2 * h + part))) & 0xFF);
+                    const int sc = (int)(int8_t)((scp >> (8 * part)) & 0xFF);
                     const int d0 = ((sc + 3) & 7) - 3;
                     const int t1 = (sc - d0) >> 3;
                     const int d1 = ((t1 + 3) & 7) - 3;
                     const int d2 = (t1 - d1) >> 3;
-                    const int sh = 2 * (2 * part + (wq >> 1));
                     uint32_t qs[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const uint32_t ql = regW[4 * h + i];
-                        const uint32_t qh = regW[8 + 4 * h + i];
-                        const uint32_t lo4 = part ? ((ql >> 4) & 0x0F0F0F0Fu) : (ql & 0x0F0F0F0Fu);
-                        qs[i] = bytes_sub32(lo4 | (((qh >> sh) & 0x03030303u) << 4));
+                        const uint32_t ql = regW[8 * j + i];
+                        const uint32_t qh = regW[8 * j + 4 + i];
+                        const uint32_t q6 = part ? (((ql >> 4) & 0x0F0F0F0Fu) | ((qh >> sa) & 0x30303030u))
+                                                 : ((ql & 0x0F0F0F0Fu) | ((qh << (4 - sa)) & 0x30303030u));
+                        qs[i] = bytes_sub32(q6);
                     }
                     const int dg[3] = {d0, d1, d2};
 #pragma unroll
                     for (int p = 0; p < 3; ++p) {
-                        int8_t* dst = sW + (p * kBN + wrow) * kLD + 128 * h + 64 * part + 16 * wq;
+                        int8_t* dst = wdst + p * kBN * kLD + 128 * h + 64 * part + 16 * v;
                         *(uint4*)dst = make_uint4(bytes_mul(qs[0], dg[p]), bytes_mul(qs[1], dg[p]),
                                                   bytes_mul(qs[2], dg[p]), bytes_mul(qs[3], dg[p]));
                     }
                 }
             }
-            if (wq == 0) sDw[wrow] = half_bits_to_float(regW[17] & 0xFFFF);
+            if (wu == 0) sDw[wr] = half_bits_to_float(regW[8 * PPT + SCW] & 0xFFFF);
         } else {
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int b = 2 * wq + j;
-                int8_t* dst = sW + wrow * kLD + 32 * b;
+            for (int j = 0; j < PPT; ++j) {
+                const int b = PPT * wu + j;
+                int8_t* dst = wdst + 32 * b;
                 *(uint4*)dst = make_uint4(regW[9 * j + 0], regW[9 * j + 1], regW[9 * j + 2], regW[9 * j + 3]);
                 *(uint4*)(dst + 16) =
                     make_uint4(regW[9 * j + 4], regW[9 * j + 5], regW[9 * j + 6], regW[9 * j + 7]);
-                sDw[wrow * 8 + b] = half_bits_to_float(regW[9 * j + 8] & 0xFFFF);
+                sDw[wr * 8 + b] = half_bits_to_float(regW[9 * j + 8] & 0xFFFF);
             }
         }
     };
@@ -381,14 +397,15 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ W
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[a][b][i] = 0.0f;
 
-    load_step(0);
+    const int wn0 = 32 * wn, wm0 = 16 * TM * wm;
+    load_step(0, -1);
     for (int s = 0; s < nsteps; ++s) {
         __syncthreads();
         store_step();
         __syncthreads();
-        if (s + 1 < nsteps) load_step(s + 1);
+        const bool more = s + 1 < nsteps;
+        if (WT == 2 && more) load_step(s + 1, -1);
 
-        const int wn0 = 32 * wn, wm0 = (BM / 2) * wm;
         if (WT == 2) {
             const int nval = min(8, nbw - 8 * s);
             for (int b = 0; b < nval; ++b) {
@@ -418,33 +435,89 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ W
                     }
                 }
             }
-        } else {
-            v4i pacc[2][TM][P];
+        } else if (WT == 1) {
+            // One accumulator per tile through the three digit planes:
+            // R = ((P2 << 3) + P1) << 3) + P0 = S, exact in int32.
+            v4i R[2][TM], bv[4][TM];
 #pragma unroll
             for (int tn = 0; tn < 2; ++tn)
 #pragma unroll
-                for (int tm = 0; tm < TM; ++tm)
+                for (int tm = 0; tm < TM; ++tm) R[tn][tm] = (v4i){0, 0, 0, 0};
 #pragma unroll
-                    for (int p = 0; p < P; ++p) pacc[tn][tm][p] = (v4i){0, 0, 0, 0};
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                v4i av[2][P], bv[TM];
-#pragma unroll
-                for (int tn = 0; tn < 2; ++tn)
-#pragma unroll
-                    for (int p = 0; p < P; ++p)
-                        av[tn][p] = *(const v4i*)(sW + (p * kBN + wn0 + 16 * tn + r16) * kLD + 64 * t + 16 * g);
+            for (int t = 0; t < 4; ++t)
 #pragma unroll
                 for (int tm = 0; tm < TM; ++tm)
-                    bv[tm] = *(const v4i*)(sA + (wm0 + 16 * tm + r16) * kLD + 64 * t + 16 * g);
+                    bv[t][tm] = *(const v4i*)(sA + (wm0 + 16 * tm + r16) * kLD + 64 * t + 16 * g);
 #pragma unroll
-                for (int tn = 0; tn < 2; ++tn)
+            for (int p = 2; p >= 0; --p) {
+                if (p < 2) {
 #pragma unroll
-                    for (int tm = 0; tm < TM; ++tm)
+                    for (int tn = 0; tn < 2; ++tn)
 #pragma unroll
-                        for (int p = 0; p < P; ++p)
-                            pacc[tn][tm][p] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[tn][p], bv[tm],
-                                                                                    pacc[tn][tm][p], 0, 0, 0);
+                        for (int tm = 0; tm < TM; ++tm) R[tn][tm] = R[tn][tm] << 3;
+                }
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    v4i av[2];
+#pragma unroll
+                    for (int tn = 0; tn < 2; ++tn)
+                        av[tn] = *(const v4i*)(sW + (p * kBN + wn0 + 16 * tn + r16) * kLD + 64 * t + 16 * g);
+#pragma unroll
+                    for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+                        for (int tm = 0; tm < TM; ++tm)
+                            R[tn][tm] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[tn], bv[t][tm], R[tn][tm], 0, 0, 0);
+                    if (p == 2 && more) load_step(s + 1, t);
+                }
+            }
+#pragma unroll
+            for (int tn = 0; tn < 2; ++tn) {
+                const float4 dv = *(const float4*)(sDw + wn0 + 16 * tn + 4 * g);
+                const float dd[4] = {dv.x, dv.y, dv.z, dv.w};
+#pragma unroll
+                for (int tm = 0; tm < TM; ++tm) {
+                    const float da = sDa[wm0 + 16 * tm + r16];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float t1 = dd[i] * (float)R[tn][tm][i];
+                        const float c = da * t1;
+                        acc[tn][tm][i] = acc[tn][tm][i] + c;
+                    }
+                }
+            }
+        } else {
+            // Q4_K: R = (P1 << 3) + P0 = S through one accumulator per tile.
+            v4i R[2][TM], bv[4][TM];
+#pragma unroll
+            for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+                for (int tm = 0; tm < TM; ++tm) R[tn][tm] = (v4i){0, 0, 0, 0};
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int tm = 0; tm < TM; ++tm)
+                    bv[t][tm] = *(const v4i*)(sA + (wm0 + 16 * tm + r16) * kLD + 64 * t + 16 * g);
+#pragma unroll
+            for (int p = 1; p >= 0; --p) {
+                if (p < 1) {
+#pragma unroll
+                    for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+                        for (int tm = 0; tm < TM; ++tm) R[tn][tm] = R[tn][tm] << 3;
+                }
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    v4i av[2];
+#pragma unroll
+                    for (int tn = 0; tn < 2; ++tn)
+                        av[tn] = *(const v4i*)(sW + (p * kBN + wn0 + 16 * tn + r16) * kLD + 64 * t + 16 * g);
+#pragma unroll
+                    for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+                        for (int tm = 0; tm < TM; ++tm)
+                            R[tn][tm] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[tn], bv[t][tm], R[tn][tm], 0, 0, 0);
+                    if (p == 1 && more) load_step(s + 1, t);
+                }
             }
             v4i mn[2][TM];
             if (WT == 0) {
@@ -475,26 +548,22 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ W
             for (int tn = 0; tn < 2; ++tn) {
                 const int nb4 = wn0 + 16 * tn + 4 * g;
                 const float4 dv = *(const float4*)(sDw + nb4);
-                const float4 dmv = *(const float4*)(sDw + kBN + nb4);
                 const float dd[4] = {dv.x, dv.y, dv.z, dv.w};
-                const float dm[4] = {dmv.x, dmv.y, dmv.z, dmv.w};
+                float dm[4] = {0.f, 0.f, 0.f, 0.f};
+                if (WT == 0) {
+                    const float4 dmv = *(const float4*)(sDw + kBN + nb4);
+                    dm[0] = dmv.x; dm[1] = dmv.y; dm[2] = dmv.z; dm[3] = dmv.w;
+                }
 #pragma unroll
                 for (int tm = 0; tm < TM; ++tm) {
                     const float da = sDa[wm0 + 16 * tm + r16];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         if (WT == 0) {
-                            const int S = (pacc[tn][tm][1][i] << 3) + pacc[tn][tm][0][i];
-                            const float t1 = dd[i] * (float)S;
+                            const float t1 = dd[i] * (float)R[tn][tm][i];
                             const float t2 = dm[i] * (float)mn[tn][tm][i];
                             const float t3 = t1 - t2;
                             const float c = da * t3;
-                            acc[tn][tm][i] = acc[tn][tm][i] + c;
-                        } else {
-                            const int S = (pacc[tn][tm][P - 1][i] << 6) + (pacc[tn][tm][1][i] << 3) +
-                                          pacc[tn][tm][0][i];
-                            const float t1 = dd[i] * (float)S;
-                            const float c = da * t1;
                             acc[tn][tm][i] = acc[tn][tm][i] + c;
                         }
                     }
@@ -504,7 +573,6 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ W
     }
 
     // Store: lane holds rows n = 4g + i of a 16x16 tile, column m = r16.
-    const int wn0 = 32 * wn, wm0 = (BM / 2) * wm;
 #pragma unroll
     for (int tn = 0; tn < 2; ++tn) {
         const int n = n0 + wn0 + 16 * tn + 4 * g;
@@ -527,13 +595,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ W
 template <int WT>
 static hipError_t launch_gemm_t(const uint8_t* W, int64_t N, int64_t K, const void* aqs, const void* ad,
                                 const void* aux, int64_t M, float* Y, int64_t ldy, hipStream_t st) {
-    constexpr int BM = 128;
+    constexpr int WM = 4, TM = 4;
+    constexpr int BM = 16 * TM * WM;
     const int nbw = (WT == 2) ? (int)(K / kQK8) : (int)(K / kQK);
     const int64_t wbytes = N * (int64_t)nbw * GemmCfg<WT>::BB;
     dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + BM - 1) / BM));
     GroupArgs ga = {};
-    gemm_kernel<WT, BM, false><<<grid, 256, 0, st>>>(W, (int)N, (int)K, wbytes, (const int8_t*)aqs, ad,
-                                                     (const int16_t*)aux, (int)M, Y, ldy, ga);
+    gemm_kernel<WT, WM, TM, false><<<grid, 128 * WM, 0, st>>>(W, (int)N, (int)K, wbytes, (const int8_t*)aqs, ad,
+                                                          (const int16_t*)aux, (int)M, Y, ldy, ga);
     return hipGetLastError();
 }
 
@@ -562,8 +631,8 @@ hipError_t launch_gemm_grouped(const uint8_t* W, int64_t E, int64_t N, int64_t K
     ga.list = ws.list;
     ga.top_k = (int)top_k;
     ga.expert_stride = estride;
-    gemm_kernel<0, kGroupBM, true><<<grid, 256, 0, st>>>(W, (int)N, (int)K, E * estride, act.qs, act.d,
-                                                         act.bsums, (int)T, Y, N * 1, ga);
+    gemm_kernel<0, 2, kGroupBM / 32, true><<<grid, 256, 0, st>>>(
+        W, (int)N, (int)K, E * estride, act.qs, act.d, act.bsums, (int)T, Y, N * 1, ga);
     return hipGetLastError();
 }
 

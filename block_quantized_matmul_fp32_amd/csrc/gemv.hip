@@ -125,7 +125,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
     constexpr int GPW = 64 / LPT;             // tasks per wave round
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar loop control
     const int nb = K / QV;
     const int rb = nb * BB;
     const int n0 = blockIdx.x * rows_per_wg;
