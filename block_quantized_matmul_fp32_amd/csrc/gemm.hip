@@ -122,10 +122,12 @@ __global__ __launch_bounds__(128 * WM, 2) void gemm_kernel(const uint8_t* __rest
     constexpr int PPT = 8 / UPR;           // 16-byte pieces per thread
     __shared__ __attribute__((aligned(16))) int8_t sA[BM * kLD];
     __shared__ __attribute__((aligned(16))) int8_t sW[P * kBN * kLD];
-    __shared__ __attribute__((aligned(16))) float sDa[(WT == 2) ? BM * 8 : BM];
-    __shared__ __attribute__((aligned(16))) float sDw[(WT == 2) ? kBN * 8 : 2 * kBN];
-    __shared__ __attribute__((aligned(16))) int8_t sMw[kBN * 8];
-    __shared__ __attribute__((aligned(16))) int8_t sHl[BM * 16];
+    // Scales, double-buffered by step parity (a late wave combines step s - 1
+    // while step s is current).
+    __shared__ __attribute__((aligned(16))) float sDa2[2][(WT == 2) ? BM * 8 : BM];
+    __shared__ __attribute__((aligned(16))) float sDw2[2][(WT == 2) ? kBN * 8 : 2 * kBN];
+    __shared__ __attribute__((aligned(16))) int8_t sMw2[2][(WT == 0) ? kBN * 8 : 16];
+    __shared__ __attribute__((aligned(16))) int8_t sHl2[2][(WT == 0) ? BM * 16 : 16];
     __shared__ int sRow[BM];    // activation row of each tile row (-1: none)
     __shared__ int sOut[BM];    // output row of each tile row (-1: none)
 
@@ -271,7 +273,11 @@ __global__ __launch_bounds__(128 * WM, 2) void gemm_kernel(const uint8_t* __rest
         }
     };
 
-    auto store_step = [&]() __attribute__((always_inline)) {
+    auto store_step = [&](int ss) __attribute__((always_inline)) {
+        float* sDa = sDa2[ss & 1];
+        float* sDw = sDw2[ss & 1];
+        int8_t* sMw = sMw2[ss & 1];
+        int8_t* sHl = sHl2[ss & 1];
 #pragma unroll
         for (int i = 0; i < ACH; ++i)
             *(u4v*)(sA + ((tid >> 4) + (NT / 16) * i) * kLD + acol) = regA[i];
@@ -398,15 +404,81 @@ __global__ __launch_bounds__(128 * WM, 2) void gemm_kernel(const uint8_t* __rest
             for (int i = 0; i < 4; ++i) acc[a][b][i] = 0.0f;
 
     const int wn0 = 32 * wn, wm0 = 16 * TM * wm;
+    const bool late = (WM >= 4) && ((wave >> 2) & 1);
+    v4i R[2][TM];  // integer sums S of the current super-block
+
+    // Binary32 combine of step ss (its scales are in buffer ss & 1).
+    auto epilogue = [&](int ss) __attribute__((always_inline)) {
+        const float* sDa = sDa2[ss & 1];
+        const float* sDw = sDw2[ss & 1];
+        v4i mn[2][TM];
+        if (WT == 0) {
+            const int8_t* sMw = sMw2[ss & 1];
+            const int8_t* sHl = sHl2[ss & 1];
+            long am[2][2], bm[TM];
+#pragma unroll
+            for (int tn = 0; tn < 2; ++tn) {
+                const long mv = *(const long*)(sMw + (wn0 + 16 * tn + r16) * 8);
+                am[tn][0] = (g == 0) ? mv : 0;
+                am[tn][1] = (g == 1) ? mv : 0;
+            }
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm) {
+                const int8_t* hp = sHl + (wm0 + 16 * tm + r16) * 16;
+                bm[tm] = (g == 0) ? *(const long*)hp : ((g == 1) ? *(const long*)(hp + 8) : 0);
+            }
+#pragma unroll
+            for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+                for (int tm = 0; tm < TM; ++tm) {
+                    v4i z = {0, 0, 0, 0};
+                    const v4i dh = __builtin_amdgcn_mfma_i32_16x16x32_i8(am[tn][0], bm[tm], z, 0, 0, 0);
+                    const v4i dl = __builtin_amdgcn_mfma_i32_16x16x32_i8(am[tn][1], bm[tm], z, 0, 0, 0);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) mn[tn][tm][i] = (dh[i] << 6) + dl[i];
+                }
+        }
+#pragma unroll
+        for (int tn = 0; tn < 2; ++tn) {
+            const int nb4 = wn0 + 16 * tn + 4 * g;
+            const float4 dv = *(const float4*)(sDw + nb4);
+            const float dd[4] = {dv.x, dv.y, dv.z, dv.w};
+            float dm[4] = {0.f, 0.f, 0.f, 0.f};
+            if (WT == 0) {
+                const float4 dmv = *(const float4*)(sDw + kBN + nb4);
+                dm[0] = dmv.x; dm[1] = dmv.y; dm[2] = dmv.z; dm[3] = dmv.w;
+            }
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm) {
+                const float da = sDa[wm0 + 16 * tm + r16];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float t1 = dd[i] * (float)R[tn][tm][i];
+                    if (WT == 0) {
+                        const float t2 = dm[i] * (float)mn[tn][tm][i];
+                        const float t3 = t1 - t2;
+                        const float c = da * t3;
+                        acc[tn][tm][i] = acc[tn][tm][i] + c;
+                    } else {
+                        const float c = da * t1;
+                        acc[tn][tm][i] = acc[tn][tm][i] + c;
+                    }
+                }
+            }
+        }
+    };
+
     load_step(0, -1);
     for (int s = 0; s < nsteps; ++s) {
         __syncthreads();
-        store_step();
+        store_step(s);
         __syncthreads();
         const bool more = s + 1 < nsteps;
         if (WT == 2 && more) load_step(s + 1, -1);
 
         if (WT == 2) {
+            const float* sDa = sDa2[s & 1];
+            const float* sDw = sDw2[s & 1];
             const int nval = min(8, nbw - 8 * s);
             for (int b = 0; b < nval; ++b) {
                 long av[2], bv[TM];
@@ -435,71 +507,23 @@ __global__ __launch_bounds__(128 * WM, 2) void gemm_kernel(const uint8_t* __rest
                     }
                 }
             }
-        } else if (WT == 1) {
-            // One accumulator per tile through the three digit planes:
-            // R = ((P2 << 3) + P1) << 3) + P0 = S, exact in int32.
-            v4i R[2][TM], bv[4][TM];
-#pragma unroll
-            for (int tn = 0; tn < 2; ++tn)
-#pragma unroll
-                for (int tm = 0; tm < TM; ++tm) R[tn][tm] = (v4i){0, 0, 0, 0};
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-#pragma unroll
-                for (int tm = 0; tm < TM; ++tm)
-                    bv[t][tm] = *(const v4i*)(sA + (wm0 + 16 * tm + r16) * kLD + 64 * t + 16 * g);
-#pragma unroll
-            for (int p = 2; p >= 0; --p) {
-                if (p < 2) {
-#pragma unroll
-                    for (int tn = 0; tn < 2; ++tn)
-#pragma unroll
-                        for (int tm = 0; tm < TM; ++tm) R[tn][tm] = R[tn][tm] << 3;
-                }
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    v4i av[2];
-#pragma unroll
-                    for (int tn = 0; tn < 2; ++tn)
-                        av[tn] = *(const v4i*)(sW + (p * kBN + wn0 + 16 * tn + r16) * kLD + 64 * t + 16 * g);
-#pragma unroll
-                    for (int tn = 0; tn < 2; ++tn)
-#pragma unroll
-                        for (int tm = 0; tm < TM; ++tm)
-                            R[tn][tm] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[tn], bv[t][tm], R[tn][tm], 0, 0, 0);
-                    if (p == 2 && more) load_step(s + 1, t);
-                }
-            }
-#pragma unroll
-            for (int tn = 0; tn < 2; ++tn) {
-                const float4 dv = *(const float4*)(sDw + wn0 + 16 * tn + 4 * g);
-                const float dd[4] = {dv.x, dv.y, dv.z, dv.w};
-#pragma unroll
-                for (int tm = 0; tm < TM; ++tm) {
-                    const float da = sDa[wm0 + 16 * tm + r16];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float t1 = dd[i] * (float)R[tn][tm][i];
-                        const float c = da * t1;
-                        acc[tn][tm][i] = acc[tn][tm][i] + c;
-                    }
-                }
-            }
         } else {
-            // Q4_K: R = (P1 << 3) + P0 = S through one accumulator per tile.
-            v4i R[2][TM], bv[4][TM];
-#pragma unroll
-            for (int tn = 0; tn < 2; ++tn)
-#pragma unroll
-                for (int tm = 0; tm < TM; ++tm) R[tn][tm] = (v4i){0, 0, 0, 0};
+            // Late waves combine the previous step before this step's MFMAs,
+            // early waves after them: each SIMD holds one of each, so one
+            // wave's epilogue VALU runs while the other's MFMAs run.
+            if (late && s > 0) epilogue(s - 1);
+            v4i bv[4][TM];
 #pragma unroll
             for (int t = 0; t < 4; ++t)
 #pragma unroll
                 for (int tm = 0; tm < TM; ++tm)
                     bv[t][tm] = *(const v4i*)(sA + (wm0 + 16 * tm + r16) * kLD + 64 * t + 16 * g);
+            // One accumulator per tile through the digit planes, high digit
+            // first: R = (((P2 << 3) + P1) << 3) + P0 (Q6_K) or (P1 << 3) + P0
+            // (Q4_K) = S, exact in int32.
 #pragma unroll
-            for (int p = 1; p >= 0; --p) {
-                if (p < 1) {
+            for (int p = P - 1; p >= 0; --p) {
+                if (p < P - 1) {
 #pragma unroll
                     for (int tn = 0; tn < 2; ++tn)
 #pragma unroll
@@ -515,62 +539,15 @@ __global__ __launch_bounds__(128 * WM, 2) void gemm_kernel(const uint8_t* __rest
                     for (int tn = 0; tn < 2; ++tn)
 #pragma unroll
                         for (int tm = 0; tm < TM; ++tm)
-                            R[tn][tm] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[tn], bv[t][tm], R[tn][tm], 0, 0, 0);
-                    if (p == 1 && more) load_step(s + 1, t);
+                            R[tn][tm] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                                av[tn], bv[t][tm], (p == P - 1 && t == 0) ? (v4i){0, 0, 0, 0} : R[tn][tm], 0, 0, 0);
+                    if (p == P - 1 && more) load_step(s + 1, t);
                 }
             }
-            v4i mn[2][TM];
-            if (WT == 0) {
-                long am[2][2], bm[TM];
-#pragma unroll
-                for (int tn = 0; tn < 2; ++tn) {
-                    const long mv = *(const long*)(sMw + (wn0 + 16 * tn + r16) * 8);
-                    am[tn][0] = (g == 0) ? mv : 0;
-                    am[tn][1] = (g == 1) ? mv : 0;
-                }
-#pragma unroll
-                for (int tm = 0; tm < TM; ++tm) {
-                    const int8_t* hp = sHl + (wm0 + 16 * tm + r16) * 16;
-                    bm[tm] = (g == 0) ? *(const long*)hp : ((g == 1) ? *(const long*)(hp + 8) : 0);
-                }
-#pragma unroll
-                for (int tn = 0; tn < 2; ++tn)
-#pragma unroll
-                    for (int tm = 0; tm < TM; ++tm) {
-                        v4i z = {0, 0, 0, 0};
-                        const v4i dh = __builtin_amdgcn_mfma_i32_16x16x32_i8(am[tn][0], bm[tm], z, 0, 0, 0);
-                        const v4i dl = __builtin_amdgcn_mfma_i32_16x16x32_i8(am[tn][1], bm[tm], z, 0, 0, 0);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) mn[tn][tm][i] = (dh[i] << 6) + dl[i];
-                    }
-            }
-#pragma unroll
-            for (int tn = 0; tn < 2; ++tn) {
-                const int nb4 = wn0 + 16 * tn + 4 * g;
-                const float4 dv = *(const float4*)(sDw + nb4);
-                const float dd[4] = {dv.x, dv.y, dv.z, dv.w};
-                float dm[4] = {0.f, 0.f, 0.f, 0.f};
-                if (WT == 0) {
-                    const float4 dmv = *(const float4*)(sDw + kBN + nb4);
-                    dm[0] = dmv.x; dm[1] = dmv.y; dm[2] = dmv.z; dm[3] = dmv.w;
-                }
-#pragma unroll
-                for (int tm = 0; tm < TM; ++tm) {
-                    const float da = sDa[wm0 + 16 * tm + r16];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        if (WT == 0) {
-                            const float t1 = dd[i] * (float)R[tn][tm][i];
-                            const float t2 = dm[i] * (float)mn[tn][tm][i];
-                            const float t3 = t1 - t2;
-                            const float c = da * t3;
-                            acc[tn][tm][i] = acc[tn][tm][i] + c;
-                        }
-                    }
-                }
-            }
+            if (!late) epilogue(s);
         }
     }
+    if (WT != 2 && late && nsteps > 0) epilogue(nsteps - 1);
 
     // Store: lane holds rows n = 4g + i of a 16x16 tile, column m = r16.
 #pragma unroll
