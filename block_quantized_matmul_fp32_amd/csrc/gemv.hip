@@ -39,8 +39,8 @@
 
 namespace vqk {
 
-constexpr int kGemvThreads = 1024;
-constexpr int kGemvWaves = kGemvThreads / 64;
+constexpr int kGemvThreads = 1024;              // most threads per workgroup
+constexpr int kGemvWaves = kGemvThreads / 64;   // most waves per workgroup
 constexpr int kLMax = 8;            // 16-byte chunks per lane: a wave span <= 8 KiB
 constexpr int kXPre = 4;            // x rounds loaded before the weights
 constexpr int kStepLoads = kLMax;   // loads parked before computing (one step: measured fastest)
@@ -65,7 +65,7 @@ struct GemvLayout {
 __host__ __device__ inline int align16i(int x) { return (x + 15) & ~15; }
 
 // LDS layout of the GEMV workgroup; identical on host and device.
-__host__ __device__ inline GemvLayout gemv_layout(int wt, int K, int rows, int region_bytes) {
+__host__ __device__ inline GemvLayout gemv_layout(int wt, int K, int rows, int region_bytes, int nwaves) {
     GemvLayout L;
     const int nbw = (wt == 2) ? K / kQK8 : K / kQK;
     L.act_qs = 0;
@@ -75,7 +75,7 @@ __host__ __device__ inline GemvLayout gemv_layout(int wt, int K, int rows, int r
     L.partial = L.act_bs + align16i(nbs_bytes);
     L.regions = L.partial + align16i(rows * nbw * 4);
     L.region_bytes = region_bytes;
-    L.total = L.regions + kGemvWaves * region_bytes;
+    L.total = L.regions + nwaves * region_bytes;
     return L;
 }
 
@@ -126,11 +126,13 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar loop control
+    const int nw = __builtin_amdgcn_readfirstlane((int)(blockDim.x >> 6));
+    const int nthr = 64 * nw;
     const int nb = K / QV;
     const int rb = nb * BB;
     const int n0 = blockIdx.x * rows_per_wg;
     const int rows = min(rows_per_wg, N - n0);
-    const GemvLayout L = gemv_layout(WT, K, rows_per_wg, region_bytes);
+    const GemvLayout L = gemv_layout(WT, K, rows_per_wg, region_bytes, nw);
     int8_t* act_qs = (int8_t*)(smem + L.act_qs);
     float* act_d = (float*)(smem + L.act_d);
     int16_t* act_bs = (int16_t*)(smem + L.act_bs);
@@ -147,7 +149,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
     float4 xv[kXPre];
 #pragma unroll
     for (int r = 0; r < kXPre; ++r) {
-        const int e = min((wave + kGemvWaves * r) * kQK + 4 * lane, K - 4);
+        const int e = min((wave + nw * r) * kQK + 4 * lane, K - 4);
         const float* src = x + e;
         xv[r] = x_vec ? *(const float4*)src : make_float4(src[0], src[1], src[2], src[3]);
     }
@@ -155,8 +157,8 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
 
     // ---- 2. every weight load of this wave's span
     const int ntask = rows * nb;
-    const int t0 = (int)((int64_t)ntask * wave / kGemvWaves);
-    const int t1 = (int)((int64_t)ntask * (wave + 1) / kGemvWaves);
+    const int t0 = (int)((int64_t)ntask * wave / nw);
+    const int t1 = (int)((int64_t)ntask * (wave + 1) / nw);
     int sb0, sb1;
     task_span(t0, t1, nb, rb, BB, &sb0, &sb1);
     const int64_t s0 = (int64_t)n0 * rb;
@@ -177,7 +179,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
         const int nsb = K / kQK;
 #pragma unroll
         for (int r = 0; r < kXPre; ++r) {
-            const int sb = wave + kGemvWaves * r;
+            const int sb = wave + nw * r;
             if (sb < nsb) {
                 const Q8KLane q = q8k_quant_lane(xv[r], lane);
                 *(uint32_t*)(act_qs + sb * kActStride + 4 * lane) = q.q4;
@@ -185,7 +187,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
                 if ((lane & 3) == 0) act_bs[sb * 16 + (lane >> 2)] = (int16_t)q.bsum;
             }
         }
-        for (int sb = wave + kGemvWaves * kXPre; sb < nsb; sb += kGemvWaves) {
+        for (int sb = wave + nw * kXPre; sb < nsb; sb += nw) {
             const float* src = x + sb * kQK + 4 * lane;
             const Q8KLane q1 = q8k_quant_lane(x_vec ? *(const float4*)src
                                                     : make_float4(src[0], src[1], src[2], src[3]), lane);
@@ -210,8 +212,8 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
         };
 #pragma unroll
         for (int r = 0; r < kXPre; ++r)
-            if (wave + kGemvWaves * r < xsteps) quant_step(wave + kGemvWaves * r, xv[r]);
-        for (int stp = wave + kGemvWaves * kXPre; stp < xsteps; stp += kGemvWaves) {
+            if (wave + nw * r < xsteps) quant_step(wave + nw * r, xv[r]);
+        for (int stp = wave + nw * kXPre; stp < xsteps; stp += nw) {
             const int e = stp * kQK + 4 * lane;
             float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
             if (e < K) {
@@ -377,7 +379,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
     lds_barrier();
 
     // ---- 5. rows: blocks summed in ascending order from 0
-    for (int r = tid; r < rows; r += kGemvThreads) {
+    for (int r = tid; r < rows; r += nthr) {
         const float* p = partial + r * nb;
         float acc = 0.0f;
         int b = 0;
@@ -401,19 +403,19 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
     if (xq_out != nullptr && blockIdx.x == 0) {
         const size_t od = align256((size_t)K);
         const int stride = (WT == 2) ? kQK : kActStride;
-        for (int i = tid; i < K / 4; i += kGemvThreads)
+        for (int i = tid; i < K / 4; i += nthr)
             ((uint32_t*)xq_out)[i] = *(const uint32_t*)(act_qs + (i / 64) * stride + 4 * (i % 64));
         if (WT != 2) {
             const int nsb = K / kQK;
             float* gd = (float*)(xq_out + od);
             int16_t* gb = (int16_t*)(xq_out + od + align256((size_t)nsb * 4));
-            for (int i = tid; i < nsb; i += kGemvThreads) gd[i] = act_d[i];
-            for (int i = tid; i < K / 16; i += kGemvThreads) gb[i] = act_bs[i];
+            for (int i = tid; i < nsb; i += nthr) gd[i] = act_d[i];
+            for (int i = tid; i < K / 16; i += nthr) gb[i] = act_bs[i];
         } else {
             const int nblk = K / kQK8;
             uint16_t* gd = (uint16_t*)(xq_out + od);
             uint16_t* gs = (uint16_t*)(xq_out + od + align256((size_t)nblk * 2));
-            for (int i = tid; i < nblk; i += kGemvThreads) {
+            for (int i = tid; i < nblk; i += nthr) {
                 gd[i] = (uint16_t)(act_ds[i] & 0xFFFF);
                 gs[i] = (uint16_t)(act_ds[i] >> 16);
             }
@@ -440,19 +442,20 @@ static int block_vals_of(int wt) { return wt == 2 ? kQK8 : kQK; }
 
 struct GemvPlan {
     int rows;          // rows per workgroup
+    int waves;         // waves per workgroup
     int region_bytes;  // LDS bytes per wave region
     int lds;           // dynamic LDS bytes
     bool ok;
 };
 
 // Largest per-wave span (bytes, incl. 16-byte alignment slack) for a given
-// rows-per-workgroup, by walking the task split the kernel uses.
-static int max_wave_span(int rows, int nb, int rb, int bb) {
+// rows-per-workgroup and wave count, by walking the task split the kernel uses.
+static int max_wave_span(int rows, int nb, int rb, int bb, int nw) {
     const int ntask = rows * nb;
     int best = 0;
-    for (int w = 0; w < kGemvWaves; ++w) {
-        const int t0 = (int)((int64_t)ntask * w / kGemvWaves);
-        const int t1 = (int)((int64_t)ntask * (w + 1) / kGemvWaves);
+    for (int w = 0; w < nw; ++w) {
+        const int t0 = (int)((int64_t)ntask * w / nw);
+        const int t1 = (int)((int64_t)ntask * (w + 1) / nw);
         int b0, b1;
         task_span(t0, t1, nb, rb, bb, &b0, &b1);
         best = b1 - b0 > best ? b1 - b0 : best;
@@ -460,22 +463,30 @@ static int max_wave_span(int rows, int nb, int rb, int bb) {
     return best;
 }
 
-// About one workgroup per CU; fewer rows per workgroup when a wave's span
-// would not fit its chunk budget or the workgroup would not fit LDS.
+// About one workgroup per CU, with just enough waves that each wave computes
+// its tasks in one pass (a pass costs the same instructions however many of
+// its lanes hold a task); more waves only when a wave's span would not fit
+// its chunk budget, fewer rows when the workgroup would not fit LDS.
 static GemvPlan gemv_plan(int wt, int64_t N, int64_t K) {
     GemvPlan p;
     const int bb = block_bytes_of(wt);
     const int nb = (int)(K / block_vals_of(wt));
     const int rb = nb * bb;
+    const int gpw = (wt == 2) ? 64 : 32;  // tasks per wave pass (64 lanes / lanes per task)
     int rows = (int)((N + num_cus() - 1) / num_cus());
     if (rows < 1) rows = 1;
     for (;;) {
-        const int span = max_wave_span(rows, nb, rb, bb);
+        const int ntask = rows * nb;
+        int nw = (ntask + gpw - 1) / gpw;
+        nw = nw < 1 ? 1 : (nw > kGemvWaves ? kGemvWaves : nw);
+        int span = max_wave_span(rows, nb, rb, bb, nw);
+        while (nw < kGemvWaves && span + 32 > kLMax * 64 * 16) span = max_wave_span(rows, nb, rb, bb, ++nw);
         const int region = align16i(span + 32) + 32;  // alignment slack + over-read slack
-        const GemvLayout L = gemv_layout(wt, (int)K, rows, region);
+        const GemvLayout L = gemv_layout(wt, (int)K, rows, region, nw);
         const bool fits = span + 32 <= kLMax * 64 * 16 && (size_t)L.total <= kMaxLds;
         if (fits || rows == 1) {
             p.rows = rows;
+            p.waves = nw;
             p.region_bytes = region;
             p.lds = L.total;
             p.ok = fits;
@@ -505,7 +516,7 @@ static hipError_t launch_gemv_t(const uint8_t* W, int64_t N, int64_t K, const fl
     const int rb = (int)(K / WFmt<WT>::kVals) * WFmt<WT>::kBlk;
     const int grid = (int)((N + p.rows - 1) / p.rows);
     const int x_vec = (((uintptr_t)x) & 15) == 0;
-    gemv_kernel<WT><<<grid, kGemvThreads, p.lds, st>>>(W, (int)N, (int)K, (int64_t)N * rb, x, y, xq_out,
+    gemv_kernel<WT><<<grid, 64 * p.waves, p.lds, st>>>(W, (int)N, (int)K, (int64_t)N * rb, x, y, xq_out,
                                                         p.rows, p.region_bytes, x_vec);
     return hipGetLastError();
 }
