@@ -139,12 +139,13 @@ __global__ __launch_bounds__(128 * WM, 2) void gemm_kernel(const uint8_t* __rest
     const int n0 = blockIdx.x * kBN;
 
     const uint8_t* W = Wbase;
+    int rows_here;  // valid activation rows of this tile
     if (kGrouped) {
         const int tix = blockIdx.y;
         if (tix >= *ga.ntiles) return;
         const int e = ga.tiles[4 * tix + 0];
         const int first = ga.tiles[4 * tix + 1];
-        const int rows_here = ga.tiles[4 * tix + 2];
+        rows_here = ga.tiles[4 * tix + 2];
         W = Wbase + (int64_t)e * ga.expert_stride;
         if (tid < BM) {
             if (tid < rows_here) {
@@ -158,12 +159,14 @@ __global__ __launch_bounds__(128 * WM, 2) void gemm_kernel(const uint8_t* __rest
         }
     } else {
         const int m0 = blockIdx.y * BM;
+        rows_here = min(BM, M - m0);
         if (tid < BM) {
             const int m = m0 + tid;
             sRow[tid] = (m < M) ? m : -1;
             sOut[tid] = (m < M) ? m : -1;
         }
     }
+    rows_here = __builtin_amdgcn_readfirstlane(rows_here);
     __syncthreads();
 
     const int nbw = (WT == 2) ? K / kQK8 : K / kQK;
@@ -172,14 +175,16 @@ __global__ __launch_bounds__(128 * WM, 2) void gemm_kernel(const uint8_t* __rest
     const int nsteps = (K + kKS - 1) / kKS;
 
     // Activation chunks of this thread: row (tid >> 4) + (NT / 16) * i, bytes
-    // 16 * (tid & 15) of each step.  Rows past the tile read activation row 0
-    // (their outputs are never stored).
+    // 16 * (tid & 15) of each step.  Rows past the tile are not loaded (zero;
+    // their outputs are never stored).
     const int acol = 16 * (tid & 15);
     const int8_t* ap[ACH];
+    uint32_t avalid = 0;
 #pragma unroll
     for (int i = 0; i < ACH; ++i) {
         const int ar = sRow[(tid >> 4) + (NT / 16) * i];
         ap[i] = aqs + (int64_t)(ar >= 0 ? ar : 0) * K + acol;
+        avalid |= (ar >= 0 ? 1u : 0u) << i;
     }
     const int my_ar = (tid < BM) ? sRow[tid] : -1;  // scale row of threads < BM
 
@@ -203,7 +208,7 @@ __global__ __launch_bounds__(128 * WM, 2) void gemm_kernel(const uint8_t* __rest
 #pragma unroll
         for (int i = 0; i < ACH; ++i) {
             if (part >= 0 && (i * 4 / ACH) != part) continue;
-            if (WT != 2 || kk + acol < K)
+            if (((avalid >> i) & 1) && (WT != 2 || kk + acol < K))
                 regA[i] = *(const u4v*)(ap[i] + kk);
             else
                 regA[i] = (u4v){0u, 0u, 0u, 0u};
@@ -405,6 +410,7 @@ __global__ __launch_bounds__(128 * WM, 2) void gemm_kernel(const uint8_t* __rest
 
     const int wn0 = 32 * wn, wm0 = 16 * TM * wm;
     const bool late = (WM >= 4) && ((wave >> 2) & 1);
+    const bool active = wm0 < rows_here;  // the wave has valid activation rows
     v4i R[2][TM];  // integer sums S of the current super-block
 
     // Binary32 combine of step ss (its scales are in buffer ss & 1).
@@ -511,6 +517,14 @@ __global__ __launch_bounds__(128 * WM, 2) void gemm_kernel(const uint8_t* __rest
             // Late waves combine the previous step before this step's MFMAs,
             // early waves after them: each SIMD holds one of each, so one
             // wave's epilogue VALU runs while the other's MFMAs run.
+            if (!active) {
+                // no valid activation rows for this wave: only its share of the loads
+                if (more) {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) load_step(s + 1, t);
+                }
+                continue;
+            }
             if (late && s > 0) epilogue(s - 1);
             v4i bv[4][TM];
 #pragma unroll
@@ -547,7 +561,7 @@ __global__ __launch_bounds__(128 * WM, 2) void gemm_kernel(const uint8_t* __rest
             if (!late) epilogue(s);
         }
     }
-    if (WT != 2 && late && nsteps > 0) epilogue(nsteps - 1);
+    if (WT != 2 && active && late && nsteps > 0) epilogue(nsteps - 1);
 
     // Store: lane holds rows n = 4g + i of a 16x16 tile, column m = r16.
 #pragma unroll
@@ -592,7 +606,9 @@ hipError_t launch_gemm(int wtype, const uint8_t* W, int64_t N, int64_t K, const 
     return launch_gemm_t<2>(W, N, K, act_qs, act_d, act_aux, M, Y, ldy, st);
 }
 
-// Grouped launch: one 64 x 64 tile per (weight-row block, routed tile).
+// Grouped launch: one 64 x 64 tile per (weight-row block, routed tile); a
+// routed tile holds up to 64 rows of one expert, and waves whose rows are all
+// past the tile's rows skip their MFMAs.
 constexpr int kGroupBM = kGroupTileRows;
 
 hipError_t launch_gemm_grouped(const uint8_t* W, int64_t E, int64_t N, int64_t K, ActQ8K act,

@@ -11,9 +11,17 @@
 // Routing is integer bookkeeping with one answer: counts per expert, the
 // exclusive prefix offsets, and the pair indices t*top_k+s listed per expert
 // in ascending (t, s) order.  It is built without atomics in three small
-// launches (per-chunk counts, one scan workgroup that also writes the tile
-// table, per-chunk placement), so the list is deterministic; the tile table
-// stays on the device, so the grouped GEMM needs no host synchronisation.
+// launches, so the list is deterministic:
+//  * one wave per chunk of 64 tokens walks the chunk's pairs 64 at a time;
+//    the lanes holding the same expert are found with one ballot per bit of
+//    the expert id, which gives each pair its rank among the chunk's earlier
+//    pairs of that expert and the chunk's per-expert counts;
+//  * one workgroup scans the per-chunk counts over chunks and experts and
+//    writes the tile table;
+//  * one thread per pair writes it to its list slot.
+// The tile table stays on the device, so the grouped GEMM needs no host
+// synchronisation.  Pairs whose id is outside [0, E) are neither counted nor
+// placed.
 #include "vq_device.h"
 #include "vq_internal.h"
 
@@ -40,6 +48,7 @@ size_t route_ws_layout(int64_t E, int64_t T, int64_t top_k, RouteWs* ws, uint8_t
     const size_t o_offsets = take(sizeof(int32_t) * (size_t)(E + 1));
     const size_t o_list = take(sizeof(int32_t) * (size_t)(T * top_k));
     const size_t o_chunk = take(sizeof(int32_t) * (size_t)(nchunks * E));
+    const size_t o_rank = take(sizeof(int32_t) * (size_t)(T * top_k));
     const size_t o_tiles = take(sizeof(int32_t) * 4 * (size_t)max_tiles);
     const size_t o_ntiles = take(sizeof(int32_t) * 4);
     if (ws) {
@@ -47,66 +56,116 @@ size_t route_ws_layout(int64_t E, int64_t T, int64_t top_k, RouteWs* ws, uint8_t
         ws->offsets = (int32_t*)(base + o_offsets);
         ws->list = (int32_t*)(base + o_list);
         ws->chunk = (int32_t*)(base + o_chunk);
+        ws->rank = (int32_t*)(base + o_rank);
         ws->tiles = (int32_t*)(base + o_tiles);
         ws->ntiles = (int32_t*)(base + o_ntiles);
     }
     return off;
 }
 
-// Per chunk of 64 tokens: chunk[c][e] = number of pairs of the chunk routed to e.
-__global__ __launch_bounds__(256) void route_count_kernel(const int32_t* __restrict__ ids, int T,
-                                                          int top_k, int E, int32_t* __restrict__ chunk) {
-    __shared__ int32_t sid[kRouteChunk * 16];
+constexpr int kIdBits = 11;  // expert ids < 1024, plus 64 distinct keys for pairs not routed
+
+// One wave per chunk of kRouteChunk tokens: rank[p] = number of earlier pairs
+// of the chunk with the same expert, chunk[c][e] = the chunk's pairs of e.
+__global__ __launch_bounds__(64) void route_count_kernel(const int32_t* __restrict__ ids, int T, int top_k,
+                                                         int E, int32_t* __restrict__ chunk,
+                                                         int32_t* __restrict__ rank) {
+    __shared__ int32_t cnt[1024];
+    const int lane = threadIdx.x;
     const int c = blockIdx.x;
-    const int t0 = c * kRouteChunk;
-    const int np = min(kRouteChunk, T - t0) * top_k;
-    for (int i = threadIdx.x; i < np; i += 256) sid[i] = ids[(int64_t)t0 * top_k + i];
+    const int64_t p0 = (int64_t)c * kRouteChunk * top_k;
+    const int np = min(kRouteChunk, T - c * kRouteChunk) * top_k;
+    for (int e = lane; e < E; e += 64) cnt[e] = 0;
     __syncthreads();
-    for (int e = threadIdx.x; e < E; e += 256) {
-        int cnt = 0;
-        for (int i = 0; i < np; ++i) cnt += (sid[i] == e);
-        chunk[(int64_t)c * E + e] = cnt;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int base = 0; base < np; base += 64) {
+        const int i = base + lane;
+        const int e = (i < np) ? ids[p0 + i] : -1;
+        const bool ok = (i < np) && e >= 0 && e < E;
+        const int key = ok ? e : 1024 + lane;  // a pair not routed matches no other lane
+        uint64_t same = ~0ull;
+#pragma unroll
+        for (int b = 0; b < kIdBits; ++b) {
+            const uint64_t set = __ballot((key >> b) & 1);
+            same &= ((key >> b) & 1) ? set : ~set;
+        }
+        const int r = __popcll(same & below);
+        const int before = ok ? cnt[e] : 0;
+        if (ok) rank[p0 + i] = before + r;
+        // the highest lane of each expert's group advances the count
+        if (ok && (same >> lane) == 1ull) cnt[e] = before + __popcll(same);
+        __syncthreads();
     }
+    for (int e = lane; e < E; e += 64) chunk[(int64_t)c * E + e] = cnt[e];
 }
 
-// One workgroup: per-expert scan over chunks (chunk[c][e] becomes the
-// exclusive offset of the chunk inside the expert), counts, expert offsets,
-// and the tile table (expert, first list slot, rows).
-__global__ __launch_bounds__(1024) void route_scan_kernel(int nchunks, int E, int32_t* __restrict__ chunk,
-                                                          int32_t* __restrict__ counts,
-                                                          int32_t* __restrict__ offsets,
-                                                          int32_t* __restrict__ tiles,
-                                                          int32_t* __restrict__ ntiles) {
+// One workgroup: chunk[c][e] becomes the exclusive offset of chunk c inside
+// expert e; counts, expert offsets and the tile table (expert, first list
+// slot, rows).  kScanThreads / E threads share one expert's chunks.
+constexpr int kScanThreads = 1024;
+__global__ __launch_bounds__(kScanThreads) void route_scan_kernel(int nchunks, int E, int32_t* __restrict__ chunk,
+                                                                  int32_t* __restrict__ counts,
+                                                                  int32_t* __restrict__ offsets,
+                                                                  int32_t* __restrict__ tiles,
+                                                                  int32_t* __restrict__ ntiles) {
+    __shared__ int32_t part[kScanThreads];
     __shared__ int32_t sc[1024];
     __shared__ int32_t st[1024];
-    const int e = threadIdx.x;
-    int total = 0;
-    if (e < E) {
-        for (int c = 0; c < nchunks; ++c) {
-            const int v = chunk[(int64_t)c * E + e];
-            chunk[(int64_t)c * E + e] = total;
+    const int tid = threadIdx.x;
+    const int tpe = kScanThreads / E;  // threads per expert (>= 1 for E <= 1024)
+    const int e = tid / tpe, q = tid % tpe;
+    const bool own = e < E;
+    const int len = (nchunks + tpe - 1) / tpe;
+    const int c0 = min(nchunks, q * len), c1 = min(nchunks, c0 + len);
+    int sum = 0;
+    if (own)
+        for (int c = c0; c < c1; ++c) sum += chunk[(int64_t)c * E + e];
+    part[tid] = sum;
+    __syncthreads();
+    int base = 0, total = 0;
+    if (own) {
+        for (int k = 0; k < tpe; ++k) {
+            const int v = part[e * tpe + k];
+            base += (k < q) ? v : 0;
             total += v;
         }
-        counts[e] = total;
+        int run = base;
+        for (int c = c0; c < c1; ++c) {
+            const int v = chunk[(int64_t)c * E + e];
+            chunk[(int64_t)c * E + e] = run;
+            run += v;
+        }
     }
-    const int nt = (e < E) ? (total + kTileRows - 1) / kTileRows : 0;
-    sc[e] = (e < E) ? total : 0;
-    st[e] = nt;
+    const bool lead = own && q == 0;
+    if (lead) counts[e] = total;
+    if (tid < 1024) {
+        const int ex = tid;
+        sc[ex] = 0;
+        st[ex] = 0;
+    }
     __syncthreads();
-    // inclusive Hillis-Steele scans of counts and tile counts
+    const int nt = lead ? (total + kTileRows - 1) / kTileRows : 0;
+    if (lead) {
+        sc[e] = total;
+        st[e] = nt;
+    }
+    __syncthreads();
+    // inclusive Hillis-Steele scans of counts and tile counts over experts
     for (int o = 1; o < 1024; o <<= 1) {
-        const int a = (e >= o) ? sc[e - o] : 0;
-        const int b = (e >= o) ? st[e - o] : 0;
+        const int a = (tid < 1024 && tid >= o) ? sc[tid - o] : 0;
+        const int b = (tid < 1024 && tid >= o) ? st[tid - o] : 0;
         __syncthreads();
-        sc[e] += a;
-        st[e] += b;
+        if (tid < 1024) {
+            sc[tid] += a;
+            st[tid] += b;
+        }
         __syncthreads();
     }
-    if (e < E) {
+    if (lead) {
         const int off = sc[e] - total;
         offsets[e] = off;
         if (e == E - 1) offsets[E] = sc[e];
-        int tbase = st[e] - nt;
+        const int tbase = st[e] - nt;
         for (int i = 0; i < nt; ++i) {
             tiles[4 * (tbase + i) + 0] = e;
             tiles[4 * (tbase + i) + 1] = off + i * kTileRows;
@@ -117,34 +176,32 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int nchunks, int E, in
     }
 }
 
-// Per chunk: list[offsets[e] + chunk offset + k] = pair index, ascending.
-__global__ __launch_bounds__(256) void route_place_kernel(const int32_t* __restrict__ ids, int T, int top_k,
-                                                          int E, const int32_t* __restrict__ chunk,
+// One thread per pair: list[offsets[e] + chunk offset + rank] = pair index.
+__global__ __launch_bounds__(256) void route_place_kernel(const int32_t* __restrict__ ids, int64_t npairs,
+                                                          int top_k, int E, const int32_t* __restrict__ chunk,
                                                           const int32_t* __restrict__ offsets,
+                                                          const int32_t* __restrict__ rank,
                                                           int32_t* __restrict__ list) {
-    __shared__ int32_t sid[kRouteChunk * 16];
-    const int c = blockIdx.x;
-    const int t0 = c * kRouteChunk;
-    const int np = min(kRouteChunk, T - t0) * top_k;
-    for (int i = threadIdx.x; i < np; i += 256) sid[i] = ids[(int64_t)t0 * top_k + i];
-    __syncthreads();
-    for (int e = threadIdx.x; e < E; e += 256) {
-        int pos = offsets[e] + chunk[(int64_t)c * E + e];
-        for (int i = 0; i < np; ++i)
-            if (sid[i] == e) list[pos++] = t0 * top_k + i;
-    }
+    const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (p >= npairs) return;
+    const int e = ids[p];
+    if (e < 0 || e >= E) return;
+    const int64_t c = (p / top_k) / kRouteChunk;
+    list[offsets[e] + chunk[c * E + e] + rank[p]] = (int32_t)p;
 }
 
 hipError_t launch_route(const int32_t* ids, int64_t T, int64_t top_k, int64_t E, RouteWs ws,
                         hipStream_t st) {
     const int nchunks = (int)((T + kRouteChunk - 1) / kRouteChunk);
     if (nchunks > 0)
-        route_count_kernel<<<nchunks, 256, 0, st>>>(ids, (int)T, (int)top_k, (int)E, ws.chunk);
-    route_scan_kernel<<<1, 1024, 0, st>>>(nchunks, (int)E, ws.chunk, ws.counts, ws.offsets, ws.tiles,
-                                          ws.ntiles);
-    if (nchunks > 0)
-        route_place_kernel<<<nchunks, 256, 0, st>>>(ids, (int)T, (int)top_k, (int)E, ws.chunk, ws.offsets,
-                                                    ws.list);
+        route_count_kernel<<<nchunks, 64, 0, st>>>(ids, (int)T, (int)top_k, (int)E, ws.chunk, ws.rank);
+    route_scan_kernel<<<1, kScanThreads, 0, st>>>(nchunks, (int)E, ws.chunk, ws.counts, ws.offsets, ws.tiles,
+                                                  ws.ntiles);
+    const int64_t npairs = T * top_k;
+    if (npairs > 0)
+        route_place_kernel<<<(unsigned)((npairs + 255) / 256), 256, 0, st>>>(ids, npairs, (int)top_k, (int)E,
+                                                                             ws.chunk, ws.offsets, ws.rank,
+                                                                             ws.list);
     return hipGetLastError();
 }
 

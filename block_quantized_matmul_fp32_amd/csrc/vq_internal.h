@@ -49,6 +49,7 @@ struct RouteWs {
     int32_t* offsets;  // [E+1]
     int32_t* list;     // [T*top_k]
     int32_t* chunk;    // [nchunks][E] per-chunk counts, then offsets
+    int32_t* rank;     // [T*top_k] rank of each pair among its chunk's pairs of the same expert
     int32_t* tiles;    // tile table
     int32_t* ntiles;   // [1]
 };

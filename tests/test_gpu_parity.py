@@ -302,8 +302,9 @@ def test_grouped_small(case):
         T = 50
         ids = synth.random_ids(1800, T, E, top_k)
     else:
-        # expert 0 empty, expert 1 in every token (rows > one tile), expert 2 once
-        T = 90
+        # expert 0 empty, expert 1 in every token (rows over several tiles),
+        # expert 2 once
+        T = 150
         hint = np.ones(E); hint[0] = 0; hint[1] = 1e6; hint[2] = 0
         ids = synth.skewed_ids(1801, T, E, top_k, hint)
         ids[5, 3] = 2 if 2 not in ids[5] else ids[5, 3]
@@ -321,6 +322,8 @@ def test_grouped_small(case):
     e = int(ids[0, 0])
     dense = oracle.gemm(oracle.Q4_K, Wq[e * N:(e + 1) * N], N, K, act)
     H.assert_bitwise(Yh[0, 0], dense[0], "slot vs dense")
+    if case == "skewed":
+        assert int(H.host(counts)[1]) == T and int(H.host(counts)[0]) == 0
     # swapped ids must change the output
     ids2 = ids.copy(); ids2[:, [0, 1]] = ids2[:, [1, 0]]
     _, _, _, Y2, _, _ = run_grouped(E, N, K, T, top_k, ids2, 1810)
