@@ -6,27 +6,29 @@
 // the CPU oracle); strix-llama.cpp PR #18, commit "mul_mat_vec_q_fq" (a
 // block quantizes the activation once into shared memory, with weight loads
 // issued before the quantization and its barrier), commit "warp reduce via
-// DPP" (lane exchange without LDS round trips) and commit "batch-one MMVQ on
-// one wave" (a fixed fp32 reduction order keeps decode deterministic).
+// DPP" (lane exchange without LDS round trips) and the overview commit that
+// keeps batch-one MMVQ in a fixed fp32 reduction order (deterministic decode).
 //
 // MI355X design.  The GEMV streams 9-20 MB of weights: a few microseconds of
-// HBM time, so everything else has to hide under the loads.
-//  * One 1024-thread workgroup per CU owns a contiguous run of rows.  Its
-//    (row, block) tasks are split into 16 contiguous ranges, one per wave; a
-//    wave's bytes are one contiguous span, fetched with aligned 16-byte
-//    loads into registers.
-//  * Order of issue: first the few x loads (L2 hits), then every weight load
-//    of the wave, so the quantizer only waits for x while the weights stream.
-//  * The 16 waves quantize x into LDS with the shared quantizer body (DPP
-//    reductions); one barrier publishes it.
-//  * Each wave then parks its own weight span in a private LDS region (the
-//    Q6_K / Q8_0 blocks are only 2-byte aligned; LDS reads at that alignment
-//    are rebuilt with v_alignbyte) and computes as soon as its own bytes are
-//    in: no workgroup barrier between a wave's loads and its compute.
-//  * Eight lanes own one (row, super-block) -- one lane per Q8_0 block: exact
-//    int32 sub-block sums with v_dot4_i32_i8, an exact DPP reduction over the
-//    eight lanes, then the block's binary32 combine into an LDS partial.
-//  * After one more barrier, one lane per row adds the row's partials in
+// HBM time, so everything else has to hide under the stream.  A CU's share of
+// the stream is ~17 KB/us and a wave that issues weight loads stalls in issue
+// until earlier misses return, so the waves of a workgroup take two roles:
+//  * One workgroup per CU owns a contiguous run of rows; its (row, block)
+//    tasks split into a first part and a last part of at most one full pass
+//    per SIMD.
+//  * Loader waves (one per SIMD) copy the workgroup's whole weight slice
+//    straight into LDS with global_load_lds_dwordx4 (no registers, no parking
+//    step), first part then last part, a fixed number of 1 KiB instructions
+//    per wave per part so that a vmcnt wait can tell the parts apart.
+//  * Quantizer waves issue no weight load: they load x, quantize it into LDS
+//    with the shared quantizer body (DPP reductions), then -- once the first
+//    part has landed -- compute it while the last part streams in; the
+//    loader waves compute the last part after it lands, so only that one pass
+//    follows the end of the stream.
+//  * Two lanes own one (row, super-block) -- one lane per Q8_0 block: exact
+//    int32 sub-block sums with v_dot4_i32_i8, a DPP exchange of the halves,
+//    then the block's binary32 combine into an LDS partial.
+//  * After the last barrier, one lane per row adds the row's partials in
 //    ascending block order from 0, so y is bit-identical to the fixed-order
 //    definition.
 #include "vq_device.h"
@@ -41,9 +43,8 @@ namespace vqk {
 
 constexpr int kGemvThreads = 1024;              // most threads per workgroup
 constexpr int kGemvWaves = kGemvThreads / 64;   // most waves per workgroup
-constexpr int kLMax = 8;            // 16-byte chunks per lane: a wave span <= 8 KiB
-constexpr int kXPre = 4;            // x rounds loaded before the weights
-constexpr int kStepLoads = kLMax;   // loads parked before computing (one step: measured fastest)
+constexpr int kXPre = 8;            // x rounds (256 values each) loaded up front per quantizer wave
+constexpr int kMaxHalfInstr = 31;   // 1 KiB load instructions per loader wave per half (vmcnt <= 63)
 constexpr size_t kMaxLds = 160 * 1024;
 // LDS bytes per quantized super-block of x: 256 + 16, so the 16 tasks of a
 // wave round (consecutive super-blocks) start on 16 different bank groups.
@@ -59,13 +60,16 @@ template <>
 struct WFmt<2> { static constexpr int kBlk = kQ80Bytes; static constexpr int kVals = kQK8; };
 
 struct GemvLayout {
-    int act_qs, act_d, act_bs, partial, regions, region_bytes, total;
+    int act_qs, act_d, act_bs, partial, wslice, slice_bytes, total;
 };
 
 __host__ __device__ inline int align16i(int x) { return (x + 15) & ~15; }
 
-// LDS layout of the GEMV workgroup; identical on host and device.
-__host__ __device__ inline GemvLayout gemv_layout(int wt, int K, int rows, int region_bytes, int nwaves) {
+// LDS layout of the GEMV workgroup; identical on host and device.  The weight
+// slice region holds the slice's 16-byte chunks, 1 KiB past the slice for the
+// last instruction's lanes beyond it, 1 KiB for padding instructions, and
+// over-read slack.
+__host__ __device__ inline GemvLayout gemv_layout(int wt, int K, int rows, int slice_bytes) {
     GemvLayout L;
     const int nbw = (wt == 2) ? K / kQK8 : K / kQK;
     L.act_qs = 0;
@@ -73,9 +77,9 @@ __host__ __device__ inline GemvLayout gemv_layout(int wt, int K, int rows, int r
     L.act_bs = L.act_d + align16i(nbw * 4);
     const int nbs_bytes = (wt == 2) ? (K / kQK8) * 4 : (K / 16) * 2;
     L.partial = L.act_bs + align16i(nbs_bytes);
-    L.regions = L.partial + align16i(rows * nbw * 4);
-    L.region_bytes = region_bytes;
-    L.total = L.regions + nwaves * region_bytes;
+    L.wslice = L.partial + align16i(rows * nbw * 4);
+    L.slice_bytes = slice_bytes;
+    L.total = L.wslice + slice_bytes;
     return L;
 }
 
@@ -106,80 +110,110 @@ __device__ __forceinline__ void lds_read32_a2(const uint8_t* p, uint32_t out[8])
     for (int i = 0; i < 8; ++i) out[i] = __builtin_amdgcn_alignbyte(w[i + 1], w[i], sh);
 }
 
-// Number of whole tasks (row-major (row, block) order) inside the first E
-// bytes of the workgroup's rows.
-__device__ __forceinline__ int tasks_within(int E, int nb, int rb, int bb) {
-    const int r = E / rb;
-    const int k = (E - r * rb) / bb;
-    return r * nb + (k < nb ? k : nb);
+// s_waitcnt vmcnt(n) for a wave-uniform n in [0, 63].
+__device__ __forceinline__ void wait_vmcnt(int n) {
+#define VQ_VMW(k) case k: __builtin_amdgcn_s_waitcnt((((k) & 15) | (((k) >> 4) << 14)) | 0x0F70); break;
+    switch (n) {
+        VQ_VMW(0) VQ_VMW(1) VQ_VMW(2) VQ_VMW(3) VQ_VMW(4) VQ_VMW(5) VQ_VMW(6) VQ_VMW(7)
+        VQ_VMW(8) VQ_VMW(9) VQ_VMW(10) VQ_VMW(11) VQ_VMW(12) VQ_VMW(13) VQ_VMW(14) VQ_VMW(15)
+        VQ_VMW(16) VQ_VMW(17) VQ_VMW(18) VQ_VMW(19) VQ_VMW(20) VQ_VMW(21) VQ_VMW(22) VQ_VMW(23)
+        VQ_VMW(24) VQ_VMW(25) VQ_VMW(26) VQ_VMW(27) VQ_VMW(28) VQ_VMW(29) VQ_VMW(30) VQ_VMW(31)
+        default: __builtin_amdgcn_s_waitcnt(0x0F70); break;  // vmcnt(0)
+    }
+#undef VQ_VMW
 }
+
+typedef __attribute__((address_space(3))) void lds_void;
 
 template <int WT>
 __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
     const uint8_t* __restrict__ W, int N, int K, int64_t wbytes, const float* __restrict__ x,
-    float* __restrict__ y, uint8_t* __restrict__ xq_out, int rows_per_wg, int region_bytes, int x_vec) {
+    float* __restrict__ y, uint8_t* __restrict__ xq_out, int rows_per_wg, int slice_bytes, int x_vec,
+    int nq, int h1_tasks, int kh0, int kh1) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     constexpr int BB = WFmt<WT>::kBlk;
     constexpr int QV = WFmt<WT>::kVals;
     constexpr int LPT = (WT == 2) ? 1 : 2;    // lanes per task
-    constexpr int GPW = 64 / LPT;             // tasks per wave round
+    constexpr int GPW = 64 / LPT;             // tasks per wave pass
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar loop control
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar control
     const int nw = __builtin_amdgcn_readfirstlane((int)(blockDim.x >> 6));
+    const int G = nq;                         // quantizer waves (first half); the rest load
+    const int GL = nw - nq;                   // loader waves (second half)
     const int nthr = 64 * nw;
     const int nb = K / QV;
     const int rb = nb * BB;
     const int n0 = blockIdx.x * rows_per_wg;
     const int rows = min(rows_per_wg, N - n0);
-    const GemvLayout L = gemv_layout(WT, K, rows_per_wg, region_bytes, nw);
+    const GemvLayout L = gemv_layout(WT, K, rows_per_wg, slice_bytes);
     int8_t* act_qs = (int8_t*)(smem + L.act_qs);
     float* act_d = (float*)(smem + L.act_d);
     int16_t* act_bs = (int16_t*)(smem + L.act_bs);
     uint32_t* act_ds = (uint32_t*)(smem + L.act_bs);  // Q8_1: binary16 d | s << 16 per block
     float* partial = (float*)(smem + L.partial);
-    uint8_t* region = smem + L.regions + wave * region_bytes;
+    uint8_t* wsl = smem + L.wslice;
+    uint8_t* dummy = wsl + slice_bytes - 1024 - 64;   // target of padding instructions
 
-    // ---- 1. x loads.  Loads are unconditional (addresses clamped into the
-    // buffers) so the code stays straight-line and each wait counts only the
-    // loads it needs.  The vector L1 returns data in order, so every wave's x
-    // loads are queued before any weight load of the workgroup: a bare
-    // s_barrier (no memory wait) separates the two.
-    const int xsteps = (K + kQK - 1) / kQK;  // 256 values per wave step
-    float4 xv[kXPre];
-#pragma unroll
-    for (int r = 0; r < kXPre; ++r) {
-        const int e = min((wave + nw * r) * kQK + 4 * lane, K - 4);
-        const float* src = x + e;
-        xv[r] = x_vec ? *(const float4*)src : make_float4(src[0], src[1], src[2], src[3]);
-    }
-    __builtin_amdgcn_s_barrier();
-
-    // ---- 2. every weight load of this wave's span
+    // Slice geometry: chunks [cb, ce) of 16 bytes hold the rows' bytes; the
+    // first part of the tasks (computed by the quantizer waves while the rest
+    // streams in) ends inside chunk cm - 1.
     const int ntask = rows * nb;
-    const int t0 = (int)((int64_t)ntask * wave / nw);
-    const int t1 = (int)((int64_t)ntask * (wave + 1) / nw);
-    int sb0, sb1;
-    task_span(t0, t1, nb, rb, BB, &sb0, &sb1);
+    const int th = ntask - min(ntask, h1_tasks);
     const int64_t s0 = (int64_t)n0 * rb;
-    const int64_t wc0 = (s0 + sb0) >> 4;
-    const int64_t wc1 = (t1 > t0) ? ((s0 + sb1 + 15) >> 4) : wc0;
-    const int64_t full = wbytes >> 4;
-    uint4 buf[kLMax];
-#pragma unroll
-    for (int i = 0; i < kLMax; ++i) {
-        // past the span: the wave's last chunk again (one cache line, no new traffic)
-        const int64_t c = max(min(wc0 + lane + 64 * i, min(wc1, full) - 1), (int64_t)0);
-        buf[i] = *(const uint4*)(W + 16 * c);
-    }
-    __builtin_amdgcn_sched_barrier(0);
+    const int64_t cb = s0 >> 4;
+    const int64_t ce = (s0 + (int64_t)rows * rb + 15) >> 4;
+    int hb0, hb1;
+    task_span(0, th, nb, rb, BB, &hb0, &hb1);
+    const int64_t cm = (th > 0) ? ((s0 + hb1 + 15) >> 4) : cb;
+    const int64_t full = wbytes >> 4;          // complete chunks of the buffer
+    const int rbase = (int)(s0 - 16 * cb);     // LDS byte of slice byte o: wsl + rbase + o
+    const bool loader = wave >= G;
 
-    // ---- 3. quantize x into LDS
+    if (loader) {
+        // ---- loaders: both parts into LDS, kh0 / kh1 instructions each
+        const int lw = wave - G;
+        auto issue_half = [&](int64_t hs, int64_t he, int kh) {
+            const int64_t ninstr = (he - hs + 63) >> 6;
+            for (int i = 0; i < kh; ++i) {
+                const int64_t j = lw + (int64_t)GL * i;
+                const uint8_t* src;
+                uint8_t* dst;
+                if (j < ninstr) {
+                    const int64_t base = hs + 64 * j;
+                    int64_t c = base + lane;
+                    c = c < ce ? c : ce - 1;           // lanes past the slice repeat its last chunk
+                    c = c < full ? c : full - 1;       // a partial last chunk is patched below
+                    src = W + 16 * c;
+                    dst = wsl + 16 * (base - cb);      // lane l lands at dst + 16 l
+                } else {
+                    int64_t c = cb + lane;
+                    c = c < ce ? c : ce - 1;
+                    c = c < full ? c : full - 1;
+                    src = W + 16 * c;
+                    dst = dummy;
+                }
+                __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)dst, 16, 0, 0);
+            }
+        };
+        issue_half(cb, cm, kh0);
+        issue_half(cm, ce, kh1);
+        wait_vmcnt(kh1);  // the first part has landed
+    } else {
+        // ---- quantizer waves: x loads, then the shared quantizer into LDS
+        const int xsteps = (K + kQK - 1) / kQK;  // 256 values per wave step
+        float4 xv[kXPre];
+#pragma unroll
+        for (int r = 0; r < kXPre; ++r) {
+            const int e = min((wave + G * r) * kQK + 4 * lane, K - 4);
+            const float* src = x + e;
+            xv[r] = x_vec ? *(const float4*)src : make_float4(src[0], src[1], src[2], src[3]);
+        }
     if (WT != 2) {
         const int nsb = K / kQK;
 #pragma unroll
         for (int r = 0; r < kXPre; ++r) {
-            const int sb = wave + nw * r;
+            const int sb = wave + G * r;
             if (sb < nsb) {
                 const Q8KLane q = q8k_quant_lane(xv[r], lane);
                 *(uint32_t*)(act_qs + sb * kActStride + 4 * lane) = q.q4;
@@ -187,7 +221,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
                 if ((lane & 3) == 0) act_bs[sb * 16 + (lane >> 2)] = (int16_t)q.bsum;
             }
         }
-        for (int sb = wave + nw * kXPre; sb < nsb; sb += nw) {
+        for (int sb = wave + G * kXPre; sb < nsb; sb += G) {
             const float* src = x + sb * kQK + 4 * lane;
             const Q8KLane q1 = q8k_quant_lane(x_vec ? *(const float4*)src
                                                     : make_float4(src[0], src[1], src[2], src[3]), lane);
@@ -212,8 +246,8 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
         };
 #pragma unroll
         for (int r = 0; r < kXPre; ++r)
-            if (wave + nw * r < xsteps) quant_step(wave + nw * r, xv[r]);
-        for (int stp = wave + nw * kXPre; stp < xsteps; stp += nw) {
+            if (wave + G * r < xsteps) quant_step(wave + G * r, xv[r]);
+        for (int stp = wave + G * kXPre; stp < xsteps; stp += G) {
             const int e = stp * kQK + 4 * lane;
             float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
             if (e < K) {
@@ -223,20 +257,12 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
             quant_step(stp, v);
         }
     }
-    lds_barrier();  // quantized x visible to every wave; weights keep streaming
+    }
+    lds_barrier();  // quantized x and the first half of the slice visible to every wave
 
-    // ---- 4. park this wave's bytes in its region and compute its tasks
-    const int rbase = (int)(s0 - 16 * wc0);  // LDS byte of task byte o: region + rbase + o
     const int grp = lane / LPT, sub = lane % LPT;
-    int next = t0;
-    int tr = (t0 + grp) / nb, tb = (t0 + grp) - ((t0 + grp) / nb) * nb;  // this lane's task (row, block)
-    auto advance = [&](int adv) {
-        next += adv;
-        tb += adv;
-        while (tb >= nb) { tb -= nb; ++tr; }
-    };
     auto compute_task = [&](int r, int blk) {
-        const uint8_t* bp = region + rbase + __mul24(r, rb) + __mul24(blk, BB);
+        const uint8_t* bp = wsl + rbase + __mul24(r, rb) + __mul24(blk, BB);
         if (WT == 0) {
             // lane half hf: sub-blocks 4hf..4hf+3 = qs bytes [64hf, 64hf+64)
             const int hf = sub;
@@ -347,34 +373,41 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
         }
     };
 
-#pragma unroll
-    for (int st = 0; st < kLMax / kStepLoads; ++st) {
-#pragma unroll
-        for (int j = 0; j < kStepLoads; ++j) {
-            const int i = kStepLoads * st + j;
-            const int64_t c = wc0 + lane + 64 * i;
-            if (c < wc1) {
-                uint4 v = buf[i];
-                if (c >= full) {  // the buffer's last partial chunk (last wave of the grid only)
-                    uint32_t wv[4] = {0, 0, 0, 0};
-                    for (int bi = 0; bi < 16; ++bi) {
-                        const int64_t a = 16 * c + bi;
-                        if (a < wbytes) wv[bi >> 2] |= (uint32_t)W[a] << (8 * (bi & 3));
-                    }
-                    v = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-                }
-                *(uint4*)(region + 16 * (int)(c - wc0)) = v;
+
+    // Tasks [t0, t1), one pass per GPW tasks.
+    auto compute_range = [&](int t0, int t1) {
+        for (int base = t0; base < t1; base += GPW) {
+            const int t = base + grp;
+            if (t < t1) {
+                const int r = t / nb;
+                compute_task(r, t - r * nb);
             }
         }
-        // LDS operations of one wave complete in order: the parked bytes are
-        // visible to this wave's later reads without a barrier.
-        const int E = (int)(16 * (wc0 + 64 * kStepLoads * (st + 1)) - s0);
-        const int ready = min(t1, tasks_within(E, nb, rb, BB));
-        while (next < ready) {
-            const int cnt = min(GPW, ready - next);
-            if (grp < cnt) compute_task(tr, tb);
-            advance(cnt);
+    };
+
+    if (!loader) {
+        compute_range((int)((int64_t)th * wave / G), (int)((int64_t)th * (wave + 1) / G));
+    } else {
+        wait_vmcnt(0);  // the second half has landed
+        // A partial last chunk of the buffer (loaded as its predecessor above)
+        // is patched byte by byte by the lane whose chunk it is.
+        if (full < ce && (wbytes & 15) != 0) {
+            const int lw = wave - G;
+            const int64_t ninstr = (ce - cm + 63) >> 6;
+            const int64_t j = (full - cm) >> 6;   // instruction of the partial chunk
+            if (full >= cm && j < ninstr && (j % GL) == lw && lane == (int)((full - cm) & 63)) {
+                uint8_t* d = wsl + 16 * (full - cb);
+                for (int bi = 0; bi < 16; ++bi) {
+                    const int64_t a = 16 * full + bi;
+                    d[bi] = (a < wbytes) ? W[a] : (uint8_t)0;
+                }
+            }
         }
+    }
+    lds_barrier();  // the second half (and any patch) visible to every wave
+    if (loader) {
+        const int lw = wave - G;
+        compute_range(th + (int)((int64_t)(ntask - th) * lw / GL), th + (int)((int64_t)(ntask - th) * (lw + 1) / GL));
     }
     lds_barrier();
 
@@ -442,52 +475,58 @@ static int block_vals_of(int wt) { return wt == 2 ? kQK8 : kQK; }
 
 struct GemvPlan {
     int rows;          // rows per workgroup
-    int waves;         // waves per workgroup
-    int region_bytes;  // LDS bytes per wave region
+    int nq, nl;        // quantizer waves (first part of the tasks), loader waves (the rest)
+    int h1;            // tasks of the second part
+    int kh0, kh1;      // load instructions per loader wave for each part
+    int slice_bytes;   // LDS bytes of the weight slice region
     int lds;           // dynamic LDS bytes
     bool ok;
 };
 
-// Largest per-wave span (bytes, incl. 16-byte alignment slack) for a given
-// rows-per-workgroup and wave count, by walking the task split the kernel uses.
-static int max_wave_span(int rows, int nb, int rb, int bb, int nw) {
-    const int ntask = rows * nb;
-    int best = 0;
-    for (int w = 0; w < nw; ++w) {
-        const int t0 = (int)((int64_t)ntask * w / nw);
-        const int t1 = (int)((int64_t)ntask * (w + 1) / nw);
-        int b0, b1;
-        task_span(t0, t1, nb, rb, bb, &b0, &b1);
-        best = b1 - b0 > best ? b1 - b0 : best;
-    }
-    return best;
-}
-
-// About one workgroup per CU, with just enough waves that each wave computes
-// its tasks in one pass (a pass costs the same instructions however many of
-// its lanes hold a task); more waves only when a wave's span would not fit
-// its chunk budget, fewer rows when the workgroup would not fit LDS.
+// About one workgroup per CU.  The loader waves compute the last part of the
+// tasks after the whole slice has landed, so that part is kept to one pass of
+// at most one wave per SIMD (4 x 32 tasks, or a third of the tasks); the
+// quantizer waves take the rest in one pass each while it streams in.  Fewer
+// rows when the slice would not fit LDS, the waves would exceed 16, or the
+// loaders would need more instructions than a vmcnt wait can count.
 static GemvPlan gemv_plan(int wt, int64_t N, int64_t K) {
     GemvPlan p;
     const int bb = block_bytes_of(wt);
     const int nb = (int)(K / block_vals_of(wt));
     const int rb = nb * bb;
-    const int gpw = (wt == 2) ? 64 : 32;  // tasks per wave pass (64 lanes / lanes per task)
+    const int gpw = (wt == 2) ? 64 : 32;  // tasks per wave pass
     int rows = (int)((N + num_cus() - 1) / num_cus());
     if (rows < 1) rows = 1;
     for (;;) {
         const int ntask = rows * nb;
-        int nw = (ntask + gpw - 1) / gpw;
-        nw = nw < 1 ? 1 : (nw > kGemvWaves ? kGemvWaves : nw);
-        int span = max_wave_span(rows, nb, rb, bb, nw);
-        while (nw < kGemvWaves && span + 32 > kLMax * 64 * 16) span = max_wave_span(rows, nb, rb, bb, ++nw);
-        const int region = align16i(span + 32) + 32;  // alignment slack + over-read slack
-        const GemvLayout L = gemv_layout(wt, (int)K, rows, region, nw);
-        const bool fits = span + 32 <= kLMax * 64 * 16 && (size_t)L.total <= kMaxLds;
+        int h1 = ntask / 3;
+        h1 = h1 < 4 * gpw ? h1 : 4 * gpw;
+        h1 = h1 < 1 ? (ntask < 1 ? 0 : 1) : h1;
+        const int th = ntask - h1;
+        int nl = (h1 + gpw - 1) / gpw;
+        nl = nl < 1 ? 1 : nl;
+        int nq = (th + gpw - 1) / gpw;
+        nq = nq < 1 ? 1 : nq;
+        int hb0, hb1;
+        task_span(0, th, nb, rb, bb, &hb0, &hb1);
+        const int64_t slice = (int64_t)rows * rb;
+        const int64_t c_h0 = (th > 0) ? (hb1 + 15) / 16 + 1 : 0;
+        const int64_t c_h1 = (slice - hb1 + 15) / 16 + 2;
+        const int kh0 = (int)(((c_h0 + 63) / 64 + nl - 1) / nl);
+        const int kh1 = (int)(((c_h1 + 63) / 64 + nl - 1) / nl);
+        const int64_t sbytes = 16 * ((slice + 15) / 16 + 2) + 1024 + 1024 + 64;
+        const bool small = sbytes < (int64_t)kMaxLds;
+        const GemvLayout L = gemv_layout(wt, (int)K, rows, small ? (int)sbytes : 0);
+        const bool fits = small && nq + nl <= kGemvWaves && kh0 + kh1 <= 63 && kh1 <= kMaxHalfInstr &&
+                          (size_t)L.total <= kMaxLds;
         if (fits || rows == 1) {
             p.rows = rows;
-            p.waves = nw;
-            p.region_bytes = region;
+            p.nq = nq;
+            p.nl = nl;
+            p.h1 = h1;
+            p.kh0 = kh0 < 1 ? 1 : kh0;
+            p.kh1 = kh1 < 1 ? 1 : kh1;
+            p.slice_bytes = (int)sbytes;
             p.lds = L.total;
             p.ok = fits;
             return p;
@@ -516,8 +555,9 @@ static hipError_t launch_gemv_t(const uint8_t* W, int64_t N, int64_t K, const fl
     const int rb = (int)(K / WFmt<WT>::kVals) * WFmt<WT>::kBlk;
     const int grid = (int)((N + p.rows - 1) / p.rows);
     const int x_vec = (((uintptr_t)x) & 15) == 0;
-    gemv_kernel<WT><<<grid, 64 * p.waves, p.lds, st>>>(W, (int)N, (int)K, (int64_t)N * rb, x, y, xq_out,
-                                                        p.rows, p.region_bytes, x_vec);
+    gemv_kernel<WT><<<grid, 64 * (p.nq + p.nl), p.lds, st>>>(W, (int)N, (int)K, (int64_t)N * rb, x, y, xq_out,
+                                                              p.rows, p.slice_bytes, x_vec, p.nq, p.h1, p.kh0,
+                                                              p.kh1);
     return hipGetLastError();
 }
 
