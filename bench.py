@@ -16,8 +16,9 @@ The same line carries:
                   cores (a bounded number of repetitions);
   prefill / q8_0 / grouped / quantizer -- the prefill GEMM (int8 TOPS), the
                   Q8_0 x Q8_1 GEMM and GEMV, the routed-expert grouped GEMM with
-                  the weighted expert sum, and the standalone quantizer, timed
-                  with HIP events in the same run (secondary numbers).
+                  the weighted expert sum (broadcast arm, and the per-row arm
+                  at the down-projection shape), and the standalone quantizer,
+                  timed with HIP events in the same run (secondary numbers).
 
 Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 20]
 """
@@ -282,6 +283,44 @@ def run_grouped(torch, vq, synth, iters):
             "rotation_sets_cold": R, "algorithmic_bytes": int(alg)}
 
 
+def run_grouped_down(torch, vq, synth, iters):
+    """The per-row arm at the MoE down-projection shape: 256 experts of Q4_K
+    [2048, 512], one activation row per (token, slot) pair, top-8 routing."""
+    dev = torch.device("cuda:0")
+    cfg = synth.WORKLOADS["grouped_moe_down"]
+    E, N, K, T, top_k = cfg["E"], cfg["N"], cfg["K"], cfg["T"], cfg["top_k"]
+    ebytes = vq.weight_bytes(vq.Q4_K, N, K)
+    Q0 = torch.empty(E * ebytes, dtype=torch.uint8, device=dev)
+    for e in range(E):
+        We = torch.from_numpy(synth.expert_weights(e, N, K, seed=cfg["W_seed"])).to(dev)
+        vq.quantize_weights(vq.Q4_K, We, Wq=Q0[e * ebytes:(e + 1) * ebytes])
+    torch.cuda.synchronize()
+    X = torch.from_numpy(synth.tensor("grouped_moe_down", "X")).to(dev)
+    ids_np, w_np = synth.routing(T, E, top_k)
+    ids = torch.from_numpy(ids_np).to(dev)
+    rw = torch.from_numpy(w_np).to(dev)
+    Xq = vq.quantize_act(vq.Q8_K, X)
+    Y = torch.empty((T, top_k, N), dtype=torch.float32, device=dev)
+    S = torch.empty((T, N), dtype=torch.float32, device=dev)
+    ws = torch.empty(vq.grouped_workspace_bytes(E, T, top_k), dtype=torch.uint8, device=dev)
+    R = max(2, math.ceil(640 * (1 << 20) / Q0.numel()))
+    Qs = [Q0] + [Q0.clone() for _ in range(R - 1)]
+
+    def call(i, sets):
+        vq.gemm_grouped(vq.Q4_K, sets[i % len(sets)], E, N, K, vq.Q8_K, Xq, T, ids, top_k, route_w=rw,
+                        Y=Y, Ysum=S, ws=ws, per_row=True)
+
+    t_cold, _ = time_graph(lambda i: call(i, Qs), R, iters)
+    ops = 2.0 * T * top_k * N * K
+    alg = Q0.numel() + Xq.numel() + Y.numel() * 4 + S.numel() * 4 + T * top_k * 8
+    return {"shape": "E=256 x Q4_K [2048,512], per-row Q8_K input [16384,512], top-8",
+            "route_gemm_sum_us_cold": round(t_cold * 1e3, 2),
+            "tops_cold": round(ops / (t_cold * 1e-3) / 1e12, 1),
+            "mfma_frac_cold": round(ops / (t_cold * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
+            "hbm_frac_cold": round(alg / (t_cold * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "rotation_sets_cold": R, "algorithmic_bytes": int(alg)}
+
+
 def calibrate_copy(torch, nbytes):
     """A plain device copy of known size, for scaling rocprofv3 FETCH_SIZE and
     WRITE_SIZE (run under rocprofv3 --pmc)."""
@@ -366,6 +405,8 @@ def main():
         line["q8_0"] = run_q8_0(torch, vq, synth, args.secondary_iters)
         log("[bench] grouped MUL_MAT_ID")
         line["grouped"] = run_grouped(torch, vq, synth, max(5, args.secondary_iters // 2))
+        log("[bench] grouped per-row arm (MoE down projection)")
+        line["grouped_down_per_row"] = run_grouped_down(torch, vq, synth, max(5, args.secondary_iters // 2))
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline (%.0f s)" % args.cpu_seconds)
         line["cpu_baseline"] = run_cpu_baseline(args.cpu_seconds)

@@ -25,11 +25,13 @@ EXPORTS = [
     "vq_status_string", "vq_last_error", "vq_type_name", "vq_is_supported", "vq_block_values",
     "vq_block_bytes", "vq_weight_bytes", "vq_act_bytes", "vq_act_d_offset", "vq_act_aux_offset",
     "vq_quantize_act", "vq_quantize_weights", "vq_gemv", "vq_gemm", "vq_grouped_workspace_bytes",
-    "vq_gemm_grouped", "vq_weighted_sum", "vq_get_stats", "vq_reset_stats", "vq_version",
+    "vq_gemm_grouped", "vq_gemm_grouped_rows", "vq_weighted_sum", "vq_get_stats", "vq_reset_stats",
+    "vq_version",
 ]
 
 STAT_FIELDS = ["quantize_q8k", "quantize_q8_1", "quantize_weights", "gemv_q4k", "gemv_q6k", "gemv_q8_0",
-               "gemm_q4k", "gemm_q6k", "gemm_q8_0", "route", "gemm_grouped_q4k", "weighted_sum"]
+               "gemm_q4k", "gemm_q6k", "gemm_q8_0", "route", "gemm_grouped_q4k", "weighted_sum",
+               "gemm_grouped_q6k", "gemm_grouped_q8_0", "gemm_grouped_rows"]
 
 
 class VQStats(ctypes.Structure):
@@ -75,10 +77,12 @@ def lib():
         L.vq_grouped_workspace_bytes.argtypes = [I64, I64, I64]
         L.vq_grouped_workspace_bytes.restype = Z
         L.vq_gemm_grouped.argtypes = [I, P, I64, I64, I64, I, P, I64, P, I64, P, P, P, P, Z, P]
+        L.vq_gemm_grouped_rows.argtypes = [I, P, I64, I64, I64, I, P, I64, P, I64, P, P, P, P, Z, P]
         L.vq_weighted_sum.argtypes = [P, P, I64, I64, I64, P, P]
         L.vq_get_stats.argtypes = [ctypes.POINTER(VQStats)]
         L.vq_version.restype = ctypes.c_char_p
         for f in ("vq_quantize_act", "vq_quantize_weights", "vq_gemv", "vq_gemm", "vq_gemm_grouped",
+                  "vq_gemm_grouped_rows",
                   "vq_weighted_sum"):
             getattr(L, f).restype = I
         _lib = L
@@ -200,8 +204,11 @@ def gemm(w: int, W, N: int, K: int, act: int, Xq, M: int, Y=None, ldy: int = Non
 
 
 def gemm_grouped(w: int, W, E: int, N: int, K: int, act: int, Xq, T: int, ids, top_k: int,
-                 route_w=None, Y=None, Ysum=None, ws=None, want_sum: bool = True, stream=None):
-    """vq_gemm_grouped: Y[T, top_k, N] and (optionally) Ysum[T, N]; returns (Y, Ysum, ws)."""
+                 route_w=None, Y=None, Ysum=None, ws=None, want_sum: bool = True, stream=None,
+                 per_row: bool = False):
+    """vq_gemm_grouped (or, with per_row, vq_gemm_grouped_rows: Xq holds one
+    row per (t, s) pair): Y[T, top_k, N] and (optionally) Ysum[T, N]; returns
+    (Y, Ysum, ws)."""
     torch = _torch()
     dev = Xq.device
     if Y is None:
@@ -211,9 +218,10 @@ def gemm_grouped(w: int, W, E: int, N: int, K: int, act: int, Xq, T: int, ids, t
     need = grouped_workspace_bytes(E, T, top_k)
     if ws is None:
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
-    _check(lib().vq_gemm_grouped(w, _ptr(W), E, N, K, act, _ptr(Xq), T, _ptr(ids), top_k, _ptr(route_w),
-                                 _ptr(Y), _ptr(Ysum), _ptr(ws), ws.numel() if hasattr(ws, "numel") else need,
-                                 _stream(stream)))
+    fn = lib().vq_gemm_grouped_rows if per_row else lib().vq_gemm_grouped
+    _check(fn(w, _ptr(W), E, N, K, act, _ptr(Xq), T, _ptr(ids), top_k, _ptr(route_w),
+              _ptr(Y), _ptr(Ysum), _ptr(ws), ws.numel() if hasattr(ws, "numel") else need,
+              _stream(stream)))
     return Y, Ysum, ws
 
 

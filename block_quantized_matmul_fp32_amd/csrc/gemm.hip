@@ -98,7 +98,8 @@ struct GroupArgs {
     const int32_t* ntiles;  // device count of valid tiles
     const int32_t* list;    // pair indices grouped per expert
     int top_k;
-    int64_t expert_stride;  // bytes of one expert's [N][K/256] blocks
+    int per_row;            // 1: pair p reads activation row p (per-row arm); 0: row p / top_k
+    int64_t expert_stride;  // bytes of one expert's [N][K/QK] blocks
 };
 
 // Workgroup of 2 x WM waves (128 * WM threads) computing a 64 x (16 * TM * WM)
@@ -150,7 +151,7 @@ __global__ __launch_bounds__(128 * WM, 2) void gemm_kernel(const uint8_t* __rest
         if (tid < BM) {
             if (tid < rows_here) {
                 const int p = ga.list[first + tid];
-                sRow[tid] = p / ga.top_k;
+                sRow[tid] = ga.per_row ? p : p / ga.top_k;
                 sOut[tid] = p;
             } else {
                 sRow[tid] = -1;
@@ -611,10 +612,12 @@ hipError_t launch_gemm(int wtype, const uint8_t* W, int64_t N, int64_t K, const 
 // past the tile's rows skip their MFMAs.
 constexpr int kGroupBM = kGroupTileRows;
 
-hipError_t launch_gemm_grouped(const uint8_t* W, int64_t E, int64_t N, int64_t K, ActQ8K act,
-                               int64_t T, int64_t top_k, RouteWs ws, float* Y, hipStream_t st) {
-    const int nbw = (int)(K / kQK);
-    const int64_t estride = N * (int64_t)nbw * kQ4KBytes;
+template <int WT>
+static hipError_t launch_gemm_grouped_t(const uint8_t* W, int64_t E, int64_t N, int64_t K, const void* aqs,
+                                        const void* ad, const void* aux, int64_t T, int64_t top_k, int per_row,
+                                        RouteWs ws, float* Y, hipStream_t st) {
+    const int nbw = (WT == 2) ? (int)(K / kQK8) : (int)(K / kQK);
+    const int64_t estride = N * (int64_t)nbw * GemmCfg<WT>::BB;
     const int64_t max_tiles = (T * top_k + kGroupBM - 1) / kGroupBM + E;
     if (max_tiles == 0) return hipSuccess;
     dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)max_tiles);
@@ -623,10 +626,21 @@ hipError_t launch_gemm_grouped(const uint8_t* W, int64_t E, int64_t N, int64_t K
     ga.ntiles = ws.ntiles;
     ga.list = ws.list;
     ga.top_k = (int)top_k;
+    ga.per_row = per_row;
     ga.expert_stride = estride;
-    gemm_kernel<0, 2, kGroupBM / 32, true><<<grid, 256, 0, st>>>(
-        W, (int)N, (int)K, E * estride, act.qs, act.d, act.bsums, (int)T, Y, N * 1, ga);
+    gemm_kernel<WT, 2, kGroupBM / 32, true><<<grid, 256, 0, st>>>(
+        W, (int)N, (int)K, E * estride, (const int8_t*)aqs, ad, (const int16_t*)aux, (int)T, Y, N * 1, ga);
     return hipGetLastError();
+}
+
+hipError_t launch_gemm_grouped(int wtype, const uint8_t* W, int64_t E, int64_t N, int64_t K, const void* act_qs,
+                               const void* act_d, const void* act_aux, int64_t T, int64_t top_k, int per_row,
+                               RouteWs ws, float* Y, hipStream_t st) {
+    if (wtype == 0)
+        return launch_gemm_grouped_t<0>(W, E, N, K, act_qs, act_d, act_aux, T, top_k, per_row, ws, Y, st);
+    if (wtype == 1)
+        return launch_gemm_grouped_t<1>(W, E, N, K, act_qs, act_d, act_aux, T, top_k, per_row, ws, Y, st);
+    return launch_gemm_grouped_t<2>(W, E, N, K, act_qs, act_d, act_aux, T, top_k, per_row, ws, Y, st);
 }
 
 }  // namespace vqk

@@ -25,6 +25,7 @@ struct Counters {
     std::atomic<uint64_t> gemv_q4k{0}, gemv_q6k{0}, gemv_q8_0{0};
     std::atomic<uint64_t> gemm_q4k{0}, gemm_q6k{0}, gemm_q8_0{0};
     std::atomic<uint64_t> route{0}, gemm_grouped_q4k{0}, weighted_sum{0};
+    std::atomic<uint64_t> gemm_grouped_q6k{0}, gemm_grouped_q8_0{0}, gemm_grouped_rows{0};
 };
 Counters g_stats;
 
@@ -152,7 +153,7 @@ int vq_is_supported(int w, int act, int op) {
     const int want = (w == VQ_Q8_0) ? VQ_Q8_1 : VQ_Q8_K;
     if (act != want) return 0;
     if (op == VQ_OP_GEMV || op == VQ_OP_GEMM) return 1;
-    if (op == VQ_OP_GEMM_GROUPED) return w == VQ_Q4_K ? 1 : 0;
+    if (op == VQ_OP_GEMM_GROUPED) return 1;
     return 0;
 }
 
@@ -295,14 +296,13 @@ size_t vq_grouped_workspace_bytes(int64_t E, int64_t T, int64_t top_k) {
     return vqk::route_ws_layout(E, T, top_k, nullptr, nullptr);
 }
 
-vq_status vq_gemm_grouped(int w, const void* W, int64_t E, int64_t N, int64_t K, int act, const void* Xq,
-                          int64_t T, const int32_t* ids, int64_t top_k, const float* route_w, float* Y,
-                          float* Ysum, void* ws, size_t ws_bytes, hipStream_t stream) {
-    const char* fn = "vq_gemm_grouped";
+// Both arms of the routed-expert GEMM: the broadcast arm reads activation row
+// t for pair (t, s); the per-row arm reads row t*top_k + s.
+static vq_status gemm_grouped_impl(const char* fn, int per_row, int w, const void* W, int64_t E, int64_t N,
+                                   int64_t K, int act, const void* Xq, int64_t T, const int32_t* ids, int64_t top_k,
+                                   const float* route_w, float* Y, float* Ysum, void* ws, size_t ws_bytes,
+                                   hipStream_t stream) {
     VQ_TRY(check_weight(w, fn));
-    if (w != VQ_Q4_K)
-        return fail(VQ_ERR_UNSUPPORTED_TYPE, "%s: grouped weights of type %s are not supported (Q4_K only)", fn,
-                    vq_type_name(w));
     VQ_TRY(check_pair(w, act, fn));
     VQ_TRY(check_k(w, K, fn));
     VQ_TRY(check_dim(N, "N", fn));
@@ -321,7 +321,8 @@ vq_status vq_gemm_grouped(int w, const void* W, int64_t E, int64_t N, int64_t K,
     if (!aligned(W, 16) || !aligned(Xq, 16) || !aligned(ids, 4) || !aligned(Y, 16) || !aligned(ws, 256) ||
         (Ysum && (!aligned(Ysum, 16) || !aligned(route_w, 4))))
         return fail(VQ_ERR_INVALID_ARG, "%s: misaligned pointer (W, Xq, Y, Ysum: 16 B; ws: 256 B)", fn);
-    const size_t wb = vq_weight_bytes(w, E * N, K), ab = vq_act_bytes(act, T, K);
+    const int64_t arows = per_row ? T * top_k : T;
+    const size_t wb = vq_weight_bytes(w, E * N, K), ab = vq_act_bytes(act, arows, K);
     const size_t yb = (size_t)T * (size_t)top_k * (size_t)N * 4, ib = (size_t)T * (size_t)top_k * 4;
     const size_t sb = (size_t)T * (size_t)N * 4;
     if (overlap(Y, yb, W, wb) || overlap(Y, yb, Xq, ab) || overlap(Y, yb, ids, ib) || overlap(Y, yb, ws, need) ||
@@ -337,13 +338,38 @@ vq_status vq_gemm_grouped(int w, const void* W, int64_t E, int64_t N, int64_t K,
     g_stats.route++;
     vq_status s = hip_status(vqk::launch_route(ids, T, top_k, E, rws, stream), fn);
     if (s != VQ_OK) return s;
-    g_stats.gemm_grouped_q4k++;
-    s = hip_status(vqk::launch_gemm_grouped((const uint8_t*)W, E, N, K, act_q8k((void*)Xq, T, K), T, top_k, rws,
-                                            Y, stream),
-                   fn);
+    if (w == VQ_Q4_K) g_stats.gemm_grouped_q4k++;
+    else if (w == VQ_Q6_K) g_stats.gemm_grouped_q6k++;
+    else g_stats.gemm_grouped_q8_0++;
+    if (per_row) g_stats.gemm_grouped_rows++;
+    hipError_t e;
+    if (act == VQ_Q8_K) {
+        const vqk::ActQ8K a = act_q8k((void*)Xq, arows, K);
+        e = vqk::launch_gemm_grouped(w, (const uint8_t*)W, E, N, K, a.qs, a.d, a.bsums, T, top_k, per_row, rws, Y,
+                                     stream);
+    } else {
+        const vqk::ActQ81 a = act_q81((void*)Xq, arows, K);
+        e = vqk::launch_gemm_grouped(w, (const uint8_t*)W, E, N, K, a.qs, a.d, nullptr, T, top_k, per_row, rws, Y,
+                                     stream);
+    }
+    s = hip_status(e, fn);
     if (s != VQ_OK || !Ysum) return s;
     g_stats.weighted_sum++;
     return hip_status(vqk::launch_weighted_sum(Y, route_w, T, top_k, N, Ysum, stream), fn);
+}
+
+vq_status vq_gemm_grouped(int w, const void* W, int64_t E, int64_t N, int64_t K, int act, const void* Xq,
+                          int64_t T, const int32_t* ids, int64_t top_k, const float* route_w, float* Y,
+                          float* Ysum, void* ws, size_t ws_bytes, hipStream_t stream) {
+    return gemm_grouped_impl("vq_gemm_grouped", 0, w, W, E, N, K, act, Xq, T, ids, top_k, route_w, Y, Ysum, ws,
+                             ws_bytes, stream);
+}
+
+vq_status vq_gemm_grouped_rows(int w, const void* W, int64_t E, int64_t N, int64_t K, int act, const void* Xq,
+                               int64_t T, const int32_t* ids, int64_t top_k, const float* route_w, float* Y,
+                               float* Ysum, void* ws, size_t ws_bytes, hipStream_t stream) {
+    return gemm_grouped_impl("vq_gemm_grouped_rows", 1, w, W, E, N, K, act, Xq, T, ids, top_k, route_w, Y, Ysum,
+                             ws, ws_bytes, stream);
 }
 
 vq_status vq_weighted_sum(const float* Y, const float* route_w, int64_t T, int64_t top_k, int64_t N, float* Ysum,
@@ -378,6 +404,9 @@ void vq_get_stats(vq_stats* out) {
     out->route = g_stats.route.load();
     out->gemm_grouped_q4k = g_stats.gemm_grouped_q4k.load();
     out->weighted_sum = g_stats.weighted_sum.load();
+    out->gemm_grouped_q6k = g_stats.gemm_grouped_q6k.load();
+    out->gemm_grouped_q8_0 = g_stats.gemm_grouped_q8_0.load();
+    out->gemm_grouped_rows = g_stats.gemm_grouped_rows.load();
 }
 
 void vq_reset_stats(void) {
@@ -393,6 +422,9 @@ void vq_reset_stats(void) {
     g_stats.route = 0;
     g_stats.gemm_grouped_q4k = 0;
     g_stats.weighted_sum = 0;
+    g_stats.gemm_grouped_q6k = 0;
+    g_stats.gemm_grouped_q8_0 = 0;
+    g_stats.gemm_grouped_rows = 0;
 }
 
 const char* vq_version(void) { return "vq 0.1.0 (gfx950)"; }

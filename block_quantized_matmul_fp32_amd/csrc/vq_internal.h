@@ -56,8 +56,9 @@ struct RouteWs {
 size_t route_ws_layout(int64_t E, int64_t T, int64_t top_k, RouteWs* ws, uint8_t* base);
 hipError_t launch_route(const int32_t* ids, int64_t T, int64_t top_k, int64_t E, RouteWs ws,
                         hipStream_t st);
-hipError_t launch_gemm_grouped(const uint8_t* W, int64_t E, int64_t N, int64_t K, ActQ8K act,
-                               int64_t T, int64_t top_k, RouteWs ws, float* Y, hipStream_t st);
+hipError_t launch_gemm_grouped(int wtype, const uint8_t* W, int64_t E, int64_t N, int64_t K, const void* act_qs,
+                               const void* act_d, const void* act_aux, int64_t T, int64_t top_k, int per_row,
+                               RouteWs ws, float* Y, hipStream_t st);
 hipError_t launch_weighted_sum(const float* Y, const float* w, int64_t T, int64_t top_k, int64_t N,
                                float* Ysum, hipStream_t st);
 

@@ -119,7 +119,7 @@ const char* vq_type_name(int t);
 
 /* 1 if weights of type w with activations of type act are supported by op,
  * else 0 (the pages' keep-quant capability query).  Q4_K and Q6_K pair with
- * Q8_K; Q8_0 pairs with Q8_1.  The grouped op supports Q4_K x Q8_K. */
+ * Q8_K; Q8_0 pairs with Q8_1; every op supports every pair. */
 int vq_is_supported(int w, int act, int op);
 
 /* Values per block (256 or 32) and bytes per block; 0 for an unknown type. */
@@ -195,14 +195,18 @@ vq_status vq_gemm(int w, const void* W, int64_t N, int64_t K, int act, const voi
 
 /* ---------------------------------------------------------------------- */
 /* Routed-expert grouped GEMM (MUL_MAT_ID, broadcast arm) with the weighted  */
-/* expert sum:                                                             */
+/* expert sum ([P3] "routed-compact J rule" and "weighted expert sum";     */
+/* [P2] "grouped Q8_0 delegation": every weight type, Q8_0 paired with a    */
+/* 32-block activation):                                                   */
 /*   Y[t][s][:] = W_(ids[t][s]) . x_t  for t < T, s < top_k                 */
 /*   Ysum[t][n] = (((w0*y0 + w1*y1) + w2*y2) + ...), slots ascending, each  */
 /*                product and sum rounded on its own (skipped if Ysum NULL) */
-/* W: [E][N][K/256] Q4_K blocks; Xq: Q8_K planar buffer of T rows; ids int32 */
-/* [T][top_k], each in [0,E) and distinct within a token (a precondition,    */
-/* not checked on the device); route_w fp32 [T][top_k] (required when Ysum  */
-/* is given); Y fp32 [T][top_k][N]; Ysum fp32 [T][N] or NULL.               */
+/* w: Q4_K, Q6_K (act Q8_K) or Q8_0 (act Q8_1).  W: [E][N][K/QK] blocks;     */
+/* Xq: planar activation buffer of T rows; ids int32 [T][top_k], each in    */
+/* [0,E) and distinct within a token (a precondition, not checked on the    */
+/* device; a pair whose id is outside [0,E) is not computed); route_w fp32  */
+/* [T][top_k] (required when Ysum is given); Y fp32 [T][top_k][N]; Ysum     */
+/* fp32 [T][N] or NULL.                                                     */
 /* ws: workspace of vq_grouped_workspace_bytes(E, T, top_k) bytes; after the */
 /* call it holds, at offset 0, int32 counts[E], then int32 offsets[E+1],     */
 /* then int32 list[T*top_k] (pair indices t*top_k+s grouped per expert in   */
@@ -215,6 +219,17 @@ vq_status vq_gemm_grouped(int w, const void* W, int64_t E, int64_t N, int64_t K,
                           const void* Xq, int64_t T, const int32_t* ids, int64_t top_k,
                           const float* route_w, float* Y, float* Ysum, void* ws,
                           size_t ws_bytes, hipStream_t stream);
+
+/* Per-row arm of the same operation ([P2] "kROCM keep-quant provider": the  */
+/* grouped towers have a broadcast and a per-row arm), e.g. an MoE down     */
+/* projection whose input differs per (token, slot):                       */
+/*   Y[t][s][:] = W_(ids[t][s]) . x_(t*top_k+s)                              */
+/* Xq holds T*top_k rows; every other argument, the workspace, limits and    */
+/* errors are those of vq_gemm_grouped.                                     */
+vq_status vq_gemm_grouped_rows(int w, const void* W, int64_t E, int64_t N, int64_t K, int act,
+                               const void* Xq, int64_t T, const int32_t* ids, int64_t top_k,
+                               const float* route_w, float* Y, float* Ysum, void* ws,
+                               size_t ws_bytes, hipStream_t stream);
 
 /* Weighted expert sum alone (same definition as in vq_gemm_grouped):
  * Y fp32 [T][top_k][N], route_w fp32 [T][top_k], Ysum fp32 [T][N]; N % 4 == 0. */
@@ -238,6 +253,9 @@ typedef struct {
     uint64_t route;
     uint64_t gemm_grouped_q4k;
     uint64_t weighted_sum;
+    uint64_t gemm_grouped_q6k;
+    uint64_t gemm_grouped_q8_0;
+    uint64_t gemm_grouped_rows;  /* calls of the per-row arm (also counted per type) */
 } vq_stats;
 
 void vq_get_stats(vq_stats* out);

@@ -68,8 +68,8 @@ def _bind(path):
                                       ctypes.c_int]
     L.oracle_subblock_sums.argtypes = [ctypes.c_int, P, P, P]
     L.oracle_route.argtypes = [P, I64, I64, I64, P, P, P]
-    L.oracle_gemm_grouped.argtypes = [ctypes.c_int, P, I64, I64, I64, P, P, P, I64, P, I64, P,
-                                      ctypes.c_int]
+    L.oracle_gemm_grouped.argtypes = [ctypes.c_int, P, I64, I64, I64, P, P, P, I64, P, I64,
+                                      ctypes.c_int, P, ctypes.c_int]
     L.oracle_weighted_sum.argtypes = [P, P, I64, I64, I64, P]
     L.oracle_max_threads.restype = ctypes.c_int
     return L
@@ -274,14 +274,17 @@ def route(ids: np.ndarray, E: int):
     return counts, offsets, lst
 
 
-def gemm_grouped(wtype, Wq, E, N, K, act: Q8K, ids, nthreads: int = 1) -> np.ndarray:
-    """Y[t, s, :] = W_{ids[t,s]} . x_t."""
+def gemm_grouped(wtype, Wq, E, N, K, act, ids, nthreads: int = 1, per_row: bool = False) -> np.ndarray:
+    """Y[t, s, :] = W_{ids[t,s]} . x, with x the token's row x_t (broadcast arm)
+    or the pair's own row x_{t*top_k+s} (per-row arm)."""
     ids = np.ascontiguousarray(ids, np.int32)
     T, top_k = ids.shape
+    qs, d, bs = _act_args(wtype, act)
+    assert qs.shape[0] == (T * top_k if per_row else T), "activation rows"
     Y = np.zeros((T, top_k, N), np.float32)
     Wq = np.ascontiguousarray(Wq, np.uint8)
-    lib().oracle_gemm_grouped(wtype, _p(Wq), E, N, K, _p(act.qs), _p(act.d), _p(act.bsums), T,
-                              _p(ids), top_k, _p(Y), int(nthreads))
+    lib().oracle_gemm_grouped(wtype, _p(Wq), E, N, K, _p(qs), _p(d), _p(bs), T,
+                              _p(ids), top_k, int(per_row), _p(Y), int(nthreads))
     return Y
 
 

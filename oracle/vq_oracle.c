@@ -615,10 +615,10 @@ void oracle_route(const int32_t* ids, int64_t T, int64_t top_k, int64_t E, int32
 /* Y[t][s][n] = dot(W_{ids[t][s]} row n, x_t) for Q8_K activations; W is
  * [E][N] rows of K/256 blocks. */
 void oracle_gemm_grouped(int type, const uint8_t* W, int64_t E, int64_t N, int64_t K,
-                         const int8_t* qs, const float* d, const int16_t* bsums, int64_t T,
-                         const int32_t* ids, int64_t top_k, float* Y, int nthreads) {
+                         const int8_t* qs, const void* d, const int16_t* bsums, int64_t T,
+                         const int32_t* ids, int64_t top_k, int per_row, float* Y, int nthreads) {
     int64_t rb = row_bytes(type, K);
-    int64_t nb = K / QK_K;
+    int64_t nbd = (type == 2) ? K / QK8 : K / QK_K;
     int64_t total = T * top_k * N;
     (void)E;
 #ifdef _OPENMP
@@ -627,11 +627,14 @@ void oracle_gemm_grouped(int type, const uint8_t* W, int64_t E, int64_t N, int64
 #endif
     for (int64_t idx = 0; idx < total; ++idx) {
         int64_t p = idx / N, n = idx % N;
-        int64_t t = p / top_k;
+        /* broadcast arm: the pair's token row; per-row arm: the pair's own row */
+        int64_t a = per_row ? p : p / top_k;
         int64_t e = ids[p];
         const uint8_t* wrow = W + (e * N + n) * rb;
-        const void* aux = (type == 0) ? (const void*)(bsums + t * (K / 16)) : NULL;
-        Y[idx] = dot_row(type, wrow, K, qs + t * K, d + t * nb, aux);
+        const void* drow = (type == 2) ? (const void*)((const uint16_t*)d + a * nbd)
+                                       : (const void*)((const float*)d + a * nbd);
+        const void* aux = (type == 0) ? (const void*)(bsums + a * (K / 16)) : NULL;
+        Y[idx] = dot_row(type, wrow, K, qs + a * K, drow, aux);
     }
 }
 

@@ -41,6 +41,12 @@ WORKLOADS = {
         "W_seed": 51, "W_sigma": 0.02, "X": ((2048, 2048), 52, 1.0),
         "ids_seed": 53, "logits_seed": 54,
     },
+    "grouped_moe_down": {
+        "desc": "per-row arm: 256 experts Q4_K [2048,512], one Q8_K row per (token, slot): "
+                "[2048*8, 512], the grouped_moe routing",
+        "E": 256, "N": 2048, "K": 512, "T": 2048, "top_k": 8,
+        "W_seed": 61, "W_sigma": 0.02, "X": ((2048 * 8, 512), 62, 1.0),
+    },
 }
 
 

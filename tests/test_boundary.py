@@ -35,8 +35,8 @@ def declared_functions():
 
 def test_header_declares_expected_api():
     names = declared_functions()
-    for f in ("vq_quantize_act", "vq_gemv", "vq_gemm", "vq_gemm_grouped", "vq_is_supported",
-              "vq_weighted_sum", "vq_quantize_weights"):
+    for f in ("vq_quantize_act", "vq_gemv", "vq_gemm", "vq_gemm_grouped", "vq_gemm_grouped_rows",
+              "vq_is_supported", "vq_weighted_sum", "vq_quantize_weights"):
         assert f in names
 
 
@@ -70,12 +70,11 @@ def test_sizes(vq):
 
 def test_capability_query(vq):
     S = vq.is_supported
-    for op in (vq.OP_GEMV, vq.OP_GEMM):
+    for op in (vq.OP_GEMV, vq.OP_GEMM, vq.OP_GEMM_GROUPED):
         assert S(vq.Q4_K, vq.Q8_K, op) and S(vq.Q6_K, vq.Q8_K, op) and S(vq.Q8_0, vq.Q8_1, op)
         assert not S(vq.Q4_K, vq.Q8_1, op) and not S(vq.Q8_0, vq.Q8_K, op)
         assert not S(vq.Q8_K, vq.Q8_K, op) and not S(17, vq.Q8_K, op)
-    assert S(vq.Q4_K, vq.Q8_K, vq.OP_GEMM_GROUPED)
-    assert not S(vq.Q6_K, vq.Q8_K, vq.OP_GEMM_GROUPED)
+    assert not S(vq.Q4_K, vq.Q8_K, 7)
 
 
 FAKE = 0x10000000  # never dereferenced: every call below fails validation first
@@ -95,9 +94,12 @@ def test_unsupported_types_are_named(vq):
     assert "Q8_K" in msg
     msg = _err(vq, 2, "vq_quantize_act", vq.Q4_K, FAKE, 4, 256, 256, FAKE, None)
     assert "Q4_K" in msg
-    msg = _err(vq, 2, "vq_gemm_grouped", vq.Q6_K, FAKE, 8, 64, 256, vq.Q8_K, FAKE, 4, FAKE, 2, FAKE,
-               FAKE, None, FAKE, 1 << 20, None)
-    assert "Q6_K" in msg
+    for fn in ("vq_gemm_grouped", "vq_gemm_grouped_rows"):
+        msg = _err(vq, 2, fn, vq.Q8_1, FAKE, 8, 64, 256, vq.Q8_K, FAKE, 4, FAKE, 2, FAKE,
+                   FAKE, None, FAKE, 1 << 20, None)
+        assert "Q8_1" in msg and fn in msg
+    _err(vq, 3, "vq_gemm_grouped_rows", vq.Q8_0, FAKE, 8, 64, 256, vq.Q8_K, FAKE, 4, FAKE, 2, FAKE,
+         FAKE, None, FAKE, 1 << 20, None)
 
 
 def test_type_pairing(vq):

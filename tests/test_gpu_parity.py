@@ -278,20 +278,21 @@ def test_determinism_and_witness():
 
 
 # ------------------------------------------------------------------ grouped
-def run_grouped(E, N, K, T, top_k, ids, seed):
+def run_grouped(E, N, K, T, top_k, ids, seed, wtype=oracle.Q4_K, per_row=False):
     W = np.stack([synth.normal((seed, e), (N, K), 0.02) for e in range(E)])
-    Wq = np.stack([oracle.quantize_weights(oracle.Q4_K, W[e]) for e in range(E)]).reshape(E * N, -1)
-    X = synth.normal(seed + 1, (T, K))
+    Wq = np.stack([oracle.quantize_weights(wtype, W[e]) for e in range(E)]).reshape(E * N, -1)
+    X = synth.normal(seed + 1, (T * top_k if per_row else T, K))
     logits = synth.normal(seed + 2, (T, top_k))
     z = np.exp(logits - logits.max(1, keepdims=True))
     rw = (z / z.sum(1, keepdims=True)).astype(np.float32)
-    act = oracle.quantize_q8k(X)
-    H.say("grouped E=%d N=%d K=%d T=%d top_k=%d" % (E, N, K, T, top_k))
-    Xq = vq.quantize_act(vq.Q8_K, H.to_dev(X))
+    act = oracle_act(wtype, X)
+    at = vq.Q8_1 if wtype == oracle.Q8_0 else vq.Q8_K
+    H.say("grouped %s per_row=%d E=%d N=%d K=%d T=%d top_k=%d" % (WNAME[wtype], per_row, E, N, K, T, top_k))
+    Xq = vq.quantize_act(at, H.to_dev(X))
     Yd = H.to_dev(np.full((T, top_k, N), np.nan, np.float32))
     Sd = H.to_dev(np.full((T, N), np.nan, np.float32))
-    Y, Ysum, ws = vq.gemm_grouped(vq.Q4_K, H.to_dev(Wq), E, N, K, vq.Q8_K, Xq, T, H.to_dev(ids), top_k,
-                                  route_w=H.to_dev(rw), Y=Yd, Ysum=Sd)
+    Y, Ysum, ws = vq.gemm_grouped(wtype, H.to_dev(Wq), E, N, K, at, Xq, T, H.to_dev(ids), top_k,
+                                  route_w=H.to_dev(rw), Y=Yd, Ysum=Sd, per_row=per_row)
     return Wq, act, rw, Y, Ysum, ws
 
 
@@ -328,6 +329,27 @@ def test_grouped_small(case):
     ids2 = ids.copy(); ids2[:, [0, 1]] = ids2[:, [1, 0]]
     _, _, _, Y2, _, _ = run_grouped(E, N, K, T, top_k, ids2, 1810)
     assert not np.array_equal(H.host(Y2), Yh)
+
+
+@pytest.mark.parametrize("per_row", [False, True])
+@pytest.mark.parametrize("wtype", WTYPES)
+def test_grouped_types_and_arms(wtype, per_row):
+    """Every weight type in both arms (broadcast: x_t; per-row: x_(t*top_k+s)):
+    routing, Y and the weighted sum bit-identical to the oracle."""
+    E, N, K, top_k, T = 10, 48, 512, 3, 70
+    ids = synth.random_ids(1850 + wtype, T, E, top_k)
+    vq.reset_stats()
+    Wq, act, rw, Y, Ysum, ws = run_grouped(E, N, K, T, top_k, ids, 1860, wtype, per_row)
+    counts, offsets, lst = vq.grouped_ws_views(ws, E, T, top_k)
+    c_ref, o_ref, l_ref = oracle.route(ids, E)
+    assert np.array_equal(H.host(counts), c_ref) and np.array_equal(H.host(lst), l_ref)
+    Y_ref = oracle.gemm_grouped(wtype, Wq, E, N, K, act, ids, nthreads=8, per_row=per_row)
+    Yh = H.host(Y)
+    H.assert_bitwise(Yh, Y_ref, "grouped %s per_row=%d" % (WNAME[wtype], per_row))
+    H.assert_bitwise(H.host(Ysum), oracle.weighted_sum(Yh, rw), "weighted sum of the GPU's Y")
+    st = vq.get_stats()
+    key = {oracle.Q4_K: "gemm_grouped_q4k", oracle.Q6_K: "gemm_grouped_q6k", oracle.Q8_0: "gemm_grouped_q8_0"}[wtype]
+    assert st[key] == 1 and st["gemm_grouped_rows"] == int(per_row) and st["route"] == 1
 
 
 def test_grouped_expert_permutation():

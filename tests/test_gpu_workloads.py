@@ -182,3 +182,29 @@ def test_grouped_moe_full_size():
     Y_ref = oracle.gemm_grouped(oracle.Q4_K, Wq, E, N, K, act_s, ids[toks], nthreads=THREADS)
     H.assert_bitwise(Yh[toks], Y_ref, "grouped Y (sampled tokens)")
     H.assert_bitwise(H.host(S), oracle.weighted_sum(Yh, rw), "Ysum")
+
+
+def test_grouped_moe_down_per_row_full_size():
+    """The per-row arm at the MoE down-projection shape: 256 experts of Q4_K
+    [2048, 512], each (token, slot) pair with its own activation row, the
+    top-8 routing of the grouped workload: Y on sampled tokens, Ysum in full."""
+    cfg = synth.WORKLOADS["grouped_moe_down"]
+    E, N, K, T, top_k = cfg["E"], cfg["N"], cfg["K"], cfg["T"], cfg["top_k"]
+    Wq = np.concatenate([oracle.quantize_weights(oracle.Q4_K, synth.expert_weights(e, N, K, seed=cfg["W_seed"]))
+                         for e in range(E)])
+    X = synth.tensor("grouped_moe_down", "X")
+    ids, rw = synth.routing(T, E, top_k)
+    H.say("grouped MoE down (per-row) E=%d N=%d K=%d T=%d top_k=%d" % (E, N, K, T, top_k))
+    Xq = vq.quantize_act(vq.Q8_K, H.to_dev(X))
+    Y, S, ws = vq.gemm_grouped(vq.Q4_K, H.to_dev(Wq), E, N, K, vq.Q8_K, Xq, T, H.to_dev(ids), top_k,
+                               route_w=H.to_dev(rw),
+                               Y=H.to_dev(np.full((T, top_k, N), np.nan, np.float32)),
+                               Ysum=H.to_dev(np.full((T, N), np.nan, np.float32)), per_row=True)
+    Yh = H.host(Y)
+    assert np.isfinite(Yh).all(), "every (t, s) row written"
+    toks = np.unique(np.concatenate([[0, T - 1], np.random.default_rng(7300).integers(0, T, 14)]))
+    rows = (toks[:, None] * top_k + np.arange(top_k)[None, :]).reshape(-1)
+    act_s = oracle.quantize_q8k(X[rows])
+    Y_ref = oracle.gemm_grouped(oracle.Q4_K, Wq, E, N, K, act_s, ids[toks], nthreads=THREADS, per_row=True)
+    H.assert_bitwise(Yh[toks], Y_ref, "grouped down Y (sampled tokens)")
+    H.assert_bitwise(H.host(S), oracle.weighted_sum(Yh, rw), "Ysum")

@@ -341,17 +341,50 @@ def test_route_golden_and_library_sort():
     assert offsets[-1] == flat.size and (np.diff(offsets) == counts).all()
 
 
-def test_grouped_matches_dense_per_expert():
+@pytest.mark.parametrize("wtype", [oracle.Q4_K, oracle.Q6_K, oracle.Q8_0])
+def test_grouped_matches_dense_per_expert(wtype):
+    """Broadcast arm: each slot is its expert's dense product with the token row."""
     E, N, K, T, top_k = 6, 24, 512, 10, 3
     W = np.stack([synth.normal((700, e), (N, K), 0.02) for e in range(E)])
-    Wq = np.stack([oracle.quantize_weights(oracle.Q4_K, W[e]) for e in range(E)])
-    act = oracle.quantize_q8k(synth.normal(701, (T, K)))
+    Wq = np.stack([oracle.quantize_weights(wtype, W[e]) for e in range(E)])
+    X = synth.normal(701, (T, K))
+    act = oracle.quantize_q8_1(X) if wtype == oracle.Q8_0 else oracle.quantize_q8k(X)
     ids = synth.random_ids(702, T, E, top_k)
-    Y = oracle.gemm_grouped(oracle.Q4_K, Wq.reshape(E * N, -1), E, N, K, act, ids)
+    Y = oracle.gemm_grouped(wtype, Wq.reshape(E * N, -1), E, N, K, act, ids)
     for e in range(E):
-        dense = oracle.gemm(oracle.Q4_K, Wq[e], N, K, act)
+        dense = oracle.gemm(wtype, Wq[e], N, K, act)
         t, s = np.nonzero(ids == e)
         assert (Y[t, s] == dense[t]).all()
+    # against the fp64 definition, slot by slot
+    r64 = np.stack([ref_fp64.gemm_fp64(wtype, Wq[ids[t, s]], N, K,
+                                       oracle.quantize_q8_1(X[t:t + 1]) if wtype == oracle.Q8_0
+                                       else oracle.quantize_q8k(X[t:t + 1]))[0]
+                    for t in range(T) for s in range(top_k)]).reshape(T, top_k, N)
+    assert ref_fp64.max_rel_err(Y, r64)[0] <= 5e-4
+
+
+@pytest.mark.parametrize("wtype", [oracle.Q4_K, oracle.Q6_K, oracle.Q8_0])
+def test_grouped_per_row_arm(wtype):
+    """Per-row arm: each pair has its own activation row.  With every pair's
+    row equal to its token's row it reduces to the broadcast arm bitwise; with
+    distinct rows each slot is its expert's dense product with that row."""
+    E, N, K, T, top_k = 5, 16, 256, 7, 2
+    W = np.stack([synth.normal((710, e), (N, K), 0.02) for e in range(E)])
+    Wq = np.stack([oracle.quantize_weights(wtype, W[e]) for e in range(E)]).reshape(E * N, -1)
+    ids = synth.random_ids(712, T, E, top_k)
+    q = oracle.quantize_q8_1 if wtype == oracle.Q8_0 else oracle.quantize_q8k
+    X = synth.normal(711, (T, K))
+    Xrep = np.repeat(X, top_k, axis=0)
+    Yb = oracle.gemm_grouped(wtype, Wq, E, N, K, q(X), ids)
+    Yr = oracle.gemm_grouped(wtype, Wq, E, N, K, q(Xrep), ids, per_row=True)
+    assert (Yb.view(np.uint32) == Yr.view(np.uint32)).all()
+    Xp = synth.normal(713, (T * top_k, K))
+    Yp = oracle.gemm_grouped(wtype, Wq, E, N, K, q(Xp), ids, per_row=True)
+    Wr = Wq.reshape(E, N, -1)
+    for t in range(T):
+        for s in range(top_k):
+            dense = oracle.gemm(wtype, Wr[ids[t, s]], N, K, q(Xp[t * top_k + s:t * top_k + s + 1]))[0]
+            assert (Yp[t, s].view(np.uint32) == dense.view(np.uint32)).all()
 
 
 def test_weighted_sum_golden():
