@@ -584,18 +584,36 @@ __global__ __launch_bounds__(128 * WM, 2) void gemm_kernel(const uint8_t* __rest
     }
 }
 
-template <int WT>
-static hipError_t launch_gemm_t(const uint8_t* W, int64_t N, int64_t K, const void* aqs, const void* ad,
-                                const void* aux, int64_t M, float* Y, int64_t ldy, hipStream_t st) {
-    constexpr int WM = 4, TM = 4;
+template <int WT, int WM, int TM>
+static hipError_t launch_gemm_cfg(const uint8_t* W, int64_t N, int64_t K, const void* aqs, const void* ad,
+                                  const void* aux, int64_t M, float* Y, int64_t ldy, hipStream_t st) {
     constexpr int BM = 16 * TM * WM;
     const int nbw = (WT == 2) ? (int)(K / kQK8) : (int)(K / kQK);
     const int64_t wbytes = N * (int64_t)nbw * GemmCfg<WT>::BB;
     dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + BM - 1) / BM));
     GroupArgs ga = {};
     gemm_kernel<WT, WM, TM, false><<<grid, 128 * WM, 0, st>>>(W, (int)N, (int)K, wbytes, (const int8_t*)aqs, ad,
-                                                          (const int16_t*)aux, (int)M, Y, ldy, ga);
+                                                              (const int16_t*)aux, (int)M, Y, ldy, ga);
     return hipGetLastError();
+}
+
+// Tile choice: 64 x 256 tiles unless they would leave CUs without a
+// workgroup (then 64 x 128 tiles on the same eight waves, twice the
+// workgroups); Q8_0, whose per-block epilogue dominates, always takes the
+// 64 x 128 tiles (measured faster at every workload shape).
+template <int WT>
+static hipError_t launch_gemm_t(const uint8_t* W, int64_t N, int64_t K, const void* aqs, const void* ad,
+                                const void* aux, int64_t M, float* Y, int64_t ldy, hipStream_t st) {
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0, v = 0;
+        (void)hipGetDevice(&dev);
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+        cus = v;
+    }
+    const int64_t wg256 = ((N + kBN - 1) / kBN) * ((M + 255) / 256);
+    if (WT == 2 || wg256 < cus) return launch_gemm_cfg<WT, 4, 2>(W, N, K, aqs, ad, aux, M, Y, ldy, st);
+    return launch_gemm_cfg<WT, 4, 4>(W, N, K, aqs, ad, aux, M, Y, ldy, st);
 }
 
 hipError_t launch_gemm(int wtype, const uint8_t* W, int64_t N, int64_t K, const void* act_qs,

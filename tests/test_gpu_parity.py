@@ -170,6 +170,28 @@ def test_gemm_bitexact(wtype):
     assert ref_fp64.max_rel_err(Yh[:, :N], r)[0] <= REL_MAX
 
 
+@pytest.mark.parametrize("wtype", [oracle.Q4_K, oracle.Q6_K])
+def test_gemm_large_tile_ragged(wtype):
+    """Enough column tiles that the 64 x 256 tile configuration runs, with a
+    ragged last row tile (M = 300) and column tile (N % 64 = 16); every
+    output written, sampled outputs bit-identical to the oracle."""
+    M, N, K = 300, 16400, 512
+    W = synth.normal(1350 + wtype, (N, K), 0.02)
+    X = synth.normal(1360 + wtype, (M, K))
+    Wq = oracle.quantize_weights(wtype, W)
+    act = oracle_act(wtype, X)
+    H.say("gemm large tile %s M=%d N=%d K=%d" % (WNAME[wtype], M, N, K))
+    Yd = H.to_dev(np.full((M, N), np.nan, np.float32))
+    vq.gemm(wtype, H.to_dev(Wq), N, K, vq.Q8_K, H.to_dev(H.pack_act(act, wtype)), M, Y=Yd)
+    Yh = H.host(Yd)
+    assert np.isfinite(Yh).all()
+    rng = np.random.default_rng(1370)
+    ms = np.concatenate([np.arange(M), rng.integers(0, M, 3000), np.full(N, M - 1)]).astype(np.int64)
+    ns = np.concatenate([np.full(M, N - 1), rng.integers(0, N, 3000), np.arange(N)]).astype(np.int64)
+    ref = oracle.gemm_sampled(wtype, Wq, N, K, act, ms, ns, nthreads=8)
+    H.assert_bitwise(Yh[ms, ns], ref, "gemm large tile %s" % WNAME[wtype])
+
+
 @pytest.mark.parametrize("wtype", WTYPES)
 def test_gemm_from_device_quantizer(wtype):
     """GPU quantize_act feeding GPU GEMM, decode-through-prefill M values."""
