@@ -31,7 +31,7 @@ EXPORTS = [
 
 STAT_FIELDS = ["quantize_q8k", "quantize_q8_1", "quantize_weights", "gemv_q4k", "gemv_q6k", "gemv_q8_0",
                "gemm_q4k", "gemm_q6k", "gemm_q8_0", "route", "gemm_grouped_q4k", "weighted_sum",
-               "gemm_grouped_q6k", "gemm_grouped_q8_0", "gemm_grouped_rows"]
+               "gemm_grouped_q6k", "gemm_grouped_q8_0", "gemm_grouped_rows", "gemm_skinny"]
 
 
 class VQStats(ctypes.Structure):

@@ -60,24 +60,27 @@ template <>
 struct WFmt<2> { static constexpr int kBlk = kQ80Bytes; static constexpr int kVals = kQK8; };
 
 struct GemvLayout {
-    int act_qs, act_d, act_bs, partial, wslice, slice_bytes, total;
+    int act_qs, act_row, act_d, act_bs, partial, wslice, slice_bytes, total;
 };
 
 __host__ __device__ inline int align16i(int x) { return (x + 15) & ~15; }
 
-// LDS layout of the GEMV workgroup; identical on host and device.  The weight
-// slice region holds the slice's 16-byte chunks, 1 KiB past the slice for the
-// last instruction's lanes beyond it, 1 KiB for padding instructions, and
-// over-read slack.
-__host__ __device__ inline GemvLayout gemv_layout(int wt, int K, int rows, int slice_bytes) {
+// LDS layout of the GEMV workgroup for mb activation rows; identical on host
+// and device.  Per activation row: the quantized bytes (act_row bytes), the
+// block scales (K/QK floats) and the Q8_K sub-block sums (K/16 int16) or the
+// Q8_1 packed d | s words (K/32).  The weight slice region holds the slice's
+// 16-byte chunks, 1 KiB past the slice for the last instruction's lanes
+// beyond it, 1 KiB for padding instructions, and over-read slack.
+__host__ __device__ inline GemvLayout gemv_layout(int wt, int K, int rows, int slice_bytes, int mb) {
     GemvLayout L;
     const int nbw = (wt == 2) ? K / kQK8 : K / kQK;
     L.act_qs = 0;
-    L.act_d = (wt == 2) ? align16i(K) : (K / kQK) * kActStride;
-    L.act_bs = L.act_d + align16i(nbw * 4);
+    L.act_row = (wt == 2) ? align16i(K) : (K / kQK) * kActStride;
+    L.act_d = mb * L.act_row;
+    L.act_bs = L.act_d + align16i(mb * nbw * 4);
     const int nbs_bytes = (wt == 2) ? (K / kQK8) * 4 : (K / 16) * 2;
-    L.partial = L.act_bs + align16i(nbs_bytes);
-    L.wslice = L.partial + align16i(rows * nbw * 4);
+    L.partial = L.act_bs + align16i(mb * nbs_bytes);
+    L.wslice = L.partial + align16i(mb * rows * nbw * 4);
     L.slice_bytes = slice_bytes;
     L.total = L.wslice + slice_bytes;
     return L;
@@ -125,11 +128,15 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int WT>
+// MB activation rows (1: the decode GEMV; 2, 4, 8: small batches).  With
+// xq_in == nullptr the quantizer waves quantize x (MB == 1); otherwise they
+// copy M rows of a planar pre-quantized activation buffer into LDS.
+template <int WT, int MB>
 __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
     const uint8_t* __restrict__ W, int N, int K, int64_t wbytes, const float* __restrict__ x,
     float* __restrict__ y, uint8_t* __restrict__ xq_out, int rows_per_wg, int slice_bytes, int x_vec,
-    int nq, int h1_tasks, int kh0, int kh1) {
+    int nq, int h1_tasks, int kh0, int kh1, const uint8_t* __restrict__ xq_in, int M, int64_t ldy,
+    int64_t xq_d_off, int64_t xq_aux_off) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     constexpr int BB = WFmt<WT>::kBlk;
     constexpr int QV = WFmt<WT>::kVals;
@@ -146,7 +153,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
     const int rb = nb * BB;
     const int n0 = blockIdx.x * rows_per_wg;
     const int rows = min(rows_per_wg, N - n0);
-    const GemvLayout L = gemv_layout(WT, K, rows_per_wg, slice_bytes);
+    const GemvLayout L = gemv_layout(WT, K, rows_per_wg, slice_bytes, MB);
     int8_t* act_qs = (int8_t*)(smem + L.act_qs);
     float* act_d = (float*)(smem + L.act_d);
     int16_t* act_bs = (int16_t*)(smem + L.act_bs);
@@ -199,6 +206,26 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
         issue_half(cb, cm, kh0);
         issue_half(cm, ce, kh1);
         wait_vmcnt(kh1);  // the first part has landed
+    } else if (xq_in != nullptr) {
+        // ---- quantizer waves, pre-quantized input: M planar rows into LDS
+        const int nbw = (WT == 2) ? K / kQK8 : K / kQK;
+        const int qtid = tid, qthr = 64 * G;
+        const int cpr = K / 16;  // 16-byte chunks per row
+        for (int i = qtid; i < M * cpr; i += qthr) {
+            const int m = i / cpr, c = i - m * cpr;
+            const uint4 v = *(const uint4*)(xq_in + (int64_t)m * K + 16 * c);
+            const int dst = (WT == 2) ? 16 * c : (c >> 4) * kActStride + 16 * (c & 15);
+            *(uint4*)(act_qs + m * L.act_row + dst) = v;
+        }
+        if (WT == 2) {
+            const uint16_t* dsrc = (const uint16_t*)(xq_in + xq_d_off);
+            for (int i = qtid; i < M * nbw; i += qthr) act_d[i] = half_bits_to_float(dsrc[i]);
+        } else {
+            const float* dsrc = (const float*)(xq_in + xq_d_off);
+            for (int i = qtid; i < M * nbw; i += qthr) act_d[i] = dsrc[i];
+            const int16_t* bsrc = (const int16_t*)(xq_in + xq_aux_off);
+            for (int i = qtid; i < M * (K / 16); i += qthr) act_bs[i] = bsrc[i];
+        }
     } else {
         // ---- quantizer waves: x loads, then the shared quantizer into LDS
         const int xsteps = (K + kQK - 1) / kQK;  // 256 values per wave step
@@ -261,57 +288,68 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
     lds_barrier();  // quantized x and the first half of the slice visible to every wave
 
     const int grp = lane / LPT, sub = lane % LPT;
+    // One (row, block) task for each of the MB activation rows: the weight
+    // bytes are read and unpacked once and reused for every row.
+    const int nbw_ = (WT == 2) ? K / kQK8 : K / kQK;
     auto compute_task = [&](int r, int blk) {
         const uint8_t* bp = wsl + rbase + __mul24(r, rb) + __mul24(blk, BB);
         if (WT == 0) {
             // lane half hf: sub-blocks 4hf..4hf+3 = qs bytes [64hf, 64hf+64)
             const int hf = sub;
             const uint4 hdr = *(const uint4*)bp;
-            uint32_t qw[16];
+            uint32_t lo[16], hi[16];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const uint4 v = *(const uint4*)(bp + 16 + 64 * hf + 16 * i);
-                qw[4 * i] = v.x; qw[4 * i + 1] = v.y; qw[4 * i + 2] = v.z; qw[4 * i + 3] = v.w;
-            }
-            const int8_t* ab = act_qs + __mul24(blk, kActStride) + 128 * hf;
-            uint32_t av[32];
+                const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint4 v = *(const uint4*)(ab + 16 * i);
-                av[4 * i] = v.x; av[4 * i + 1] = v.y; av[4 * i + 2] = v.z; av[4 * i + 3] = v.w;
-            }
-            int P[4] = {0, 0, 0, 0};  // sub-blocks 4hf + j
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const uint32_t w = qw[8 * c + i];
-                    P[2 * c] = sdot4((int)(w & 0x0F0F0F0Fu), (int)av[16 * c + i], P[2 * c]);
-                    P[2 * c + 1] = sdot4((int)((w >> 4) & 0x0F0F0F0Fu), (int)av[16 * c + 8 + i], P[2 * c + 1]);
+                for (int k = 0; k < 4; ++k) {
+                    lo[4 * i + k] = w4[k] & 0x0F0F0F0Fu;
+                    hi[4 * i + k] = (w4[k] >> 4) & 0x0F0F0F0Fu;
                 }
+            }
             const uint32_t sw = hf ? hdr.z : hdr.y;             // scales bytes 4hf..4hf+3
             const uint32_t mw = hdr.w >> (16 * hf);             // min high nibbles, 2 bytes
-            const uint4 bsv = *(const uint4*)(act_bs + blk * 16 + 8 * hf);
-            const uint32_t bw[4] = {bsv.x, bsv.y, bsv.z, bsv.w};
-            int S = 0, Mn = 0;
+            const float d = half_bits_to_float(hdr.x & 0xFFFF);
+            const float dmin = half_bits_to_float(hdr.x >> 16);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t sj = (sw >> (8 * j)) & 0xFF;
-                const uint32_t mh = (mw >> (4 * j)) & 15;
-                const int m = (int)((sj >> 6) | (mh << 2));
-                const int bs32 = (int)(int16_t)(bw[j] & 0xFFFF) + (int)(int16_t)(bw[j] >> 16);
-                S += __mul24((int)(sj & 63), P[j]);
-                Mn += __mul24(m, bs32);
-            }
-            S += dppi<0xB1>(S);
-            Mn += dppi<0xB1>(Mn);
-            if (hf == 0) {
-                const float d = half_bits_to_float(hdr.x & 0xFFFF);
-                const float dmin = half_bits_to_float(hdr.x >> 16);
-                const float t1f = d * (float)S;
-                const float t2f = dmin * (float)Mn;
-                const float t3f = t1f - t2f;
-                partial[__mul24(r, nb) + blk] = act_d[blk] * t3f;
+            for (int m = 0; m < MB; ++m) {
+                if (m >= M) break;
+                const int8_t* ab = act_qs + m * L.act_row + __mul24(blk, kActStride) + 128 * hf;
+                uint32_t av[32];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const uint4 v = *(const uint4*)(ab + 16 * i);
+                    av[4 * i] = v.x; av[4 * i + 1] = v.y; av[4 * i + 2] = v.z; av[4 * i + 3] = v.w;
+                }
+                int P[4] = {0, 0, 0, 0};  // sub-blocks 4hf + j
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        P[2 * c] = sdot4((int)lo[8 * c + i], (int)av[16 * c + i], P[2 * c]);
+                        P[2 * c + 1] = sdot4((int)hi[8 * c + i], (int)av[16 * c + 8 + i], P[2 * c + 1]);
+                    }
+                const uint4 bsv = *(const uint4*)(act_bs + m * (K / 16) + blk * 16 + 8 * hf);
+                const uint32_t bw[4] = {bsv.x, bsv.y, bsv.z, bsv.w};
+                int S = 0, Mn = 0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t sj = (sw >> (8 * j)) & 0xFF;
+                    const uint32_t mh = (mw >> (4 * j)) & 15;
+                    const int mm = (int)((sj >> 6) | (mh << 2));
+                    const int bs32 = (int)(int16_t)(bw[j] & 0xFFFF) + (int)(int16_t)(bw[j] >> 16);
+                    S += __mul24((int)(sj & 63), P[j]);
+                    Mn += __mul24(mm, bs32);
+                }
+                S += dppi<0xB1>(S);
+                Mn += dppi<0xB1>(Mn);
+                if (hf == 0) {
+                    const float t1f = d * (float)S;
+                    const float t2f = dmin * (float)Mn;
+                    const float t3f = t1f - t2f;
+                    partial[(m * rows_per_wg + r) * nb + blk] = act_d[m * nbw_ + blk] * t3f;
+                }
             }
         } else if (WT == 1) {
             // lane half h: values 128h..128h+127 (sub-blocks 8h..8h+7)
@@ -321,15 +359,8 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
             lds_read32_a2(bp + 64 * h + 32, ql + 8);
             lds_read32_a2(bp + 128 + 32 * h, qh);
             const uint16_t* scp = (const uint16_t*)(bp + 192 + 8 * h);
-            const uint32_t sc01 = scp[0], sc23 = scp[1], sc45 = scp[2], sc67 = scp[3];
-            const int8_t* ab = act_qs + __mul24(blk, kActStride) + 128 * h;
-            uint32_t av[32];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint4 v = *(const uint4*)(ab + 16 * i);
-                av[4 * i] = v.x; av[4 * i + 1] = v.y; av[4 * i + 2] = v.z; av[4 * i + 3] = v.w;
-            }
-            int I[8] = {0, 0, 0, 0, 0, 0, 0, 0};  // sub-blocks 8h + j
+            const uint32_t scw[4] = {scp[0], scp[1], scp[2], scp[3]};
+            uint32_t qa[16], qb[16];  // 6-bit quants of sub-blocks 8h + k (qa) and 8h + 4 + k (qb)
 #pragma unroll
             for (int k = 0; k < 4; ++k)
 #pragma unroll
@@ -337,42 +368,62 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
                     const uint32_t l = ql[4 * k + i];
                     const uint32_t hq = qh[4 * (k & 1) + i];
                     const int sa = 2 * (k >> 1), sb = 2 * (2 + (k >> 1));
-                    const uint32_t qa = (l & 0x0F0F0F0Fu) | (((hq >> sa) & 0x03030303u) << 4);
-                    const uint32_t qb = ((l >> 4) & 0x0F0F0F0Fu) | (((hq >> sb) & 0x03030303u) << 4);
-                    I[k] = sdot4((int)qa, (int)av[4 * k + i], I[k]);
-                    I[4 + k] = sdot4((int)qb, (int)av[16 + 4 * k + i], I[4 + k]);
+                    qa[4 * k + i] = (l & 0x0F0F0F0Fu) | (((hq >> sa) & 0x03030303u) << 4);
+                    qb[4 * k + i] = ((l >> 4) & 0x0F0F0F0Fu) | (((hq >> sb) & 0x03030303u) << 4);
                 }
-            const uint4 bsv = *(const uint4*)(act_bs + blk * 16 + 8 * h);
-            const uint32_t bw[4] = {bsv.x, bsv.y, bsv.z, bsv.w};
-            const uint32_t scw[4] = {sc01, sc23, sc45, sc67};
-            int S = 0;
+            const float d = half_bits_to_float(*(const uint16_t*)(bp + 208));
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int bsj = (int)(int16_t)((bw[j >> 1] >> (16 * (j & 1))) & 0xFFFF);
-                const int scj = (int)(int8_t)((scw[j >> 1] >> (8 * (j & 1))) & 0xFF);
-                S += __mul24(scj, I[j] - 32 * bsj);
-            }
-            S += dppi<0xB1>(S);
-            if (h == 0) {
-                const float d = half_bits_to_float(*(const uint16_t*)(bp + 208));
-                const float t1f = d * (float)S;
-                partial[__mul24(r, nb) + blk] = act_d[blk] * t1f;
+            for (int m = 0; m < MB; ++m) {
+                if (m >= M) break;
+                const int8_t* ab = act_qs + m * L.act_row + __mul24(blk, kActStride) + 128 * h;
+                uint32_t av[32];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const uint4 v = *(const uint4*)(ab + 16 * i);
+                    av[4 * i] = v.x; av[4 * i + 1] = v.y; av[4 * i + 2] = v.z; av[4 * i + 3] = v.w;
+                }
+                int I[8] = {0, 0, 0, 0, 0, 0, 0, 0};  // sub-blocks 8h + j
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        I[k] = sdot4((int)qa[4 * k + i], (int)av[4 * k + i], I[k]);
+                        I[4 + k] = sdot4((int)qb[4 * k + i], (int)av[16 + 4 * k + i], I[4 + k]);
+                    }
+                const uint4 bsv = *(const uint4*)(act_bs + m * (K / 16) + blk * 16 + 8 * h);
+                const uint32_t bw[4] = {bsv.x, bsv.y, bsv.z, bsv.w};
+                int S = 0;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int bsj = (int)(int16_t)((bw[j >> 1] >> (16 * (j & 1))) & 0xFFFF);
+                    const int scj = (int)(int8_t)((scw[j >> 1] >> (8 * (j & 1))) & 0xFF);
+                    S += __mul24(scj, I[j] - 32 * bsj);
+                }
+                S += dppi<0xB1>(S);
+                if (h == 0) {
+                    const float t1f = d * (float)S;
+                    partial[(m * rows_per_wg + r) * nb + blk] = act_d[m * nbw_ + blk] * t1f;
+                }
             }
         } else {
             uint32_t qw[8];
             lds_read32_a2(bp + 2, qw);
-            const uint4 a0 = *(const uint4*)(act_qs + blk * kQK8);
-            const uint4 a1 = *(const uint4*)(act_qs + blk * kQK8 + 16);
-            const uint32_t av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-            int I = 0;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) I = sdot4((int)qw[i], (int)av[i], I);
             const float dw = half_bits_to_float(*(const uint16_t*)bp);
-            const float sc = dw * act_d[blk];
-            partial[__mul24(r, nb) + blk] = sc * (float)I;
+#pragma unroll
+            for (int m = 0; m < MB; ++m) {
+                if (m >= M) break;
+                const int8_t* ab = act_qs + m * L.act_row + blk * kQK8;
+                const uint4 a0 = *(const uint4*)ab;
+                const uint4 a1 = *(const uint4*)(ab + 16);
+                const uint32_t av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+                int I = 0;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) I = sdot4((int)qw[i], (int)av[i], I);
+                const float sc = dw * act_d[m * nbw_ + blk];
+                partial[(m * rows_per_wg + r) * nb + blk] = sc * (float)I;
+            }
         }
     };
-
 
     // Tasks [t0, t1), one pass per GPW tasks.
     auto compute_range = [&](int t0, int t1) {
@@ -412,8 +463,10 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
     lds_barrier();
 
     // ---- 5. rows: blocks summed in ascending order from 0
-    for (int r = tid; r < rows; r += nthr) {
-        const float* p = partial + r * nb;
+    for (int idx = tid; idx < MB * rows; idx += nthr) {
+        const int m = idx / rows, r = idx - m * rows;
+        if (m >= M) break;
+        const float* p = partial + (m * rows_per_wg + r) * nb;
         float acc = 0.0f;
         int b = 0;
         if ((nb & 3) == 0) {
@@ -429,7 +482,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
             }
         }
         for (; b < nb; ++b) acc = acc + p[b];
-        y[n0 + r] = acc;
+        y[m * ldy + n0 + r] = acc;
     }
 
     // ---- 6. the fused quantizer's bytes, for callers that want them
@@ -489,7 +542,7 @@ struct GemvPlan {
 // quantizer waves take the rest in one pass each while it streams in.  Fewer
 // rows when the slice would not fit LDS, the waves would exceed 16, or the
 // loaders would need more instructions than a vmcnt wait can count.
-static GemvPlan gemv_plan(int wt, int64_t N, int64_t K) {
+static GemvPlan gemv_plan(int wt, int64_t N, int64_t K, int mb) {
     GemvPlan p;
     const int bb = block_bytes_of(wt);
     const int nb = (int)(K / block_vals_of(wt));
@@ -516,7 +569,7 @@ static GemvPlan gemv_plan(int wt, int64_t N, int64_t K) {
         const int kh1 = (int)(((c_h1 + 63) / 64 + nl - 1) / nl);
         const int64_t sbytes = 16 * ((slice + 15) / 16 + 2) + 1024 + 1024 + 64;
         const bool small = sbytes < (int64_t)kMaxLds;
-        const GemvLayout L = gemv_layout(wt, (int)K, rows, small ? (int)sbytes : 0);
+        const GemvLayout L = gemv_layout(wt, (int)K, rows, small ? (int)sbytes : 0, mb);
         const bool fits = small && nq + nl <= kGemvWaves && kh0 + kh1 <= 63 && kh1 <= kMaxHalfInstr &&
                           (size_t)L.total <= kMaxLds;
         if (fits || rows == 1) {
@@ -535,38 +588,63 @@ static GemvPlan gemv_plan(int wt, int64_t N, int64_t K) {
     }
 }
 
-size_t gemv_lds_bytes(int wtype, int64_t N, int64_t K) {
-    const GemvPlan p = gemv_plan(wtype, N, K);
+size_t gemv_lds_bytes(int wtype, int64_t N, int64_t K, int mb) {
+    const GemvPlan p = gemv_plan(wtype, N, K, mb);
     return p.ok ? (size_t)p.lds : (size_t)-1;
 }
 
-template <int WT>
-static hipError_t launch_gemv_t(const uint8_t* W, int64_t N, int64_t K, const float* x, float* y,
-                                uint8_t* xq_out, hipStream_t st) {
+static int mb_for(int64_t M) { return M <= 1 ? 1 : (M <= 2 ? 2 : (M <= 4 ? 4 : 8)); }
+
+template <int WT, int MB>
+static hipError_t launch_gemv_t(const uint8_t* W, int64_t N, int64_t K, const float* x, float* y, int64_t ldy,
+                                uint8_t* xq_out, const uint8_t* xq_in, int64_t M, int64_t d_off, int64_t aux_off,
+                                hipStream_t st) {
     static bool attr_set = false;
-    const GemvPlan p = gemv_plan(WT, N, K);
+    const GemvPlan p = gemv_plan(WT, N, K, MB);
     if (!p.ok) return hipErrorInvalidValue;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)gemv_kernel<WT>,
+        hipError_t e = hipFuncSetAttribute((const void*)gemv_kernel<WT, MB>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
     const int rb = (int)(K / WFmt<WT>::kVals) * WFmt<WT>::kBlk;
     const int grid = (int)((N + p.rows - 1) / p.rows);
-    const int x_vec = (((uintptr_t)x) & 15) == 0;
-    gemv_kernel<WT><<<grid, 64 * (p.nq + p.nl), p.lds, st>>>(W, (int)N, (int)K, (int64_t)N * rb, x, y, xq_out,
-                                                              p.rows, p.slice_bytes, x_vec, p.nq, p.h1, p.kh0,
-                                                              p.kh1);
+    const int x_vec = (x != nullptr && (((uintptr_t)x) & 15) == 0) ? 1 : 0;
+    gemv_kernel<WT, MB><<<grid, 64 * (p.nq + p.nl), p.lds, st>>>(
+        W, (int)N, (int)K, (int64_t)N * rb, x, y, xq_out, p.rows, p.slice_bytes, x_vec, p.nq, p.h1, p.kh0, p.kh1,
+        xq_in, (int)M, ldy, d_off, aux_off);
     return hipGetLastError();
 }
 
 hipError_t launch_gemv(int wtype, const uint8_t* W, int64_t N, int64_t K, const float* x, float* y,
                        uint8_t* xq_out, hipStream_t st) {
     if (N == 0) return hipSuccess;
-    if (wtype == 0) return launch_gemv_t<0>(W, N, K, x, y, xq_out, st);
-    if (wtype == 1) return launch_gemv_t<1>(W, N, K, x, y, xq_out, st);
-    return launch_gemv_t<2>(W, N, K, x, y, xq_out, st);
+    if (wtype == 0) return launch_gemv_t<0, 1>(W, N, K, x, y, N, xq_out, nullptr, 1, 0, 0, st);
+    if (wtype == 1) return launch_gemv_t<1, 1>(W, N, K, x, y, N, xq_out, nullptr, 1, 0, 0, st);
+    return launch_gemv_t<2, 1>(W, N, K, x, y, N, xq_out, nullptr, 1, 0, 0, st);
+}
+
+template <int WT>
+static hipError_t launch_skinny_t(const uint8_t* W, int64_t N, int64_t K, const uint8_t* xq, int64_t M,
+                                  int64_t d_off, int64_t aux_off, float* Y, int64_t ldy, hipStream_t st) {
+    switch (mb_for(M)) {
+        case 1: return launch_gemv_t<WT, 1>(W, N, K, nullptr, Y, ldy, nullptr, xq, M, d_off, aux_off, st);
+        case 2: return launch_gemv_t<WT, 2>(W, N, K, nullptr, Y, ldy, nullptr, xq, M, d_off, aux_off, st);
+        case 4: return launch_gemv_t<WT, 4>(W, N, K, nullptr, Y, ldy, nullptr, xq, M, d_off, aux_off, st);
+        default: return launch_gemv_t<WT, 8>(W, N, K, nullptr, Y, ldy, nullptr, xq, M, d_off, aux_off, st);
+    }
+}
+
+bool gemm_skinny_ok(int wtype, int64_t N, int64_t K, int64_t M) {
+    return M >= 1 && M <= kSkinnyMaxM && N > 0 && gemv_lds_bytes(wtype, N, K, mb_for(M)) <= kMaxLds;
+}
+
+hipError_t launch_gemm_skinny(int wtype, const uint8_t* W, int64_t N, int64_t K, const uint8_t* xq, int64_t M,
+                              int64_t d_off, int64_t aux_off, float* Y, int64_t ldy, hipStream_t st) {
+    if (wtype == 0) return launch_skinny_t<0>(W, N, K, xq, M, d_off, aux_off, Y, ldy, st);
+    if (wtype == 1) return launch_skinny_t<1>(W, N, K, xq, M, d_off, aux_off, Y, ldy, st);
+    return launch_skinny_t<2>(W, N, K, xq, M, d_off, aux_off, Y, ldy, st);
 }
 
 }  // namespace vqk

@@ -26,6 +26,7 @@ struct Counters {
     std::atomic<uint64_t> gemm_q4k{0}, gemm_q6k{0}, gemm_q8_0{0};
     std::atomic<uint64_t> route{0}, gemm_grouped_q4k{0}, weighted_sum{0};
     std::atomic<uint64_t> gemm_grouped_q6k{0}, gemm_grouped_q8_0{0}, gemm_grouped_rows{0};
+    std::atomic<uint64_t> gemm_skinny{0};
 };
 Counters g_stats;
 
@@ -245,7 +246,7 @@ vq_status vq_gemv(int w, const void* W, int64_t N, int64_t K, const float* x, fl
     VQ_TRY(check_k(w, K, fn));
     VQ_TRY(check_dim(N, "N", fn));
     const int act = (w == VQ_Q8_0) ? VQ_Q8_1 : VQ_Q8_K;
-    if (vqk::gemv_lds_bytes(w, N > 0 ? N : 1, K) > 160 * 1024)
+    if (vqk::gemv_lds_bytes(w, N > 0 ? N : 1, K, 1) > 160 * 1024)
         return fail(VQ_ERR_SHAPE, "%s: K = %lld is too long for the fused %s GEMV (one row and the quantized "
                     "activation must fit the 160 KiB LDS)", fn, (long long)K, vq_type_name(w));
     if (N == 0) return VQ_OK;
@@ -288,6 +289,14 @@ vq_status vq_gemm(int w, const void* W, int64_t N, int64_t K, int act, const voi
     if (w == VQ_Q4_K) g_stats.gemm_q4k++;
     else if (w == VQ_Q6_K) g_stats.gemm_q6k++;
     else g_stats.gemm_q8_0++;
+    if (vqk::gemm_skinny_ok(w, N, K, M)) {
+        // small batch: the weights streamed once through the GEMV kernel for all M rows
+        g_stats.gemm_skinny++;
+        return hip_status(vqk::launch_gemm_skinny(w, (const uint8_t*)W, N, K, base, M,
+                                                  (int64_t)vq_act_d_offset(act, M, K),
+                                                  (int64_t)vq_act_aux_offset(act, M, K), Y, ldy, stream),
+                          fn);
+    }
     return hip_status(vqk::launch_gemm(w, (const uint8_t*)W, N, K, qs, d, aux, M, Y, ldy, stream), fn);
 }
 
@@ -407,6 +416,7 @@ void vq_get_stats(vq_stats* out) {
     out->gemm_grouped_q6k = g_stats.gemm_grouped_q6k.load();
     out->gemm_grouped_q8_0 = g_stats.gemm_grouped_q8_0.load();
     out->gemm_grouped_rows = g_stats.gemm_grouped_rows.load();
+    out->gemm_skinny = g_stats.gemm_skinny.load();
 }
 
 void vq_reset_stats(void) {
@@ -425,6 +435,7 @@ void vq_reset_stats(void) {
     g_stats.gemm_grouped_q6k = 0;
     g_stats.gemm_grouped_q8_0 = 0;
     g_stats.gemm_grouped_rows = 0;
+    g_stats.gemm_skinny = 0;
 }
 
 const char* vq_version(void) { return "vq 0.1.0 (gfx950)"; }

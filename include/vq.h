@@ -189,6 +189,9 @@ vq_status vq_gemv(int w, const void* W, int64_t N, int64_t K, const float* x, fl
 /* n < N, through exact int32 sub-block sums and binary32 scale combines.   */
 /* Xq is the planar activation buffer of type act (Q8_K for Q4_K/Q6_K,      */
 /* Q8_1 for Q8_0) holding M rows; Y fp32 with row stride ldy >= N.          */
+/* M <= 8 runs on the decode GEMV kernel over the pre-quantized rows (the    */
+/* weights streamed once for all rows), larger M on the int8 MFMA GEMM; the  */
+/* result is the same fixed-order definition either way.                    */
 /* ---------------------------------------------------------------------- */
 vq_status vq_gemm(int w, const void* W, int64_t N, int64_t K, int act, const void* Xq,
                   int64_t M, float* Y, int64_t ldy, hipStream_t stream);
@@ -256,6 +259,7 @@ typedef struct {
     uint64_t gemm_grouped_q6k;
     uint64_t gemm_grouped_q8_0;
     uint64_t gemm_grouped_rows;  /* calls of the per-row arm (also counted per type) */
+    uint64_t gemm_skinny;        /* vq_gemm calls with M <= 8 run on the GEMV kernel (also counted per type) */
 } vq_stats;
 
 void vq_get_stats(vq_stats* out);

@@ -207,6 +207,37 @@ def test_gemm_from_device_quantizer(wtype):
         H.assert_bitwise(H.host(Y), oracle.gemm(wtype, Wq, N, K, oracle_act(wtype, X)), "M=%d" % M)
 
 
+SKINNY_SHAPES = {oracle.Q4_K: (300, 2560), oracle.Q6_K: (131, 1536), oracle.Q8_0: (300, 2080)}
+
+
+@pytest.mark.parametrize("wtype", WTYPES)
+def test_gemm_small_batch(wtype):
+    """M = 1..8 runs on the GEMV kernel reading the pre-quantized rows (the
+    weights streamed once for all rows), M = 9 on the MFMA GEMM; both
+    bit-identical to the oracle, padding columns untouched, and row m equal
+    to the decode GEMV of x_m."""
+    N, K = SKINNY_SHAPES[wtype]
+    W = synth.normal(1450 + wtype, (N, K), 0.02)
+    Wq = oracle.quantize_weights(wtype, W)
+    Wd = H.to_dev(Wq)
+    ldy = N + 5
+    for M in (1, 2, 3, 4, 5, 8, 9):
+        X = synth.normal((1451, wtype, M), (M, K))
+        X[:, ::61] *= np.float32(15.0)
+        act = oracle_act(wtype, X)
+        H.say("gemm small batch %s M=%d N=%d K=%d" % (WNAME[wtype], M, N, K))
+        vq.reset_stats()
+        Yd = H.to_dev(np.full((M, ldy), np.nan, np.float32))
+        vq.gemm(wtype, Wd, N, K, vq.act_for(wtype), H.to_dev(H.pack_act(act, wtype)), M, Y=Yd, ldy=ldy)
+        Yh = H.host(Yd)
+        assert vq.get_stats()["gemm_skinny"] == (1 if M <= 8 else 0)
+        H.assert_bitwise(Yh[:, :N], oracle.gemm(wtype, Wq, N, K, act, nthreads=8), "M=%d" % M)
+        assert np.isnan(Yh[:, N:]).all(), "padding columns written"
+        for m in sorted({0, M - 1}):
+            y = vq.gemv(wtype, Wd, N, K, H.to_dev(np.ascontiguousarray(X[m])))
+            H.assert_bitwise(H.host(y), Yh[m, :N], "gemv row %d vs gemm M=%d" % (m, M))
+
+
 @pytest.mark.parametrize("wtype", WTYPES)
 def test_random_byte_blocks(wtype):
     """Random block bytes (random scales, mins, quants incl. negative Q6_K scales),

@@ -95,6 +95,26 @@ def test_decode_gemv_full(which):
     assert ref_fp64.nmse(yh, ref) <= 1e-6
 
 
+@pytest.mark.parametrize("M", [2, 8])
+@pytest.mark.parametrize("which", ["Q4_K", "Q6_K"])
+def test_decode_small_batch_full(which, M):
+    """A small decode batch (M rows of the prefill activations) against the
+    decode step's matrices: the GEMV-kernel arm of vq_gemm, every output."""
+    wtype = oracle.Q4_K if which == "Q4_K" else oracle.Q6_K
+    wn, xn = ("Wa", "Xh") if which == "Q4_K" else ("Wb", "Xi")
+    W = synth.tensor("decode_gemv", wn)
+    N, K = W.shape
+    X = synth.prefill_activations(xn, M)
+    Wq = oracle.quantize_weights(wtype, W)
+    H.say("decode small batch %s M=%d N=%d K=%d" % (which, M, N, K))
+    Xq = vq.quantize_act(vq.Q8_K, H.to_dev(X))
+    act = check_act_bytes(wtype, Xq, X)
+    vq.reset_stats()
+    Y = vq.gemm(wtype, H.to_dev(Wq), N, K, vq.Q8_K, Xq, M, Y=H.to_dev(np.full((M, N), np.nan, np.float32)))
+    assert vq.get_stats()["gemm_skinny"] == 1
+    H.assert_bitwise(H.host(Y), oracle.gemm(wtype, Wq, N, K, act, nthreads=THREADS), "small batch " + which)
+
+
 def test_q8_0_gemv_full():
     """Q8_0 [4096, 2048] against row 0 of the Q8_0 workload's X, fused Q8_1."""
     W = synth.tensor("q8_0_gemm", "W")
