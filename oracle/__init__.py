@@ -71,6 +71,8 @@ def _bind(path):
     L.oracle_gemm_grouped.argtypes = [ctypes.c_int, P, I64, I64, I64, P, P, P, I64, P, I64,
                                       ctypes.c_int, P, ctypes.c_int]
     L.oracle_weighted_sum.argtypes = [P, P, I64, I64, I64, P]
+    L.oracle_rmsnorm.argtypes = [P, P, I64, I64, I64, ctypes.c_double, P]
+    L.oracle_silu_mul.argtypes = [P, P, I64, I64, I64, P]
     L.oracle_max_threads.restype = ctypes.c_int
     return L
 
@@ -295,6 +297,30 @@ def weighted_sum(Y: np.ndarray, w: np.ndarray) -> np.ndarray:
     T, top_k, N = Y.shape
     out = np.zeros((T, N), np.float32)
     lib().oracle_weighted_sum(_p(Y), _p(w), T, top_k, N, _p(out))
+    return out
+
+
+def rmsnorm(X: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """[P2] norm-quant epilogue's producer: RMSNorm of each row, float64
+    y = x / sqrt(mean(x^2) + eps) * gamma from binary32 X [M, K], gamma [K]."""
+    X = np.ascontiguousarray(np.atleast_2d(X), np.float32)
+    gamma = np.ascontiguousarray(gamma, np.float32)
+    M, K = X.shape
+    assert gamma.shape == (K,)
+    out = np.zeros((M, K), np.float64)
+    lib().oracle_rmsnorm(_p(X), _p(gamma), M, K, K, float(eps), _p(out))
+    return out
+
+
+def silu_mul(G: np.ndarray, U: np.ndarray) -> np.ndarray:
+    """[P2] silu-mul quant epilogue's producer, float64
+    y = g / (1 + exp(-g)) * u from binary32 G, U [M, K]."""
+    G = np.ascontiguousarray(np.atleast_2d(G), np.float32)
+    U = np.ascontiguousarray(np.atleast_2d(U), np.float32)
+    assert G.shape == U.shape
+    M, K = G.shape
+    out = np.zeros((M, K), np.float64)
+    lib().oracle_silu_mul(_p(G), _p(U), M, K, K, _p(out))
     return out
 
 

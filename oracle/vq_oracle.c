@@ -653,6 +653,37 @@ void oracle_weighted_sum(const float* Y, const float* w, int64_t T, int64_t top_
         }
 }
 
+/* ------------------------------------------------------------------------ */
+/* Producers whose output feeds the activation quantizer ([P2] commits       */
+/* "Norm epilogue" (RMSNorm row kernel emitting the row's Q8_K blocks) and    */
+/* "SiLU-mul quant" (silu(gate)*up emitting Q8_K)).  The pages name the       */
+/* operations, not their formulas; the textbook definitions are taken, in    */
+/* binary64 from the binary32 inputs:                                        */
+/*   RMSNorm: y_i = x_i / sqrt(mean_j(x_j^2) + eps) * gamma_i                */
+/*   SiLU-mul: y_i = g_i / (1 + exp(-g_i)) * u_i  (silu(g) = g*sigmoid(g))   */
+/* The fused producer's quantized bytes are checked against                  */
+/* oracle_quantize_q8k / _q8_1 applied to the producer's own binary32        */
+/* output (the pages' byte-identity with the unfused path).                  */
+/* ------------------------------------------------------------------------ */
+void oracle_rmsnorm(const float* X, const float* gamma, int64_t M, int64_t K, int64_t ldx, double eps,
+                    double* Y) {
+    for (int64_t m = 0; m < M; ++m) {
+        const float* x = X + m * ldx;
+        double ss = 0.0;
+        for (int64_t i = 0; i < K; ++i) ss += (double)x[i] * (double)x[i];
+        const double r = 1.0 / sqrt(ss / (double)K + eps);
+        for (int64_t i = 0; i < K; ++i) Y[m * K + i] = (double)x[i] * r * (double)gamma[i];
+    }
+}
+
+void oracle_silu_mul(const float* G, const float* U, int64_t M, int64_t K, int64_t ldx, double* Y) {
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t i = 0; i < K; ++i) {
+            const double g = (double)G[m * ldx + i];
+            Y[m * K + i] = g / (1.0 + exp(-g)) * (double)U[m * ldx + i];
+        }
+}
+
 int oracle_max_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

@@ -411,3 +411,41 @@ def test_workload_shapes_and_routing():
     cols = synth.outlier_columns(2560)
     assert cols.size == 26 and np.unique(cols).size == 26
     assert synth.outlier_columns(9728).size == 97
+
+
+# ------------------------------------------------------------------ producers
+def test_rmsnorm_pins():
+    """RMSNorm pins from the mathematics: a worked example, unit output RMS,
+    scale invariance, eps inside the root, gamma per position."""
+    # [3, 4]: mean of squares 12.5 = 25/2, so x / rms = x * sqrt(2) / 5
+    y = oracle.rmsnorm(np.array([[3.0, 4.0]], np.float32), np.array([1.0, 2.0], np.float32), 0.0)
+    assert np.allclose(y, [[3 * np.sqrt(2) / 5, 8 * np.sqrt(2) / 5]], rtol=1e-15, atol=0)
+    X = synth.normal(3100, (5, 768))
+    ones = np.ones(768, np.float32)
+    y = oracle.rmsnorm(X, ones, 0.0)
+    assert np.allclose(np.sqrt(np.mean(y * y, axis=1)), 1.0, rtol=1e-12, atol=0)
+    assert np.allclose(oracle.rmsnorm(X * np.float32(8.0), ones, 0.0), y, rtol=1e-13, atol=0)
+    # constant rows c with eps: c / sqrt(c^2 + eps); c = 1, eps = 3 -> 1/2
+    g = np.arange(1, 257, dtype=np.float32)
+    y = oracle.rmsnorm(np.ones((2, 256), np.float32), g, 3.0)
+    assert np.array_equal(y, np.stack([g.astype(np.float64) / 2] * 2))
+    # zero row: zero output for any eps > 0
+    assert not oracle.rmsnorm(np.zeros((1, 256), np.float32), g, 1e-6).any()
+
+
+def test_silu_mul_pins():
+    """SiLU-mul pins: sigmoid(ln 3) = 3/4, the odd part silu(x) - silu(-x) = x,
+    the even part silu(x) + silu(-x) = x tanh(x/2), linearity in up."""
+    l3 = np.float32(np.log(3.0))
+    y = oracle.silu_mul(np.array([[0.0, l3, -l3]], np.float32), np.ones((1, 3), np.float32))
+    assert y[0, 0] == 0.0
+    assert abs(y[0, 1] - 0.75 * float(l3)) <= 1e-7 * float(l3)
+    assert abs(y[0, 2] + 0.25 * float(l3)) <= 1e-7 * float(l3)
+    x = synth.normal(3101, (3, 512), 4.0)
+    ones = np.ones_like(x)
+    p, n = oracle.silu_mul(x, ones), oracle.silu_mul(-x, ones)
+    xd = x.astype(np.float64)
+    assert np.allclose(p - n, xd, rtol=1e-12, atol=1e-12)
+    assert np.allclose(p + n, xd * np.tanh(xd / 2), rtol=1e-10, atol=1e-12)
+    u = synth.normal(3102, (3, 512))
+    assert np.allclose(oracle.silu_mul(x, u), p * u.astype(np.float64), rtol=1e-15, atol=0)

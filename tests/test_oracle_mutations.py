@@ -48,6 +48,13 @@ MUTANTS = {
                        ["test_route_golden_and_library_sort"]),
     "expert sum fma": ("acc = acc + p;", "acc = fmaf(w[t * top_k + s], Y[(t * top_k + s) * N + n], acc); (void)p;",
                        ["test_weighted_sum_golden"]),
+    "rmsnorm sum not mean": ("sqrt(ss / (double)K + eps)", "sqrt(ss + eps)", ["test_rmsnorm_pins"]),
+    "rmsnorm eps outside root": ("sqrt(ss / (double)K + eps)", "(sqrt(ss / (double)K) + eps)",
+                                 ["test_rmsnorm_pins"]),
+    "rmsnorm gamma reversed": ("* r * (double)gamma[i];", "* r * (double)gamma[K - 1 - i];",
+                               ["test_rmsnorm_pins"]),
+    "silu sigmoid sign": ("g / (1.0 + exp(-g))", "g / (1.0 + exp(g))", ["test_silu_mul_pins"]),
+    "silu drops up": ("* (double)U[m * ldx + i];", "* 1.0;", ["test_silu_mul_pins"]),
     "f16 ties up": ("if (rem > 0x1000u || (rem == 0x1000u && (h & 1u))) h += 1u;",
                     "if (rem >= 0x1000u) h += 1u;", ["test_f16_encode_matches_numpy_rne"]),
 }
