@@ -244,6 +244,55 @@ def run_q8_0(torch, vq, synth, iters):
             "gemv_frac": round(gbytes / (tv * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def run_small_batch(torch, vq, synth, iters):
+    """vq_gemm at M = 2, 4, 8 on the decode matrices (the GEMV-kernel arm),
+    weights rotated past the Infinity Cache; rate = weight bytes + activation
+    bytes + output bytes per call."""
+    dev = torch.device("cuda:0")
+    out = {}
+    for name, wt, wn, xn in (("q4k", vq.Q4_K, "Wa", "Xh"), ("q6k", vq.Q6_K, "Wb", "Xi")):
+        W = torch.from_numpy(synth.tensor("decode_gemv", wn)).to(dev)
+        N, K = W.shape
+        Q = vq.quantize_weights(wt, W)
+        del W
+        R = max(2, math.ceil(640 * (1 << 20) / Q.numel()))
+        Qs = [Q] + [Q.clone() for _ in range(R - 1)]
+        X = torch.from_numpy(synth.prefill_activations(xn, 8)).to(dev)
+        for M in (2, 4, 8):
+            Xq = vq.quantize_act(vq.Q8_K, X[:M].contiguous())
+            Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+            t, _ = time_graph(lambda i: vq.gemm(wt, Qs[i % R], N, K, vq.Q8_K, Xq, M, Y=Y), R, max(iters, 5 * R))
+            b = Q.numel() + vq.act_bytes(vq.Q8_K, M, K) + 4 * M * N
+            out["%s_M%d" % (name, M)] = {"us": round(t * 1e3, 2), "gbs": round(b / (t * 1e-3) / 1e9, 1),
+                                         "frac": round(b / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del Qs, Q
+    return out
+
+
+def run_producers(torch, vq, synth, iters):
+    """RMSNorm -> Q8_K and SiLU-mul -> Q8_K in one launch, decode (M = 1) and
+    prefill (M = 2048) rows; bytes = inputs read + Y written + Q8_K written."""
+    dev = torch.device("cuda:0")
+    out = {}
+    for M, K in ((1, 2560), (2048, 2560), (1, 9728), (2048, 9728)):
+        X = torch.from_numpy(synth.normal(71, (M, K))).to(dev)
+        U = torch.from_numpy(synth.normal(72, (M, K))).to(dev)
+        g = torch.from_numpy((1.0 + synth.normal(73, (K,), 0.1)).astype("float32")).to(dev)
+        Y = torch.empty((M, K), dtype=torch.float32, device=dev)
+        Xq = torch.empty(vq.act_bytes(vq.Q8_K, M, K), dtype=torch.uint8, device=dev)
+        n = 16 if M == 1 else 4
+        tr, _ = time_graph(lambda i: vq.rmsnorm_quant(vq.Q8_K, X, g, 1e-6, Y=Y, Xq=Xq), n, max(iters, 4 * n))
+        ts, _ = time_graph(lambda i: vq.silu_mul_quant(vq.Q8_K, X, U, Y=Y, Xq=Xq), n, max(iters, 4 * n))
+        tq, _ = time_graph(lambda i: vq.quantize_act(vq.Q8_K, X, Xq=Xq), n, max(iters, 4 * n))
+        qb = vq.act_bytes(vq.Q8_K, M, K)
+        br, bs = 4 * M * K + 4 * K + 4 * M * K + qb, 8 * M * K + 4 * M * K + qb
+        out["M%d_K%d" % (M, K)] = {
+            "rmsnorm_quant_us": round(tr * 1e3, 2), "rmsnorm_quant_gbs": round(br / (tr * 1e-3) / 1e9, 1),
+            "silu_mul_quant_us": round(ts * 1e3, 2), "silu_mul_quant_gbs": round(bs / (ts * 1e-3) / 1e9, 1),
+            "quantize_only_us": round(tq * 1e3, 2)}
+    return out
+
+
 def run_grouped(torch, vq, synth, iters):
     dev = torch.device("cuda:0")
     cfg = synth.WORKLOADS["grouped_moe"]
@@ -374,7 +423,7 @@ def main():
     b4 = 9728 * (2560 // 256) * 144 + 4 * 2560 + 4 * 9728
     ach4 = b4 / (dec["q4k_ms"] * 1e-3) / 1e9
     sha = source_sha(GEMV_SOURCES)
-    roofline = {"bound": "hbm", "kernel": "gemv_kernel<1> (Q6_K [2560,9728] x fused Q8_K)",
+    roofline = {"bound": "hbm", "kernel": "gemv_kernel<1, 1> (Q6_K [2560,9728] x fused Q8_K)",
                 "achieved": round(ach6, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach6 / HBM_PEAK_GBS, 4),
                 "traffic": traffic_from_profiles("gemv_q6k_decode", sha, b6),
@@ -403,6 +452,10 @@ def main():
         line["prefill"] = run_prefill(torch, vq, synth, args.secondary_iters)
         log("[bench] Q8_0 GEMM and GEMV")
         line["q8_0"] = run_q8_0(torch, vq, synth, args.secondary_iters)
+        log("[bench] small batches")
+        line["small_batch"] = run_small_batch(torch, vq, synth, args.secondary_iters)
+        log("[bench] producers with the quantizer epilogue")
+        line["producers"] = run_producers(torch, vq, synth, args.secondary_iters)
         log("[bench] grouped MUL_MAT_ID")
         line["grouped"] = run_grouped(torch, vq, synth, max(5, args.secondary_iters // 2))
         log("[bench] grouped per-row arm (MoE down projection)")

@@ -26,12 +26,13 @@ EXPORTS = [
     "vq_block_bytes", "vq_weight_bytes", "vq_act_bytes", "vq_act_d_offset", "vq_act_aux_offset",
     "vq_quantize_act", "vq_quantize_weights", "vq_gemv", "vq_gemm", "vq_grouped_workspace_bytes",
     "vq_gemm_grouped", "vq_gemm_grouped_rows", "vq_weighted_sum", "vq_get_stats", "vq_reset_stats",
-    "vq_version",
+    "vq_version", "vq_rmsnorm_quant", "vq_silu_mul_quant",
 ]
 
 STAT_FIELDS = ["quantize_q8k", "quantize_q8_1", "quantize_weights", "gemv_q4k", "gemv_q6k", "gemv_q8_0",
                "gemm_q4k", "gemm_q6k", "gemm_q8_0", "route", "gemm_grouped_q4k", "weighted_sum",
-               "gemm_grouped_q6k", "gemm_grouped_q8_0", "gemm_grouped_rows", "gemm_skinny"]
+               "gemm_grouped_q6k", "gemm_grouped_q8_0", "gemm_grouped_rows", "gemm_skinny",
+               "rmsnorm_quant", "silu_mul_quant"]
 
 
 class VQStats(ctypes.Structure):
@@ -79,11 +80,12 @@ def lib():
         L.vq_gemm_grouped.argtypes = [I, P, I64, I64, I64, I, P, I64, P, I64, P, P, P, P, Z, P]
         L.vq_gemm_grouped_rows.argtypes = [I, P, I64, I64, I64, I, P, I64, P, I64, P, P, P, P, Z, P]
         L.vq_weighted_sum.argtypes = [P, P, I64, I64, I64, P, P]
+        L.vq_rmsnorm_quant.argtypes = [I, P, P, I64, I64, I64, ctypes.c_float, P, I64, P, P]
+        L.vq_silu_mul_quant.argtypes = [I, P, P, I64, I64, I64, P, I64, P, P]
         L.vq_get_stats.argtypes = [ctypes.POINTER(VQStats)]
         L.vq_version.restype = ctypes.c_char_p
         for f in ("vq_quantize_act", "vq_quantize_weights", "vq_gemv", "vq_gemm", "vq_gemm_grouped",
-                  "vq_gemm_grouped_rows",
-                  "vq_weighted_sum"):
+                  "vq_gemm_grouped_rows", "vq_weighted_sum", "vq_rmsnorm_quant", "vq_silu_mul_quant"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -168,11 +170,53 @@ def quantize_act(act: int, X, M: int = None, K: int = None, ldx: int = None, Xq=
     if M is None:
         M, K = (1, X.shape[0]) if X.dim() == 1 else (X.shape[0], X.shape[1])
     if ldx is None:
-        ldx = K if X.dim() == 1 else X.stride(0)
+        ldx = K if X.dim() == 1 or X.shape[0] == 1 else X.stride(0)
     if Xq is None:
         Xq = _torch().empty(act_bytes(act, M, K), dtype=_torch().uint8, device=X.device)
     _check(lib().vq_quantize_act(act, _ptr(X), M, K, ldx, _ptr(Xq), _stream(stream)))
     return Xq
+
+
+def _rows(X, M, K, ldx):
+    if M is None:
+        M, K = (1, X.shape[0]) if X.dim() == 1 else (X.shape[0], X.shape[1])
+    if ldx is None:
+        # a single row may carry any stride in its leading dimension
+        ldx = K if X.dim() == 1 or X.shape[0] == 1 else X.stride(0)
+    return M, K, ldx
+
+
+def rmsnorm_quant(act: int, X, gamma, eps: float = 1e-6, M: int = None, K: int = None, ldx: int = None,
+                  Y=None, want_y: bool = True, ldy: int = None, Xq=None, stream=None):
+    """vq_rmsnorm_quant: (Y, Xq) with Y = RMSNorm(X) * gamma (None if not
+    wanted) and Xq its planar Q8_K / Q8_1 bytes, from one launch."""
+    M, K, ldx = _rows(X, M, K, ldx)
+    torch = _torch()
+    if Y is None and want_y:
+        Y = torch.empty((M, K), dtype=torch.float32, device=X.device)
+    if ldy is None:
+        ldy = K if Y is None or Y.dim() == 1 or Y.shape[0] == 1 else Y.stride(0)
+    if Xq is None:
+        Xq = torch.empty(act_bytes(act, M, K), dtype=torch.uint8, device=X.device)
+    _check(lib().vq_rmsnorm_quant(act, _ptr(X), _ptr(gamma), M, K, ldx, float(eps), _ptr(Y), ldy, _ptr(Xq),
+                                  _stream(stream)))
+    return Y, Xq
+
+
+def silu_mul_quant(act: int, G, U, M: int = None, K: int = None, ldx: int = None, Y=None, want_y: bool = True,
+                   ldy: int = None, Xq=None, stream=None):
+    """vq_silu_mul_quant: (Y, Xq) with Y = silu(G) * U (None if not wanted)
+    and Xq its planar Q8_K / Q8_1 bytes, from one launch."""
+    M, K, ldx = _rows(G, M, K, ldx)
+    torch = _torch()
+    if Y is None and want_y:
+        Y = torch.empty((M, K), dtype=torch.float32, device=G.device)
+    if ldy is None:
+        ldy = K if Y is None or Y.dim() == 1 or Y.shape[0] == 1 else Y.stride(0)
+    if Xq is None:
+        Xq = torch.empty(act_bytes(act, M, K), dtype=torch.uint8, device=G.device)
+    _check(lib().vq_silu_mul_quant(act, _ptr(G), _ptr(U), M, K, ldx, _ptr(Y), ldy, _ptr(Xq), _stream(stream)))
+    return Y, Xq
 
 
 def quantize_weights(w: int, W, N: int = None, K: int = None, Wq=None, stream=None):
@@ -198,7 +242,7 @@ def gemm(w: int, W, N: int, K: int, act: int, Xq, M: int, Y=None, ldy: int = Non
     if Y is None:
         Y = _torch().empty((M, N), dtype=_torch().float32, device=Xq.device)
     if ldy is None:
-        ldy = N if Y.dim() == 1 else Y.stride(0)
+        ldy = N if Y.dim() == 1 or Y.shape[0] == 1 else Y.stride(0)
     _check(lib().vq_gemm(w, _ptr(W), N, K, act, _ptr(Xq), M, _ptr(Y), ldy, _stream(stream)))
     return Y
 

@@ -7,6 +7,7 @@
 // the activation type each weight type pairs with).  Nothing here computes:
 // the only compute path is the gfx950 kernels.
 #include <atomic>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -26,7 +27,7 @@ struct Counters {
     std::atomic<uint64_t> gemm_q4k{0}, gemm_q6k{0}, gemm_q8_0{0};
     std::atomic<uint64_t> route{0}, gemm_grouped_q4k{0}, weighted_sum{0};
     std::atomic<uint64_t> gemm_grouped_q6k{0}, gemm_grouped_q8_0{0}, gemm_grouped_rows{0};
-    std::atomic<uint64_t> gemm_skinny{0};
+    std::atomic<uint64_t> gemm_skinny{0}, rmsnorm_quant{0}, silu_mul_quant{0};
 };
 Counters g_stats;
 
@@ -224,6 +225,52 @@ vq_status vq_quantize_act(int act, const float* X, int64_t M, int64_t K, int64_t
     return hip_status(e, fn);
 }
 
+// Shared checks and launch of the two producers (kind 0: RMSNorm, 1: SiLU-mul).
+static vq_status produce_impl(const char* fn, int kind, int act, const float* A, const float* B, int64_t M,
+                              int64_t K, int64_t ldx, float eps, float* Y, int64_t ldy, void* Xq,
+                              hipStream_t stream) {
+    if (!is_act(act))
+        return fail(VQ_ERR_UNSUPPORTED_TYPE, "%s: type %s (%d) is not an activation type (Q8_K, Q8_1)", fn,
+                    vq_type_name(act), act);
+    VQ_TRY(check_k(act, K, fn));
+    VQ_TRY(check_dim(M, "M", fn));
+    if (ldx < K) return fail(VQ_ERR_SHAPE, "%s: ldx = %lld < K = %lld", fn, (long long)ldx, (long long)K);
+    if (Y && ldy < K) return fail(VQ_ERR_SHAPE, "%s: ldy = %lld < K = %lld", fn, (long long)ldy, (long long)K);
+    if (kind == 0 && !(eps >= 0.0f && eps < INFINITY))
+        return fail(VQ_ERR_INVALID_ARG, "%s: eps = %g must be finite and >= 0", fn, (double)eps);
+    if (M == 0) return VQ_OK;
+    if (!A || !B || !Xq) return fail(VQ_ERR_INVALID_ARG, "%s: null input or Xq pointer", fn);
+    if (!aligned(A, 4) || !aligned(B, 4) || (Y && !aligned(Y, 4)) || !aligned(Xq, 16))
+        return fail(VQ_ERR_INVALID_ARG, "%s: inputs and Y must be 4-byte, Xq 16-byte aligned", fn);
+    const size_t ab = ((size_t)(M - 1) * (size_t)ldx + (size_t)K) * 4;
+    const size_t bb = (kind == 0) ? (size_t)K * 4 : ab;
+    const size_t qb = vq_act_bytes(act, M, K);
+    if (overlap(Xq, qb, A, ab) || overlap(Xq, qb, B, bb)) return fail(VQ_ERR_ALIAS, "%s: Xq overlaps an input", fn);
+    if (Y) {
+        const size_t yb = ((size_t)(M - 1) * (size_t)ldy + (size_t)K) * 4;
+        if (overlap(Y, yb, A, ab) || overlap(Y, yb, B, bb) || overlap(Y, yb, Xq, qb))
+            return fail(VQ_ERR_ALIAS, "%s: Y overlaps an input or Xq", fn);
+    }
+    if (kind == 1 && M * ((K + 1023) / 1024) > INT32_MAX)
+        return fail(VQ_ERR_SHAPE, "%s: M * ceil(K / 1024) exceeds the grid limit", fn);
+    if (kind == 0) g_stats.rmsnorm_quant++;
+    else g_stats.silu_mul_quant++;
+    return hip_status(vqk::launch_produce_quant(kind, act == VQ_Q8_K ? 0 : 1, A, B, ldx, M, K, eps, Y, ldy,
+                                                act == VQ_Q8_K ? act_q8k(Xq, M, K) : vqk::ActQ8K{},
+                                                act == VQ_Q8_1 ? act_q81(Xq, M, K) : vqk::ActQ81{}, stream),
+                      fn);
+}
+
+vq_status vq_rmsnorm_quant(int act, const float* X, const float* gamma, int64_t M, int64_t K, int64_t ldx,
+                           float eps, float* Y, int64_t ldy, void* Xq, hipStream_t stream) {
+    return produce_impl("vq_rmsnorm_quant", 0, act, X, gamma, M, K, ldx, eps, Y, ldy, Xq, stream);
+}
+
+vq_status vq_silu_mul_quant(int act, const float* G, const float* U, int64_t M, int64_t K, int64_t ldx, float* Y,
+                            int64_t ldy, void* Xq, hipStream_t stream) {
+    return produce_impl("vq_silu_mul_quant", 1, act, G, U, M, K, ldx, 0.0f, Y, ldy, Xq, stream);
+}
+
 vq_status vq_quantize_weights(int w, const float* W, int64_t N, int64_t K, void* Wq, hipStream_t stream) {
     const char* fn = "vq_quantize_weights";
     VQ_TRY(check_weight(w, fn));
@@ -417,6 +464,8 @@ void vq_get_stats(vq_stats* out) {
     out->gemm_grouped_q8_0 = g_stats.gemm_grouped_q8_0.load();
     out->gemm_grouped_rows = g_stats.gemm_grouped_rows.load();
     out->gemm_skinny = g_stats.gemm_skinny.load();
+    out->rmsnorm_quant = g_stats.rmsnorm_quant.load();
+    out->silu_mul_quant = g_stats.silu_mul_quant.load();
 }
 
 void vq_reset_stats(void) {
@@ -436,6 +485,8 @@ void vq_reset_stats(void) {
     g_stats.gemm_grouped_q8_0 = 0;
     g_stats.gemm_grouped_rows = 0;
     g_stats.gemm_skinny = 0;
+    g_stats.rmsnorm_quant = 0;
+    g_stats.silu_mul_quant = 0;
 }
 
 const char* vq_version(void) { return "vq 0.1.0 (gfx950)"; }

@@ -26,6 +26,11 @@ struct ActQ81 {
     uint16_t* s;     // [M][K/32] binary16
 };
 
+// Producers with the quantizer as epilogue: kind 0 RMSNorm (B = gamma),
+// kind 1 SiLU-mul (A = gate, B = up); act 0 Q8_K (o8k), 1 Q8_1 (o81).
+hipError_t launch_produce_quant(int kind, int act, const float* A, const float* B, int64_t lda, int64_t M,
+                                int64_t K, float eps, float* Y, int64_t ldy, ActQ8K o8k, ActQ81 o81,
+                                hipStream_t st);
 hipError_t launch_quantize_q8k(const float* X, int64_t M, int64_t K, int64_t ldx, ActQ8K out,
                                hipStream_t st);
 hipError_t launch_quantize_q8_1(const float* X, int64_t M, int64_t K, int64_t ldx, ActQ81 out,

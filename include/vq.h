@@ -171,6 +171,27 @@ vq_status vq_quantize_weights(int w, const float* W, int64_t N, int64_t K, void*
                               hipStream_t stream);
 
 /* ---------------------------------------------------------------------- */
+/* Producers with the activation quantizer as their epilogue (vllm.cpp PR   */
+/* #2890, commits "Norm epilogue" and "SiLU-mul quant"): one launch writes   */
+/* the producer's binary32 output Y (optional) and its quantized blocks Xq, */
+/* which are byte-identical to vq_quantize_act applied to that Y.  Xq then  */
+/* goes to vq_gemm (any M, including the decode case M = 1) or the grouped  */
+/* calls in place of a separate quantizer launch.                           */
+/*   vq_rmsnorm_quant: Y = X * r * gamma per row, r = 1/sqrt(sum(x^2)/K +    */
+/*     eps) (binary32; the sum's order is the kernel's own).  gamma fp32 [K]. */
+/*   vq_silu_mul_quant: Y = silu(G) * U = G / (1 + exp(-G)) * U (binary32).  */
+/*     G and U share the row stride ldx (a [M][2K] gate|up buffer works with */
+/*     U = G + K, ldx = 2K).                                                 */
+/* act: VQ_Q8_K or VQ_Q8_1 (K a multiple of its block); X, G, U:             */
+/* fp32 [M][ldx]; Y: NULL or fp32 [M][ldy]; Xq: vq_act_bytes(act, M, K)     */
+/* bytes.  Y and Xq must not overlap the inputs or each other.             */
+/* ---------------------------------------------------------------------- */
+vq_status vq_rmsnorm_quant(int act, const float* X, const float* gamma, int64_t M, int64_t K, int64_t ldx,
+                           float eps, float* Y, int64_t ldy, void* Xq, hipStream_t stream);
+vq_status vq_silu_mul_quant(int act, const float* G, const float* U, int64_t M, int64_t K, int64_t ldx,
+                            float* Y, int64_t ldy, void* Xq, hipStream_t stream);
+
+/* ---------------------------------------------------------------------- */
 /* Decode GEMV (M = 1), activation quantizer fused into the prologue:       */
 /*   y[n] = sum over blocks b ascending of c_b, binary32, where for Q4_K     */
 /*   c = da*(d*S - dmin*Mn) with S = sum_j sc_j*I_j, Mn = sum_j m_j*bsum32_j */
@@ -260,6 +281,8 @@ typedef struct {
     uint64_t gemm_grouped_q8_0;
     uint64_t gemm_grouped_rows;  /* calls of the per-row arm (also counted per type) */
     uint64_t gemm_skinny;        /* vq_gemm calls with M <= 8 run on the GEMV kernel (also counted per type) */
+    uint64_t rmsnorm_quant;      /* vq_rmsnorm_quant calls */
+    uint64_t silu_mul_quant;     /* vq_silu_mul_quant calls */
 } vq_stats;
 
 void vq_get_stats(vq_stats* out);
