@@ -46,6 +46,7 @@ constexpr int kGemvWaves = kGemvThreads / 64;   // most waves per workgroup
 constexpr int kXPre = 8;            // x rounds (256 values each) loaded up front per quantizer wave
 constexpr int kMaxHalfInstr = 31;   // 1 KiB load instructions per loader wave per half (vmcnt <= 63)
 constexpr size_t kMaxLds = 160 * 1024;
+constexpr size_t kStaticLds = 64;   // the kernel's static LDS (the loaders' counter), rounded up
 // LDS bytes per quantized super-block of x: 256 + 16, so the 16 tasks of a
 // wave round (consecutive super-blocks) start on 16 different bank groups.
 constexpr int kActStride = kQK + 16;
@@ -80,7 +81,7 @@ __host__ __device__ inline GemvLayout gemv_layout(int wt, int K, int rows, int s
     L.act_bs = L.act_d + align16i(mb * nbw * 4);
     const int nbs_bytes = (wt == 2) ? (K / kQK8) * 4 : (K / 16) * 2;
     L.partial = L.act_bs + align16i(mb * nbs_bytes);
-    L.wslice = L.partial + align16i(mb * rows * nbw * 4);
+    L.wslice = L.partial + align16i(mb * rows * ((nbw + 3) & ~3) * 4);
     L.slice_bytes = slice_bytes;
     L.total = L.wslice + slice_bytes;
     return L;
@@ -138,6 +139,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
     int nq, int h1_tasks, int kh0, int kh1, const uint8_t* __restrict__ xq_in, int M, int64_t ldy,
     int64_t xq_d_off, int64_t xq_aux_off) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    __shared__ int s_loaders_done;  // loader waves whose second part has landed
     constexpr int BB = WFmt<WT>::kBlk;
     constexpr int QV = WFmt<WT>::kVals;
     constexpr int LPT = (WT == 2) ? 1 : 2;    // lanes per task
@@ -285,12 +287,14 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
         }
     }
     }
+    if (tid == 0) s_loaders_done = 0;  // wave 0 is a quantizer wave; visible after the barrier
     lds_barrier();  // quantized x and the first half of the slice visible to every wave
 
     const int grp = lane / LPT, sub = lane % LPT;
     // One (row, block) task for each of the MB activation rows: the weight
     // bytes are read and unpacked once and reused for every row.
     const int nbw_ = (WT == 2) ? K / kQK8 : K / kQK;
+    const int nbp = (nb + 3) & ~3;  // partial row stride: 16-byte aligned rows
     auto compute_task = [&](int r, int blk) {
         const uint8_t* bp = wsl + rbase + __mul24(r, rb) + __mul24(blk, BB);
         if (WT == 0) {
@@ -348,7 +352,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
                     const float t1f = d * (float)S;
                     const float t2f = dmin * (float)Mn;
                     const float t3f = t1f - t2f;
-                    partial[(m * rows_per_wg + r) * nb + blk] = act_d[m * nbw_ + blk] * t3f;
+                    partial[(m * rows_per_wg + r) * nbp + blk] = act_d[m * nbw_ + blk] * t3f;
                 }
             }
         } else if (WT == 1) {
@@ -402,7 +406,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
                 S += dppi<0xB1>(S);
                 if (h == 0) {
                     const float t1f = d * (float)S;
-                    partial[(m * rows_per_wg + r) * nb + blk] = act_d[m * nbw_ + blk] * t1f;
+                    partial[(m * rows_per_wg + r) * nbp + blk] = act_d[m * nbw_ + blk] * t1f;
                 }
             }
         } else {
@@ -420,7 +424,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
 #pragma unroll
                 for (int i = 0; i < 8; ++i) I = sdot4((int)qw[i], (int)av[i], I);
                 const float sc = dw * act_d[m * nbw_ + blk];
-                partial[(m * rows_per_wg + r) * nb + blk] = sc * (float)I;
+                partial[(m * rows_per_wg + r) * nbp + blk] = sc * (float)I;
             }
         }
     };
@@ -455,33 +459,56 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
             }
         }
     }
-    lds_barrier();  // the second half (and any patch) visible to every wave
     if (loader) {
+        // The loaders alone meet here (the quantizer waves may still be on the
+        // first part): each signals that its loads (and any patch) are in LDS,
+        // then waits for the others, whose chunks its tasks read.  Bounded, so
+        // the wave always moves on.
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the patch bytes are written
+        if (lane == 0) atomicAdd(&s_loaders_done, 1);
+        for (int spin = 0; spin < (1 << 20); ++spin) {
+            const int done = __builtin_amdgcn_readfirstlane(
+                __hip_atomic_load(&s_loaders_done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
+            if (done >= GL) break;
+            __builtin_amdgcn_s_sleep(1);
+        }
         const int lw = wave - G;
         compute_range(th + (int)((int64_t)(ntask - th) * lw / GL), th + (int)((int64_t)(ntask - th) * (lw + 1) / GL));
     }
-    lds_barrier();
+    lds_barrier();  // every partial written
 
-    // ---- 5. rows: blocks summed in ascending order from 0
+    // ---- 5. rows: blocks summed in ascending order from 0.  The partials
+    // are read 16 at a time with independent float4 loads before the adds,
+    // so a row costs a few LDS round trips, not one per block.
     for (int idx = tid; idx < MB * rows; idx += nthr) {
         const int m = idx / rows, r = idx - m * rows;
         if (m >= M) break;
-        const float* p = partial + (m * rows_per_wg + r) * nb;
+        const float* p = partial + (m * rows_per_wg + r) * nbp;
         float acc = 0.0f;
         int b = 0;
-        if ((nb & 3) == 0) {
-            for (; b + 16 <= nb; b += 16) {
-                const float4 u0 = *(const float4*)(p + b);
-                const float4 u1 = *(const float4*)(p + b + 4);
-                const float4 u2 = *(const float4*)(p + b + 8);
-                const float4 u3 = *(const float4*)(p + b + 12);
-                acc = acc + u0.x; acc = acc + u0.y; acc = acc + u0.z; acc = acc + u0.w;
-                acc = acc + u1.x; acc = acc + u1.y; acc = acc + u1.z; acc = acc + u1.w;
-                acc = acc + u2.x; acc = acc + u2.y; acc = acc + u2.z; acc = acc + u2.w;
-                acc = acc + u3.x; acc = acc + u3.y; acc = acc + u3.z; acc = acc + u3.w;
-            }
+        for (; b + 16 <= nb; b += 16) {
+            const float4 u0 = *(const float4*)(p + b);
+            const float4 u1 = *(const float4*)(p + b + 4);
+            const float4 u2 = *(const float4*)(p + b + 8);
+            const float4 u3 = *(const float4*)(p + b + 12);
+            acc = acc + u0.x; acc = acc + u0.y; acc = acc + u0.z; acc = acc + u0.w;
+            acc = acc + u1.x; acc = acc + u1.y; acc = acc + u1.z; acc = acc + u1.w;
+            acc = acc + u2.x; acc = acc + u2.y; acc = acc + u2.z; acc = acc + u2.w;
+            acc = acc + u3.x; acc = acc + u3.y; acc = acc + u3.z; acc = acc + u3.w;
         }
-        for (; b < nb; ++b) acc = acc + p[b];
+        if (b < nb) {
+            // fewer than 16 left: the float4s that hold them (inside the padded row)
+            float t[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (b + 4 * q < nb) u = *(const float4*)(p + b + 4 * q);
+                t[4 * q] = u.x; t[4 * q + 1] = u.y; t[4 * q + 2] = u.z; t[4 * q + 3] = u.w;
+            }
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                if (b + j < nb) acc = acc + t[j];
+        }
         y[m * ldy + n0 + r] = acc;
     }
 
@@ -571,7 +598,7 @@ static GemvPlan gemv_plan(int wt, int64_t N, int64_t K, int mb) {
         const bool small = sbytes < (int64_t)kMaxLds;
         const GemvLayout L = gemv_layout(wt, (int)K, rows, small ? (int)sbytes : 0, mb);
         const bool fits = small && nq + nl <= kGemvWaves && kh0 + kh1 <= 63 && kh1 <= kMaxHalfInstr &&
-                          (size_t)L.total <= kMaxLds;
+                          (size_t)L.total + kStaticLds <= kMaxLds;
         if (fits || rows == 1) {
             p.rows = rows;
             p.nq = nq;
@@ -604,7 +631,7 @@ static hipError_t launch_gemv_t(const uint8_t* W, int64_t N, int64_t K, const fl
     if (!p.ok) return hipErrorInvalidValue;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void*)gemv_kernel<WT, MB>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)(kMaxLds - kStaticLds));
         if (e != hipSuccess) return e;
         attr_set = true;
     }
