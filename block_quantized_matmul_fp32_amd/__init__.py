@@ -26,7 +26,7 @@ EXPORTS = [
     "vq_block_bytes", "vq_weight_bytes", "vq_act_bytes", "vq_act_d_offset", "vq_act_aux_offset",
     "vq_quantize_act", "vq_quantize_weights", "vq_gemv", "vq_gemm", "vq_grouped_workspace_bytes",
     "vq_gemm_grouped", "vq_gemm_grouped_rows", "vq_weighted_sum", "vq_get_stats", "vq_reset_stats",
-    "vq_version", "vq_rmsnorm_quant", "vq_silu_mul_quant",
+    "vq_version", "vq_rmsnorm_quant", "vq_silu_mul_quant", "vq_set_small_batch_max", "vq_small_batch_max",
 ]
 
 STAT_FIELDS = ["quantize_q8k", "quantize_q8_1", "quantize_weights", "gemv_q4k", "gemv_q6k", "gemv_q8_0",
@@ -80,6 +80,10 @@ def lib():
         L.vq_gemm_grouped.argtypes = [I, P, I64, I64, I64, I, P, I64, P, I64, P, P, P, P, Z, P]
         L.vq_gemm_grouped_rows.argtypes = [I, P, I64, I64, I64, I, P, I64, P, I64, P, P, P, P, Z, P]
         L.vq_weighted_sum.argtypes = [P, P, I64, I64, I64, P, P]
+        L.vq_set_small_batch_max.argtypes = [I, I64]
+        L.vq_set_small_batch_max.restype = I
+        L.vq_small_batch_max.argtypes = [I]
+        L.vq_small_batch_max.restype = I64
         L.vq_rmsnorm_quant.argtypes = [I, P, P, I64, I64, I64, ctypes.c_float, P, I64, P, P]
         L.vq_silu_mul_quant.argtypes = [I, P, P, I64, I64, I64, P, I64, P, P]
         L.vq_get_stats.argtypes = [ctypes.POINTER(VQStats)]
@@ -141,6 +145,15 @@ def act_d_offset(act: int, M: int, K: int) -> int:
 
 def act_aux_offset(act: int, M: int, K: int) -> int:
     return lib().vq_act_aux_offset(act, M, K)
+
+
+def set_small_batch_max(w: int, max_m: int):
+    """vq_set_small_batch_max: vq_gemm runs M <= max_m on the GEMV kernel (-1: default)."""
+    _check(lib().vq_set_small_batch_max(w, max_m))
+
+
+def small_batch_max(w: int) -> int:
+    return int(lib().vq_small_batch_max(w))
 
 
 def grouped_workspace_bytes(E: int, T: int, top_k: int) -> int:

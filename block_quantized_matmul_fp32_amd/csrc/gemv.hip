@@ -43,6 +43,7 @@ namespace vqk {
 
 constexpr int kGemvThreads = 1024;              // most threads per workgroup
 constexpr int kGemvWaves = kGemvThreads / 64;   // most waves per workgroup
+constexpr int kGroupMB = 4;         // rows per group when a small batch runs in several groups
 constexpr int kXPre = 8;            // x rounds (256 values each) loaded up front per quantizer wave
 constexpr int kMaxHalfInstr = 31;   // 1 KiB load instructions per loader wave per half (vmcnt <= 63)
 constexpr size_t kMaxLds = 160 * 1024;
@@ -179,6 +180,30 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
     const int rbase = (int)(s0 - 16 * cb);     // LDS byte of slice byte o: wsl + rbase + o
     const bool loader = wave >= G;
 
+    // Activation rows [row0, row0 + n) of a planar pre-quantized buffer into
+    // the LDS rows 0..n-1 (threads t0, t0 + stride, ...).
+    auto copy_rows = [&](int row0, int n, int t0, int stride) {
+        const int nbw = (WT == 2) ? K / kQK8 : K / kQK;
+        const int cpr = K / 16;  // 16-byte chunks per row
+        for (int i = t0; i < n * cpr; i += stride) {
+            const int m = i / cpr, c = i - m * cpr;
+            const uint4 v = *(const uint4*)(xq_in + (int64_t)(row0 + m) * K + 16 * c);
+            const int dst = (WT == 2) ? 16 * c : (c >> 4) * kActStride + 16 * (c & 15);
+            *(uint4*)(act_qs + m * L.act_row + dst) = v;
+        }
+        if (WT == 2) {
+            const uint16_t* dsrc = (const uint16_t*)(xq_in + xq_d_off) + (int64_t)row0 * nbw;
+            for (int i = t0; i < n * nbw; i += stride) act_d[i] = half_bits_to_float(dsrc[i]);
+        } else {
+            const float* dsrc = (const float*)(xq_in + xq_d_off) + (int64_t)row0 * nbw;
+            for (int i = t0; i < n * nbw; i += stride) act_d[i] = dsrc[i];
+            const int16_t* bsrc = (const int16_t*)(xq_in + xq_aux_off) + (int64_t)row0 * (K / 16);
+            for (int i = t0; i < n * (K / 16); i += stride) act_bs[i] = bsrc[i];
+        }
+    };
+    // rows of activations in LDS (the current group of at most MB rows)
+    int Mg = M < MB ? M : MB;
+
     if (loader) {
         // ---- loaders: both parts into LDS, kh0 / kh1 instructions each
         const int lw = wave - G;
@@ -209,25 +234,8 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
         issue_half(cm, ce, kh1);
         wait_vmcnt(kh1);  // the first part has landed
     } else if (xq_in != nullptr) {
-        // ---- quantizer waves, pre-quantized input: M planar rows into LDS
-        const int nbw = (WT == 2) ? K / kQK8 : K / kQK;
-        const int qtid = tid, qthr = 64 * G;
-        const int cpr = K / 16;  // 16-byte chunks per row
-        for (int i = qtid; i < M * cpr; i += qthr) {
-            const int m = i / cpr, c = i - m * cpr;
-            const uint4 v = *(const uint4*)(xq_in + (int64_t)m * K + 16 * c);
-            const int dst = (WT == 2) ? 16 * c : (c >> 4) * kActStride + 16 * (c & 15);
-            *(uint4*)(act_qs + m * L.act_row + dst) = v;
-        }
-        if (WT == 2) {
-            const uint16_t* dsrc = (const uint16_t*)(xq_in + xq_d_off);
-            for (int i = qtid; i < M * nbw; i += qthr) act_d[i] = half_bits_to_float(dsrc[i]);
-        } else {
-            const float* dsrc = (const float*)(xq_in + xq_d_off);
-            for (int i = qtid; i < M * nbw; i += qthr) act_d[i] = dsrc[i];
-            const int16_t* bsrc = (const int16_t*)(xq_in + xq_aux_off);
-            for (int i = qtid; i < M * (K / 16); i += qthr) act_bs[i] = bsrc[i];
-        }
+        // ---- quantizer waves, pre-quantized input: the first group of rows into LDS
+        copy_rows(0, Mg, tid, 64 * G);
     } else {
         // ---- quantizer waves: x loads, then the shared quantizer into LDS
         const int xsteps = (K + kQK - 1) / kQK;  // 256 values per wave step
@@ -318,7 +326,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
             const float dmin = half_bits_to_float(hdr.x >> 16);
 #pragma unroll
             for (int m = 0; m < MB; ++m) {
-                if (m >= M) break;
+                if (m >= Mg) break;
                 const int8_t* ab = act_qs + m * L.act_row + __mul24(blk, kActStride) + 128 * hf;
                 uint32_t av[32];
 #pragma unroll
@@ -378,7 +386,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
             const float d = half_bits_to_float(*(const uint16_t*)(bp + 208));
 #pragma unroll
             for (int m = 0; m < MB; ++m) {
-                if (m >= M) break;
+                if (m >= Mg) break;
                 const int8_t* ab = act_qs + m * L.act_row + __mul24(blk, kActStride) + 128 * h;
                 uint32_t av[32];
 #pragma unroll
@@ -415,7 +423,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
             const float dw = half_bits_to_float(*(const uint16_t*)bp);
 #pragma unroll
             for (int m = 0; m < MB; ++m) {
-                if (m >= M) break;
+                if (m >= Mg) break;
                 const int8_t* ab = act_qs + m * L.act_row + blk * kQK8;
                 const uint4 a0 = *(const uint4*)ab;
                 const uint4 a1 = *(const uint4*)(ab + 16);
@@ -440,9 +448,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
         }
     };
 
-    if (!loader) {
-        compute_range((int)((int64_t)th * wave / G), (int)((int64_t)th * (wave + 1) / G));
-    } else {
+    if (loader) {
         wait_vmcnt(0);  // the second half has landed
         // A partial last chunk of the buffer (loaded as its predecessor above)
         // is patched byte by byte by the lane whose chunk it is.
@@ -458,8 +464,6 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
                 }
             }
         }
-    }
-    if (loader) {
         // The loaders alone meet here (the quantizer waves may still be on the
         // first part): each signals that its loads (and any patch) are in LDS,
         // then waits for the others, whose chunks its tasks read.  Bounded, so
@@ -472,17 +476,15 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
             if (done >= GL) break;
             __builtin_amdgcn_s_sleep(1);
         }
-        const int lw = wave - G;
-        compute_range(th + (int)((int64_t)(ntask - th) * lw / GL), th + (int)((int64_t)(ntask - th) * (lw + 1) / GL));
     }
-    lds_barrier();  // every partial written
 
     // ---- 5. rows: blocks summed in ascending order from 0.  The partials
     // are read 16 at a time with independent float4 loads before the adds,
     // so a row costs a few LDS round trips, not one per block.
+    auto sum_rows = [&](int row0) {
     for (int idx = tid; idx < MB * rows; idx += nthr) {
         const int m = idx / rows, r = idx - m * rows;
-        if (m >= M) break;
+        if (m >= Mg) break;
         const float* p = partial + (m * rows_per_wg + r) * nbp;
         float acc = 0.0f;
         int b = 0;
@@ -509,7 +511,39 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
             for (int j = 0; j < 16; ++j)
                 if (b + j < nb) acc = acc + t[j];
         }
-        y[m * ldy + n0 + r] = acc;
+        y[(row0 + m) * ldy + n0 + r] = acc;
+    }
+    };
+
+    // The first group of rows: the quantizer waves compute the first part of
+    // the tasks while the rest streams in, the loaders the last part.  Further
+    // groups of MB rows (small batches above 8 rows, built with MB = 4 only):
+    // the slice stays in LDS, every wave copies the group's rows, then takes
+    // an equal share of all tasks.  One compute call site for all groups.
+    for (int row0 = 0;;) {
+        int t0, t1;
+        if (row0 == 0) {
+            if (!loader) {
+                t0 = (int)((int64_t)th * wave / G);
+                t1 = (int)((int64_t)th * (wave + 1) / G);
+            } else {
+                const int lw = wave - G;
+                t0 = th + (int)((int64_t)(ntask - th) * lw / GL);
+                t1 = th + (int)((int64_t)(ntask - th) * (lw + 1) / GL);
+            }
+        } else {
+            t0 = (int)((int64_t)ntask * wave / nw);
+            t1 = (int)((int64_t)ntask * (wave + 1) / nw);
+        }
+        compute_range(t0, t1);
+        lds_barrier();  // every partial of the group written
+        sum_rows(row0);
+        row0 += MB;
+        if (MB != kGroupMB || row0 >= M) break;
+        Mg = (M - row0) < MB ? (M - row0) : MB;
+        __syncthreads();  // the previous group's rows and partials are no longer read
+        copy_rows(row0, Mg, tid, nthr);
+        __syncthreads();
     }
 
     // ---- 6. the fused quantizer's bytes, for callers that want them
@@ -620,7 +654,19 @@ size_t gemv_lds_bytes(int wtype, int64_t N, int64_t K, int mb) {
     return p.ok ? (size_t)p.lds : (size_t)-1;
 }
 
-static int mb_for(int64_t M) { return M <= 1 ? 1 : (M <= 2 ? 2 : (M <= 4 ? 4 : 8)); }
+// Rows per group for M activation rows: 1, 2, 4 or 8 in one group; above 8
+// rows (or when the 8-row plan would need a second round of workgroups),
+// groups of 4.
+static int mb_for(int wt, int64_t N, int64_t K, int64_t M) {
+    if (M <= 1) return 1;
+    if (M <= 2) return 2;
+    if (M <= 4) return 4;
+    if (M <= 8) {
+        const GemvPlan p = gemv_plan(wt, N, K, 8);
+        if (p.ok && (N + p.rows - 1) / p.rows <= num_cus()) return 8;
+    }
+    return kGroupMB;
+}
 
 template <int WT, int MB>
 static hipError_t launch_gemv_t(const uint8_t* W, int64_t N, int64_t K, const float* x, float* y, int64_t ldy,
@@ -655,7 +701,7 @@ hipError_t launch_gemv(int wtype, const uint8_t* W, int64_t N, int64_t K, const 
 template <int WT>
 static hipError_t launch_skinny_t(const uint8_t* W, int64_t N, int64_t K, const uint8_t* xq, int64_t M,
                                   int64_t d_off, int64_t aux_off, float* Y, int64_t ldy, hipStream_t st) {
-    switch (mb_for(M)) {
+    switch (mb_for(WT, N, K, M)) {
         case 1: return launch_gemv_t<WT, 1>(W, N, K, nullptr, Y, ldy, nullptr, xq, M, d_off, aux_off, st);
         case 2: return launch_gemv_t<WT, 2>(W, N, K, nullptr, Y, ldy, nullptr, xq, M, d_off, aux_off, st);
         case 4: return launch_gemv_t<WT, 4>(W, N, K, nullptr, Y, ldy, nullptr, xq, M, d_off, aux_off, st);
@@ -663,8 +709,9 @@ static hipError_t launch_skinny_t(const uint8_t* W, int64_t N, int64_t K, const 
     }
 }
 
-bool gemm_skinny_ok(int wtype, int64_t N, int64_t K, int64_t M) {
-    return M >= 1 && M <= kSkinnyMaxM && N > 0 && gemv_lds_bytes(wtype, N, K, mb_for(M)) <= kMaxLds;
+bool gemm_skinny_ok(int wtype, int64_t N, int64_t K, int64_t M, int64_t max_m) {
+    return M >= 1 && M <= max_m && M <= kSkinnyMaxM && N > 0 &&
+           gemv_lds_bytes(wtype, N, K, mb_for(wtype, N, K, M)) <= kMaxLds;
 }
 
 hipError_t launch_gemm_skinny(int wtype, const uint8_t* W, int64_t N, int64_t K, const uint8_t* xq, int64_t M,

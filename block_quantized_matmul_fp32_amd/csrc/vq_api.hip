@@ -31,6 +31,11 @@ struct Counters {
 };
 Counters g_stats;
 
+// Largest M that vq_gemm runs on the GEMV kernel, per weight type (Q4_K,
+// Q6_K, Q8_0): the GEMV <-> GEMM crossover.
+constexpr int64_t kSmallMaxDefault[3] = {16, 64, 32};
+std::atomic<int64_t> g_small_max[3] = {{kSmallMaxDefault[0]}, {kSmallMaxDefault[1]}, {kSmallMaxDefault[2]}};
+
 vq_status fail(vq_status s, const char* fmt, ...) {
     char buf[512];
     va_list ap;
@@ -336,7 +341,7 @@ vq_status vq_gemm(int w, const void* W, int64_t N, int64_t K, int act, const voi
     if (w == VQ_Q4_K) g_stats.gemm_q4k++;
     else if (w == VQ_Q6_K) g_stats.gemm_q6k++;
     else g_stats.gemm_q8_0++;
-    if (vqk::gemm_skinny_ok(w, N, K, M)) {
+    if (vqk::gemm_skinny_ok(w, N, K, M, g_small_max[w == VQ_Q4_K ? 0 : (w == VQ_Q6_K ? 1 : 2)].load())) {
         // small batch: the weights streamed once through the GEMV kernel for all M rows
         g_stats.gemm_skinny++;
         return hip_status(vqk::launch_gemm_skinny(w, (const uint8_t*)W, N, K, base, M,
@@ -345,6 +350,22 @@ vq_status vq_gemm(int w, const void* W, int64_t N, int64_t K, int act, const voi
                           fn);
     }
     return hip_status(vqk::launch_gemm(w, (const uint8_t*)W, N, K, qs, d, aux, M, Y, ldy, stream), fn);
+}
+
+vq_status vq_set_small_batch_max(int w, int64_t max_m) {
+    const char* fn = "vq_set_small_batch_max";
+    VQ_TRY(check_weight(w, fn));
+    if (max_m < -1 || max_m > vqk::kSkinnyMaxM)
+        return fail(VQ_ERR_INVALID_ARG, "%s: max_m = %lld outside [-1, %d]", fn, (long long)max_m,
+                    vqk::kSkinnyMaxM);
+    const int i = w == VQ_Q4_K ? 0 : (w == VQ_Q6_K ? 1 : 2);
+    g_small_max[i] = (max_m < 0) ? kSmallMaxDefault[i] : max_m;
+    return VQ_OK;
+}
+
+int64_t vq_small_batch_max(int w) {
+    if (!is_weight(w)) return -1;
+    return g_small_max[w == VQ_Q4_K ? 0 : (w == VQ_Q6_K ? 1 : 2)].load();
 }
 
 size_t vq_grouped_workspace_bytes(int64_t E, int64_t T, int64_t top_k) {

@@ -42,10 +42,11 @@ hipError_t launch_quantize_weights(int wtype, const float* W, int64_t N, int64_t
 hipError_t launch_gemv(int wtype, const uint8_t* W, int64_t N, int64_t K, const float* x,
                        float* y, uint8_t* xq_out, hipStream_t st);
 size_t gemv_lds_bytes(int wtype, int64_t N, int64_t K, int mb);
-// Small batches (M <= kSkinnyMaxM) of pre-quantized activations run on the
-// GEMV kernel, which streams the weights once for all M rows.
-constexpr int kSkinnyMaxM = 8;
-bool gemm_skinny_ok(int wtype, int64_t N, int64_t K, int64_t M);
+// Small batches (M <= max_m <= kSkinnyMaxM) of pre-quantized activations run
+// on the GEMV kernel, which streams the weights once for all M rows (in
+// groups of rows above 8).
+constexpr int kSkinnyMaxM = 64;
+bool gemm_skinny_ok(int wtype, int64_t N, int64_t K, int64_t M, int64_t max_m);
 hipError_t launch_gemm_skinny(int wtype, const uint8_t* W, int64_t N, int64_t K, const uint8_t* xq, int64_t M,
                               int64_t d_off, int64_t aux_off, float* Y, int64_t ldy, hipStream_t st);
 

@@ -210,12 +210,24 @@ vq_status vq_gemv(int w, const void* W, int64_t N, int64_t K, const float* x, fl
 /* n < N, through exact int32 sub-block sums and binary32 scale combines.   */
 /* Xq is the planar activation buffer of type act (Q8_K for Q4_K/Q6_K,      */
 /* Q8_1 for Q8_0) holding M rows; Y fp32 with row stride ldy >= N.          */
-/* M <= 8 runs on the decode GEMV kernel over the pre-quantized rows (the    */
-/* weights streamed once for all rows), larger M on the int8 MFMA GEMM; the  */
-/* result is the same fixed-order definition either way.                    */
+/* Small batches, M <= vq_small_batch_max(w), run on the decode GEMV kernel */
+/* over the pre-quantized rows (the weights streamed once for all rows, in  */
+/* groups of 4 rows above 8), larger M on the int8 MFMA GEMM; the result is */
+/* the same fixed-order definition either way.                             */
 /* ---------------------------------------------------------------------- */
 vq_status vq_gemm(int w, const void* W, int64_t N, int64_t K, int act, const void* Xq,
                   int64_t M, float* Y, int64_t ldy, hipStream_t stream);
+
+/* ---------------------------------------------------------------------- */
+/* The GEMV <-> GEMM crossover of vq_gemm (vllm.cpp PR #2890, "lever-B1":  */
+/* the fold crossover made tunable at run time): vq_gemm with weight type w */
+/* runs M <= max_m on the GEMV kernel.  max_m in [0, 64] (0: never), -1     */
+/* restores the default (Q4_K 16, Q6_K 64, Q8_0 32, from measurements on    */
+/* the decode shapes).  Process-wide; not synchronised with calls in flight.*/
+/* vq_small_batch_max returns the current value (-1 for a non-weight type). */
+/* ---------------------------------------------------------------------- */
+vq_status vq_set_small_batch_max(int w, int64_t max_m);
+int64_t vq_small_batch_max(int w);
 
 /* ---------------------------------------------------------------------- */
 /* Routed-expert grouped GEMM (MUL_MAT_ID, broadcast arm) with the weighted  */

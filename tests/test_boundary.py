@@ -154,3 +154,25 @@ def test_status_strings_and_stats(vq):
     vq.reset_stats()
     st = vq.get_stats()
     assert set(st) == set(vq.STAT_FIELDS) and all(v == 0 for v in st.values())
+
+
+def test_small_batch_crossover_setting(vq):
+    """vq_set_small_batch_max: defaults, range and type checks (host only)."""
+    defaults = {vq.Q4_K: 16, vq.Q6_K: 64, vq.Q8_0: 32}
+    for w, d in defaults.items():
+        assert vq.small_batch_max(w) == d
+    try:
+        vq.set_small_batch_max(vq.Q6_K, 3)
+        assert vq.small_batch_max(vq.Q6_K) == 3
+        vq.set_small_batch_max(vq.Q6_K, -1)
+        assert vq.small_batch_max(vq.Q6_K) == 64
+        with pytest.raises(vq.VQError, match="INVALID_ARG"):
+            vq.set_small_batch_max(vq.Q4_K, 65)
+        with pytest.raises(vq.VQError, match="INVALID_ARG"):
+            vq.set_small_batch_max(vq.Q4_K, -2)
+        with pytest.raises(vq.VQError, match="UNSUPPORTED_TYPE"):
+            vq.set_small_batch_max(vq.Q8_K, 4)
+        assert vq.small_batch_max(vq.Q8_K) == -1
+    finally:
+        for w in defaults:
+            vq.set_small_batch_max(w, -1)

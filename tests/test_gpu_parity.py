@@ -212,8 +212,9 @@ SKINNY_SHAPES = {oracle.Q4_K: (300, 2560), oracle.Q6_K: (131, 1536), oracle.Q8_0
 
 @pytest.mark.parametrize("wtype", WTYPES)
 def test_gemm_small_batch(wtype):
-    """M = 1..8 runs on the GEMV kernel reading the pre-quantized rows (the
-    weights streamed once for all rows), M = 9 on the MFMA GEMM; both
+    """M = 1..8 in one group and M > 8 in groups of four rows on the GEMV
+    kernel reading the pre-quantized rows (the weights streamed once), and
+    the same M on the MFMA GEMM with the crossover set to 0; both
     bit-identical to the oracle, padding columns untouched, and row m equal
     to the decode GEMV of x_m."""
     N, K = SKINNY_SHAPES[wtype]
@@ -221,21 +222,28 @@ def test_gemm_small_batch(wtype):
     Wq = oracle.quantize_weights(wtype, W)
     Wd = H.to_dev(Wq)
     ldy = N + 5
-    for M in (1, 2, 3, 4, 5, 8, 9):
-        X = synth.normal((1451, wtype, M), (M, K))
-        X[:, ::61] *= np.float32(15.0)
-        act = oracle_act(wtype, X)
-        H.say("gemm small batch %s M=%d N=%d K=%d" % (WNAME[wtype], M, N, K))
-        vq.reset_stats()
-        Yd = H.to_dev(np.full((M, ldy), np.nan, np.float32))
-        vq.gemm(wtype, Wd, N, K, vq.act_for(wtype), H.to_dev(H.pack_act(act, wtype)), M, Y=Yd, ldy=ldy)
-        Yh = H.host(Yd)
-        assert vq.get_stats()["gemm_skinny"] == (1 if M <= 8 else 0)
-        H.assert_bitwise(Yh[:, :N], oracle.gemm(wtype, Wq, N, K, act, nthreads=8), "M=%d" % M)
-        assert np.isnan(Yh[:, N:]).all(), "padding columns written"
-        for m in sorted({0, M - 1}):
-            y = vq.gemv(wtype, Wd, N, K, H.to_dev(np.ascontiguousarray(X[m])))
-            H.assert_bitwise(H.host(y), Yh[m, :N], "gemv row %d vs gemm M=%d" % (m, M))
+    try:
+        for M in (1, 2, 3, 4, 5, 8, 9, 13, 16, 33):
+            X = synth.normal((1451, wtype, M), (M, K))
+            X[:, ::61] *= np.float32(15.0)
+            act = oracle_act(wtype, X)
+            ref = oracle.gemm(wtype, Wq, N, K, act, nthreads=8)
+            Xq = H.to_dev(H.pack_act(act, wtype))
+            for max_m, skinny in ((64, 1), (0, 0)):
+                H.say("gemm small batch %s M=%d N=%d K=%d crossover %d" % (WNAME[wtype], M, N, K, max_m))
+                vq.set_small_batch_max(wtype, max_m)
+                vq.reset_stats()
+                Yd = H.to_dev(np.full((M, ldy), np.nan, np.float32))
+                vq.gemm(wtype, Wd, N, K, vq.act_for(wtype), Xq, M, Y=Yd, ldy=ldy)
+                Yh = H.host(Yd)
+                assert vq.get_stats()["gemm_skinny"] == skinny
+                H.assert_bitwise(Yh[:, :N], ref, "M=%d crossover %d" % (M, max_m))
+                assert np.isnan(Yh[:, N:]).all(), "padding columns written"
+            for m in sorted({0, M - 1}):
+                y = vq.gemv(wtype, Wd, N, K, H.to_dev(np.ascontiguousarray(X[m])))
+                H.assert_bitwise(H.host(y), Yh[m, :N], "gemv row %d vs gemm M=%d" % (m, M))
+    finally:
+        vq.set_small_batch_max(wtype, -1)
 
 
 @pytest.mark.parametrize("wtype", WTYPES)

@@ -95,7 +95,7 @@ def test_decode_gemv_full(which):
     assert ref_fp64.nmse(yh, ref) <= 1e-6
 
 
-@pytest.mark.parametrize("M", [2, 8])
+@pytest.mark.parametrize("M", [2, 8, 16])
 @pytest.mark.parametrize("which", ["Q4_K", "Q6_K"])
 def test_decode_small_batch_full(which, M):
     """A small decode batch (M rows of the prefill activations) against the
