@@ -245,7 +245,7 @@ def run_q8_0(torch, vq, synth, iters):
 
 
 def run_small_batch(torch, vq, synth, iters):
-    """vq_gemm at M = 2, 4, 8 on the decode matrices (the GEMV-kernel arm),
+    """vq_gemm at M = 2, 4, 8, 16 on the decode matrices (the GEMV-kernel arm),
     weights rotated past the Infinity Cache; rate = weight bytes + activation
     bytes + output bytes per call."""
     dev = torch.device("cuda:0")
@@ -257,8 +257,8 @@ def run_small_batch(torch, vq, synth, iters):
         del W
         R = max(2, math.ceil(640 * (1 << 20) / Q.numel()))
         Qs = [Q] + [Q.clone() for _ in range(R - 1)]
-        X = torch.from_numpy(synth.prefill_activations(xn, 8)).to(dev)
-        for M in (2, 4, 8):
+        X = torch.from_numpy(synth.prefill_activations(xn, 16)).to(dev)
+        for M in (2, 4, 8, 16):
             Xq = vq.quantize_act(vq.Q8_K, X[:M].contiguous())
             Y = torch.empty((M, N), dtype=torch.float32, device=dev)
             t, _ = time_graph(lambda i: vq.gemm(wt, Qs[i % R], N, K, vq.Q8_K, Xq, M, Y=Y), R, max(iters, 5 * R))

@@ -600,10 +600,9 @@ static hipError_t launch_gemm_cfg(const uint8_t* W, int64_t N, int64_t K, const 
 // Tile choice: 64 x 256 tiles unless they would leave CUs without a
 // workgroup (then 64 x 128 tiles on the same eight waves, twice the
 // workgroups); Q8_0, whose per-block epilogue dominates, always takes the
-// 64 x 128 tiles (measured faster at every workload shape).  Q4_K takes
-// 64 x 64 tiles (four waves) when even 64 x 128 tiles leave CUs idle
-// (M = 512 of the gate projection: 86.7 -> 80.5 us); Q6_K measured slower
-// there and keeps 64 x 128.
+// 64 x 128 tiles (measured faster at every workload shape).  (64 x 64
+// tiles for still smaller grids measured no faster: the time of a column
+// tile is its sequence of super-block steps, not the number of tiles.)
 template <int WT>
 static hipError_t launch_gemm_t(const uint8_t* W, int64_t N, int64_t K, const void* aqs, const void* ad,
                                 const void* aux, int64_t M, float* Y, int64_t ldy, hipStream_t st) {
@@ -615,8 +614,6 @@ static hipError_t launch_gemm_t(const uint8_t* W, int64_t N, int64_t K, const vo
         cus = v;
     }
     const int64_t wg256 = ((N + kBN - 1) / kBN) * ((M + 255) / 256);
-    const int64_t wg128 = ((N + kBN - 1) / kBN) * ((M + 127) / 128);
-    if (WT == 0 && wg128 < cus) return launch_gemm_cfg<WT, 2, 2>(W, N, K, aqs, ad, aux, M, Y, ldy, st);
     if (WT == 2 || wg256 < cus) return launch_gemm_cfg<WT, 4, 2>(W, N, K, aqs, ad, aux, M, Y, ldy, st);
     return launch_gemm_cfg<WT, 4, 4>(W, N, K, aqs, ad, aux, M, Y, ldy, st);
 }
