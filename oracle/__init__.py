@@ -29,10 +29,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "vq_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
-Q4_K, Q6_K, Q8_0 = 0, 1, 2
+Q4_K, Q6_K, Q8_0, Q5_K = 0, 1, 2, 5
 WEIGHT_TYPES = {"Q4_K": Q4_K, "Q6_K": Q6_K, "Q8_0": Q8_0}
-BLOCK_BYTES = {Q4_K: 144, Q6_K: 210, Q8_0: 34}
-BLOCK_ELEMS = {Q4_K: 256, Q6_K: 256, Q8_0: 32}
+BLOCK_BYTES = {Q4_K: 144, Q6_K: 210, Q8_0: 34, Q5_K: 176}
+BLOCK_ELEMS = {Q4_K: 256, Q6_K: 256, Q8_0: 32, Q5_K: 256}
 
 _lib = None
 
@@ -59,6 +59,8 @@ def _bind(path):
     L.oracle_q4k_fields.argtypes = [P, P, P, P, P]
     L.oracle_q6k_fields.argtypes = [P, P, P, P]
     L.oracle_q4k_build.argtypes = [ctypes.c_uint16, ctypes.c_uint16, P, P, P, P]
+    L.oracle_q5k_fields.argtypes = [P, P, P, P, P]
+    L.oracle_q5k_build.argtypes = [ctypes.c_uint16, ctypes.c_uint16, P, P, P, P]
     L.oracle_q6k_build.argtypes = [ctypes.c_uint16, P, P, P]
     L.oracle_quantize_weights.argtypes = [ctypes.c_int, P, I64, I64, P]
     L.oracle_quantize_q8k.argtypes = [P, I64, I64, I64, P, P, P]
@@ -140,6 +142,26 @@ def q6k_fields(block: np.ndarray):
     q = np.zeros(256, np.int32)
     lib().oracle_q6k_fields(_p(b), _p(d), _p(sc), _p(q))
     return float(d[0]), sc, q
+
+
+def q5k_fields(block: np.ndarray):
+    """(d, dmin, sc[8], m[8], q[256]) of one 176-byte Q5_K block."""
+    b = np.ascontiguousarray(block, dtype=np.uint8)
+    dd = np.zeros(2, np.float32)
+    sc = np.zeros(8, np.int32)
+    m = np.zeros(8, np.int32)
+    q = np.zeros(256, np.int32)
+    lib().oracle_q5k_fields(_p(b), _p(dd), _p(sc), _p(m), _p(q))
+    return float(dd[0]), float(dd[1]), sc, m, q
+
+
+def q5k_build(d16: int, dmin16: int, sc, m, q) -> np.ndarray:
+    out = np.zeros(176, np.uint8)
+    sc = np.ascontiguousarray(sc, np.int32)
+    m = np.ascontiguousarray(m, np.int32)
+    q = np.ascontiguousarray(q, np.int32)
+    lib().oracle_q5k_build(d16, dmin16, _p(sc), _p(m), _p(q), _p(out))
+    return out
 
 
 def q4k_build(d16: int, dmin16: int, sc, m, q) -> np.ndarray:
@@ -257,7 +279,7 @@ def gemm_sampled(wtype, Wq, N, K, act, ms, ns, nthreads: int = 1) -> np.ndarray:
 
 
 def subblock_sums(wtype: int, wblock: np.ndarray, a: np.ndarray) -> np.ndarray:
-    n = {Q4_K: 8, Q6_K: 16, Q8_0: 1}[wtype]
+    n = {Q4_K: 8, Q6_K: 16, Q8_0: 1, Q5_K: 8}[wtype]
     out = np.zeros(n, np.int32)
     wb = np.ascontiguousarray(wblock, np.uint8)
     aa = np.ascontiguousarray(a, np.int8)

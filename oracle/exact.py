@@ -25,8 +25,11 @@ def _fr(x) -> Fraction:
 def deq_weights_exact(wtype: int, Wq: np.ndarray, N: int, K: int):
     Wq = np.asarray(Wq, np.uint8).reshape(N, -1)
     out = [[Fraction(0)] * K for _ in range(N)]
-    if wtype == 0:
-        d, dmin, sc, m, q = ref_fp64.q4k_decode_fields(Wq.reshape(N, K // 256, 144))
+    if wtype in (0, 5):
+        if wtype == 0:
+            d, dmin, sc, m, q = ref_fp64.q4k_decode_fields(Wq.reshape(N, K // 256, 144))
+        else:
+            d, dmin, sc, m, q = ref_fp64.q5k_decode_fields(Wq.reshape(N, K // 256, 176))
         for n in range(N):
             for b in range(K // 256):
                 dd, dm = _fr(d[n, b]), _fr(dmin[n, b])

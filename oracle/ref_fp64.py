@@ -16,6 +16,8 @@ The block layouts are decoded here with numpy, independently of vq_oracle.c:
   Element e (h=e//128, r=e%128): low nibble r//64 of ql[64h + r%64], bit pair
   r//32 of qh[32h + r%32].  value = d*sc[e//16]*(q-32).
 * Q8_0 (34 B): d f16 @0, int8 q @2.  value = d*q.
+* Q5_K (176 B): the Q4_K header @0..16, fifth-bit plane @16..48 (bit j of
+  byte 16+l = bit 4 of element 32j+l), the Q4_K nibbles @48..176.
 * Q8_K activation: a = d[m, i//256] * qs[m, i].
 * Q8_1 activation: a = f16(d)[m, i//32] * qs[m, i].
 """
@@ -48,6 +50,19 @@ def q4k_decode_fields(blocks: np.ndarray):
     return d, dmin, sc, m, q
 
 
+def q5k_decode_fields(blocks: np.ndarray):
+    """blocks uint8 [..., 176] -> d, dmin [...]; sc, m [..., 8]; q [..., 256] in 0..31.
+    Bytes 0..15 and 48..175 are a Q4_K block's header and nibbles; bit j of
+    byte 16 + l is bit 4 of element 32j + l."""
+    b = np.asarray(blocks, np.uint8)
+    as_q4k = np.concatenate([b[..., 0:16], b[..., 48:176]], axis=-1)
+    d, dmin, sc, m, q = q4k_decode_fields(as_q4k)
+    e = np.arange(256)
+    qh = b[..., 16:48].astype(np.int64)
+    q = q | (((qh[..., e % 32] >> (e // 32)) & 1) << 4)
+    return d, dmin, sc, m, q
+
+
 def q6k_decode_fields(blocks: np.ndarray):
     """blocks uint8 [..., 210] -> d [...]; sc [..., 16] (int8); q [..., 256] in 0..63."""
     b = np.asarray(blocks, np.uint8)
@@ -69,6 +84,12 @@ def dequant_weights(wtype: int, Wq: np.ndarray, N: int, K: int) -> np.ndarray:
     if wtype == 0:
         blocks = Wq.reshape(N, K // 256, 144)
         d, dmin, sc, m, q = q4k_decode_fields(blocks)
+        sub = np.arange(256) // 32
+        w = d[..., None] * sc[..., sub] * q - dmin[..., None] * m[..., sub]
+        return w.reshape(N, K)
+    if wtype == 5:
+        blocks = Wq.reshape(N, K // 256, 176)
+        d, dmin, sc, m, q = q5k_decode_fields(blocks)
         sub = np.arange(256) // 32
         w = d[..., None] * sc[..., sub] * q - dmin[..., None] * m[..., sub]
         return w.reshape(N, K)

@@ -40,6 +40,7 @@
 #define QK8 32     /* block length of Q8_0 and Q8_1 */
 
 #define Q4K_BYTES 144
+#define Q5K_BYTES 176
 #define Q6K_BYTES 210
 #define Q8_0_BYTES 34
 
@@ -118,6 +119,11 @@ static int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v
 /*   value_e = d*sc_{e/16}*(q_e - 32)                                         */
 /* Q8_0, 34 bytes per 32 weights: [0,2) d (binary16), [2,34) int8 qs          */
 /*   value_i = d*q_i                                                          */
+/* Q5_K, 176 bytes per 256 weights (the pages name Q5_K but give no layout;   */
+/* this one is a Q4_K block plus a plane of fifth bits):                      */
+/*   [0,16) d, dmin and scales exactly as Q4_K   [16,48) qh   [48,176) qs as  */
+/*   the Q4_K nibbles; bit j of qh byte l is bit 4 of element 32j+l, so       */
+/*   q_i = nibble_i | qhbit_i << 4 in 0..31; value_i = d*sc*q_i - dmin*m      */
 /* ------------------------------------------------------------------------ */
 
 typedef struct {
@@ -164,6 +170,26 @@ static void q4k_pack(const q4k_fields* f, uint16_t d16, uint16_t dmin16, uint8_t
             qs[32 * c + l] = (uint8_t)((f->q[64 * c + l] & 15) | ((f->q[64 * c + 32 + l] & 15) << 4));
 }
 
+/* Q5_K: the Q4_K header and nibbles, then the fifth bit of every element. */
+static void q5k_unpack(const uint8_t* b, q4k_fields* f) {
+    uint8_t as_q4k[Q4K_BYTES];
+    memcpy(as_q4k, b, 16);
+    memcpy(as_q4k + 16, b + 48, 128);
+    q4k_unpack(as_q4k, f);
+    const uint8_t* qh = b + 16;
+    for (int e = 0; e < 256; ++e) f->q[e] |= ((qh[e % 32] >> (e / 32)) & 1) << 4;
+}
+
+static void q5k_pack(const q4k_fields* f, uint16_t d16, uint16_t dmin16, uint8_t* b) {
+    uint8_t as_q4k[Q4K_BYTES];
+    q4k_pack(f, d16, dmin16, as_q4k);  /* keeps the low four bits of each q */
+    memset(b, 0, Q5K_BYTES);
+    memcpy(b, as_q4k, 16);
+    memcpy(b + 48, as_q4k + 16, 128);
+    uint8_t* qh = b + 16;
+    for (int e = 0; e < 256; ++e) qh[e % 32] |= (uint8_t)(((f->q[e] >> 4) & 1) << (e / 32));
+}
+
 static void q6k_unpack(const uint8_t* b, q6k_fields* f) {
     const uint8_t* ql = b;
     const uint8_t* qh = b + 128;
@@ -200,6 +226,15 @@ void oracle_q4k_fields(const uint8_t* blk, float* d_dmin, int32_t* sc, int32_t* 
     for (int i = 0; i < 256; ++i) q[i] = f.q[i];
 }
 
+void oracle_q5k_fields(const uint8_t* blk, float* d_dmin, int32_t* sc, int32_t* m, int32_t* q) {
+    q4k_fields f;
+    q5k_unpack(blk, &f);
+    d_dmin[0] = f.d;
+    d_dmin[1] = f.dmin;
+    for (int j = 0; j < 8; ++j) { sc[j] = f.sc[j]; m[j] = f.m[j]; }
+    for (int i = 0; i < 256; ++i) q[i] = f.q[i];
+}
+
 void oracle_q6k_fields(const uint8_t* blk, float* d, int32_t* sc, int32_t* q) {
     q6k_fields f;
     q6k_unpack(blk, &f);
@@ -217,6 +252,14 @@ void oracle_q4k_build(uint16_t d16, uint16_t dmin16, const int32_t* sc, const in
     q4k_pack(&f, d16, dmin16, blk);
 }
 
+void oracle_q5k_build(uint16_t d16, uint16_t dmin16, const int32_t* sc, const int32_t* m,
+                      const int32_t* q, uint8_t* blk) {
+    q4k_fields f;
+    for (int j = 0; j < 8; ++j) { f.sc[j] = sc[j]; f.m[j] = m[j]; }
+    for (int i = 0; i < 256; ++i) f.q[i] = q[i];
+    q5k_pack(&f, d16, dmin16, blk);
+}
+
 void oracle_q6k_build(uint16_t d16, const int32_t* sc, const int32_t* q, uint8_t* blk) {
     q6k_fields f;
     for (int j = 0; j < 16; ++j) f.sc[j] = sc[j];
@@ -231,11 +274,12 @@ void oracle_q6k_build(uint16_t d16, const int32_t* sc, const int32_t* q, uint8_t
 /* binary16 before the sub-block scales are fitted against them.             */
 /* ------------------------------------------------------------------------ */
 
-/* Q4_K: per sub-block j of 32: lo=min(0,min w), hi=max w, s=(hi-lo)/15,
- * o=-lo; d=f16(max s/63), dmin=f16(max o/63); sc=clamp(rint(s/d),0,63),
- * m=clamp(rint(o/dmin),0,63); q=clamp(rint((w+dmin*m)/(d*sc)),0,15);
- * a zero divisor gives 0. */
-static void encode_q4k_block(const float* w, uint8_t* blk) {
+/* Q4_K (qmax 15) and Q5_K (qmax 31): per sub-block j of 32: lo=min(0,min w),
+ * hi=max w, s=(hi-lo)/qmax, o=-lo; d=f16(max s/63), dmin=f16(max o/63);
+ * sc=clamp(rint(s/d),0,63), m=clamp(rint(o/dmin),0,63);
+ * q=clamp(rint((w+dmin*m)/(d*sc)),0,qmax); a zero divisor gives 0. */
+static void fit_min_blocks(const float* w, int qmax, q4k_fields* f, uint16_t* d16_out,
+                           uint16_t* dmin16_out) {
     float s[8], o[8];
     for (int j = 0; j < 8; ++j) {
         float lo = 0.0f, hi = w[32 * j];
@@ -245,7 +289,7 @@ static void encode_q4k_block(const float* w, uint8_t* blk) {
             if (v > hi) hi = v;
         }
         float span = hi - lo;
-        s[j] = span / 15.0f;
+        s[j] = span / (float)qmax;
         o[j] = -lo;
     }
     float maxs = s[0], maxo = o[0];
@@ -256,22 +300,36 @@ static void encode_q4k_block(const float* w, uint8_t* blk) {
     uint16_t d16 = oracle_f32_to_f16(maxs / 63.0f);
     uint16_t dmin16 = oracle_f32_to_f16(maxo / 63.0f);
     float d = oracle_f16_to_f32(d16), dmin = oracle_f16_to_f32(dmin16);
-    q4k_fields f;
     for (int j = 0; j < 8; ++j) {
-        f.sc[j] = (d != 0.0f) ? clampi((int)rintf(s[j] / d), 0, 63) : 0;
-        f.m[j] = (dmin != 0.0f) ? clampi((int)rintf(o[j] / dmin), 0, 63) : 0;
-        float off = dmin * (float)f.m[j];
-        float div = d * (float)f.sc[j];
+        f->sc[j] = (d != 0.0f) ? clampi((int)rintf(s[j] / d), 0, 63) : 0;
+        f->m[j] = (dmin != 0.0f) ? clampi((int)rintf(o[j] / dmin), 0, 63) : 0;
+        float off = dmin * (float)f->m[j];
+        float div = d * (float)f->sc[j];
         for (int i = 0; i < 32; ++i) {
             int q = 0;
             if (div != 0.0f) {
                 float num = w[32 * j + i] + off;
-                q = clampi((int)rintf(num / div), 0, 15);
+                q = clampi((int)rintf(num / div), 0, qmax);
             }
-            f.q[32 * j + i] = q;
+            f->q[32 * j + i] = q;
         }
     }
+    *d16_out = d16;
+    *dmin16_out = dmin16;
+}
+
+static void encode_q4k_block(const float* w, uint8_t* blk) {
+    q4k_fields f;
+    uint16_t d16, dmin16;
+    fit_min_blocks(w, 15, &f, &d16, &dmin16);
     q4k_pack(&f, d16, dmin16, blk);
+}
+
+static void encode_q5k_block(const float* w, uint8_t* blk) {
+    q4k_fields f;
+    uint16_t d16, dmin16;
+    fit_min_blocks(w, 31, &f, &d16, &dmin16);
+    q5k_pack(&f, d16, dmin16, blk);
 }
 
 /* Q6_K: per sub-block j of 16: s=max|w|/31; d=f16(max s/127);
@@ -322,9 +380,15 @@ static void encode_q8_0_block(const float* w, uint8_t* blk) {
     }
 }
 
-/* type codes shared with the Python wrapper: 0 = Q4_K, 1 = Q6_K, 2 = Q8_0 */
+/* type codes shared with the Python wrapper: 0 = Q4_K, 1 = Q6_K, 2 = Q8_0,
+ * 5 = Q5_K */
 void oracle_quantize_weights(int type, const float* W, int64_t N, int64_t K, uint8_t* out) {
-    if (type == 0) {
+    if (type == 5) {
+        int64_t nb = K / QK_K;
+        for (int64_t n = 0; n < N; ++n)
+            for (int64_t b = 0; b < nb; ++b)
+                encode_q5k_block(W + n * K + b * QK_K, out + (n * nb + b) * Q5K_BYTES);
+    } else if (type == 0) {
         int64_t nb = K / QK_K;
         for (int64_t n = 0; n < N; ++n)
             for (int64_t b = 0; b < nb; ++b)
@@ -497,7 +561,17 @@ static float dot_q8_0_q8_1_block(const uint8_t* blk, const int8_t* a, float da, 
 static float dot_row(int type, const uint8_t* wrow, int64_t K, const int8_t* qs_row,
                      const void* d_row, const void* aux_row) {
     float y = 0.0f;
-    if (type == 0) {
+    if (type == 5) {
+        /* Q5_K: the Q4_K definition with q in 0..31 */
+        const float* da = (const float*)d_row;
+        const int16_t* bs = (const int16_t*)aux_row;
+        q4k_fields f;
+        for (int64_t b = 0; b < K / QK_K; ++b) {
+            q5k_unpack(wrow + b * Q5K_BYTES, &f);
+            float c = dot_q4k_q8k_block(&f, qs_row + b * QK_K, da[b], bs + b * 16, NULL);
+            y = y + c;
+        }
+    } else if (type == 0) {
         const float* da = (const float*)d_row;
         const int16_t* bs = (const int16_t*)aux_row;
         q4k_fields f;
@@ -526,6 +600,7 @@ static float dot_row(int type, const uint8_t* wrow, int64_t K, const int8_t* qs_
 }
 
 static int64_t row_bytes(int type, int64_t K) {
+    if (type == 5) return (K / QK_K) * Q5K_BYTES;
     if (type == 0) return (K / QK_K) * Q4K_BYTES;
     if (type == 1) return (K / QK_K) * Q6K_BYTES;
     return (K / QK8) * Q8_0_BYTES;
@@ -550,7 +625,7 @@ void oracle_gemm(int type, const uint8_t* W, int64_t N, int64_t K, const int8_t*
         int64_t m = idx / N, n = idx % N;
         const void* drow = (type == 2) ? (const void*)((const uint16_t*)d + m * nbd)
                                        : (const void*)((const float*)d + m * nbd);
-        const void* aux = (type == 0) ? (const void*)(bsums + m * (K / 16)) : NULL;
+        const void* aux = (type == 0 || type == 5) ? (const void*)(bsums + m * (K / 16)) : NULL;
         Y[m * ldy + n] = dot_row(type, W + n * rb, K, qs + m * K, drow, aux);
     }
 }
@@ -571,15 +646,20 @@ void oracle_gemm_sampled(int type, const uint8_t* W, int64_t N, int64_t K, const
         int64_t m = ms[i], n = ns[i];
         const void* drow = (type == 2) ? (const void*)((const uint16_t*)d + m * nbd)
                                        : (const void*)((const float*)d + m * nbd);
-        const void* aux = (type == 0) ? (const void*)(bsums + m * (K / 16)) : NULL;
+        const void* aux = (type == 0 || type == 5) ? (const void*)(bsums + m * (K / 16)) : NULL;
         out[i] = dot_row(type, W + n * rb, K, qs + m * K, drow, aux);
     }
 }
 
 /* The exact int32 sub-block sums I_j of one (weight block, activation block)
- * pair: 8 values for Q4_K, 16 for Q6_K, 1 for Q8_0. */
+ * pair: 8 values for Q4_K and Q5_K, 16 for Q6_K, 1 for Q8_0. */
 void oracle_subblock_sums(int type, const uint8_t* wblk, const int8_t* a, int32_t* I_out) {
-    if (type == 0) {
+    if (type == 5) {
+        q4k_fields f;
+        q5k_unpack(wblk, &f);
+        int16_t bs[16] = {0};
+        dot_q4k_q8k_block(&f, a, 1.0f, bs, I_out);
+    } else if (type == 0) {
         q4k_fields f;
         q4k_unpack(wblk, &f);
         int16_t bs[16] = {0};
@@ -633,7 +713,7 @@ void oracle_gemm_grouped(int type, const uint8_t* W, int64_t E, int64_t N, int64
         const uint8_t* wrow = W + (e * N + n) * rb;
         const void* drow = (type == 2) ? (const void*)((const uint16_t*)d + a * nbd)
                                        : (const void*)((const float*)d + a * nbd);
-        const void* aux = (type == 0) ? (const void*)(bsums + a * (K / 16)) : NULL;
+        const void* aux = (type == 0 || type == 5) ? (const void*)(bsums + a * (K / 16)) : NULL;
         Y[idx] = dot_row(type, wrow, K, qs + a * K, drow, aux);
     }
 }

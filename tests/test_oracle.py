@@ -56,6 +56,9 @@ def test_f16_encode_matches_numpy_rne():
     assert np.isnan(got[nan].view(np.float16)).all()
 
 
+WTYPES = [oracle.Q4_K, oracle.Q6_K, oracle.Q8_0, oracle.Q5_K]
+
+
 # ---------------------------------------------------------------- block layouts
 def test_q4k_layout_golden():
     g = _load("q4k_block.json")
@@ -84,6 +87,20 @@ def test_q6k_layout_golden():
         assert w[int(k)] == v, k
 
 
+def test_q5k_layout_golden():
+    g = _load("q5k_block.json")
+    q = np.arange(256) % 32
+    blk = oracle.q5k_build(g["d16"], g["dmin16"], g["sc"], g["m"], q)
+    for k, v in g["bytes_expected"].items():
+        assert int(blk[int(k)]) == v, k
+    d, dmin, sc, m, qq = oracle.q5k_fields(blk)
+    assert (sc == g["sc"]).all() and (m == g["m"]).all() and (qq == q).all()
+    assert d == 1.0 and dmin == 0.5
+    w = ref_fp64.dequant_weights(oracle.Q5_K, blk[None, :], 1, 256)[0]
+    for k, v in g["values_expected"].items():
+        assert w[int(k)] == v, k
+
+
 def test_layout_decoders_agree_on_random_bytes():
     """The C decoder and the independent numpy decoder read the same fields."""
     rng = np.random.default_rng(5)
@@ -97,10 +114,14 @@ def test_layout_decoders_agree_on_random_bytes():
         d, sc, q = oracle.q6k_fields(b6)
         d2, sc2, q2 = ref_fp64.q6k_decode_fields(b6)
         assert (sc == sc2).all() and (q == q2).all()
+        b5 = rng.integers(0, 256, 176, dtype=np.uint8)
+        d, dmin, sc, m, q = oracle.q5k_fields(b5)
+        d2, dmin2, sc2, m2, q2 = ref_fp64.q5k_decode_fields(b5)
+        assert (sc == sc2).all() and (m == m2).all() and (q == q2).all()
 
 
 # ---------------------------------------------------------------- weight encoders
-@pytest.mark.parametrize("wtype", [oracle.Q4_K, oracle.Q6_K, oracle.Q8_0])
+@pytest.mark.parametrize("wtype", WTYPES)
 def test_weight_encoder_roundtrip_bounds(wtype):
     W = synth.normal(7, (64, 1024), 0.02)
     Wq = oracle.quantize_weights(wtype, W)
@@ -110,6 +131,10 @@ def test_weight_encoder_roundtrip_bounds(wtype):
         d, dmin, sc, m, q = ref_fp64.q4k_decode_fields(Wq.reshape(64, 4, 144))
         sub = np.arange(256) // 32
         bound = (0.5 * d[..., None] * sc[..., sub] + 7.5 * d[..., None] + 0.5 * dmin[..., None])
+    elif wtype == oracle.Q5_K:
+        d, dmin, sc, m, q = ref_fp64.q5k_decode_fields(Wq.reshape(64, 4, 176))
+        sub = np.arange(256) // 32
+        bound = (0.5 * d[..., None] * sc[..., sub] + 15.5 * d[..., None] + 0.5 * dmin[..., None])
     elif wtype == oracle.Q6_K:
         d, sc, q = ref_fp64.q6k_decode_fields(Wq.reshape(64, 4, 210))
         sub = np.arange(256) // 16
@@ -120,6 +145,9 @@ def test_weight_encoder_roundtrip_bounds(wtype):
         amax = np.abs(W.reshape(64, 32, 32)).max(-1)
         bound = (0.5 * d + 127 * np.abs(amax / 127 - d))[..., None] * np.ones(32)
     assert (err.reshape(bound.shape) <= bound * (1 + 1e-6) + 1e-12).all()
+    if wtype in (oracle.Q4_K, oracle.Q5_K, oracle.Q6_K):
+        # the quants use the whole range of the format
+        assert q.max() == {oracle.Q4_K: 15, oracle.Q5_K: 31, oracle.Q6_K: 63}[wtype]
     # the fit is not degenerate: error well below the signal
     assert np.sqrt(np.mean(err ** 2)) < 0.2 * 0.02
 
@@ -214,7 +242,7 @@ def _case(wtype, M, N, K, seed):
     return Wq, act
 
 
-@pytest.mark.parametrize("wtype", [oracle.Q4_K, oracle.Q6_K, oracle.Q8_0])
+@pytest.mark.parametrize("wtype", WTYPES)
 def test_oracle_gemm_vs_fp64_definition(wtype):
     Wq, act = _case(wtype, 8, 96, 2048, 100 + wtype)
     y = oracle.gemm(wtype, Wq, 96, 2048, act)
@@ -224,7 +252,7 @@ def test_oracle_gemm_vs_fp64_definition(wtype):
     assert ref_fp64.nmse(y, r) <= 1e-11
 
 
-@pytest.mark.parametrize("wtype", [oracle.Q4_K, oracle.Q6_K, oracle.Q8_0])
+@pytest.mark.parametrize("wtype", WTYPES)
 def test_oracle_gemm_vs_exact_rationals(wtype):
     K = 512 if wtype != oracle.Q8_0 else 128
     Wq, act = _case(wtype, 2, 3, K, 200 + wtype)
@@ -239,7 +267,7 @@ def test_oracle_gemm_vs_exact_rationals(wtype):
             assert err <= 1e-6 * scale[m, n] + 1e-30, (m, n, err, scale[m, n])
 
 
-@pytest.mark.parametrize("wtype", [oracle.Q4_K, oracle.Q6_K, oracle.Q8_0])
+@pytest.mark.parametrize("wtype", WTYPES)
 def test_random_byte_blocks_vs_definitions(wtype):
     """Random-byte fuzz: random sc/m/q bytes, binary16 d in [2^-10, 1]."""
     rng = np.random.default_rng(300 + wtype)
@@ -249,7 +277,7 @@ def test_random_byte_blocks_vs_definitions(wtype):
     Wq = rng.integers(0, 256, (N, nb, bb), dtype=np.uint8)
     dvals = (2.0 ** rng.uniform(-10, 0, (N, nb, 2))).astype(np.float16).view(np.uint8)
     dvals = dvals.reshape(N, nb, 4)
-    if wtype == oracle.Q4_K:
+    if wtype in (oracle.Q4_K, oracle.Q5_K):
         Wq[..., 0:4] = dvals
     elif wtype == oracle.Q6_K:
         Wq[..., 208:210] = dvals[..., 0:2]
@@ -285,6 +313,15 @@ def test_unit_scale_probes_give_exact_subblock_sums():
         I_brute = int(sum(int(q[i]) * int(a[i]) for i in range(32 * j, 32 * j + 32)))
         assert y == I_brute
         assert oracle.subblock_sums(oracle.Q4_K, blk, act.qs[0])[j] == I_brute
+    q5 = rng.integers(0, 32, 256)
+    for j in range(8):
+        sc = np.zeros(8, np.int32)
+        sc[j] = 1
+        blk = oracle.q5k_build(0x3C00, 0, sc, np.zeros(8, np.int32), q5)
+        y = oracle.gemm(oracle.Q5_K, blk[None, :], 1, 256, act)[0, 0]
+        I_brute = int(sum(int(q5[i]) * int(a[i]) for i in range(32 * j, 32 * j + 32)))
+        assert y == I_brute
+        assert oracle.subblock_sums(oracle.Q5_K, blk, act.qs[0])[j] == I_brute
     q6 = rng.integers(0, 64, 256)
     for j in range(16):
         sc = np.zeros(16, np.int32)
@@ -341,7 +378,7 @@ def test_route_golden_and_library_sort():
     assert offsets[-1] == flat.size and (np.diff(offsets) == counts).all()
 
 
-@pytest.mark.parametrize("wtype", [oracle.Q4_K, oracle.Q6_K, oracle.Q8_0])
+@pytest.mark.parametrize("wtype", WTYPES)
 def test_grouped_matches_dense_per_expert(wtype):
     """Broadcast arm: each slot is its expert's dense product with the token row."""
     E, N, K, T, top_k = 6, 24, 512, 10, 3
@@ -363,7 +400,7 @@ def test_grouped_matches_dense_per_expert(wtype):
     assert ref_fp64.max_rel_err(Y, r64)[0] <= 5e-4
 
 
-@pytest.mark.parametrize("wtype", [oracle.Q4_K, oracle.Q6_K, oracle.Q8_0])
+@pytest.mark.parametrize("wtype", WTYPES)
 def test_grouped_per_row_arm(wtype):
     """Per-row arm: each pair has its own activation row.  With every pair's
     row equal to its token's row it reduces to the broadcast arm bitwise; with

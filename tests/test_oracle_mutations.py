@@ -55,6 +55,13 @@ MUTANTS = {
                                ["test_rmsnorm_pins"]),
     "silu sigmoid sign": ("g / (1.0 + exp(-g))", "g / (1.0 + exp(g))", ["test_silu_mul_pins"]),
     "silu drops up": ("* (double)U[m * ldx + i];", "* 1.0;", ["test_silu_mul_pins"]),
+    "q5k fifth bit index": ("f->q[e] |= ((qh[e % 32] >> (e / 32)) & 1) << 4;",
+                            "f->q[e] |= ((qh[e % 32] >> (e % 8)) & 1) << 4;",
+                            ["test_q5k_layout_golden", "test_layout_decoders_agree_on_random_bytes"]),
+    "q5k quant levels": ("fit_min_blocks(w, 31, &f, &d16, &dmin16);", "fit_min_blocks(w, 15, &f, &d16, &dmin16);",
+                         ["test_weight_encoder_roundtrip_bounds"]),
+    "q5k read as q4k": ("q5k_unpack(wrow + b * Q5K_BYTES, &f);", "q4k_unpack(wrow + b * Q5K_BYTES, &f);",
+                        ["test_oracle_gemm_vs_fp64_definition"]),
     "f16 ties up": ("if (rem > 0x1000u || (rem == 0x1000u && (h & 1u))) h += 1u;",
                     "if (rem >= 0x1000u) h += 1u;", ["test_f16_encode_matches_numpy_rne"]),
 }
@@ -65,7 +72,7 @@ def _call(name):
     import inspect
     params = inspect.signature(fn).parameters
     if "wtype" in params:
-        for w in (oracle.Q4_K, oracle.Q6_K, oracle.Q8_0):
+        for w in (oracle.Q4_K, oracle.Q6_K, oracle.Q8_0, oracle.Q5_K):
             fn(w)
     else:
         fn()
