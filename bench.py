@@ -244,6 +244,32 @@ def run_q8_0(torch, vq, synth, iters):
             "gemv_frac": round(gbytes / (tv * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def run_q5k(torch, vq, synth, iters):
+    """Q5_K [8192,2560]: the decode GEMV (fused quantizer, weights rotated past
+    the Infinity Cache) and the GEMM at M = 2048."""
+    dev = torch.device("cuda:0")
+    W = torch.from_numpy(synth.tensor("q5k_decode", "W")).to(dev)
+    N, K = W.shape
+    Q = vq.quantize_weights(vq.Q5_K, W)
+    del W
+    R = max(2, math.ceil(640 * (1 << 20) / Q.numel()))
+    Qs = [Q] + [Q.clone() for _ in range(R - 1)]
+    x = torch.from_numpy(synth.tensor("q5k_decode", "x")).to(dev)
+    y = torch.empty(N, dtype=torch.float32, device=dev)
+    tv, _ = time_graph(lambda i: vq.gemv(vq.Q5_K, Qs[i % R], N, K, x, y=y), R, max(200, 4 * R))
+    gbytes = Q.numel() + 4 * K + 4 * N
+    del Qs
+    X = torch.from_numpy(synth.prefill_activations("Xh", 2048)).to(dev)
+    Xq = vq.quantize_act(vq.Q8_K, X)
+    Y = torch.empty((2048, N), dtype=torch.float32, device=dev)
+    tg, _ = time_graph(lambda i: vq.gemm(vq.Q5_K, Q, N, K, vq.Q8_K, Xq, 2048, Y=Y), 4, iters)
+    ops = 2.0 * 2048 * N * K
+    return {"gemv_us": round(tv * 1e3, 2), "gemv_gbs": round(gbytes / (tv * 1e-3) / 1e9, 1),
+            "gemv_frac": round(gbytes / (tv * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "gemm_M2048_us": round(tg * 1e3, 2), "gemm_tops": round(ops / (tg * 1e-3) / 1e12, 1),
+            "gemm_frac": round(ops / (tg * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)}
+
+
 def run_small_batch(torch, vq, synth, iters):
     """vq_gemm at M = 2, 4, 8, 16 on the decode matrices (the GEMV-kernel arm),
     weights rotated past the Infinity Cache; rate = weight bytes + activation
@@ -452,6 +478,8 @@ def main():
         line["prefill"] = run_prefill(torch, vq, synth, args.secondary_iters)
         log("[bench] Q8_0 GEMM and GEMV")
         line["q8_0"] = run_q8_0(torch, vq, synth, args.secondary_iters)
+        log("[bench] Q5_K GEMV and GEMM")
+        line["q5k"] = run_q5k(torch, vq, synth, args.secondary_iters)
         log("[bench] small batches")
         line["small_batch"] = run_small_batch(torch, vq, synth, args.secondary_iters)
         log("[bench] producers with the quantizer epilogue")

@@ -14,7 +14,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libvq.so")
 
-Q4_K, Q6_K, Q8_0, Q8_K, Q8_1 = 0, 1, 2, 3, 4
+Q4_K, Q6_K, Q8_0, Q8_K, Q8_1, Q5_K = 0, 1, 2, 3, 4, 5
 TYPE_NAMES = {Q4_K: "Q4_K", Q6_K: "Q6_K", Q8_0: "Q8_0", Q8_K: "Q8_K", Q8_1: "Q8_1"}
 OP_GEMV, OP_GEMM, OP_GEMM_GROUPED = 0, 1, 2
 
@@ -32,7 +32,7 @@ EXPORTS = [
 STAT_FIELDS = ["quantize_q8k", "quantize_q8_1", "quantize_weights", "gemv_q4k", "gemv_q6k", "gemv_q8_0",
                "gemm_q4k", "gemm_q6k", "gemm_q8_0", "route", "gemm_grouped_q4k", "weighted_sum",
                "gemm_grouped_q6k", "gemm_grouped_q8_0", "gemm_grouped_rows", "gemm_skinny",
-               "rmsnorm_quant", "silu_mul_quant"]
+               "gemv_q5k", "gemm_q5k", "gemm_grouped_q5k", "rmsnorm_quant", "silu_mul_quant"]
 
 
 class VQStats(ctypes.Structure):

@@ -23,6 +23,8 @@
 //            runs on two 16x16x32 MFMAs with bs32 = 64*h + l.
 //      Q6_K: sc (int8) = 64*d2 + 8*d1 + d0 with digits in [-3,4]; planes
 //            (q-32)*d_i fit int8 -> S = 64*P2 + 8*P1 + P0.
+//      Q5_K: q up to 31, so sc = 16*d2 + 4*d1 + d0 with digits in [0,3];
+//            planes q*d_i <= 93 -> S = 16*P2 + 4*P1 + P0; mins as Q4_K.
 //      Q8_0: one 16x16x32 MFMA per 32-block, combined per block.
 //    The integer sums are exact, and the binary32 combine of each block and
 //    the ascending-block accumulation follow the fixed-order definition, so Y
@@ -91,6 +93,8 @@ template <>
 struct GemmCfg<1> { static constexpr int P = 3; static constexpr int BB = kQ6KBytes; };
 template <>
 struct GemmCfg<2> { static constexpr int P = 1; static constexpr int BB = kQ80Bytes; };
+template <>
+struct GemmCfg<3> { static constexpr int P = 3; static constexpr int BB = kQ5KBytes; };
 
 // Row indirection of the grouped (MUL_MAT_ID) variant.
 struct GroupArgs {
@@ -116,6 +120,8 @@ __global__ __launch_bounds__(128 * WM, 2) void gemm_kernel(const uint8_t* __rest
                                                            GroupArgs ga) {
     constexpr int P = GemmCfg<WT>::P;
     constexpr int BB = GemmCfg<WT>::BB;
+    constexpr bool kMin = (WT == 0 || WT == 3);  // Q4_K, Q5_K: scales and mins
+    constexpr int kShift = (WT == 3) ? 2 : 3;     // digit base of the scale planes (4 or 8)
     constexpr int NT = 128 * WM;           // threads
     constexpr int BM = 16 * TM * WM;       // activation rows per workgroup
     constexpr int ACH = BM * 16 / NT;      // 16-byte activation chunks per thread per step
@@ -127,8 +133,8 @@ __global__ __launch_bounds__(128 * WM, 2) void gemm_kernel(const uint8_t* __rest
     // while step s is current).
     __shared__ __attribute__((aligned(16))) float sDa2[2][(WT == 2) ? BM * 8 : BM];
     __shared__ __attribute__((aligned(16))) float sDw2[2][(WT == 2) ? kBN * 8 : 2 * kBN];
-    __shared__ __attribute__((aligned(16))) int8_t sMw2[2][(WT == 0) ? kBN * 8 : 16];
-    __shared__ __attribute__((aligned(16))) int8_t sHl2[2][(WT == 0) ? BM * 16 : 16];
+    __shared__ __attribute__((aligned(16))) int8_t sMw2[2][kMin ? kBN * 8 : 16];
+    __shared__ __attribute__((aligned(16))) int8_t sHl2[2][kMin ? BM * 16 : 16];
     __shared__ int sRow[BM];    // activation row of each tile row (-1: none)
     __shared__ int sOut[BM];    // output row of each tile row (-1: none)
 
@@ -197,7 +203,7 @@ __global__ __launch_bounds__(128 * WM, 2) void gemm_kernel(const uint8_t* __rest
     // Register-staged global data of one step.
     u4v regA[ACH];
     constexpr int SCW = (PPT + 1) / 2;     // Q6_K: words of per-piece scale byte pairs
-    uint32_t regW[(WT == 0) ? 4 + 4 * PPT : ((WT == 1) ? 8 * PPT + SCW + 1 : 9 * PPT)];
+    uint32_t regW[(WT == 0) ? 4 + 4 * PPT : ((WT == 3) ? 4 + 8 * PPT : ((WT == 1) ? 8 * PPT + SCW + 1 : 9 * PPT))];
     float regDa;
     uint4 regBs[2];
 
@@ -229,7 +235,7 @@ __global__ __launch_bounds__(128 * WM, 2) void gemm_kernel(const uint8_t* __rest
                                       h[6] | (h[7] << 16));
             } else {
                 regDa = ((const float*)ad)[(int64_t)ar * nbw + s];
-                if (WT == 0) {
+                if (kMin) {
                     const uint4* bp = (const uint4*)(abs_ + ((int64_t)ar * nbw + s) * 16);
                     regBs[0] = bp[0];
                     regBs[1] = bp[1];
@@ -237,14 +243,22 @@ __global__ __launch_bounds__(128 * WM, 2) void gemm_kernel(const uint8_t* __rest
             }
         }
         if (part == 0) return;
-        if (WT == 0) {
-            const uint8_t* bp = wrow_p + (int64_t)s * kQ4KBytes;
+        if (WT == 0 || WT == 3) {
+            // Q5_K: the nibbles at byte 48, and for piece pc the 16 fifth-bit
+            // bytes 16 + 16 (pc % 2) .. that cover its values
+            const uint8_t* bp = wrow_p + (int64_t)s * BB;
             const uint4 h = *(const uint4*)bp;
             regW[0] = h.x; regW[1] = h.y; regW[2] = h.z; regW[3] = h.w;
 #pragma unroll
             for (int j = 0; j < PPT; ++j) {
-                const uint4 q = *(const uint4*)(bp + 16 + 16 * (PPT * wu + j));
+                const int pc = PPT * wu + j;
+                const uint4 q = *(const uint4*)(bp + ((WT == 3) ? 48 : 16) + 16 * pc);
                 regW[4 + 4 * j] = q.x; regW[5 + 4 * j] = q.y; regW[6 + 4 * j] = q.z; regW[7 + 4 * j] = q.w;
+                if (WT == 3) {
+                    const uint4 hq = *(const uint4*)(bp + 16 + 16 * (pc & 1));
+                    regW[4 + 4 * PPT + 4 * j] = hq.x; regW[5 + 4 * PPT + 4 * j] = hq.y;
+                    regW[6 + 4 * PPT + 4 * j] = hq.z; regW[7 + 4 * PPT + 4 * j] = hq.w;
+                }
             }
         } else if (WT == 1) {
             const uint8_t* bp = wrow_p + (int64_t)s * kQ6KBytes;
@@ -295,7 +309,7 @@ __global__ __launch_bounds__(128 * WM, 2) void gemm_kernel(const uint8_t* __rest
                     sDa[tid * 8 + b] = half_bits_to_float((hw[b >> 1] >> (16 * (b & 1))) & 0xFFFF);
             } else {
                 sDa[tid] = regDa;
-                if (WT == 0) {
+                if (kMin) {
                     // bs32_j = bsums[2j] + bsums[2j+1] = 64 * h + l, 0 <= l < 64 (int8 operands)
                     const uint32_t bw[8] = {regBs[0].x, regBs[0].y, regBs[0].z, regBs[0].w,
                                             regBs[1].x, regBs[1].y, regBs[1].z, regBs[1].w};
@@ -311,27 +325,46 @@ __global__ __launch_bounds__(128 * WM, 2) void gemm_kernel(const uint8_t* __rest
             }
         }
         int8_t* wdst = sW + wr * kLD;
-        if (WT == 0) {
+        if (WT == 0 || WT == 3) {
             // piece pc = 16 qs bytes at 16 * pc: low nibbles are values
             // 64c + 16hf + i (sub-block 2c), high nibbles 64c + 32 + 16hf + i
-            // (sub-block 2c + 1), c = pc / 2, hf = pc % 2.  Plane 0 holds
-            // q * (sc & 7), plane 1 q * (sc >> 3).
+            // (sub-block 2c + 1), c = pc / 2, hf = pc % 2.  Q4_K: plane 0
+            // holds q * (sc & 7), plane 1 q * (sc >> 3).  Q5_K (q up to 31,
+            // bits 2c and 2c + 1 of the fifth-bit bytes 16hf + i): planes of
+            // the base-4 digits of sc, q * digit <= 93.
 #pragma unroll
             for (int j = 0; j < PPT; ++j) {
                 const int pc = PPT * wu + j, c = pc >> 1, hf = pc & 1;
                 const uint32_t sw = (c < 2) ? regW[1] : regW[2];
                 const int sh = 16 * (c & 1);
                 const int scl = (int)((sw >> sh) & 63), sch = (int)((sw >> (sh + 8)) & 63);
-                const int fl[2] = {scl & 7, scl >> 3};
-                const int fh[2] = {sch & 7, sch >> 3};
+                int fl[P], fh[P];
+                if (WT == 0) {
+                    fl[0] = scl & 7; fl[1] = scl >> 3;
+                    fh[0] = sch & 7; fh[1] = sch >> 3;
+                } else {
+                    fl[0] = scl & 3; fl[1] = (scl >> 2) & 3; fl[P - 1] = scl >> 4;
+                    fh[0] = sch & 3; fh[1] = (sch >> 2) & 3; fh[P - 1] = sch >> 4;
+                }
+                uint32_t ql[4], qh[4];
 #pragma unroll
-                for (int p = 0; p < 2; ++p) {
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t q = regW[4 + 4 * j + i];
+                    ql[i] = q & 0x0F0F0F0Fu;
+                    qh[i] = (q >> 4) & 0x0F0F0F0Fu;
+                    if (WT == 3) {
+                        const uint32_t hw = regW[4 + 4 * PPT + 4 * j + i];
+                        ql[i] |= ((hw >> (2 * c)) & 0x01010101u) << 4;
+                        qh[i] |= ((hw >> (2 * c + 1)) & 0x01010101u) << 4;
+                    }
+                }
+#pragma unroll
+                for (int p = 0; p < P; ++p) {
                     uint32_t lo[4], hi[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const uint32_t q = regW[4 + 4 * j + i];
-                        lo[i] = bytes_mul(q & 0x0F0F0F0Fu, fl[p]);
-                        hi[i] = bytes_mul((q >> 4) & 0x0F0F0F0Fu, fh[p]);
+                        lo[i] = bytes_mul(ql[i], fl[p]);
+                        hi[i] = bytes_mul(qh[i], fh[p]);
                     }
                     int8_t* dst = wdst + p * kBN * kLD + 64 * c + 16 * hf;
                     *(uint4*)dst = make_uint4(lo[0], lo[1], lo[2], lo[3]);
@@ -419,7 +452,7 @@ __global__ __launch_bounds__(128 * WM, 2) void gemm_kernel(const uint8_t* __rest
         const float* sDa = sDa2[ss & 1];
         const float* sDw = sDw2[ss & 1];
         v4i mn[2][TM];
-        if (WT == 0) {
+        if (kMin) {
             const int8_t* sMw = sMw2[ss & 1];
             const int8_t* sHl = sHl2[ss & 1];
             long am[2][2], bm[TM];
@@ -451,7 +484,7 @@ __global__ __launch_bounds__(128 * WM, 2) void gemm_kernel(const uint8_t* __rest
             const float4 dv = *(const float4*)(sDw + nb4);
             const float dd[4] = {dv.x, dv.y, dv.z, dv.w};
             float dm[4] = {0.f, 0.f, 0.f, 0.f};
-            if (WT == 0) {
+            if (kMin) {
                 const float4 dmv = *(const float4*)(sDw + kBN + nb4);
                 dm[0] = dmv.x; dm[1] = dmv.y; dm[2] = dmv.z; dm[3] = dmv.w;
             }
@@ -461,7 +494,7 @@ __global__ __launch_bounds__(128 * WM, 2) void gemm_kernel(const uint8_t* __rest
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const float t1 = dd[i] * (float)R[tn][tm][i];
-                    if (WT == 0) {
+                    if (kMin) {
                         const float t2 = dm[i] * (float)mn[tn][tm][i];
                         const float t3 = t1 - t2;
                         const float c = da * t3;
@@ -534,15 +567,15 @@ __global__ __launch_bounds__(128 * WM, 2) void gemm_kernel(const uint8_t* __rest
                 for (int tm = 0; tm < TM; ++tm)
                     bv[t][tm] = *(const v4i*)(sA + (wm0 + 16 * tm + r16) * kLD + 64 * t + 16 * g);
             // One accumulator per tile through the digit planes, high digit
-            // first: R = (((P2 << 3) + P1) << 3) + P0 (Q6_K) or (P1 << 3) + P0
-            // (Q4_K) = S, exact in int32.
+            // first: R = (((P2 << 3) + P1) << 3) + P0 (Q6_K), (P1 << 3) + P0
+            // (Q4_K) or (((P2 << 2) + P1) << 2) + P0 (Q5_K) = S, exact in int32.
 #pragma unroll
             for (int p = P - 1; p >= 0; --p) {
                 if (p < P - 1) {
 #pragma unroll
                     for (int tn = 0; tn < 2; ++tn)
 #pragma unroll
-                        for (int tm = 0; tm < TM; ++tm) R[tn][tm] = R[tn][tm] << 3;
+                        for (int tm = 0; tm < TM; ++tm) R[tn][tm] = R[tn][tm] << kShift;
                 }
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
@@ -624,6 +657,7 @@ hipError_t launch_gemm(int wtype, const uint8_t* W, int64_t N, int64_t K, const 
     if (M == 0 || N == 0) return hipSuccess;
     if (wtype == 0) return launch_gemm_t<0>(W, N, K, act_qs, act_d, act_aux, M, Y, ldy, st);
     if (wtype == 1) return launch_gemm_t<1>(W, N, K, act_qs, act_d, act_aux, M, Y, ldy, st);
+    if (wtype == 5) return launch_gemm_t<3>(W, N, K, act_qs, act_d, act_aux, M, Y, ldy, st);
     return launch_gemm_t<2>(W, N, K, act_qs, act_d, act_aux, M, Y, ldy, st);
 }
 
@@ -660,6 +694,8 @@ hipError_t launch_gemm_grouped(int wtype, const uint8_t* W, int64_t E, int64_t N
         return launch_gemm_grouped_t<0>(W, E, N, K, act_qs, act_d, act_aux, T, top_k, per_row, ws, Y, st);
     if (wtype == 1)
         return launch_gemm_grouped_t<1>(W, E, N, K, act_qs, act_d, act_aux, T, top_k, per_row, ws, Y, st);
+    if (wtype == 5)
+        return launch_gemm_grouped_t<3>(W, E, N, K, act_qs, act_d, act_aux, T, top_k, per_row, ws, Y, st);
     return launch_gemm_grouped_t<2>(W, E, N, K, act_qs, act_d, act_aux, T, top_k, per_row, ws, Y, st);
 }
 

@@ -60,6 +60,8 @@ template <>
 struct WFmt<1> { static constexpr int kBlk = kQ6KBytes; static constexpr int kVals = kQK; };
 template <>
 struct WFmt<2> { static constexpr int kBlk = kQ80Bytes; static constexpr int kVals = kQK8; };
+template <>
+struct WFmt<3> { static constexpr int kBlk = kQ5KBytes; static constexpr int kVals = kQK; };
 
 struct GemvLayout {
     int act_qs, act_row, act_d, act_bs, partial, wslice, slice_bytes, total;
@@ -305,19 +307,39 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
     const int nbp = (nb + 3) & ~3;  // partial row stride: 16-byte aligned rows
     auto compute_task = [&](int r, int blk) {
         const uint8_t* bp = wsl + rbase + __mul24(r, rb) + __mul24(blk, BB);
-        if (WT == 0) {
-            // lane half hf: sub-blocks 4hf..4hf+3 = qs bytes [64hf, 64hf+64)
+        if (WT == 0 || WT == 3) {
+            // lane half hf: sub-blocks 4hf..4hf+3 = qs bytes [64hf, 64hf+64);
+            // Q5_K: the nibbles start at byte 48 and bit j of byte 16 + l
+            // adds bit 4 to element 32j + l.
+            constexpr int kQsOff = (WT == 3) ? 48 : 16;
             const int hf = sub;
             const uint4 hdr = *(const uint4*)bp;
             uint32_t lo[16], hi[16];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const uint4 v = *(const uint4*)(bp + 16 + 64 * hf + 16 * i);
+                const uint4 v = *(const uint4*)(bp + kQsOff + 64 * hf + 16 * i);
                 const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     lo[4 * i + k] = w4[k] & 0x0F0F0F0Fu;
                     hi[4 * i + k] = (w4[k] >> 4) & 0x0F0F0F0Fu;
+                }
+            }
+            if (WT == 3) {
+                // qs piece i holds bytes l = 16 (i & 1) + 4k + byte of chunk
+                // c = 2hf + (i >> 1): low nibbles are sub-block 2c, high 2c + 1
+                const uint4 h0 = *(const uint4*)(bp + 16);
+                const uint4 h1 = *(const uint4*)(bp + 32);
+                const uint32_t qh[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int c = 2 * hf + (i >> 1);
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const uint32_t hw = qh[4 * (i & 1) + k];
+                        lo[4 * i + k] |= ((hw >> (2 * c)) & 0x01010101u) << 4;
+                        hi[4 * i + k] |= ((hw >> (2 * c + 1)) & 0x01010101u) << 4;
+                    }
                 }
             }
             const uint32_t sw = hf ? hdr.z : hdr.y;             // scales bytes 4hf..4hf+3
@@ -584,7 +606,11 @@ static int num_cus() {
     return g_num_cus;
 }
 
-static int block_bytes_of(int wt) { return wt == 0 ? kQ4KBytes : (wt == 1 ? kQ6KBytes : kQ80Bytes); }
+static int block_bytes_of(int wt) {
+    return wt == 0 ? kQ4KBytes : (wt == 1 ? kQ6KBytes : (wt == 3 ? kQ5KBytes : kQ80Bytes));
+}
+// Kernel template index of a library weight type (Q5_K = 5 is index 3).
+static int wt_of(int wtype) { return wtype == 5 ? 3 : wtype; }
 static int block_vals_of(int wt) { return wt == 2 ? kQK8 : kQK; }
 
 struct GemvPlan {
@@ -650,7 +676,7 @@ static GemvPlan gemv_plan(int wt, int64_t N, int64_t K, int mb) {
 }
 
 size_t gemv_lds_bytes(int wtype, int64_t N, int64_t K, int mb) {
-    const GemvPlan p = gemv_plan(wtype, N, K, mb);
+    const GemvPlan p = gemv_plan(wt_of(wtype), N, K, mb);
     return p.ok ? (size_t)p.lds : (size_t)-1;
 }
 
@@ -695,6 +721,7 @@ hipError_t launch_gemv(int wtype, const uint8_t* W, int64_t N, int64_t K, const 
     if (N == 0) return hipSuccess;
     if (wtype == 0) return launch_gemv_t<0, 1>(W, N, K, x, y, N, xq_out, nullptr, 1, 0, 0, st);
     if (wtype == 1) return launch_gemv_t<1, 1>(W, N, K, x, y, N, xq_out, nullptr, 1, 0, 0, st);
+    if (wtype == 5) return launch_gemv_t<3, 1>(W, N, K, x, y, N, xq_out, nullptr, 1, 0, 0, st);
     return launch_gemv_t<2, 1>(W, N, K, x, y, N, xq_out, nullptr, 1, 0, 0, st);
 }
 
@@ -711,13 +738,14 @@ static hipError_t launch_skinny_t(const uint8_t* W, int64_t N, int64_t K, const 
 
 bool gemm_skinny_ok(int wtype, int64_t N, int64_t K, int64_t M, int64_t max_m) {
     return M >= 1 && M <= max_m && M <= kSkinnyMaxM && N > 0 &&
-           gemv_lds_bytes(wtype, N, K, mb_for(wtype, N, K, M)) <= kMaxLds;
+           gemv_lds_bytes(wtype, N, K, mb_for(wt_of(wtype), N, K, M)) <= kMaxLds;
 }
 
 hipError_t launch_gemm_skinny(int wtype, const uint8_t* W, int64_t N, int64_t K, const uint8_t* xq, int64_t M,
                               int64_t d_off, int64_t aux_off, float* Y, int64_t ldy, hipStream_t st) {
     if (wtype == 0) return launch_skinny_t<0>(W, N, K, xq, M, d_off, aux_off, Y, ldy, st);
     if (wtype == 1) return launch_skinny_t<1>(W, N, K, xq, M, d_off, aux_off, Y, ldy, st);
+    if (wtype == 5) return launch_skinny_t<3>(W, N, K, xq, M, d_off, aux_off, Y, ldy, st);
     return launch_skinny_t<2>(W, N, K, xq, M, d_off, aux_off, Y, ldy, st);
 }
 

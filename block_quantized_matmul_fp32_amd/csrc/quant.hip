@@ -1,5 +1,5 @@
 // quant.hip -- activation quantizers (Q8_K, Q8_1) and weight encoders
-// (Q4_K, Q6_K, Q8_0) for gfx950.
+// (Q4_K, Q5_K, Q6_K, Q8_0) for gfx950.
 //
 // Activation quantizers: HBM-bound elementwise passes (read 4 B, write about
 // 1.14 B per value); one wave per Q8_K super-block, eight lanes per Q8_1
@@ -121,9 +121,14 @@ __device__ __forceinline__ int clamp_rint(float x, int lo, int hi) {
     return q < lo ? lo : (q > hi ? hi : q);
 }
 
-// Q4_K: one wave per super-block; lane l holds values 4l..4l+3 (sub-block l/8).
+// Q4_K (QMAX 15) and Q5_K (QMAX 31): one wave per super-block; lane l holds
+// values 4l..4l+3 (sub-block l/8).  Q5_K is the Q4_K block with the nibbles
+// moved 32 bytes up and a plane of fifth bits in between.
+template <int QMAX>
 __global__ __launch_bounds__(256) void encode_q4k_kernel(const float* __restrict__ W, int64_t N,
                                                          int64_t K, uint8_t* __restrict__ out) {
+    constexpr int kBytes = (QMAX == 15) ? kQ4KBytes : kQ5KBytes;
+    constexpr int kQsOff = (QMAX == 15) ? 16 : 48;
     const int lane = threadIdx.x & 63;
     const int64_t nb = K / kQK;
     const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -139,7 +144,7 @@ __global__ __launch_bounds__(256) void encode_q4k_kernel(const float* __restrict
     for (int i = 1; i < 4; ++i) hi = (w[i] > hi) ? w[i] : hi;
     hi = ordered_max(hi, lane, 1, 8);
     const float span = hi - lo;
-    const float s = span / 15.0f;
+    const float s = span / (float)QMAX;
     const float o_ = -lo;
     const float maxs = ordered_max(s, lane, 8, 64);
     const float maxo = ordered_max(o_, lane, 8, 64);
@@ -155,17 +160,27 @@ __global__ __launch_bounds__(256) void encode_q4k_kernel(const float* __restrict
         int q = 0;
         if (div != 0.0f) {
             float num = w[i] + off;
-            q = clamp_rint(num / div, 0, 15);
+            q = clamp_rint(num / div, 0, QMAX);
         }
         q4 |= (uint32_t)q << (8 * i);
     }
-    uint8_t* blkp = out + (n * nb + b) * kQ4KBytes;
+    uint8_t* blkp = out + (n * nb + b) * kBytes;
     // nibbles: byte 32c + l holds element 64c+l (low) and 64c+32+l (high);
     // element 64c+32+l lives 8 lanes above element 64c+l.
     const uint32_t hi4 = (uint32_t)shfl_xor_i((int)q4, 8);
     if (((lane >> 3) & 1) == 0) {
         const int c = lane >> 4, u = lane & 7;
-        *(uint32_t*)(blkp + 16 + 32 * c + 4 * u) = q4 | (hi4 << 4);
+        *(uint32_t*)(blkp + kQsOff + 32 * c + 4 * u) = (q4 & 0x0F0F0F0Fu) | ((hi4 & 0x0F0F0F0Fu) << 4);
+    }
+    if (QMAX == 31) {
+        // fifth bits: bit j of byte 16 + l is bit 4 of element 32j + l; lane
+        // 8j + u holds elements 32j + 4u .. 32j + 4u + 3, i.e. bit j of bytes
+        // 16 + 4u .. 16 + 4u + 3; the eight lanes u, u + 8, ... are OR-ed.
+        uint32_t hb = ((q4 >> 4) & 0x01010101u) << (lane >> 3);
+        hb |= (uint32_t)shfl_xor_i((int)hb, 8);
+        hb |= (uint32_t)shfl_xor_i((int)hb, 16);
+        hb |= (uint32_t)shfl_xor_i((int)hb, 32);
+        if (lane < 8) *(uint32_t*)(blkp + 16 + 4 * lane) = hb;
     }
     // header: d, dmin, 12 bytes of 6-bit scales and mins
     int scj[8], mj[8];
@@ -293,12 +308,14 @@ __global__ __launch_bounds__(256) void encode_q8_0_kernel(const float* __restric
 
 hipError_t launch_quantize_weights(int wtype, const float* W, int64_t N, int64_t K, uint8_t* out,
                                    hipStream_t st) {
-    if (wtype == 0 || wtype == 1) {
+    if (wtype == 0 || wtype == 1 || wtype == 5) {
         const int64_t blocks = N * (K / kQK);
         if (blocks == 0) return hipSuccess;
         dim3 grid((unsigned)((blocks + 3) / 4));
         if (wtype == 0)
-            encode_q4k_kernel<<<grid, 256, 0, st>>>(W, N, K, out);
+            encode_q4k_kernel<15><<<grid, 256, 0, st>>>(W, N, K, out);
+        else if (wtype == 5)
+            encode_q4k_kernel<31><<<grid, 256, 0, st>>>(W, N, K, out);
         else
             encode_q6k_kernel<<<grid, 256, 0, st>>>(W, N, K, out);
     } else {

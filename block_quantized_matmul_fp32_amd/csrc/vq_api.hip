@@ -28,13 +28,15 @@ struct Counters {
     std::atomic<uint64_t> route{0}, gemm_grouped_q4k{0}, weighted_sum{0};
     std::atomic<uint64_t> gemm_grouped_q6k{0}, gemm_grouped_q8_0{0}, gemm_grouped_rows{0};
     std::atomic<uint64_t> gemm_skinny{0}, rmsnorm_quant{0}, silu_mul_quant{0};
+    std::atomic<uint64_t> gemv_q5k{0}, gemm_q5k{0}, gemm_grouped_q5k{0};
 };
 Counters g_stats;
 
 // Largest M that vq_gemm runs on the GEMV kernel, per weight type (Q4_K,
 // Q6_K, Q8_0): the GEMV <-> GEMM crossover.
-constexpr int64_t kSmallMaxDefault[3] = {16, 64, 32};
-std::atomic<int64_t> g_small_max[3] = {{kSmallMaxDefault[0]}, {kSmallMaxDefault[1]}, {kSmallMaxDefault[2]}};
+constexpr int64_t kSmallMaxDefault[4] = {16, 64, 32, 16};
+std::atomic<int64_t> g_small_max[4] = {{kSmallMaxDefault[0]}, {kSmallMaxDefault[1]}, {kSmallMaxDefault[2]},
+                                       {kSmallMaxDefault[3]}};
 
 vq_status fail(vq_status s, const char* fmt, ...) {
     char buf[512];
@@ -51,7 +53,9 @@ vq_status hip_status(hipError_t e, const char* what) {
     return fail(VQ_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
 }
 
-bool is_weight(int t) { return t == VQ_Q4_K || t == VQ_Q6_K || t == VQ_Q8_0; }
+bool is_weight(int t) { return t == VQ_Q4_K || t == VQ_Q6_K || t == VQ_Q8_0 || t == VQ_Q5_K; }
+// index of a weight type in the per-type tables (Q4_K, Q6_K, Q8_0, Q5_K)
+int widx(int w) { return w == VQ_Q4_K ? 0 : (w == VQ_Q6_K ? 1 : (w == VQ_Q8_0 ? 2 : 3)); }
 bool is_act(int t) { return t == VQ_Q8_K || t == VQ_Q8_1; }
 
 int64_t qk_of(int t) { return (t == VQ_Q8_0 || t == VQ_Q8_1) ? 32 : 256; }
@@ -69,7 +73,7 @@ constexpr int64_t kMaxK = (int64_t)1 << 20;
 
 vq_status check_weight(int w, const char* fn) {
     if (!is_weight(w))
-        return fail(VQ_ERR_UNSUPPORTED_TYPE, "%s: weight type %s (%d) is not a weight type (Q4_K, Q6_K, Q8_0)",
+        return fail(VQ_ERR_UNSUPPORTED_TYPE, "%s: weight type %s (%d) is not a weight type (Q4_K, Q5_K, Q6_K, Q8_0)",
                     fn, vq_type_name(w), w);
     return VQ_OK;
 }
@@ -151,6 +155,7 @@ const char* vq_type_name(int t) {
         case VQ_Q8_0: return "Q8_0";
         case VQ_Q8_K: return "Q8_K";
         case VQ_Q8_1: return "Q8_1";
+        case VQ_Q5_K: return "Q5_K";
     }
     return "unknown";
 }
@@ -165,7 +170,7 @@ int vq_is_supported(int w, int act, int op) {
 }
 
 int vq_block_values(int t) {
-    if (t == VQ_Q4_K || t == VQ_Q6_K || t == VQ_Q8_K) return 256;
+    if (t == VQ_Q4_K || t == VQ_Q5_K || t == VQ_Q6_K || t == VQ_Q8_K) return 256;
     if (t == VQ_Q8_0 || t == VQ_Q8_1) return 32;
     return 0;
 }
@@ -173,6 +178,7 @@ int vq_block_values(int t) {
 size_t vq_block_bytes(int t) {
     switch (t) {
         case VQ_Q4_K: return 144;
+        case VQ_Q5_K: return 176;
         case VQ_Q6_K: return 210;
         case VQ_Q8_0: return 34;
         case VQ_Q8_K: return 256 + 4 + 32;
@@ -314,6 +320,7 @@ vq_status vq_gemv(int w, const void* W, int64_t N, int64_t K, const float* x, fl
         return fail(VQ_ERR_ALIAS, "%s: xq_out overlaps another buffer", fn);
     if (w == VQ_Q4_K) g_stats.gemv_q4k++;
     else if (w == VQ_Q6_K) g_stats.gemv_q6k++;
+    else if (w == VQ_Q5_K) g_stats.gemv_q5k++;
     else g_stats.gemv_q8_0++;
     return hip_status(vqk::launch_gemv(w, (const uint8_t*)W, N, K, x, y, (uint8_t*)xq_out, stream), fn);
 }
@@ -340,8 +347,9 @@ vq_status vq_gemm(int w, const void* W, int64_t N, int64_t K, int act, const voi
     const void* aux = base + vq_act_aux_offset(act, M, K);
     if (w == VQ_Q4_K) g_stats.gemm_q4k++;
     else if (w == VQ_Q6_K) g_stats.gemm_q6k++;
+    else if (w == VQ_Q5_K) g_stats.gemm_q5k++;
     else g_stats.gemm_q8_0++;
-    if (vqk::gemm_skinny_ok(w, N, K, M, g_small_max[w == VQ_Q4_K ? 0 : (w == VQ_Q6_K ? 1 : 2)].load())) {
+    if (vqk::gemm_skinny_ok(w, N, K, M, g_small_max[widx(w)].load())) {
         // small batch: the weights streamed once through the GEMV kernel for all M rows
         g_stats.gemm_skinny++;
         return hip_status(vqk::launch_gemm_skinny(w, (const uint8_t*)W, N, K, base, M,
@@ -358,14 +366,14 @@ vq_status vq_set_small_batch_max(int w, int64_t max_m) {
     if (max_m < -1 || max_m > vqk::kSkinnyMaxM)
         return fail(VQ_ERR_INVALID_ARG, "%s: max_m = %lld outside [-1, %d]", fn, (long long)max_m,
                     vqk::kSkinnyMaxM);
-    const int i = w == VQ_Q4_K ? 0 : (w == VQ_Q6_K ? 1 : 2);
+    const int i = widx(w);
     g_small_max[i] = (max_m < 0) ? kSmallMaxDefault[i] : max_m;
     return VQ_OK;
 }
 
 int64_t vq_small_batch_max(int w) {
     if (!is_weight(w)) return -1;
-    return g_small_max[w == VQ_Q4_K ? 0 : (w == VQ_Q6_K ? 1 : 2)].load();
+    return g_small_max[widx(w)].load();
 }
 
 size_t vq_grouped_workspace_bytes(int64_t E, int64_t T, int64_t top_k) {
@@ -417,6 +425,7 @@ static vq_status gemm_grouped_impl(const char* fn, int per_row, int w, const voi
     if (s != VQ_OK) return s;
     if (w == VQ_Q4_K) g_stats.gemm_grouped_q4k++;
     else if (w == VQ_Q6_K) g_stats.gemm_grouped_q6k++;
+    else if (w == VQ_Q5_K) g_stats.gemm_grouped_q5k++;
     else g_stats.gemm_grouped_q8_0++;
     if (per_row) g_stats.gemm_grouped_rows++;
     hipError_t e;
@@ -485,6 +494,9 @@ void vq_get_stats(vq_stats* out) {
     out->gemm_grouped_q8_0 = g_stats.gemm_grouped_q8_0.load();
     out->gemm_grouped_rows = g_stats.gemm_grouped_rows.load();
     out->gemm_skinny = g_stats.gemm_skinny.load();
+    out->gemv_q5k = g_stats.gemv_q5k.load();
+    out->gemm_q5k = g_stats.gemm_q5k.load();
+    out->gemm_grouped_q5k = g_stats.gemm_grouped_q5k.load();
     out->rmsnorm_quant = g_stats.rmsnorm_quant.load();
     out->silu_mul_quant = g_stats.silu_mul_quant.load();
 }
@@ -506,6 +518,9 @@ void vq_reset_stats(void) {
     g_stats.gemm_grouped_q8_0 = 0;
     g_stats.gemm_grouped_rows = 0;
     g_stats.gemm_skinny = 0;
+    g_stats.gemv_q5k = 0;
+    g_stats.gemm_q5k = 0;
+    g_stats.gemm_grouped_q5k = 0;
     g_stats.rmsnorm_quant = 0;
     g_stats.silu_mul_quant = 0;
 }

@@ -20,6 +20,7 @@ constexpr int kQK = 256;    // super-block of Q4_K, Q6_K, Q8_K
 constexpr int kQK8 = 32;    // block of Q8_0, Q8_1
 constexpr int kQ4KBytes = 144;
 constexpr int kQ6KBytes = 210;
+constexpr int kQ5KBytes = 176;
 constexpr int kQ80Bytes = 34;
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }

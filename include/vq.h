@@ -2,7 +2,7 @@
  * vq.h -- C ABI of the block-quantized matmul library for AMD Instinct MI355X
  * (gfx950).
  *
- * Y = X * W^T with block-quantized weights (Q4_K, Q6_K, Q8_0) and activations
+ * Y = X * W^T with block-quantized weights (Q4_K, Q5_K, Q6_K, Q8_0) and activations
  * quantized on the device to Q8_K (paired with the K-quants) or Q8_1 (paired
  * with Q8_0): decode GEMV, prefill GEMM and the routed-expert grouped GEMM
  * with the weighted expert sum.
@@ -68,6 +68,10 @@ extern "C" {
 /*   value_e = d*sc_(e/16)*(q_e - 32), q_e in 0..63                         */
 /* VQ_Q8_0  weights, 34 bytes per 32 values: [0,2) d (binary16), [2,34)     */
 /*   int8 q; value_i = d*q_i                                                */
+/* VQ_Q5_K  weights, 176 bytes per 256 values (the pages name Q5_K without  */
+/*   a layout): [0,16) d, dmin and scales exactly as Q4_K; [16,48) qh, bit */
+/*   j of byte 16+l = bit 4 of element 32j+l; [48,176) the Q4_K nibbles;    */
+/*   q_i = nibble_i | qhbit_i << 4 in 0..31; value_i = d*sc*q_i - dmin*m    */
 /* Weight matrices [N][K] are stored row-major: row n is K/QK consecutive   */
 /* blocks with no padding.  Grouped weights are [E][N][K/QK] blocks.        */
 /*                                                                         */
@@ -87,7 +91,8 @@ typedef enum {
     VQ_Q6_K = 1,
     VQ_Q8_0 = 2,
     VQ_Q8_K = 3,
-    VQ_Q8_1 = 4
+    VQ_Q8_1 = 4,
+    VQ_Q5_K = 5
 } vq_type;
 
 typedef enum {
@@ -222,7 +227,7 @@ vq_status vq_gemm(int w, const void* W, int64_t N, int64_t K, int act, const voi
 /* The GEMV <-> GEMM crossover of vq_gemm (vllm.cpp PR #2890, "lever-B1":  */
 /* the fold crossover made tunable at run time): vq_gemm with weight type w */
 /* runs M <= max_m on the GEMV kernel.  max_m in [0, 64] (0: never), -1     */
-/* restores the default (Q4_K 16, Q6_K 64, Q8_0 32, from measurements on    */
+/* restores the default (Q4_K 16, Q5_K 16, Q6_K 64, Q8_0 32, measured on   */
 /* the decode shapes).  Process-wide; not synchronised with calls in flight.*/
 /* vq_small_batch_max returns the current value (-1 for a non-weight type). */
 /* ---------------------------------------------------------------------- */
@@ -237,7 +242,7 @@ int64_t vq_small_batch_max(int w);
 /*   Y[t][s][:] = W_(ids[t][s]) . x_t  for t < T, s < top_k                 */
 /*   Ysum[t][n] = (((w0*y0 + w1*y1) + w2*y2) + ...), slots ascending, each  */
 /*                product and sum rounded on its own (skipped if Ysum NULL) */
-/* w: Q4_K, Q6_K (act Q8_K) or Q8_0 (act Q8_1).  W: [E][N][K/QK] blocks;     */
+/* w: Q4_K, Q5_K, Q6_K (act Q8_K) or Q8_0 (act Q8_1).  W: [E][N][K/QK] blocks; */
 /* Xq: planar activation buffer of T rows; ids int32 [T][top_k], each in    */
 /* [0,E) and distinct within a token (a precondition, not checked on the    */
 /* device; a pair whose id is outside [0,E) is not computed); route_w fp32  */
@@ -293,6 +298,7 @@ typedef struct {
     uint64_t gemm_grouped_q8_0;
     uint64_t gemm_grouped_rows;  /* calls of the per-row arm (also counted per type) */
     uint64_t gemm_skinny;        /* vq_gemm calls with M <= 8 run on the GEMV kernel (also counted per type) */
+    uint64_t gemv_q5k, gemm_q5k, gemm_grouped_q5k;  /* Q5_K calls of vq_gemv, vq_gemm, grouped calls */
     uint64_t rmsnorm_quant;      /* vq_rmsnorm_quant calls */
     uint64_t silu_mul_quant;     /* vq_silu_mul_quant calls */
 } vq_stats;

@@ -41,6 +41,10 @@ WORKLOADS = {
         "W_seed": 51, "W_sigma": 0.02, "X": ((2048, 2048), 52, 1.0),
         "ids_seed": 53, "logits_seed": 54,
     },
+    "q5k_decode": {
+        "desc": "Q5_K [8192,2560] decode GEMV (the GDN qkv projection shape the pages keep in Q5_K)",
+        "W": ((8192, 2560), 81, 0.02), "x": ((2560,), 82, 1.0), "X": ((16, 2560), 83, 1.0),
+    },
     "grouped_moe_down": {
         "desc": "per-row arm: 256 experts Q4_K [2048,512], one Q8_K row per (token, slot): "
                 "[2048*8, 512], the grouped_moe routing",

@@ -27,8 +27,8 @@ import block_quantized_matmul_fp32_amd as vq  # noqa: E402
 NMSE_MAX = 1e-6
 REL_MAX = 5e-4
 
-WTYPES = [oracle.Q4_K, oracle.Q6_K, oracle.Q8_0]
-WNAME = {oracle.Q4_K: "Q4_K", oracle.Q6_K: "Q6_K", oracle.Q8_0: "Q8_0"}
+WTYPES = [oracle.Q4_K, oracle.Q6_K, oracle.Q8_0, oracle.Q5_K]
+WNAME = {oracle.Q4_K: "Q4_K", oracle.Q6_K: "Q6_K", oracle.Q8_0: "Q8_0", oracle.Q5_K: "Q5_K"}
 
 
 def oracle_act(wtype, X):
@@ -105,7 +105,8 @@ def test_quantize_weights_bitexact(wtype):
 
 
 # ------------------------------------------------------------------ GEMV
-GEMV_SHAPES = {oracle.Q4_K: (300, 2560), oracle.Q6_K: (131, 1536), oracle.Q8_0: (300, 2080)}
+GEMV_SHAPES = {oracle.Q4_K: (300, 2560), oracle.Q6_K: (131, 1536), oracle.Q8_0: (300, 2080),
+               oracle.Q5_K: (301, 4096)}
 
 
 @pytest.mark.parametrize("wtype", WTYPES)
@@ -146,7 +147,8 @@ def test_gemv_edge_rows(wtype):
 
 
 # ------------------------------------------------------------------ GEMM
-GEMM_SHAPES = {oracle.Q4_K: (150, 200, 1024), oracle.Q6_K: (150, 200, 1024), oracle.Q8_0: (150, 200, 2080)}
+GEMM_SHAPES = {oracle.Q4_K: (150, 200, 1024), oracle.Q6_K: (150, 200, 1024), oracle.Q8_0: (150, 200, 2080),
+               oracle.Q5_K: (150, 200, 1024)}
 
 
 @pytest.mark.parametrize("wtype", WTYPES)
@@ -170,7 +172,7 @@ def test_gemm_bitexact(wtype):
     assert ref_fp64.max_rel_err(Yh[:, :N], r)[0] <= REL_MAX
 
 
-@pytest.mark.parametrize("wtype", [oracle.Q4_K, oracle.Q6_K])
+@pytest.mark.parametrize("wtype", [oracle.Q4_K, oracle.Q6_K, oracle.Q5_K])
 def test_gemm_large_tile_ragged(wtype):
     """Enough column tiles that the 64 x 256 tile configuration runs, with a
     ragged last row tile (M = 300) and column tile (N % 64 = 16); every
@@ -207,7 +209,8 @@ def test_gemm_from_device_quantizer(wtype):
         H.assert_bitwise(H.host(Y), oracle.gemm(wtype, Wq, N, K, oracle_act(wtype, X)), "M=%d" % M)
 
 
-SKINNY_SHAPES = {oracle.Q4_K: (300, 2560), oracle.Q6_K: (131, 1536), oracle.Q8_0: (300, 2080)}
+SKINNY_SHAPES = {oracle.Q4_K: (300, 2560), oracle.Q6_K: (131, 1536), oracle.Q8_0: (300, 2080),
+                 oracle.Q5_K: (133, 2816)}
 
 
 @pytest.mark.parametrize("wtype", WTYPES)
@@ -256,7 +259,7 @@ def test_random_byte_blocks(wtype):
     nb = K // oracle.BLOCK_ELEMS[wtype]
     Wq = rng.integers(0, 256, (N, nb, bb), dtype=np.uint8)
     dv = (2.0 ** rng.uniform(-10, 0, (N, nb, 2))).astype(np.float16).view(np.uint8).reshape(N, nb, 4)
-    if wtype == oracle.Q4_K:
+    if wtype in (oracle.Q4_K, oracle.Q5_K):
         Wq[..., 0:4] = dv
     elif wtype == oracle.Q6_K:
         Wq[..., 208:210] = dv[..., 0:2]
@@ -304,6 +307,27 @@ def test_unit_scale_probes_exact_int32():
     assert np.array_equal(H.host(y), want)
     Y = vq.gemm(vq.Q6_K, H.to_dev(Wq), 16, 256, vq.Q8_K, Xq, 3)
     assert np.array_equal(H.host(Y), np.stack([want] * 3))
+    # Q5_K: quants 0..31 (fifth bits set), GEMV, GEMV-kernel batch and MFMA GEMM (70 rows)
+    q5 = rng.integers(0, 32, 256)
+    blocks = []
+    for j in range(8):
+        sc = np.zeros(8, np.int32); sc[j] = 1
+        blocks.append(oracle.q5k_build(0x3C00, 0, sc, np.zeros(8, np.int32), q5))
+    for j in range(8):  # scale 63 = 3 * 16 + 3 * 4 + 3: every base-4 digit plane at its largest
+        sc = np.zeros(8, np.int32); sc[j] = 63
+        blocks.append(oracle.q5k_build(0x3C00, 0, sc, np.zeros(8, np.int32), q5))
+    Wq = np.stack(blocks)
+    I = np.array([sum(int(q5[i]) * int(a[i]) for i in range(32 * j, 32 * j + 32)) for j in range(8)], np.int64)
+    want = np.concatenate([I, 63 * I]).astype(np.float32)
+    assert np.array_equal(want.astype(np.int64), np.concatenate([I, 63 * I]))  # exact in binary32
+    H.say("unit-scale probes Q5_K")
+    y = vq.gemv(vq.Q5_K, H.to_dev(Wq), 16, 256, H.to_dev(a))
+    assert np.array_equal(H.host(y), want)
+    Y = vq.gemm(vq.Q5_K, H.to_dev(Wq), 16, 256, vq.Q8_K, Xq, 3)
+    assert np.array_equal(H.host(Y), np.stack([want] * 3))
+    Xq70 = vq.quantize_act(vq.Q8_K, H.to_dev(np.stack([a] * 70)))
+    Y = vq.gemm(vq.Q5_K, H.to_dev(Wq), 16, 256, vq.Q8_K, Xq70, 70)
+    assert np.array_equal(H.host(Y), np.stack([want] * 70))
     # Q8_0: d = 1 weights, activations with amax 127 give d = 1
     a32 = ((np.arange(64) * 29) % 255 - 127).astype(np.float32)
     a32[0] = 127.0; a32[32] = -127.0
@@ -409,7 +433,8 @@ def test_grouped_types_and_arms(wtype, per_row):
     H.assert_bitwise(Yh, Y_ref, "grouped %s per_row=%d" % (WNAME[wtype], per_row))
     H.assert_bitwise(H.host(Ysum), oracle.weighted_sum(Yh, rw), "weighted sum of the GPU's Y")
     st = vq.get_stats()
-    key = {oracle.Q4_K: "gemm_grouped_q4k", oracle.Q6_K: "gemm_grouped_q6k", oracle.Q8_0: "gemm_grouped_q8_0"}[wtype]
+    key = {oracle.Q4_K: "gemm_grouped_q4k", oracle.Q6_K: "gemm_grouped_q6k", oracle.Q8_0: "gemm_grouped_q8_0",
+           oracle.Q5_K: "gemm_grouped_q5k"}[wtype]
     assert st[key] == 1 and st["gemm_grouped_rows"] == int(per_row) and st["route"] == 1
 
 

@@ -115,6 +115,27 @@ def test_decode_small_batch_full(which, M):
     H.assert_bitwise(H.host(Y), oracle.gemm(wtype, Wq, N, K, act, nthreads=THREADS), "small batch " + which)
 
 
+def test_q5k_decode_full():
+    """Q5_K [8192, 2560]: the GPU encoder's bytes, the decode GEMV with the
+    fused quantizer and a 16-row small batch, every output."""
+    W = synth.tensor("q5k_decode", "W")
+    x = synth.tensor("q5k_decode", "x")
+    X = synth.tensor("q5k_decode", "X")
+    N, K = W.shape
+    Wq = oracle.quantize_weights(oracle.Q5_K, W)
+    H.say("Q5_K decode N=%d K=%d" % (N, K))
+    assert np.array_equal(H.host(vq.quantize_weights(vq.Q5_K, H.to_dev(W))), Wq.reshape(-1)), "encoder bytes"
+    Wd = H.to_dev(Wq)
+    xq = H.to_dev(np.zeros(vq.act_bytes(vq.Q8_K, 1, K), np.uint8))
+    y = vq.gemv(vq.Q5_K, Wd, N, K, H.to_dev(x), xq_out=xq)
+    act = check_act_bytes(oracle.Q5_K, xq, x[None, :])
+    H.assert_bitwise(H.host(y), oracle.gemm(oracle.Q5_K, Wq, N, K, act, nthreads=THREADS)[0], "Q5_K GEMV")
+    Xq = vq.quantize_act(vq.Q8_K, H.to_dev(X))
+    actX = check_act_bytes(oracle.Q5_K, Xq, X)
+    Y = vq.gemm(vq.Q5_K, Wd, N, K, vq.Q8_K, Xq, X.shape[0])
+    H.assert_bitwise(H.host(Y), oracle.gemm(oracle.Q5_K, Wq, N, K, actX, nthreads=THREADS), "Q5_K batch")
+
+
 def test_q8_0_gemv_full():
     """Q8_0 [4096, 2048] against row 0 of the Q8_0 workload's X, fused Q8_1."""
     W = synth.tensor("q8_0_gemm", "W")
