@@ -639,13 +639,7 @@ static hipError_t launch_gemm_cfg(const uint8_t* W, int64_t N, int64_t K, const 
 template <int WT>
 static hipError_t launch_gemm_t(const uint8_t* W, int64_t N, int64_t K, const void* aqs, const void* ad,
                                 const void* aux, int64_t M, float* Y, int64_t ldy, hipStream_t st) {
-    static int cus = 0;
-    if (cus == 0) {
-        int dev = 0, v = 0;
-        (void)hipGetDevice(&dev);
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
-        cus = v;
-    }
+    const int cus = num_cus();
     const int64_t wg256 = ((N + kBN - 1) / kBN) * ((M + 255) / 256);
     if (WT == 2 || wg256 < cus) return launch_gemm_cfg<WT, 4, 2>(W, N, K, aqs, ad, aux, M, Y, ldy, st);
     return launch_gemm_cfg<WT, 4, 4>(W, N, K, aqs, ad, aux, M, Y, ldy, st);

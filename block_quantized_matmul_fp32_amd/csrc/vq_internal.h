@@ -38,6 +38,10 @@ hipError_t launch_quantize_q8_1(const float* X, int64_t M, int64_t K, int64_t ld
 hipError_t launch_quantize_weights(int wtype, const float* W, int64_t N, int64_t K, uint8_t* out,
                                    hipStream_t st);
 
+constexpr int kMaxDevices = 64;
+// Compute units of the current device (cached per device).
+int num_cus();
+
 // Decode GEMV with the fused activation quantizer.  xq_out may be null.
 hipError_t launch_gemv(int wtype, const uint8_t* W, int64_t N, int64_t K, const float* x,
                        float* y, uint8_t* xq_out, hipStream_t st);
