@@ -232,6 +232,7 @@ def run_q8_0(torch, vq, synth, iters):
     Xq = vq.quantize_act(vq.Q8_1, X)
     Y = torch.empty((2048, 4096), dtype=torch.float32, device=dev)
     t, _ = time_graph(lambda i: vq.gemm(vq.Q8_0, Q, 4096, 2048, vq.Q8_1, Xq, 2048, Y=Y), 4, iters)
+    tq, _ = time_graph(lambda i: vq.quantize_act(vq.Q8_1, X, Xq=Xq), 8, iters)
     R = max(2, math.ceil(640 * (1 << 20) / Q.numel()))
     Qs = [Q] + [Q.clone() for _ in range(R - 1)]
     y = torch.empty(4096, dtype=torch.float32, device=dev)
@@ -241,7 +242,9 @@ def run_q8_0(torch, vq, synth, iters):
     return {"gemm_M2048_us": round(t * 1e3, 2), "gemm_tops": round(ops / (t * 1e-3) / 1e12, 1),
             "gemm_frac": round(ops / (t * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
             "gemv_us": round(tv * 1e3, 2), "gemv_gbs": round(gbytes / (tv * 1e-3) / 1e9, 1),
-            "gemv_frac": round(gbytes / (tv * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            "gemv_frac": round(gbytes / (tv * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "quantize_q8_1_us": round(tq * 1e3, 2),
+            "quantize_q8_1_gbs": round(2048 * 2048 * (4 + 1 + 4 / 32) / (tq * 1e-3) / 1e9, 1)}
 
 
 def run_q5k(torch, vq, synth, iters):
@@ -419,6 +422,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--secondary-iters", type=int, default=20)
+    ap.add_argument("--sections", default="prefill,q8_0,q5k,small_batch,producers,grouped,grouped_down_per_row",
+                    help="comma-separated secondary sections to run (all by default)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (rocprofv3 counter scaling)")
     args = ap.parse_args()
@@ -474,20 +479,25 @@ def main():
                            "q6k_frac": round(ach6 / HBM_PEAK_GBS, 4)},
     }
     if not args.no_secondary:
-        log("[bench] prefill GEMM")
-        line["prefill"] = run_prefill(torch, vq, synth, args.secondary_iters)
-        log("[bench] Q8_0 GEMM and GEMV")
-        line["q8_0"] = run_q8_0(torch, vq, synth, args.secondary_iters)
-        log("[bench] Q5_K GEMV and GEMM")
-        line["q5k"] = run_q5k(torch, vq, synth, args.secondary_iters)
-        log("[bench] small batches")
-        line["small_batch"] = run_small_batch(torch, vq, synth, args.secondary_iters)
-        log("[bench] producers with the quantizer epilogue")
-        line["producers"] = run_producers(torch, vq, synth, args.secondary_iters)
-        log("[bench] grouped MUL_MAT_ID")
-        line["grouped"] = run_grouped(torch, vq, synth, max(5, args.secondary_iters // 2))
-        log("[bench] grouped per-row arm (MoE down projection)")
-        line["grouped_down_per_row"] = run_grouped_down(torch, vq, synth, max(5, args.secondary_iters // 2))
+        it = args.secondary_iters
+        sections = [
+            ("prefill", "prefill GEMM", lambda: run_prefill(torch, vq, synth, it)),
+            ("q8_0", "Q8_0 GEMM, GEMV and quantizer", lambda: run_q8_0(torch, vq, synth, it)),
+            ("q5k", "Q5_K GEMV and GEMM", lambda: run_q5k(torch, vq, synth, it)),
+            ("small_batch", "small batches", lambda: run_small_batch(torch, vq, synth, it)),
+            ("producers", "producers with the quantizer epilogue", lambda: run_producers(torch, vq, synth, it)),
+            ("grouped", "grouped MUL_MAT_ID", lambda: run_grouped(torch, vq, synth, max(5, it // 2))),
+            ("grouped_down_per_row", "grouped per-row arm (MoE down projection)",
+             lambda: run_grouped_down(torch, vq, synth, max(5, it // 2))),
+        ]
+        wanted = set(x for x in args.sections.split(",") if x)
+        unknown = wanted - set(k for k, _, _ in sections)
+        if unknown:
+            sys.exit("unknown --sections entries: %s" % ", ".join(sorted(unknown)))
+        for key, what, fn in sections:
+            if key in wanted:
+                log("[bench] " + what)
+                line[key] = fn()
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline (%.0f s)" % args.cpu_seconds)
         line["cpu_baseline"] = run_cpu_baseline(args.cpu_seconds)
