@@ -205,7 +205,9 @@ vq_status vq_silu_mul_quant(int act, const float* G, const float* U, int64_t M, 
 /*   bit-identical to that fixed-order definition.                         */
 /* W: [N][K] blocks of type w; x: fp32 [K]; y: fp32 [N]; xq_out: NULL or      */
 /* vq_act_bytes(act, 1, K) bytes that receive the fused quantizer's          */
-/* activation bytes (identical to vq_quantize_act's).  K <= 65536.           */
+/* activation bytes (identical to vq_quantize_act's).  One weight row and  */
+/* the quantized activation must fit the 160 KiB LDS: K up to about 90K     */
+/* (Q4_K), 84K (Q5_K), 78K (Q6_K), 32K (Q8_0); longer K is VQ_ERR_SHAPE.    */
 /* ---------------------------------------------------------------------- */
 vq_status vq_gemv(int w, const void* W, int64_t N, int64_t K, const float* x, float* y,
                   void* xq_out, hipStream_t stream);

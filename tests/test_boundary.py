@@ -176,3 +176,13 @@ def test_small_batch_crossover_setting(vq):
     finally:
         for w in defaults:
             vq.set_small_batch_max(w, -1)
+
+
+def test_gemv_rejects_rows_too_long_for_lds(vq):
+    """The fused GEMV keeps a weight row and the quantized activation in LDS:
+    K past that limit is a shape error, checked on the host before any
+    pointer is looked at (no GPU needed)."""
+    L = vq.lib()
+    assert L.vq_gemv(vq.Q8_0, None, 1, 65536, None, None, None, None) == 4  # VQ_ERR_SHAPE
+    assert L.vq_gemv(vq.Q4_K, None, 1, 65536, None, None, None, None) == 1  # fits: then the null pointers
+    assert L.vq_gemv(vq.Q6_K, None, 1, 1 << 17, None, None, None, None) == 4
