@@ -103,11 +103,13 @@ __global__ __launch_bounds__(64) void route_count_kernel(const int32_t* __restri
 // expert e; counts, expert offsets and the tile table (expert, first list
 // slot, rows).  kScanThreads / E threads share one expert's chunks.
 constexpr int kScanThreads = 1024;
+constexpr int64_t kScanStageCells = 12288;  // chunk-table cells staged in LDS (48 KiB)
 __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(int nchunks, int E, int32_t* __restrict__ chunk,
                                                                   int32_t* __restrict__ counts,
                                                                   int32_t* __restrict__ offsets,
                                                                   int32_t* __restrict__ tiles,
                                                                   int32_t* __restrict__ ntiles) {
+    extern __shared__ int32_t cstage[];  // the chunk table, when it fits (dynamic LDS)
     __shared__ int32_t part[kScanThreads];
     __shared__ int32_t sc[1024];
     __shared__ int32_t st[1024];
@@ -117,9 +119,18 @@ __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(int nchunks, i
     const bool own = e < E;
     const int len = (nchunks + tpe - 1) / tpe;
     const int c0 = min(nchunks, q * len), c1 = min(nchunks, c0 + len);
+    const int64_t ncell = (int64_t)nchunks * E;
+    // Staged: one coalesced copy into LDS, the two passes over it there, one
+    // coalesced copy back (instead of two rounds of strided global reads).
+    const bool staged = ncell <= kScanStageCells;
+    int32_t* tab = staged ? cstage : chunk;
+    if (staged) {
+        for (int64_t i = tid; i < ncell; i += kScanThreads) cstage[i] = chunk[i];
+        __syncthreads();
+    }
     int sum = 0;
     if (own)
-        for (int c = c0; c < c1; ++c) sum += chunk[(int64_t)c * E + e];
+        for (int c = c0; c < c1; ++c) sum += tab[(int64_t)c * E + e];
     part[tid] = sum;
     __syncthreads();
     int base = 0, total = 0;
@@ -131,10 +142,14 @@ __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(int nchunks, i
         }
         int run = base;
         for (int c = c0; c < c1; ++c) {
-            const int v = chunk[(int64_t)c * E + e];
-            chunk[(int64_t)c * E + e] = run;
+            const int v = tab[(int64_t)c * E + e];
+            tab[(int64_t)c * E + e] = run;
             run += v;
         }
+    }
+    if (staged) {
+        __syncthreads();
+        for (int64_t i = tid; i < ncell; i += kScanThreads) chunk[i] = cstage[i];
     }
     const bool lead = own && q == 0;
     if (lead) counts[e] = total;
@@ -150,15 +165,21 @@ __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(int nchunks, i
         st[e] = nt;
     }
     __syncthreads();
-    // inclusive Hillis-Steele scans of counts and tile counts over experts
-    for (int o = 1; o < 1024; o <<= 1) {
-        const int a = (tid < 1024 && tid >= o) ? sc[tid - o] : 0;
-        const int b = (tid < 1024 && tid >= o) ? st[tid - o] : 0;
-        __syncthreads();
-        if (tid < 1024) {
-            sc[tid] += a;
-            st[tid] += b;
+    // inclusive scans of counts and tile counts over experts (index = tid):
+    // within each wave by shuffles, then the earlier waves' totals added
+    {
+        __shared__ int32_t wsc[kScanThreads / 64], wst[kScanThreads / 64];
+        const int lane = tid & 63, w = tid >> 6;
+        int a = sc[tid], b = st[tid];
+        for (int o = 1; o < 64; o <<= 1) {
+            const int ua = __shfl_up(a, o, 64), ub = __shfl_up(b, o, 64);
+            if (lane >= o) { a += ua; b += ub; }
         }
+        if (lane == 63) { wsc[w] = a; wst[w] = b; }
+        __syncthreads();
+        for (int k = 0; k < w; ++k) { a += wsc[k]; b += wst[k]; }
+        sc[tid] = a;
+        st[tid] = b;
         __syncthreads();
     }
     if (lead) {
@@ -195,8 +216,10 @@ hipError_t launch_route(const int32_t* ids, int64_t T, int64_t top_k, int64_t E,
     const int nchunks = (int)((T + kRouteChunk - 1) / kRouteChunk);
     if (nchunks > 0)
         route_count_kernel<<<nchunks, 64, 0, st>>>(ids, (int)T, (int)top_k, (int)E, ws.chunk, ws.rank);
-    route_scan_kernel<<<1, kScanThreads, 0, st>>>(nchunks, (int)E, ws.chunk, ws.counts, ws.offsets, ws.tiles,
-                                                  ws.ntiles);
+    const int64_t ncell = (int64_t)nchunks * E;
+    const size_t stage = (ncell <= kScanStageCells) ? (size_t)ncell * 4 : 0;
+    route_scan_kernel<<<1, kScanThreads, stage, st>>>(nchunks, (int)E, ws.chunk, ws.counts, ws.offsets, ws.tiles,
+                                                      ws.ntiles);
     const int64_t npairs = T * top_k;
     if (npairs > 0)
         route_place_kernel<<<(unsigned)((npairs + 255) / 256), 256, 0, st>>>(ids, npairs, (int)top_k, (int)E,
