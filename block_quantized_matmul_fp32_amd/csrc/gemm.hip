@@ -182,16 +182,14 @@ __global__ __launch_bounds__(128 * WM, 2) void gemm_kernel(const uint8_t* __rest
     const int nsteps = (K + kKS - 1) / kKS;
 
     // Activation chunks of this thread: row (tid >> 4) + (NT / 16) * i, bytes
-    // 16 * (tid & 15) of each step.  Rows past the tile are not loaded (zero;
-    // their outputs are never stored).
+    // 16 * (tid & 15) of each step.  Rows past the tile read activation row 0
+    // (their outputs are never stored).
     const int acol = 16 * (tid & 15);
     const int8_t* ap[ACH];
-    uint32_t avalid = 0;
 #pragma unroll
     for (int i = 0; i < ACH; ++i) {
         const int ar = sRow[(tid >> 4) + (NT / 16) * i];
         ap[i] = aqs + (int64_t)(ar >= 0 ? ar : 0) * K + acol;
-        avalid |= (ar >= 0 ? 1u : 0u) << i;
     }
     const int my_ar = (tid < BM) ? sRow[tid] : -1;  // scale row of threads < BM
 
@@ -215,10 +213,12 @@ __global__ __launch_bounds__(128 * WM, 2) void gemm_kernel(const uint8_t* __rest
 #pragma unroll
         for (int i = 0; i < ACH; ++i) {
             if (part >= 0 && (i * 4 / ACH) != part) continue;
-            if (((avalid >> i) & 1) && (WT != 2 || kk + acol < K))
-                regA[i] = *(const u4v*)(ap[i] + kk);
-            else
-                regA[i] = (u4v){0u, 0u, 0u, 0u};
+            // Branch-free: a row past the tile reads row 0 (its outputs are
+            // never stored, and every output depends on its own row only);
+            // Q8_0 columns past K read inside the row and are never used.
+            int64_t off = kk;
+            if (WT == 2 && kk + acol >= K) off = (int64_t)K - 16 - acol;
+            regA[i] = *(const u4v*)(ap[i] + off);
         }
         if (part > 1) return;
         if (part <= 0 && tid < BM) {
