@@ -66,23 +66,28 @@ __device__ __forceinline__ void gload16_a2(const uint8_t* p, const uint8_t* end,
     out[3] = __builtin_amdgcn_alignbyte(w4, w3, sh);
 }
 
-// Multiply the four int8 bytes of v by a small integer f (every true product
-// fits int8): even and odd bytes go through 16-bit lanes, so no carry crosses
-// a byte, and the low bytes are repacked with v_perm.
-__device__ __forceinline__ uint32_t bytes_mul(uint32_t v, int f) {
+// Multiply the four bytes of v by f when every byte's product lies in
+// [0, 255] (Q4_K / Q5_K quants times a scale digit): each 16-bit lane holds
+// two bytes, the low byte's product cannot carry into the high byte, and the
+// high byte's product times 256 stays below 2^16, so one packed 16-bit
+// multiply is exact.
+__device__ __forceinline__ uint32_t bytes_mul_u(uint32_t v, int f) {
     const us2 fe = (us2){(unsigned short)f, (unsigned short)f};
-    const us2 e = __builtin_bit_cast(us2, v & 0x00FF00FFu) * fe;
-    const us2 o = __builtin_bit_cast(us2, (v >> 8) & 0x00FF00FFu) * fe;
-    return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, o), __builtin_bit_cast(uint32_t, e),
-                                 0x06020400u);
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(us2, v) * fe);
 }
 
-// Unsigned 6-bit quants (bytes 0..63) -> signed (q - 32) bytes.
-__device__ __forceinline__ uint32_t bytes_sub32(uint32_t q) {
-    const us2 e = __builtin_bit_cast(us2, q & 0x00FF00FFu) - (us2){32, 32};
-    const us2 o = __builtin_bit_cast(us2, (q >> 8) & 0x00FF00FFu) - (us2){32, 32};
-    return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, o), __builtin_bit_cast(uint32_t, e),
-                                 0x06020400u);
+// Q6_K plane bytes ((q - 32) * d) mod 256 for 6-bit quants q, given as their
+// even bytes (ev = q & 0x00FF00FF) and odd bytes (od = q & 0xFF00FF00).  The
+// even products sit in the low byte of each 16-bit lane (carries land in the
+// high byte, masked off); the odd products sit in the high byte and their low
+// byte stays zero.  The offset -32 * d is added in the same multiply-add.
+__device__ __forceinline__ uint32_t q6_plane_bytes(uint32_t ev, uint32_t od, int d) {
+    const unsigned short f = (unsigned short)d;
+    const unsigned short c = (unsigned short)(-32 * d);
+    const unsigned short c8 = (unsigned short)(c << 8);
+    const us2 e = __builtin_bit_cast(us2, ev) * (us2){f, f} + (us2){c, c};
+    const us2 o = __builtin_bit_cast(us2, od) * (us2){f, f} + (us2){c8, c8};
+    return (__builtin_bit_cast(uint32_t, e) & 0x00FF00FFu) | __builtin_bit_cast(uint32_t, o);
 }
 
 template <int WT>
@@ -363,8 +368,8 @@ __global__ __launch_bounds__(128 * WM, 2) void gemm_kernel(const uint8_t* __rest
                     uint32_t lo[4], hi[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        lo[i] = bytes_mul(ql[i], fl[p]);
-                        hi[i] = bytes_mul(qh[i], fh[p]);
+                        lo[i] = bytes_mul_u(ql[i], fl[p]);
+                        hi[i] = bytes_mul_u(qh[i], fh[p]);
                     }
                     int8_t* dst = wdst + p * kBN * kLD + 64 * c + 16 * hf;
                     *(uint4*)dst = make_uint4(lo[0], lo[1], lo[2], lo[3]);
@@ -402,21 +407,22 @@ __global__ __launch_bounds__(128 * WM, 2) void gemm_kernel(const uint8_t* __rest
                     const int t1 = (sc - d0) >> 3;
                     const int d1 = ((t1 + 3) & 7) - 3;
                     const int d2 = (t1 - d1) >> 3;
-                    uint32_t qs[4];
+                    uint32_t ev[4], od[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const uint32_t ql = regW[8 * j + i];
                         const uint32_t qh = regW[8 * j + 4 + i];
                         const uint32_t q6 = part ? (((ql >> 4) & 0x0F0F0F0Fu) | ((qh >> sa) & 0x30303030u))
                                                  : ((ql & 0x0F0F0F0Fu) | ((qh << (4 - sa)) & 0x30303030u));
-                        qs[i] = bytes_sub32(q6);
+                        ev[i] = q6 & 0x00FF00FFu;
+                        od[i] = q6 & 0xFF00FF00u;
                     }
                     const int dg[3] = {d0, d1, d2};
 #pragma unroll
                     for (int p = 0; p < 3; ++p) {
                         int8_t* dst = wdst + p * kBN * kLD + 128 * h + 64 * part + 16 * v;
-                        *(uint4*)dst = make_uint4(bytes_mul(qs[0], dg[p]), bytes_mul(qs[1], dg[p]),
-                                                  bytes_mul(qs[2], dg[p]), bytes_mul(qs[3], dg[p]));
+                        *(uint4*)dst = make_uint4(q6_plane_bytes(ev[0], od[0], dg[p]), q6_plane_bytes(ev[1], od[1], dg[p]),
+                                                  q6_plane_bytes(ev[2], od[2], dg[p]), q6_plane_bytes(ev[3], od[3], dg[p]));
                     }
                 }
             }
