@@ -9,10 +9,11 @@
 // and "routed-compact" (MUL_MAT_ID tiles sized to the rows of each expert).
 //
 // MI355X design (not the pages' RDNA WMMA tiles):
-//  * 256 threads, a 2x2 grid of waves; each wave owns 32 weight rows x BM/2
-//    activation rows as 16x16 MFMA tiles; the workgroup tile is 64 x BM.
+//  * A 2 x WM grid of waves (8 or 16 for the prefill GEMM, 4 for the grouped
+//    one); each wave owns 32 weight rows x 16 TM activation rows as 16x16
+//    MFMA tiles; the workgroup tile is 64 x BM (BM = 16 TM WM).
 //  * Per 256-wide K step the workgroup stages ONE activation tile (int8 Q8_K
-//    or Q8_1 bytes plus scales) in LDS, shared by all four waves, and ONE
+//    or Q8_1 bytes plus scales) in LDS, shared by all its waves, and ONE
 //    unpacked weight tile, also shared; the next step's global bytes are
 //    already in flight in registers while the current step computes.
 //  * The per-sub-block integer scales are folded into the int8 MFMA operand
@@ -41,6 +42,7 @@ namespace vqk {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+typedef short ss2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u4v __attribute__((ext_vector_type(4)));  // native vector: plain loads and stores
 
 constexpr int kBN = 64;   // weight rows per workgroup
@@ -114,8 +116,9 @@ struct GroupArgs {
 // Workgroup of 2 x WM waves (128 * WM threads) computing a 64 x (16 * TM * WM)
 // output tile; each wave owns 32 weight rows x 16 * TM activation rows
 // (2 x TM MFMA tiles of 16 x 16).  A weight row's step (one super-block, or eight
-// Q8_0 blocks) is unpacked by 2 * WM threads, each taking 8 / (2 * WM) of
-// its eight 16-byte pieces, so the unpack cost per output falls as WM grows.
+// Q8_0 blocks) is unpacked by 2 * WM threads (by the first 512 threads, eight
+// per row, when there are more), each taking an equal share of its eight
+// 16-byte pieces, so the unpack cost per output falls as the tile grows.
 template <int WT, int WM, int TM, bool kGrouped>
 __global__ __launch_bounds__(128 * WM, 2) void gemm_kernel(const uint8_t* __restrict__ Wbase, int N, int K,
                                                            int64_t wbytes, const int8_t* __restrict__ aqs,
@@ -130,7 +133,8 @@ __global__ __launch_bounds__(128 * WM, 2) void gemm_kernel(const uint8_t* __rest
     constexpr int NT = 128 * WM;           // threads
     constexpr int BM = 16 * TM * WM;       // activation rows per workgroup
     constexpr int ACH = BM * 16 / NT;      // 16-byte activation chunks per thread per step
-    constexpr int UPR = NT / kBN;          // threads per weight row
+    constexpr int NU = (NT < 512) ? NT : 512;  // threads that load and unpack weights
+    constexpr int UPR = NU / kBN;          // threads per weight row
     constexpr int PPT = 8 / UPR;           // 16-byte pieces per thread
     __shared__ __attribute__((aligned(16))) int8_t sA[BM * kLD];
     __shared__ __attribute__((aligned(16))) int8_t sW[P * kBN * kLD];
@@ -198,7 +202,9 @@ __global__ __launch_bounds__(128 * WM, 2) void gemm_kernel(const uint8_t* __rest
     }
     const int my_ar = (tid < BM) ? sRow[tid] : -1;  // scale row of threads < BM
 
-    // Weight unpack role: row wr, pieces [PPT * wu, PPT * wu + PPT).
+    // Weight unpack role (threads below NU, whole waves): row wr, pieces
+    // [PPT * wu, PPT * wu + PPT).
+    const bool wthr = (NT <= NU) || tid < NU;
     const int wr = tid / UPR, wu = tid % UPR;
     const bool wvalid = (n0 + wr) < N;
     const uint8_t* wrow_p = W + (int64_t)(wvalid ? n0 + wr : 0) * rb;
@@ -247,7 +253,7 @@ __global__ __launch_bounds__(128 * WM, 2) void gemm_kernel(const uint8_t* __rest
                 }
             }
         }
-        if (part == 0) return;
+        if (part == 0 || !wthr) return;
         if (WT == 0 || WT == 3) {
             // Q5_K: the nibbles at byte 48, and for piece pc the 16 fifth-bit
             // bytes 16 + 16 (pc % 2) .. that cover its values
@@ -315,20 +321,27 @@ __global__ __launch_bounds__(128 * WM, 2) void gemm_kernel(const uint8_t* __rest
             } else {
                 sDa[tid] = regDa;
                 if (kMin) {
-                    // bs32_j = bsums[2j] + bsums[2j+1] = 64 * h + l, 0 <= l < 64 (int8 operands)
+                    // bs32_j = bsums[2j] + bsums[2j+1] = 64 * h + l, 0 <= l < 64 (int8
+                    // operands).  Two sums per word in 16-bit halves (|bs32| < 2^15),
+                    // then the low byte of each half.
                     const uint32_t bw[8] = {regBs[0].x, regBs[0].y, regBs[0].z, regBs[0].w,
                                             regBs[1].x, regBs[1].y, regBs[1].z, regBs[1].w};
-                    uint32_t hh[2] = {0, 0}, ll[2] = {0, 0};
+                    uint32_t hp[4], lp[4];
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const int bs32 = (int)(int16_t)(bw[j] & 0xFFFF) + (int)(int16_t)(bw[j] >> 16);
-                        hh[j >> 2] |= ((uint32_t)((bs32 >> 6) & 0xFF)) << (8 * (j & 3));
-                        ll[j >> 2] |= ((uint32_t)(bs32 & 63)) << (8 * (j & 3));
+                    for (int k = 0; k < 4; ++k) {
+                        const uint32_t ev = __builtin_amdgcn_perm(bw[2 * k + 1], bw[2 * k], 0x05040100u);
+                        const uint32_t od = __builtin_amdgcn_perm(bw[2 * k + 1], bw[2 * k], 0x07060302u);
+                        const us2 sum = __builtin_bit_cast(us2, ev) + __builtin_bit_cast(us2, od);
+                        hp[k] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(ss2, sum) >> (ss2){6, 6});
+                        lp[k] = __builtin_bit_cast(uint32_t, sum) & 0x003F003Fu;
                     }
-                    *(uint4*)(sHl + tid * 16) = make_uint4(hh[0], hh[1], ll[0], ll[1]);
+                    *(uint4*)(sHl + tid * 16) = make_uint4(
+                        __builtin_amdgcn_perm(hp[1], hp[0], 0x06040200u), __builtin_amdgcn_perm(hp[3], hp[2], 0x06040200u),
+                        __builtin_amdgcn_perm(lp[1], lp[0], 0x06040200u), __builtin_amdgcn_perm(lp[3], lp[2], 0x06040200u));
                 }
             }
         }
+        if (!wthr) return;
         int8_t* wdst = sW + wr * kLD;
         if (WT == 0 || WT == 3) {
             // piece pc = 16 qs bytes at 16 * pc: low nibbles are values
@@ -376,18 +389,17 @@ __global__ __launch_bounds__(128 * WM, 2) void gemm_kernel(const uint8_t* __rest
                     *(uint4*)(dst + 32) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
                 }
             }
-            if (wu == 0) {
-                sDw[wr] = half_bits_to_float(regW[0] & 0xFFFF);
-                sDw[kBN + wr] = half_bits_to_float(regW[0] >> 16);
-                // mins: m_j = (scales[j] >> 6) | (nibble j&1 of scales[8 + j/2]) << 2
-                uint32_t mw[2] = {0, 0};
+            // d and dmin from two lanes of the row; the eight 6-bit mins
+            // m_j = (scales[j] >> 6) | (nibble j % 2 of scales[8 + j / 2]) << 2
+            // spread over the row's lanes, PPT each.
+            if (wu == 0) sDw[wr] = half_bits_to_float(regW[0] & 0xFFFF);
+            if (wu == 1 % UPR) sDw[kBN + wr] = half_bits_to_float(regW[0] >> 16);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const uint32_t sj = ((j < 4 ? regW[1] : regW[2]) >> (8 * (j & 3))) & 0xFF;
-                    const uint32_t nb_ = (regW[3] >> (4 * j)) & 15;
-                    mw[j >> 2] |= ((sj >> 6) | (nb_ << 2)) << (8 * (j & 3));
-                }
-                *(uint2*)(sMw + wr * 8) = make_uint2(mw[0], mw[1]);
+            for (int jj = 0; jj < PPT; ++jj) {
+                const int j = PPT * wu + jj;
+                const uint32_t sj = ((j < 4 ? regW[1] : regW[2]) >> (8 * (j & 3))) & 0xFF;
+                const uint32_t nb_ = (regW[3] >> (4 * j)) & 15;
+                sMw[wr * 8 + j] = (int8_t)((sj >> 6) | (nb_ << 2));
             }
         } else if (WT == 1) {
             // piece pc = (h, v): ql bytes 64h + 16v.. hold values 128h + 16v + i
@@ -639,15 +651,20 @@ static hipError_t launch_gemm_cfg(const uint8_t* W, int64_t N, int64_t K, const 
 // Tile choice: 64 x 256 tiles unless they would leave CUs without a
 // workgroup (then 64 x 128 tiles on the same eight waves, twice the
 // workgroups); Q8_0, whose per-block epilogue dominates, always takes the
-// 64 x 128 tiles (measured faster at every workload shape).  (64 x 64
-// tiles for still smaller grids measured no faster: the time of a column
-// tile is its sequence of super-block steps, not the number of tiles.)
+// 64 x 128 tiles (measured faster at every workload shape).  Q6_K runs its
+// 64 x 256 tiles on sixteen waves of 32 x 32 (four per SIMD, 128 VGPRs):
+// with three planes its waves wait longest on LDS and MFMA results, and the
+// extra waves cover that (9% faster at M = 2048); Q4_K and Q5_K measured
+// slower that way (register spills).  (64 x 64 tiles for still smaller grids
+// measured no faster: the time of a column tile is its sequence of
+// super-block steps, not the number of tiles.)
 template <int WT>
 static hipError_t launch_gemm_t(const uint8_t* W, int64_t N, int64_t K, const void* aqs, const void* ad,
                                 const void* aux, int64_t M, float* Y, int64_t ldy, hipStream_t st) {
     const int cus = num_cus();
     const int64_t wg256 = ((N + kBN - 1) / kBN) * ((M + 255) / 256);
     if (WT == 2 || wg256 < cus) return launch_gemm_cfg<WT, 4, 2>(W, N, K, aqs, ad, aux, M, Y, ldy, st);
+    if (WT == 1) return launch_gemm_cfg<WT, 8, 2>(W, N, K, aqs, ad, aux, M, Y, ldy, st);
     return launch_gemm_cfg<WT, 4, 4>(W, N, K, aqs, ad, aux, M, Y, ldy, st);
 }
 
