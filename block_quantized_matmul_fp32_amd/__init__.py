@@ -27,6 +27,7 @@ EXPORTS = [
     "vq_quantize_act", "vq_quantize_weights", "vq_gemv", "vq_gemm", "vq_grouped_workspace_bytes",
     "vq_gemm_grouped", "vq_gemm_grouped_rows", "vq_weighted_sum", "vq_get_stats", "vq_reset_stats",
     "vq_version", "vq_rmsnorm_quant", "vq_silu_mul_quant", "vq_set_small_batch_max", "vq_small_batch_max",
+    "vq_set_gemm_row_block",
 ]
 
 STAT_FIELDS = ["quantize_q8k", "quantize_q8_1", "quantize_weights", "gemv_q4k", "gemv_q6k", "gemv_q8_0",
@@ -84,6 +85,8 @@ def lib():
         L.vq_set_small_batch_max.restype = I
         L.vq_small_batch_max.argtypes = [I]
         L.vq_small_batch_max.restype = I64
+        L.vq_set_gemm_row_block.argtypes = [I64]
+        L.vq_set_gemm_row_block.restype = I
         L.vq_rmsnorm_quant.argtypes = [I, P, P, I64, I64, I64, ctypes.c_float, P, I64, P, P]
         L.vq_silu_mul_quant.argtypes = [I, P, P, I64, I64, I64, P, I64, P, P]
         L.vq_get_stats.argtypes = [ctypes.POINTER(VQStats)]
@@ -154,6 +157,11 @@ def set_small_batch_max(w: int, max_m: int):
 
 def small_batch_max(w: int) -> int:
     return int(lib().vq_small_batch_max(w))
+
+
+def set_gemm_row_block(rows: int):
+    """vq_set_gemm_row_block: cap the rows of one MFMA GEMM launch (0: default)."""
+    _check(lib().vq_set_gemm_row_block(rows))
 
 
 def grouped_workspace_bytes(E: int, T: int, top_k: int) -> int:

@@ -30,6 +30,10 @@
 //    The integer sums are exact, and the binary32 combine of each block and
 //    the ascending-block accumulation follow the fixed-order definition, so Y
 //    is bit-identical to it.
+#include <algorithm>
+#include <atomic>
+#include <type_traits>
+
 #include "vq_device.h"
 #include "vq_internal.h"
 
@@ -192,13 +196,17 @@ __global__ __launch_bounds__(128 * WM, 2) void gemm_kernel(const uint8_t* __rest
 
     // Activation chunks of this thread: row (tid >> 4) + (NT / 16) * i, bytes
     // 16 * (tid & 15) of each step.  Rows past the tile read activation row 0
-    // (their outputs are never stored).
+    // (their outputs are never stored).  The prefill launch keeps the
+    // activation bytes of one launch below 2^31, so their offsets from aqs are
+    // 32-bit (one VGPR per chunk, no 64-bit address arithmetic per load); the
+    // grouped variant gathers rows from the whole activation matrix.
+    typedef typename std::conditional<kGrouped, int64_t, uint32_t>::type AOff;
     const int acol = 16 * (tid & 15);
-    const int8_t* ap[ACH];
+    AOff aoff[ACH];
 #pragma unroll
     for (int i = 0; i < ACH; ++i) {
         const int ar = sRow[(tid >> 4) + (NT / 16) * i];
-        ap[i] = aqs + (int64_t)(ar >= 0 ? ar : 0) * K + acol;
+        aoff[i] = (AOff)(ar >= 0 ? ar : 0) * (AOff)K + (AOff)acol;
     }
     const int my_ar = (tid < BM) ? sRow[tid] : -1;  // scale row of threads < BM
 
@@ -227,9 +235,9 @@ __global__ __launch_bounds__(128 * WM, 2) void gemm_kernel(const uint8_t* __rest
             // Branch-free: a row past the tile reads row 0 (its outputs are
             // never stored, and every output depends on its own row only);
             // Q8_0 columns past K read inside the row and are never used.
-            int64_t off = kk;
-            if (WT == 2 && kk + acol >= K) off = (int64_t)K - 16 - acol;
-            regA[i] = *(const u4v*)(ap[i] + off);
+            AOff off = (AOff)kk;
+            if (WT == 2 && kk + acol >= K) off = (AOff)(K - 16 - acol);
+            regA[i] = *(const u4v*)(aqs + (aoff[i] + off));
         }
         if (part > 1) return;
         if (part <= 0 && tid < BM) {
@@ -635,17 +643,37 @@ __global__ __launch_bounds__(128 * WM, 2) void gemm_kernel(const uint8_t* __rest
     }
 }
 
+static std::atomic<int64_t> g_row_block{0};
+
+void set_gemm_row_block(int64_t rows) { g_row_block = rows; }
+
 template <int WT, int WM, int TM>
 static hipError_t launch_gemm_cfg(const uint8_t* W, int64_t N, int64_t K, const void* aqs, const void* ad,
                                   const void* aux, int64_t M, float* Y, int64_t ldy, hipStream_t st) {
     constexpr int BM = 16 * TM * WM;
     const int nbw = (WT == 2) ? (int)(K / kQK8) : (int)(K / kQK);
     const int64_t wbytes = N * (int64_t)nbw * GemmCfg<WT>::BB;
-    dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + BM - 1) / BM));
+    // Row blocks of at most 2^31 activation bytes per launch (the kernel's
+    // 32-bit activation offsets); one launch for every practical shape.
+    int64_t rows_max = ((int64_t(1) << 31) / K) / BM * BM;
+    if (rows_max < BM) return hipErrorInvalidValue;
+    const int64_t rb = g_row_block.load();
+    if (rb > 0) rows_max = std::min(rows_max, rb);
+    // bytes per activation row in the planar planes: per block a binary32 d
+    // and sixteen int16 sums (Q8_K), or a binary16 d and a binary16 s (Q8_1)
+    const int64_t d_row = (WT == 2) ? (int64_t)nbw * 2 : (int64_t)nbw * 4;
+    const int64_t aux_row = (WT == 2) ? (int64_t)nbw * 2 : (int64_t)nbw * 32;
     GroupArgs ga = {};
-    gemm_kernel<WT, WM, TM, false><<<grid, 128 * WM, 0, st>>>(W, (int)N, (int)K, wbytes, (const int8_t*)aqs, ad,
-                                                              (const int16_t*)aux, (int)M, Y, ldy, ga);
-    return hipGetLastError();
+    for (int64_t m0 = 0; m0 < M; m0 += rows_max) {
+        const int64_t mc = std::min(rows_max, M - m0);
+        dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((mc + BM - 1) / BM));
+        gemm_kernel<WT, WM, TM, false><<<grid, 128 * WM, 0, st>>>(
+            W, (int)N, (int)K, wbytes, (const int8_t*)aqs + m0 * K, (const uint8_t*)ad + m0 * d_row,
+            aux ? (const int16_t*)((const uint8_t*)aux + m0 * aux_row) : nullptr, (int)mc, Y + m0 * ldy, ldy, ga);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 // Tile choice: 64 x 256 tiles unless they would leave CUs without a
@@ -664,8 +692,8 @@ static hipError_t launch_gemm_t(const uint8_t* W, int64_t N, int64_t K, const vo
     const int cus = num_cus();
     const int64_t wg256 = ((N + kBN - 1) / kBN) * ((M + 255) / 256);
     if (WT == 2 || wg256 < cus) return launch_gemm_cfg<WT, 4, 2>(W, N, K, aqs, ad, aux, M, Y, ldy, st);
-    if (WT == 1) return launch_gemm_cfg<WT, 8, 2>(W, N, K, aqs, ad, aux, M, Y, ldy, st);
-    return launch_gemm_cfg<WT, 4, 4>(W, N, K, aqs, ad, aux, M, Y, ldy, st);
+    if constexpr (WT == 1) return launch_gemm_cfg<WT, 8, 2>(W, N, K, aqs, ad, aux, M, Y, ldy, st);
+    else return launch_gemm_cfg<WT, 4, 4>(W, N, K, aqs, ad, aux, M, Y, ldy, st);
 }
 
 hipError_t launch_gemm(int wtype, const uint8_t* W, int64_t N, int64_t K, const void* act_qs,

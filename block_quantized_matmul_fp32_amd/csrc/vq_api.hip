@@ -376,6 +376,13 @@ int64_t vq_small_batch_max(int w) {
     return g_small_max[widx(w)].load();
 }
 
+vq_status vq_set_gemm_row_block(int64_t rows) {
+    if (rows < 0)
+        return fail(VQ_ERR_INVALID_ARG, "vq_set_gemm_row_block: rows = %lld < 0", (long long)rows);
+    vqk::set_gemm_row_block(rows);
+    return VQ_OK;
+}
+
 size_t vq_grouped_workspace_bytes(int64_t E, int64_t T, int64_t top_k) {
     if (E <= 0 || T < 0 || top_k <= 0) return 0;
     return vqk::route_ws_layout(E, T, top_k, nullptr, nullptr);

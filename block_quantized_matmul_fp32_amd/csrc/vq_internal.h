@@ -42,6 +42,10 @@ constexpr int kMaxDevices = 64;
 // Compute units of the current device (cached per device).
 int num_cus();
 
+// Prefill GEMM row blocking: one launch covers at most this many activation
+// rows (0: as many as keep the launch's activation bytes below 2^31).
+void set_gemm_row_block(int64_t rows);
+
 // Decode GEMV with the fused activation quantizer.  xq_out may be null.
 hipError_t launch_gemv(int wtype, const uint8_t* W, int64_t N, int64_t K, const float* x,
                        float* y, uint8_t* xq_out, hipStream_t st);

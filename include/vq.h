@@ -237,6 +237,18 @@ vq_status vq_set_small_batch_max(int w, int64_t max_m);
 int64_t vq_small_batch_max(int w);
 
 /* ---------------------------------------------------------------------- */
+/* Row blocks of the MFMA arm of vq_gemm.  The GEMM kernel addresses the    */
+/* activation bytes of one launch with 32-bit offsets, so vq_gemm launches  */
+/* it once per block of at most floor(2^31 / K) rows (rounded down to the   */
+/* tile height), which is one launch for every practical shape.  rows > 0   */
+/* caps the block at that many rows (any value; for tests of the blocking); */
+/* 0 restores the default.  The result does not depend on the blocking.     */
+/* Process-wide; not synchronised with calls in flight.  rows < 0:          */
+/* VQ_ERR_INVALID_ARG.                                                      */
+/* ---------------------------------------------------------------------- */
+vq_status vq_set_gemm_row_block(int64_t rows);
+
+/* ---------------------------------------------------------------------- */
 /* Routed-expert grouped GEMM (MUL_MAT_ID, broadcast arm) with the weighted  */
 /* expert sum ([P3] "routed-compact J rule" and "weighted expert sum";     */
 /* [P2] "grouped Q8_0 delegation": every weight type, Q8_0 paired with a    */

@@ -178,6 +178,18 @@ def test_small_batch_crossover_setting(vq):
             vq.set_small_batch_max(w, -1)
 
 
+def test_gemm_row_block_setting(vq):
+    """vq_set_gemm_row_block: 0 and positive caps accepted, negative rejected
+    (host only; the blocked launches are checked against one launch on the GPU)."""
+    try:
+        vq.set_gemm_row_block(200)
+        vq.set_gemm_row_block(0)
+        with pytest.raises(vq.VQError, match="INVALID_ARG"):
+            vq.set_gemm_row_block(-1)
+    finally:
+        vq.set_gemm_row_block(0)
+
+
 def test_gemv_rejects_rows_too_long_for_lds(vq):
     """The fused GEMV keeps a weight row and the quantized activation in LDS:
     K past that limit is a shape error, checked on the host before any

@@ -195,6 +195,39 @@ def test_gemm_large_tile_ragged(wtype):
 
 
 @pytest.mark.parametrize("wtype", WTYPES)
+def test_gemm_row_blocks(wtype):
+    """The MFMA GEMM split into launches of at most 200 or 256 activation rows
+    (the path vq_gemm takes when one launch would address 2^31 activation
+    bytes) gives the bytes of the single launch, on the large-tile grid with a
+    ragged last block; sampled outputs bit-identical to the oracle."""
+    M, N, K = 600, 16400, 512
+    W = synth.normal(1380 + wtype, (N, K), 0.02)
+    X = synth.normal(1390 + wtype, (M, K))
+    Wq = oracle.quantize_weights(wtype, W)
+    act = oracle_act(wtype, X)
+    at = vq.Q8_1 if wtype == oracle.Q8_0 else vq.Q8_K
+    Wd, Xd = H.to_dev(Wq), H.to_dev(H.pack_act(act, wtype))
+    outs = []
+    try:
+        for rows in (0, 200, 256):
+            H.say("gemm row blocks %s rows=%d M=%d N=%d K=%d" % (WNAME[wtype], rows, M, N, K))
+            vq.set_gemm_row_block(rows)
+            Yd = H.to_dev(np.full((M, N), np.nan, np.float32))
+            vq.gemm(wtype, Wd, N, K, at, Xd, M, Y=Yd)
+            outs.append(H.host(Yd))
+    finally:
+        vq.set_gemm_row_block(0)
+    assert np.isfinite(outs[0]).all()
+    for Y in outs[1:]:
+        H.assert_bitwise(Y, outs[0], "gemm row blocks %s" % WNAME[wtype])
+    rng = np.random.default_rng(1395)
+    ms = np.concatenate([np.arange(M), rng.integers(0, M, 2000)]).astype(np.int64)
+    ns = np.concatenate([rng.integers(0, N, M), rng.integers(0, N, 2000)]).astype(np.int64)
+    ref = oracle.gemm_sampled(wtype, Wq, N, K, act, ms, ns, nthreads=8)
+    H.assert_bitwise(outs[1][ms, ns], ref, "gemm row blocks %s vs oracle" % WNAME[wtype])
+
+
+@pytest.mark.parametrize("wtype", WTYPES)
 def test_gemm_from_device_quantizer(wtype):
     """GPU quantize_act feeding GPU GEMM, decode-through-prefill M values."""
     N, K = 128, 512 if wtype != oracle.Q8_0 else 544
