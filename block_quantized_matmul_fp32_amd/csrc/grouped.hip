@@ -76,11 +76,26 @@ __global__ __launch_bounds__(64) void route_count_kernel(const int32_t* __restri
     const int64_t p0 = (int64_t)c * kRouteChunk * top_k;
     const int np = min(kRouteChunk, T - c * kRouteChunk) * top_k;
     for (int e = lane; e < E; e += 64) cnt[e] = 0;
+    // The chunk's ids are requested up front, kIdBatch rounds of 64 at a time,
+    // so the rounds do not wait on one global load each.
+    constexpr int kIdBatch = 8;
+    int idv[kIdBatch];
     __syncthreads();
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (int base = 0; base < np; base += 64) {
+        const int j = (base / 64) % kIdBatch;
+        if (j == 0) {
+#pragma unroll
+            for (int k = 0; k < kIdBatch; ++k) {
+                const int ik = base + 64 * k + lane;
+                idv[k] = (ik < np) ? ids[p0 + ik] : -1;
+            }
+        }
         const int i = base + lane;
-        const int e = (i < np) ? ids[p0 + i] : -1;
+        int e = -1;
+#pragma unroll
+        for (int k = 0; k < kIdBatch; ++k)
+            if (k == j) e = idv[k];
         const bool ok = (i < np) && e >= 0 && e < E;
         const int key = ok ? e : 1024 + lane;  // a pair not routed matches no other lane
         uint64_t same = ~0ull;
@@ -125,7 +140,19 @@ __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(int nchunks, i
     const bool staged = ncell <= kScanStageCells;
     int32_t* tab = staged ? cstage : chunk;
     if (staged) {
-        for (int64_t i = tid; i < ncell; i += kScanThreads) cstage[i] = chunk[i];
+        // all of a thread's loads in flight before its first LDS store
+        constexpr int kMaxPer = (int)((kScanStageCells + kScanThreads - 1) / kScanThreads);
+        int32_t v[kMaxPer];
+#pragma unroll
+        for (int k = 0; k < kMaxPer; ++k) {
+            const int64_t i = tid + (int64_t)k * kScanThreads;
+            v[k] = (i < ncell) ? chunk[i] : 0;
+        }
+#pragma unroll
+        for (int k = 0; k < kMaxPer; ++k) {
+            const int64_t i = tid + (int64_t)k * kScanThreads;
+            if (i < ncell) cstage[i] = v[k];
+        }
         __syncthreads();
     }
     int sum = 0;
