@@ -706,10 +706,11 @@ hipError_t launch_gemm(int wtype, const uint8_t* W, int64_t N, int64_t K, const 
     return launch_gemm_t<2>(W, N, K, act_qs, act_d, act_aux, M, Y, ldy, st);
 }
 
-// Grouped launch: one 64 x 64 tile per (weight-row block, routed tile); a
-// routed tile holds up to 64 rows of one expert, and waves whose rows are all
-// past the tile's rows skip their MFMAs.
+// Grouped launch: one 64 x kGroupTileRows tile per (weight-row block, routed
+// tile) on four waves; a routed tile holds up to kGroupTileRows rows of one
+// expert, and waves whose rows are all past the tile's rows skip their MFMAs.
 constexpr int kGroupBM = kGroupTileRows;
+static_assert(kGroupBM % 32 == 0, "two rows of waves, each wave 16 * (kGroupBM / 32) activation rows");
 
 template <int WT>
 static hipError_t launch_gemm_grouped_t(const uint8_t* W, int64_t E, int64_t N, int64_t K, const void* aqs,
