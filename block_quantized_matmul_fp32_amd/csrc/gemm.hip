@@ -137,9 +137,11 @@ __global__ __launch_bounds__(128 * WM, 2) void gemm_kernel(const uint8_t* __rest
     constexpr int NT = 128 * WM;           // threads
     constexpr int BM = 16 * TM * WM;       // activation rows per workgroup
     constexpr int ACH = BM * 16 / NT;      // 16-byte activation chunks per thread per step
-    constexpr int NU = (NT < 512) ? NT : 512;  // threads that load and unpack weights
+    constexpr int NU = (NT >= 512) ? 512 : ((NT >= 256) ? 256 : NT);  // threads that load and unpack weights
     constexpr int UPR = NU / kBN;          // threads per weight row
     constexpr int PPT = 8 / UPR;           // 16-byte pieces per thread
+    static_assert(UPR * PPT == 8, "a weight row's eight 16-byte pieces are split evenly");
+    static_assert((BM * 16) % NT == 0, "activation chunks are split evenly");
     __shared__ __attribute__((aligned(16))) int8_t sA[BM * kLD];
     __shared__ __attribute__((aligned(16))) int8_t sW[P * kBN * kLD];
     // Scales, double-buffered by step parity (a late wave combines step s - 1
@@ -676,24 +678,48 @@ static hipError_t launch_gemm_cfg(const uint8_t* W, int64_t N, int64_t K, const 
     return hipSuccess;
 }
 
-// Tile choice: 64 x 256 tiles unless they would leave CUs without a
-// workgroup (then 64 x 128 tiles on the same eight waves, twice the
-// workgroups); Q8_0, whose per-block epilogue dominates, always takes the
-// 64 x 128 tiles (measured faster at every workload shape).  Q6_K runs its
-// 64 x 256 tiles on sixteen waves of 32 x 32 (four per SIMD, 128 VGPRs):
-// with three planes its waves wait longest on LDS and MFMA results, and the
-// extra waves cover that (9% faster at M = 2048); Q4_K and Q5_K measured
-// slower that way (register spills).  (64 x 64 tiles for still smaller grids
-// measured no faster: the time of a column tile is its sequence of
-// super-block steps, not the number of tiles.)
+// Tile choice (weight rows x activation rows): 64 x 256, 64 x 192 or 64 x 128,
+// whichever gives the least estimated time = workgroup rounds (workgroups /
+// CUs, rounded up: one workgroup per CU) x the relative time of one
+// workgroup of that height.  The relative times, per mille of the 64 x 256
+// workgroup, were measured on the prefill shapes:
+//   Q4_K / Q5_K (eight waves of 32 x 64, 32 x 48, 32 x 32): 1000, 856, 610;
+//   Q6_K (sixteen, twelve, eight waves of 32 x 32):           1000, 905, 850.
+// So a grid that would leave a mostly empty last round takes the shorter
+// tiles: Q4_K at M = 512 (304 workgroups of 64 x 256 on 256 CUs; 64 x 192:
+// 14% faster) and Q6_K at M = 2048 (320 workgroups; 64 x 192: 9% faster).
+// Ties go to the taller tile.  Q8_0, whose per-block epilogue dominates,
+// always takes 64 x 128 tiles (measured faster at every workload shape).
+// Q6_K runs on 32 x 32 waves (four per SIMD at 64 x 256): with three planes
+// its waves wait longest on LDS and MFMA results, and the extra waves cover
+// that; Q4_K and Q5_K measured slower that way (register spills).  (64 x 64
+// tiles for still smaller grids measured no faster: the time of a column
+// tile is its sequence of super-block steps, not the number of tiles.)
 template <int WT>
 static hipError_t launch_gemm_t(const uint8_t* W, int64_t N, int64_t K, const void* aqs, const void* ad,
                                 const void* aux, int64_t M, float* Y, int64_t ldy, hipStream_t st) {
-    const int cus = num_cus();
-    const int64_t wg256 = ((N + kBN - 1) / kBN) * ((M + 255) / 256);
-    if (WT == 2 || wg256 < cus) return launch_gemm_cfg<WT, 4, 2>(W, N, K, aqs, ad, aux, M, Y, ldy, st);
-    if constexpr (WT == 1) return launch_gemm_cfg<WT, 8, 2>(W, N, K, aqs, ad, aux, M, Y, ldy, st);
-    else return launch_gemm_cfg<WT, 4, 4>(W, N, K, aqs, ad, aux, M, Y, ldy, st);
+    if constexpr (WT == 2) {
+        return launch_gemm_cfg<WT, 4, 2>(W, N, K, aqs, ad, aux, M, Y, ldy, st);
+    } else {
+        const int64_t cus = num_cus();
+        const int64_t ncol = (N + kBN - 1) / kBN;
+        auto cost = [&](int64_t bm, int64_t rel) {
+            const int64_t wg = ncol * ((M + bm - 1) / bm);
+            return ((wg + cus - 1) / cus) * rel;
+        };
+        const int64_t t256 = cost(256, 1000);
+        const int64_t t192 = cost(192, WT == 1 ? 905 : 856);
+        const int64_t t128 = cost(128, WT == 1 ? 850 : 610);
+        if (t256 <= t192 && t256 <= t128) {
+            if constexpr (WT == 1) return launch_gemm_cfg<WT, 8, 2>(W, N, K, aqs, ad, aux, M, Y, ldy, st);
+            else return launch_gemm_cfg<WT, 4, 4>(W, N, K, aqs, ad, aux, M, Y, ldy, st);
+        }
+        if (t192 <= t128) {
+            if constexpr (WT == 1) return launch_gemm_cfg<WT, 6, 2>(W, N, K, aqs, ad, aux, M, Y, ldy, st);
+            else return launch_gemm_cfg<WT, 4, 3>(W, N, K, aqs, ad, aux, M, Y, ldy, st);
+        }
+        return launch_gemm_cfg<WT, 4, 2>(W, N, K, aqs, ad, aux, M, Y, ldy, st);
+    }
 }
 
 hipError_t launch_gemm(int wtype, const uint8_t* W, int64_t N, int64_t K, const void* act_qs,

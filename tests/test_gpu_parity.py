@@ -172,14 +172,22 @@ def test_gemm_bitexact(wtype):
     assert ref_fp64.max_rel_err(Yh[:, :N], r)[0] <= REL_MAX
 
 
-@pytest.mark.parametrize("wtype", [oracle.Q4_K, oracle.Q6_K, oracle.Q5_K])
-def test_gemm_large_tile_ragged(wtype):
-    """Enough column tiles that the 64 x 256 tile configuration runs, with a
-    ragged last row tile (M = 300) and column tile (N % 64 = 16); every
-    output written, sampled outputs bit-identical to the oracle."""
-    M, N, K = 300, 16400, 512
+# (weight type, M): with N = 16400 (257 column tiles) on 256 CUs the tile
+# choice takes 64 x 256 tiles at M = 700, 64 x 192 at M = 1100 (Q4_K, Q5_K)
+# or 300 (Q6_K), and 64 x 128 at M = 300 (Q4_K, Q5_K) or 100 (Q6_K); each
+# leaves a ragged last row tile.
+LARGE_TILE_CASES = [(w, M) for w in (oracle.Q4_K, oracle.Q5_K) for M in (700, 1100, 300)] + \
+                   [(oracle.Q6_K, M) for M in (700, 300, 100)]
+
+
+@pytest.mark.parametrize("wtype,M", LARGE_TILE_CASES)
+def test_gemm_large_tile_ragged(wtype, M):
+    """Enough column tiles for the tall tile configurations, with a ragged
+    last row tile and column tile (N % 64 = 16); every output written,
+    sampled outputs bit-identical to the oracle."""
+    N, K = 16400, 512
     W = synth.normal(1350 + wtype, (N, K), 0.02)
-    X = synth.normal(1360 + wtype, (M, K))
+    X = synth.normal(1360 + wtype + M, (M, K))
     Wq = oracle.quantize_weights(wtype, W)
     act = oracle_act(wtype, X)
     H.say("gemm large tile %s M=%d N=%d K=%d" % (WNAME[wtype], M, N, K))
