@@ -479,6 +479,25 @@ def test_grouped_types_and_arms(wtype, per_row):
     assert st[key] == 1 and st["gemm_grouped_rows"] == int(per_row) and st["route"] == 1
 
 
+def test_grouped_route_unstaged_scan():
+    """Many experts and tokens (1000 x top-4 over 1024 experts): the routing
+    scan's chunk table (16 chunks x 1024 experts) is too large to stage in
+    LDS, so the scan reads and writes it in global memory; routing and Y
+    bit-identical to the oracle."""
+    E, N, K, T, top_k = 1024, 16, 256, 1000, 4
+    ids = synth.random_ids(1880, T, E, top_k)
+    Wq, act, rw, Y, Ysum, ws = run_grouped(E, N, K, T, top_k, ids, 1890)
+    counts, offsets, lst = vq.grouped_ws_views(ws, E, T, top_k)
+    c_ref, o_ref, l_ref = oracle.route(ids, E)
+    assert np.array_equal(H.host(counts), c_ref)
+    assert np.array_equal(H.host(offsets), o_ref)
+    assert np.array_equal(H.host(lst), l_ref)
+    Y_ref = oracle.gemm_grouped(oracle.Q4_K, Wq, E, N, K, act, ids, nthreads=8)
+    Yh = H.host(Y)
+    H.assert_bitwise(Yh, Y_ref, "grouped Y (unstaged routing scan)")
+    H.assert_bitwise(H.host(Ysum), oracle.weighted_sum(Yh, rw), "weighted sum of the GPU's Y")
+
+
 def test_grouped_expert_permutation():
     """Permuting expert storage and remapping ids gives the same Y bitwise."""
     E, N, K, T, top_k = 12, 64, 256, 40, 3
