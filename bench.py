@@ -151,10 +151,22 @@ def run_cpu_baseline(seconds: float):
         if el >= seconds or reps >= 100000:
             break
     return {"value": round(step_bytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": "%d repetitions of the full decode step (Q8_K quantization of x plus the Q4_K "
                       "[9728,2560] and Q6_K [2560,9728] GEMVs) in %.1f s with %d threads" % (reps, el, threads),
             "ms_per_step": round(1e3 * el / reps, 3)}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (first entry of /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def decode_step_bytes():
