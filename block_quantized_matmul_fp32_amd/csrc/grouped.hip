@@ -257,6 +257,7 @@ hipError_t launch_route(const int32_t* ids, int64_t T, int64_t top_k, int64_t E,
 
 // Ysum[t][n..n+3] = (((w0*y0 + w1*y1) + w2*y2) + ...): one thread per four
 // adjacent channels.
+constexpr int kSumPre = 8;  // slots whose loads are all issued before the first product
 __global__ __launch_bounds__(256) void weighted_sum_kernel(const float* __restrict__ Y,
                                                            const float* __restrict__ w, int T, int top_k,
                                                            int N, float* __restrict__ Ysum) {
@@ -267,13 +268,29 @@ __global__ __launch_bounds__(256) void weighted_sum_kernel(const float* __restri
     const int n = (int)(q - t * n4) * 4;
     const float* yp = Y + t * top_k * (int64_t)N + n;
     const float* wp = w + t * top_k;
-    float4 v = *(const float4*)yp;
-    float w0 = wp[0];
-    float a0 = w0 * v.x, a1 = w0 * v.y, a2 = w0 * v.z, a3 = w0 * v.w;
-    for (int s = 1; s < top_k; ++s) {
-        const float4 u = *(const float4*)(yp + (int64_t)s * N);
-        const float ws = wp[s];
-        const float p0 = ws * u.x, p1 = ws * u.y, p2 = ws * u.z, p3 = ws * u.w;
+    // the first kSumPre slots' channels and weights requested before the
+    // first product; later slots (top_k > kSumPre) follow one at a time
+    float4 u[kSumPre];
+    float ws[kSumPre];
+#pragma unroll
+    for (int s = 0; s < kSumPre; ++s) {
+        if (s < top_k) {
+            u[s] = *(const float4*)(yp + (int64_t)s * N);
+            ws[s] = wp[s];
+        }
+    }
+    float a0 = ws[0] * u[0].x, a1 = ws[0] * u[0].y, a2 = ws[0] * u[0].z, a3 = ws[0] * u[0].w;
+#pragma unroll
+    for (int s = 1; s < kSumPre; ++s) {
+        if (s < top_k) {
+            const float p0 = ws[s] * u[s].x, p1 = ws[s] * u[s].y, p2 = ws[s] * u[s].z, p3 = ws[s] * u[s].w;
+            a0 = a0 + p0; a1 = a1 + p1; a2 = a2 + p2; a3 = a3 + p3;
+        }
+    }
+    for (int s = kSumPre; s < top_k; ++s) {
+        const float4 v = *(const float4*)(yp + (int64_t)s * N);
+        const float wv = wp[s];
+        const float p0 = wv * v.x, p1 = wv * v.y, p2 = wv * v.z, p3 = wv * v.w;
         a0 = a0 + p0; a1 = a1 + p1; a2 = a2 + p2; a3 = a3 + p3;
     }
     *(float4*)(Ysum + t * (int64_t)N + n) = make_float4(a0, a1, a2, a3);

@@ -514,10 +514,13 @@ def test_grouped_expert_permutation():
     H.assert_bitwise(H.host(Y2), H.host(Y), "permuted experts")
 
 
-def test_weighted_sum_standalone():
-    T, top_k, N = 33, 8, 512
-    Y = synth.normal(2000, (T, top_k, N))
-    w = synth.normal(2001, (T, top_k))
+@pytest.mark.parametrize("top_k", [8, 3, 20])
+def test_weighted_sum_standalone(top_k):
+    """Slot-ordered sum, bit-identical to the oracle, with top_k below, at and
+    above the eight slots whose loads the kernel issues up front."""
+    T, N = 33, 512
+    Y = synth.normal(2000 + top_k, (T, top_k, N))
+    w = synth.normal(2001 + top_k, (T, top_k))
     H.say("weighted sum T=%d top_k=%d N=%d" % (T, top_k, N))
     S = vq.weighted_sum(H.to_dev(Y), H.to_dev(w), T, top_k, N)
     H.assert_bitwise(H.host(S), oracle.weighted_sum(Y, w), "weighted sum")
