@@ -115,7 +115,12 @@ struct GroupArgs {
     int top_k;
     int per_row;            // 1: pair p reads activation row p (per-row arm); 0: row p / top_k
     int64_t expert_stride;  // bytes of one expert's [N][K/QK] blocks
+    int tile_base;          // routed tile of blockIdx.y = 0 (launches of at most kMaxGridY tiles)
 };
+
+// Most workgroup rows (gridDim.y) per launch; larger grids run as several
+// launches.
+constexpr int64_t kMaxGridY = 32768;
 
 // Workgroup of 2 x WM waves (128 * WM threads) computing a 64 x (16 * TM * WM)
 // output tile; each wave owns 32 weight rows x 16 * TM activation rows
@@ -163,7 +168,7 @@ __global__ __launch_bounds__(128 * WM, 2) void gemm_kernel(const uint8_t* __rest
     const uint8_t* W = Wbase;
     int rows_here;  // valid activation rows of this tile
     if (kGrouped) {
-        const int tix = blockIdx.y;
+        const int tix = ga.tile_base + (int)blockIdx.y;
         if (tix >= *ga.ntiles) return;
         const int e = ga.tiles[4 * tix + 0];
         const int first = ga.tiles[4 * tix + 1];
@@ -659,6 +664,7 @@ static hipError_t launch_gemm_cfg(const uint8_t* W, int64_t N, int64_t K, const 
     // 32-bit activation offsets); one launch for every practical shape.
     int64_t rows_max = ((int64_t(1) << 31) / K) / BM * BM;
     if (rows_max < BM) return hipErrorInvalidValue;
+    rows_max = std::min(rows_max, kMaxGridY * BM);
     const int64_t rb = g_row_block.load();
     if (rb > 0) rows_max = std::min(rows_max, rb);
     // bytes per activation row in the planar planes: per block a binary32 d
@@ -746,7 +752,6 @@ static hipError_t launch_gemm_grouped_t(const uint8_t* W, int64_t E, int64_t N, 
     const int64_t estride = N * (int64_t)nbw * GemmCfg<WT>::BB;
     const int64_t max_tiles = (T * top_k + kGroupBM - 1) / kGroupBM + E;
     if (max_tiles == 0) return hipSuccess;
-    dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)max_tiles);
     GroupArgs ga;
     ga.tiles = ws.tiles;
     ga.ntiles = ws.ntiles;
@@ -754,9 +759,18 @@ static hipError_t launch_gemm_grouped_t(const uint8_t* W, int64_t E, int64_t N, 
     ga.top_k = (int)top_k;
     ga.per_row = per_row;
     ga.expert_stride = estride;
-    gemm_kernel<WT, 2, kGroupBM / 32, true><<<grid, 256, 0, st>>>(
-        W, (int)N, (int)K, E * estride, (const int8_t*)aqs, ad, (const int16_t*)aux, (int)T, Y, N * 1, ga);
-    return hipGetLastError();
+    int64_t per = kMaxGridY;  // routed tiles per launch
+    const int64_t rb = g_row_block.load();
+    if (rb > 0) per = std::min(per, std::max<int64_t>(1, rb / kGroupBM));
+    for (int64_t t0 = 0; t0 < max_tiles; t0 += per) {
+        ga.tile_base = (int)t0;
+        dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)std::min(per, max_tiles - t0));
+        gemm_kernel<WT, 2, kGroupBM / 32, true><<<grid, 256, 0, st>>>(
+            W, (int)N, (int)K, E * estride, (const int8_t*)aqs, ad, (const int16_t*)aux, (int)T, Y, N * 1, ga);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_gemm_grouped(int wtype, const uint8_t* W, int64_t E, int64_t N, int64_t K, const void* act_qs,

@@ -240,9 +240,12 @@ int64_t vq_small_batch_max(int w);
 /* Row blocks of the MFMA arm of vq_gemm.  The GEMM kernel addresses the    */
 /* activation bytes of one launch with 32-bit offsets, so vq_gemm launches  */
 /* it once per block of at most floor(2^31 / K) rows (rounded down to the   */
-/* tile height), which is one launch for every practical shape.  rows > 0   */
-/* caps the block at that many rows (any value; for tests of the blocking); */
-/* 0 restores the default.  The result does not depend on the blocking.     */
+/* tile height) and at most 32768 tile rows, which is one launch for every  */
+/* practical shape; the grouped calls likewise launch their GEMM once per   */
+/* 32768 routed tiles.  rows > 0 caps the block at that many rows (any      */
+/* value; for tests of the blocking) and the grouped launches at           */
+/* max(1, rows / 96) routed tiles of 96 rows; 0 restores the default.  The  */
+/* results do not depend on the blocking.                                   */
 /* Process-wide; not synchronised with calls in flight.  rows < 0:          */
 /* VQ_ERR_INVALID_ARG.                                                      */
 /* ---------------------------------------------------------------------- */

@@ -498,6 +498,28 @@ def test_grouped_route_unstaged_scan():
     H.assert_bitwise(H.host(Ysum), oracle.weighted_sum(Yh, rw), "weighted sum of the GPU's Y")
 
 
+@pytest.mark.parametrize("per_row", [False, True])
+def test_grouped_tile_launches(per_row):
+    """The grouped GEMM split into launches of one or two routed tiles (the
+    row-block hook; large calls launch once per 32768 tiles) gives the bytes of
+    the single launch, and they match the oracle."""
+    E, N, K, T, top_k = 12, 64, 512, 150, 4
+    ids = synth.random_ids(1870, T, E, top_k)
+    outs = []
+    try:
+        for rows in (0, 96, 200):
+            vq.set_gemm_row_block(rows)
+            Wq, act, rw, Y, Ysum, ws = run_grouped(E, N, K, T, top_k, ids, 1875, per_row=per_row)
+            outs.append((H.host(Y), H.host(Ysum)))
+    finally:
+        vq.set_gemm_row_block(0)
+    for Yb, Sb in outs[1:]:
+        H.assert_bitwise(Yb, outs[0][0], "grouped tile launches Y")
+        H.assert_bitwise(Sb, outs[0][1], "grouped tile launches Ysum")
+    Y_ref = oracle.gemm_grouped(oracle.Q4_K, Wq, E, N, K, act, ids, nthreads=8, per_row=per_row)
+    H.assert_bitwise(outs[1][0], Y_ref, "grouped tile launches vs oracle")
+
+
 def test_grouped_expert_permutation():
     """Permuting expert storage and remapping ids gives the same Y bitwise."""
     E, N, K, T, top_k = 12, 64, 256, 40, 3
