@@ -146,6 +146,49 @@ def test_gemv_edge_rows(wtype):
         H.assert_bitwise(H.host(y), y_ref, "gemv edge %s N=%d K=%d" % (WNAME[wtype], N, K))
 
 
+def gemv_max_k(wtype):
+    """Largest K the fused GEMV accepts (its weight row and quantized x must
+    fit LDS), found from the library's host-side shape check, which rejects
+    an oversized K before it looks at any pointer."""
+    L = vq.lib()
+    qk = 32 if wtype == oracle.Q8_0 else 256
+    lo, hi = 1, 1 << 20  # blocks
+    while lo < hi:
+        mid = (lo + hi + 1) // 2
+        if L.vq_gemv(wtype, None, 1, mid * qk, None, None, None, None) == 4:  # VQ_ERR_SHAPE
+            hi = mid - 1
+        else:
+            lo = mid
+    return lo * qk
+
+
+@pytest.mark.parametrize("wtype", WTYPES)
+def test_gemv_max_k(wtype):
+    """The GEMV at the largest accepted K (one row per workgroup, LDS nearly
+    full), N = 1 and N = 300, and a three-row batch at that K (the GEMV
+    kernel if its rows fit, else the MFMA GEMM): bit-identical to the oracle;
+    one block more is a shape error."""
+    K = gemv_max_k(wtype)
+    qk = 32 if wtype == oracle.Q8_0 else 256
+    assert K >= 32768
+    assert vq.lib().vq_gemv(wtype, None, 1, K + qk, None, None, None, None) == 4
+    N = 300
+    W = synth.normal((1250, wtype), (N, K), 0.02)
+    X = synth.normal((1251, wtype), (3, K))
+    Wq = oracle.quantize_weights(wtype, W)
+    Wd = H.to_dev(Wq)
+    act = oracle_act(wtype, X)
+    Y_ref = oracle.gemm(wtype, Wq, N, K, act, nthreads=8)
+    for n in (1, N):
+        H.say("gemv max K %s N=%d K=%d" % (WNAME[wtype], n, K))
+        y = vq.gemv(wtype, Wd[:n] if n == 1 else Wd, n, K, H.to_dev(X[0]))
+        H.assert_bitwise(H.host(y), Y_ref[0, :n], "gemv max K %s N=%d" % (WNAME[wtype], n))
+    H.say("gemm M=3 at max K %s K=%d" % (WNAME[wtype], K))
+    at = vq.Q8_1 if wtype == oracle.Q8_0 else vq.Q8_K
+    Y = vq.gemm(wtype, Wd, N, K, at, H.to_dev(H.pack_act(act, wtype)), 3)
+    H.assert_bitwise(H.host(Y), Y_ref, "gemm M=3 at max K %s" % WNAME[wtype])
+
+
 # ------------------------------------------------------------------ GEMM
 GEMM_SHAPES = {oracle.Q4_K: (150, 200, 1024), oracle.Q6_K: (150, 200, 1024), oracle.Q8_0: (150, 200, 2080),
                oracle.Q5_K: (150, 200, 1024)}
