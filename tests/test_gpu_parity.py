@@ -245,6 +245,31 @@ def test_gemm_large_tile_ragged(wtype, M):
     H.assert_bitwise(Yh[ms, ns], ref, "gemm large tile %s" % WNAME[wtype])
 
 
+@pytest.mark.parametrize("wtype,M,N,K", [(oracle.Q4_K, 700, 16400, 256), (oracle.Q5_K, 700, 16400, 256),
+                                          (oracle.Q6_K, 700, 16400, 256), (oracle.Q8_0, 300, 200, 32),
+                                          (oracle.Q8_0, 300, 200, 96)])
+def test_gemm_single_step(wtype, M, N, K):
+    """K of one super-block (one Q8_0 block, or three: a partial step): the
+    tall tiles' late-epilogue waves combine their only step after the loop;
+    sampled outputs (whole first and last rows and columns) bit-identical to
+    the oracle."""
+    W = synth.normal((1460, wtype, K), (N, K), 0.02)
+    X = synth.normal((1461, wtype, K), (M, K))
+    Wq = oracle.quantize_weights(wtype, W)
+    act = oracle_act(wtype, X)
+    at = vq.Q8_1 if wtype == oracle.Q8_0 else vq.Q8_K
+    H.say("gemm single step %s M=%d N=%d K=%d" % (WNAME[wtype], M, N, K))
+    Yd = H.to_dev(np.full((M, N), np.nan, np.float32))
+    vq.gemm(wtype, H.to_dev(Wq), N, K, at, H.to_dev(H.pack_act(act, wtype)), M, Y=Yd)
+    Yh = H.host(Yd)
+    assert np.isfinite(Yh).all()
+    rng = np.random.default_rng(1462)
+    ms = np.concatenate([np.arange(M), rng.integers(0, M, 2000), np.full(N, M - 1)]).astype(np.int64)
+    ns = np.concatenate([np.full(M, N - 1), rng.integers(0, N, 2000), np.arange(N)]).astype(np.int64)
+    ref = oracle.gemm_sampled(wtype, Wq, N, K, act, ms, ns, nthreads=8)
+    H.assert_bitwise(Yh[ms, ns], ref, "gemm single step %s K=%d" % (WNAME[wtype], K))
+
+
 @pytest.mark.parametrize("wtype", WTYPES)
 def test_gemm_row_blocks(wtype):
     """The MFMA GEMM split into launches of at most 200 or 256 activation rows
