@@ -588,6 +588,29 @@ def test_grouped_tile_launches(per_row):
     H.assert_bitwise(outs[1][0], Y_ref, "grouped tile launches vs oracle")
 
 
+@pytest.mark.parametrize("E,top_k", [(1, 1), (4, 4)])
+def test_grouped_degenerate_routing(E, top_k):
+    """One expert at top-1 (the grouped call is the dense GEMM of that expert,
+    over several routed tiles) and top_k = E (every token in every expert):
+    routing, Y and the weighted sum bit-identical to the oracle."""
+    N, K, T = 64, 512, 300
+    ids = np.tile(np.arange(top_k, dtype=np.int32), (T, 1))
+    if E > 1:
+        ids = synth.random_ids(1920, T, E, top_k)  # a permutation of all E per token
+    Wq, act, rw, Y, Ysum, ws = run_grouped(E, N, K, T, top_k, ids, 1925)
+    counts, offsets, lst = vq.grouped_ws_views(ws, E, T, top_k)
+    c_ref, o_ref, l_ref = oracle.route(ids, E)
+    assert np.array_equal(H.host(counts), c_ref) and np.array_equal(H.host(lst), l_ref)
+    assert (H.host(counts) == T).all()
+    Y_ref = oracle.gemm_grouped(oracle.Q4_K, Wq, E, N, K, act, ids, nthreads=8)
+    Yh = H.host(Y)
+    H.assert_bitwise(Yh, Y_ref, "grouped degenerate E=%d top_k=%d" % (E, top_k))
+    H.assert_bitwise(H.host(Ysum), oracle.weighted_sum(Yh, rw), "weighted sum of the GPU's Y")
+    if E == 1:
+        dense = vq.gemm(vq.Q4_K, H.to_dev(Wq), N, K, vq.Q8_K, H.to_dev(H.pack_act(act, oracle.Q4_K)), T)
+        H.assert_bitwise(Yh[:, 0, :], H.host(dense), "grouped E=1 vs dense GEMM")
+
+
 def test_grouped_expert_permutation():
     """Permuting expert storage and remapping ids gives the same Y bitwise."""
     E, N, K, T, top_k = 12, 64, 256, 40, 3
