@@ -103,11 +103,42 @@ def _check(status: int):
         raise VQError(status, lib().vq_last_error().decode())
 
 
-def _ptr(t):
-    if t is None:
-        return None
-    if isinstance(t, int):
+def _on_gpu(t, name):
+    if t.device.type != "cuda":
+        raise ValueError("%s is on %s: the library takes GPU device memory" % (name, t.device))
+
+
+def _dev(t, name, nbytes=None, dtype=None):
+    """Device address of a dense buffer argument.  A tensor must be on a GPU,
+    contiguous, of the given dtype and at least nbytes long, so that the
+    kernels never touch memory outside it; None and raw integer addresses
+    pass through unchecked."""
+    if t is None or isinstance(t, int):
         return t
+    _on_gpu(t, name)
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s has dtype %s, %s expected" % (name, t.dtype, dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s is not contiguous" % name)
+    if nbytes is not None and t.numel() * t.element_size() < nbytes:
+        raise ValueError("%s holds %d bytes, %d needed" % (name, t.numel() * t.element_size(), nbytes))
+    return t.data_ptr()
+
+
+def _dev_rows(t, name, M, K, ld, dtype=None):
+    """Device address of a row-strided fp32 argument (rows of K values, ld
+    apart): on a GPU, unit stride inside a row, and (M - 1) * ld + K values
+    inside the tensor's storage."""
+    if t is None or isinstance(t, int):
+        return t
+    _on_gpu(t, name)
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s has dtype %s, %s expected" % (name, t.dtype, dtype))
+    if t.dim() >= 1 and t.numel() > 1 and t.stride(-1) != 1:
+        raise ValueError("%s: the values of a row must be contiguous" % name)
+    avail = t.untyped_storage().nbytes() // t.element_size() - t.storage_offset()
+    if M > 0 and (M - 1) * ld + K > avail:
+        raise ValueError("%s: %d rows of %d values, %d apart, do not fit its storage" % (name, M, K, ld))
     return t.data_ptr()
 
 
@@ -194,7 +225,9 @@ def quantize_act(act: int, X, M: int = None, K: int = None, ldx: int = None, Xq=
         ldx = K if X.dim() == 1 or X.shape[0] == 1 else X.stride(0)
     if Xq is None:
         Xq = _torch().empty(act_bytes(act, M, K), dtype=_torch().uint8, device=X.device)
-    _check(lib().vq_quantize_act(act, _ptr(X), M, K, ldx, _ptr(Xq), _stream(stream)))
+    f32, u8 = _torch().float32, _torch().uint8
+    _check(lib().vq_quantize_act(act, _dev_rows(X, "X", M, K, ldx, f32), M, K, ldx,
+                                 _dev(Xq, "Xq", act_bytes(act, M, K), u8), _stream(stream)))
     return Xq
 
 
@@ -219,8 +252,10 @@ def rmsnorm_quant(act: int, X, gamma, eps: float = 1e-6, M: int = None, K: int =
         ldy = K if Y is None or Y.dim() == 1 or Y.shape[0] == 1 else Y.stride(0)
     if Xq is None:
         Xq = torch.empty(act_bytes(act, M, K), dtype=torch.uint8, device=X.device)
-    _check(lib().vq_rmsnorm_quant(act, _ptr(X), _ptr(gamma), M, K, ldx, float(eps), _ptr(Y), ldy, _ptr(Xq),
-                                  _stream(stream)))
+    f32 = torch.float32
+    _check(lib().vq_rmsnorm_quant(act, _dev_rows(X, "X", M, K, ldx, f32), _dev(gamma, "gamma", 4 * K, f32), M, K,
+                                  ldx, float(eps), _dev_rows(Y, "Y", M, K, ldy, f32), ldy,
+                                  _dev(Xq, "Xq", act_bytes(act, M, K), torch.uint8), _stream(stream)))
     return Y, Xq
 
 
@@ -236,7 +271,10 @@ def silu_mul_quant(act: int, G, U, M: int = None, K: int = None, ldx: int = None
         ldy = K if Y is None or Y.dim() == 1 or Y.shape[0] == 1 else Y.stride(0)
     if Xq is None:
         Xq = torch.empty(act_bytes(act, M, K), dtype=torch.uint8, device=G.device)
-    _check(lib().vq_silu_mul_quant(act, _ptr(G), _ptr(U), M, K, ldx, _ptr(Y), ldy, _ptr(Xq), _stream(stream)))
+    f32 = torch.float32
+    _check(lib().vq_silu_mul_quant(act, _dev_rows(G, "G", M, K, ldx, f32), _dev_rows(U, "U", M, K, ldx, f32), M, K,
+                                   ldx, _dev_rows(Y, "Y", M, K, ldy, f32), ldy,
+                                   _dev(Xq, "Xq", act_bytes(act, M, K), torch.uint8), _stream(stream)))
     return Y, Xq
 
 
@@ -246,7 +284,8 @@ def quantize_weights(w: int, W, N: int = None, K: int = None, Wq=None, stream=No
         N, K = W.shape
     if Wq is None:
         Wq = _torch().empty(weight_bytes(w, N, K), dtype=_torch().uint8, device=W.device)
-    _check(lib().vq_quantize_weights(w, _ptr(W), N, K, _ptr(Wq), _stream(stream)))
+    _check(lib().vq_quantize_weights(w, _dev(W, "W", 4 * N * K, _torch().float32), N, K,
+                                     _dev(Wq, "Wq", weight_bytes(w, N, K)), _stream(stream)))
     return Wq
 
 
@@ -254,7 +293,10 @@ def gemv(w: int, W, N: int, K: int, x, y=None, xq_out=None, stream=None):
     """vq_gemv: y[N] = W . x with the activation quantizer fused in."""
     if y is None:
         y = _torch().empty(N, dtype=_torch().float32, device=x.device)
-    _check(lib().vq_gemv(w, _ptr(W), N, K, _ptr(x), _ptr(y), _ptr(xq_out), _stream(stream)))
+    f32 = _torch().float32
+    _check(lib().vq_gemv(w, _dev(W, "W", weight_bytes(w, N, K)), N, K, _dev(x, "x", 4 * K, f32),
+                         _dev(y, "y", 4 * N, f32), _dev(xq_out, "xq_out", act_bytes(act_for(w), 1, K)),
+                         _stream(stream)))
     return y
 
 
@@ -264,7 +306,8 @@ def gemm(w: int, W, N: int, K: int, act: int, Xq, M: int, Y=None, ldy: int = Non
         Y = _torch().empty((M, N), dtype=_torch().float32, device=Xq.device)
     if ldy is None:
         ldy = N if Y.dim() == 1 or Y.shape[0] == 1 else Y.stride(0)
-    _check(lib().vq_gemm(w, _ptr(W), N, K, act, _ptr(Xq), M, _ptr(Y), ldy, _stream(stream)))
+    _check(lib().vq_gemm(w, _dev(W, "W", weight_bytes(w, N, K)), N, K, act, _dev(Xq, "Xq", act_bytes(act, M, K)), M,
+                         _dev_rows(Y, "Y", M, N, ldy, _torch().float32), ldy, _stream(stream)))
     return Y
 
 
@@ -284,8 +327,12 @@ def gemm_grouped(w: int, W, E: int, N: int, K: int, act: int, Xq, T: int, ids, t
     if ws is None:
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
     fn = lib().vq_gemm_grouped_rows if per_row else lib().vq_gemm_grouped
-    _check(fn(w, _ptr(W), E, N, K, act, _ptr(Xq), T, _ptr(ids), top_k, _ptr(route_w),
-              _ptr(Y), _ptr(Ysum), _ptr(ws), ws.numel() if hasattr(ws, "numel") else need,
+    f32 = torch.float32
+    pairs = T * top_k
+    _check(fn(w, _dev(W, "W", weight_bytes(w, E * N, K)), E, N, K, act,
+              _dev(Xq, "Xq", act_bytes(act, pairs if per_row else T, K)), T, _dev(ids, "ids", 4 * pairs, torch.int32),
+              top_k, _dev(route_w, "route_w", 4 * pairs, f32), _dev(Y, "Y", 4 * pairs * N, f32),
+              _dev(Ysum, "Ysum", 4 * T * N, f32), _dev(ws, "ws", need), ws.numel() * ws.element_size() if hasattr(ws, "numel") else need,
               _stream(stream)))
     return Y, Ysum, ws
 
@@ -294,7 +341,9 @@ def weighted_sum(Y, route_w, T: int, top_k: int, N: int, Ysum=None, stream=None)
     """vq_weighted_sum: Ysum[T, N] = sum_s w[t, s] * Y[t, s, :] (slot order, no FMA)."""
     if Ysum is None:
         Ysum = _torch().empty((T, N), dtype=_torch().float32, device=Y.device)
-    _check(lib().vq_weighted_sum(_ptr(Y), _ptr(route_w), T, top_k, N, _ptr(Ysum), _stream(stream)))
+    f32 = _torch().float32
+    _check(lib().vq_weighted_sum(_dev(Y, "Y", 4 * T * top_k * N, f32), _dev(route_w, "route_w", 4 * T * top_k, f32),
+                                 T, top_k, N, _dev(Ysum, "Ysum", 4 * T * N, f32), _stream(stream)))
     return Ysum
 
 

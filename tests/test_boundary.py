@@ -198,3 +198,50 @@ def test_gemv_rejects_rows_too_long_for_lds(vq):
     assert L.vq_gemv(vq.Q8_0, None, 1, 65536, None, None, None, None) == 4  # VQ_ERR_SHAPE
     assert L.vq_gemv(vq.Q4_K, None, 1, 65536, None, None, None, None) == 1  # fits: then the null pointers
     assert L.vq_gemv(vq.Q6_K, None, 1, 1 << 17, None, None, None, None) == 4
+
+
+def test_binding_rejects_host_short_and_strided_buffers(vq, monkeypatch):
+    """The Python binding checks every tensor it hands to the C ABI: a host
+    tensor, a non-contiguous dense buffer, a wrong dtype or a buffer shorter
+    than what the call reads or writes raises ValueError before the library
+    is called (so no case here reaches a kernel)."""
+    import torch
+    K, N = 512, 64
+    x = torch.zeros(K)
+    with pytest.raises(ValueError, match="GPU device memory"):
+        vq.gemv(vq.Q4_K, torch.zeros(vq.weight_bytes(vq.Q4_K, N, K), dtype=torch.uint8), N, K, x,
+                y=torch.zeros(N))
+    with pytest.raises(ValueError, match="GPU device memory"):
+        vq.quantize_act(vq.Q8_K, torch.zeros(4, K))
+    # The remaining checks hold for any device: let CPU tensors past the
+    # device check to reach them (each case still fails before the call).
+    monkeypatch.setattr(vq, "_on_gpu", lambda t, name: None)
+    W = torch.zeros(vq.weight_bytes(vq.Q4_K, N, K), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="W holds"):
+        vq.gemv(vq.Q4_K, W[:-1], N, K, x, y=torch.zeros(N))
+    with pytest.raises(ValueError, match="x holds"):
+        vq.gemv(vq.Q4_K, W, N, K, x[:-4], y=torch.zeros(N))
+    with pytest.raises(ValueError, match="x has dtype"):
+        vq.gemv(vq.Q4_K, W, N, K, x.double(), y=torch.zeros(N))
+    with pytest.raises(ValueError, match="y is not contiguous"):
+        vq.gemv(vq.Q4_K, W, N, K, x, y=torch.zeros(N, 2)[:, 0])
+    Xq = torch.zeros(vq.act_bytes(vq.Q8_K, 8, K), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="Xq holds"):
+        vq.gemm(vq.Q4_K, W, N, K, vq.Q8_K, Xq, 9, Y=torch.zeros(9, N))
+    with pytest.raises(ValueError, match="do not fit"):
+        vq.gemm(vq.Q4_K, W, N, K, vq.Q8_K, Xq, 8, Y=torch.zeros(8 * N)[1:], ldy=N)
+    with pytest.raises(ValueError, match="row must be contiguous"):
+        vq.quantize_act(vq.Q8_K, torch.zeros(K, 4).t(), M=4, K=K, ldx=1, Xq=Xq)
+    with pytest.raises(ValueError, match="do not fit"):
+        vq.quantize_act(vq.Q8_K, torch.zeros(4 * K)[K:], M=4, K=K, ldx=K, Xq=Xq)
+    T, top_k, E = 4, 2, 8
+    ids = torch.zeros(T, top_k, dtype=torch.int64)
+    with pytest.raises(ValueError, match="ids has dtype"):
+        vq.gemm_grouped(vq.Q4_K, torch.zeros(vq.weight_bytes(vq.Q4_K, E * N, K), dtype=torch.uint8), E, N, K,
+                        vq.Q8_K, Xq, T, ids, top_k, route_w=torch.zeros(T, top_k))
+    ws = torch.zeros(vq.grouped_workspace_bytes(E, T, top_k) - 256, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="ws holds"):
+        vq.gemm_grouped(vq.Q4_K, torch.zeros(vq.weight_bytes(vq.Q4_K, E * N, K), dtype=torch.uint8), E, N, K,
+                        vq.Q8_K, Xq, T, ids.int(), top_k, route_w=torch.zeros(T, top_k), ws=ws)
+    with pytest.raises(ValueError, match="Ysum holds"):
+        vq.weighted_sum(torch.zeros(T, top_k, N), torch.zeros(T, top_k), T, top_k, N, Ysum=torch.zeros(T - 1, N))
