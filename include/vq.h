@@ -262,9 +262,10 @@ vq_status vq_set_gemm_row_block(int64_t rows);
 /* w: Q4_K, Q5_K, Q6_K (act Q8_K) or Q8_0 (act Q8_1).  W: [E][N][K/QK] blocks; */
 /* Xq: planar activation buffer of T rows; ids int32 [T][top_k], each in    */
 /* [0,E) and distinct within a token (a precondition, not checked on the    */
-/* device; a pair whose id is outside [0,E) is not computed); route_w fp32  */
-/* [T][top_k] (required when Ysum is given); Y fp32 [T][top_k][N]; Ysum     */
-/* fp32 [T][N] or NULL.                                                     */
+/* device; a pair whose id is outside [0,E) is not computed: its Y row keeps */
+/* what it held, and Ysum adds that row like any other, so such ids must    */
+/* not be used with Ysum); route_w fp32 [T][top_k] (required when Ysum is   */
+/* given); Y fp32 [T][top_k][N]; Ysum fp32 [T][N] or NULL.                  */
 /* ws: workspace of vq_grouped_workspace_bytes(E, T, top_k) bytes; after the */
 /* call it holds, at offset 0, int32 counts[E], then int32 offsets[E+1],     */
 /* then int32 list[T*top_k] (pair indices t*top_k+s grouped per expert in   */
