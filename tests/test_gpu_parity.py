@@ -611,6 +611,36 @@ def test_grouped_degenerate_routing(E, top_k):
         H.assert_bitwise(Yh[:, 0, :], H.host(dense), "grouped E=1 vs dense GEMM")
 
 
+def test_grouped_out_of_range_ids_skipped():
+    """A pair whose expert id lies outside [0, E) is not routed: counts and
+    the pair list hold only the valid pairs (stable per expert), the valid
+    pairs' rows are bit-identical to the oracle, the skipped pairs' rows keep
+    their NaN poison, and tokens with only valid pairs sum as usual."""
+    E, N, K, T, top_k = 8, 64, 512, 70, 3
+    ids = synth.random_ids(1930, T, E, top_k)
+    bad = [(3, 1, -1), (10, 0, E), (41, 2, 1 << 20), (69, 2, -7)]
+    for t, s_, v in bad:
+        ids[t, s_] = v
+    Wq, act, rw, Y, Ysum, ws = run_grouped(E, N, K, T, top_k, ids, 1935)
+    flat = ids.reshape(-1)
+    valid = (flat >= 0) & (flat < E)
+    counts, offsets, lst = vq.grouped_ws_views(ws, E, T, top_k)
+    assert np.array_equal(H.host(counts), np.bincount(flat[valid], minlength=E))
+    nvalid = int(valid.sum())
+    assert int(H.host(offsets)[E]) == nvalid
+    pairs = np.nonzero(valid)[0]
+    expect_list = pairs[np.argsort(flat[pairs], kind="stable")]
+    assert np.array_equal(H.host(lst)[:nvalid], expect_list)
+    ids_ok = np.where(ids >= 0, np.where(ids < E, ids, 0), 0).astype(np.int32)
+    Y_ref = oracle.gemm_grouped(oracle.Q4_K, Wq, E, N, K, act, ids_ok, nthreads=8)
+    Yh = H.host(Y)
+    vmask = valid.reshape(T, top_k)
+    H.assert_bitwise(Yh[vmask], Y_ref[vmask], "valid pairs")
+    assert np.isnan(Yh[~vmask]).all(), "a skipped pair's row was written"
+    full = vmask.all(1)
+    H.assert_bitwise(H.host(Ysum)[full], oracle.weighted_sum(Yh[full], rw[full]), "tokens with valid pairs")
+
+
 def test_grouped_expert_permutation():
     """Permuting expert storage and remapping ids gives the same Y bitwise."""
     E, N, K, T, top_k = 12, 64, 256, 40, 3
