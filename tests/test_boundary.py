@@ -245,3 +245,28 @@ def test_binding_rejects_host_short_and_strided_buffers(vq, monkeypatch):
                         vq.Q8_K, Xq, T, ids.int(), top_k, route_w=torch.zeros(T, top_k), ws=ws)
     with pytest.raises(ValueError, match="Ysum holds"):
         vq.weighted_sum(torch.zeros(T, top_k, N), torch.zeros(T, top_k), T, top_k, N, Ysum=torch.zeros(T - 1, N))
+
+
+def test_product_and_oracle_share_no_code():
+    """The HIP path and the oracle are independent: no package or kernel
+    source names the oracle, the oracle includes or imports nothing of the
+    package, and bench.py touches the oracle only in its CPU-baseline leg."""
+    pkg = os.path.join(ROOT, "block_quantized_matmul_fp32_amd")
+    srcs = [os.path.join(pkg, f) for f in os.listdir(pkg) if f.endswith(".py")]
+    srcs += [os.path.join(pkg, "csrc", f) for f in os.listdir(os.path.join(pkg, "csrc"))]
+    for path in srcs:
+        text = open(path).read()
+        assert not re.search(r"^\s*(import oracle|from oracle|#include\s+\S*oracle)", text, flags=re.M), path
+    odir = os.path.join(ROOT, "oracle")
+    for f in os.listdir(odir):
+        if f.endswith((".py", ".c", ".h")):
+            text = open(os.path.join(odir, f)).read()
+            assert not re.search(r"^\s*(import|from)\s+(block_quantized_matmul_fp32_amd|\.\.)", text, flags=re.M), f
+            assert not re.search(r'#include\s+"', text), f  # only system headers
+    bench = open(os.path.join(ROOT, "bench.py")).read()
+    uses = [m.start() for m in re.finditer(r"\boracle\.|^\s*(import|from) oracle", bench, flags=re.M)]
+    assert uses
+    for pos in uses:
+        func = bench.rfind("\ndef ", 0, pos)
+        name = re.match(r"\ndef (\w+)", bench[func:]).group(1) if func >= 0 else "<module>"
+        assert "cpu" in name, "bench.py uses the oracle outside its CPU baseline (in %s)" % name
