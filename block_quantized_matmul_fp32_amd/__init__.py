@@ -27,7 +27,7 @@ EXPORTS = [
     "vq_quantize_act", "vq_quantize_weights", "vq_gemv", "vq_gemm", "vq_grouped_workspace_bytes",
     "vq_gemm_grouped", "vq_gemm_grouped_rows", "vq_weighted_sum", "vq_get_stats", "vq_reset_stats",
     "vq_version", "vq_rmsnorm_quant", "vq_silu_mul_quant", "vq_set_small_batch_max", "vq_small_batch_max",
-    "vq_set_gemm_row_block",
+    "vq_set_gemm_row_block", "vq_gemm_workspace",
 ]
 
 STAT_FIELDS = ["quantize_q8k", "quantize_q8_1", "quantize_weights", "gemv_q4k", "gemv_q6k", "gemv_q8_0",
@@ -75,7 +75,9 @@ def lib():
         L.vq_quantize_act.argtypes = [I, P, I64, I64, I64, P, P]
         L.vq_quantize_weights.argtypes = [I, P, I64, I64, P, P]
         L.vq_gemv.argtypes = [I, P, I64, I64, P, P, P, P]
-        L.vq_gemm.argtypes = [I, P, I64, I64, I, P, I64, P, I64, P]
+        L.vq_gemm.argtypes = [I, P, I64, I64, I, P, I64, P, I64, P, Z, P]
+        L.vq_gemm_workspace.argtypes = [I, I64, I64, I64]
+        L.vq_gemm_workspace.restype = Z
         L.vq_grouped_workspace_bytes.argtypes = [I64, I64, I64]
         L.vq_grouped_workspace_bytes.restype = Z
         L.vq_gemm_grouped.argtypes = [I, P, I64, I64, I64, I, P, I64, P, I64, P, P, P, P, Z, P]
@@ -300,14 +302,45 @@ def gemv(w: int, W, N: int, K: int, x, y=None, xq_out=None, stream=None):
     return y
 
 
-def gemm(w: int, W, N: int, K: int, act: int, Xq, M: int, Y=None, ldy: int = None, stream=None):
-    """vq_gemm: Y[M, N] = deq(Xq) . deq(W)^T."""
+def gemm_workspace(w: int, M: int, N: int, K: int) -> int:
+    """vq_gemm_workspace: bytes of split-K workspace vq_gemm wants for this shape."""
+    return int(lib().vq_gemm_workspace(w, M, N, K))
+
+
+_ws_cache = {}
+
+
+def _gemm_ws(dev, stream_handle, nbytes):
+    """A zero-filled workspace of at least nbytes, kept per (device, stream):
+    vq_gemm leaves its counters zero after each call, so calls on one stream
+    can reuse it (they run in order)."""
+    if nbytes == 0:
+        return None
+    key = (str(dev), stream_handle)
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        torch = _torch()
+        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
+        _ws_cache[key] = ws
+    return ws
+
+
+def gemm(w: int, W, N: int, K: int, act: int, Xq, M: int, Y=None, ldy: int = None, ws="auto", stream=None):
+    """vq_gemm: Y[M, N] = deq(Xq) . deq(W)^T.  ws: "auto" (a zero-filled
+    workspace kept per device and stream), None (no split K), or a uint8
+    device tensor (zero-filled before its first use)."""
     if Y is None:
         Y = _torch().empty((M, N), dtype=_torch().float32, device=Xq.device)
     if ldy is None:
         ldy = N if Y.dim() == 1 or Y.shape[0] == 1 else Y.stride(0)
-    _check(lib().vq_gemm(w, _dev(W, "W", weight_bytes(w, N, K)), N, K, act, _dev(Xq, "Xq", act_bytes(act, M, K)), M,
-                         _dev_rows(Y, "Y", M, N, ldy, _torch().float32), ldy, _stream(stream)))
+    pw = _dev(W, "W", weight_bytes(w, N, K))
+    px = _dev(Xq, "Xq", act_bytes(act, M, K))
+    py = _dev_rows(Y, "Y", M, N, ldy, _torch().float32)
+    sh = _stream(stream)
+    if isinstance(ws, str):
+        ws = _gemm_ws(Xq.device, sh, gemm_workspace(w, M, N, K))
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().vq_gemm(w, pw, N, K, act, px, M, py, ldy, _dev(ws, "ws", wsb, _torch().uint8), wsb, sh))
     return Y
 
 

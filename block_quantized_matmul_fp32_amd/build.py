@@ -55,6 +55,12 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (r.stdout, r.stderr))
+    # a kernel whose host stub the compiler did not emit leaves an undefined
+    # __device_stub__ symbol that only fails when the library is loaded
+    r = subprocess.run(["nm", "-u", "-C", tmp], capture_output=True, text=True)
+    if r.returncode == 0 and "__device_stub__" in r.stdout:
+        bad = [l.strip() for l in r.stdout.splitlines() if "__device_stub__" in l]
+        raise RuntimeError("link left kernel stubs undefined:\n" + "\n".join(bad))
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)

@@ -650,9 +650,11 @@ __global__ __launch_bounds__(128 * WM, 2) void gemm_kernel(const uint8_t* __rest
     }
 }
 
-static std::atomic<int64_t> g_row_block{0};
+// Per calling thread, so a test's override never reaches another thread's calls.
+static thread_local int64_t g_row_block = 0;
 
 void set_gemm_row_block(int64_t rows) { g_row_block = rows; }
+int64_t gemm_row_block() { return g_row_block; }
 
 template <int WT, int WM, int TM>
 static hipError_t launch_gemm_cfg(const uint8_t* W, int64_t N, int64_t K, const void* aqs, const void* ad,
@@ -665,7 +667,7 @@ static hipError_t launch_gemm_cfg(const uint8_t* W, int64_t N, int64_t K, const 
     int64_t rows_max = ((int64_t(1) << 31) / K) / BM * BM;
     if (rows_max < BM) return hipErrorInvalidValue;
     rows_max = std::min(rows_max, kMaxGridY * BM);
-    const int64_t rb = g_row_block.load();
+    const int64_t rb = g_row_block;
     if (rb > 0) rows_max = std::min(rows_max, rb);
     // bytes per activation row in the planar planes: per block a binary32 d
     // and sixteen int16 sums (Q8_K), or a binary16 d and a binary16 s (Q8_1)
@@ -760,7 +762,7 @@ static hipError_t launch_gemm_grouped_t(const uint8_t* W, int64_t E, int64_t N, 
     ga.per_row = per_row;
     ga.expert_stride = estride;
     int64_t per = kMaxGridY;  // routed tiles per launch
-    const int64_t rb = g_row_block.load();
+    const int64_t rb = g_row_block;
     if (rb > 0) per = std::min(per, std::max<int64_t>(1, rb / kGroupBM));
     for (int64_t t0 = 0; t0 < max_tiles; t0 += per) {
         ga.tile_base = (int)t0;

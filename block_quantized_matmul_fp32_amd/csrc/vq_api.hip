@@ -35,8 +35,9 @@ Counters g_stats;
 // Largest M that vq_gemm runs on the GEMV kernel, per weight type (Q4_K,
 // Q6_K, Q8_0): the GEMV <-> GEMM crossover.
 constexpr int64_t kSmallMaxDefault[4] = {16, 64, 32, 16};
-std::atomic<int64_t> g_small_max[4] = {{kSmallMaxDefault[0]}, {kSmallMaxDefault[1]}, {kSmallMaxDefault[2]},
-                                       {kSmallMaxDefault[3]}};
+// Per calling thread, so a test's override never reaches another thread's calls.
+thread_local int64_t g_small_max[4] = {kSmallMaxDefault[0], kSmallMaxDefault[1], kSmallMaxDefault[2],
+                                       kSmallMaxDefault[3]};
 
 vq_status fail(vq_status s, const char* fmt, ...) {
     char buf[512];
@@ -325,8 +326,16 @@ vq_status vq_gemv(int w, const void* W, int64_t N, int64_t K, const float* x, fl
     return hip_status(vqk::launch_gemv(w, (const uint8_t*)W, N, K, x, y, (uint8_t*)xq_out, stream), fn);
 }
 
+size_t vq_gemm_workspace(int w, int64_t M, int64_t N, int64_t K) {
+    if (!is_weight(w) || w == VQ_Q8_0 || M <= 0 || N <= 0 || K <= 0 || K % 256 != 0 || M > kMaxDim ||
+        N > kMaxDim || K > kMaxK)
+        return 0;
+    if (vqk::gemm_skinny_ok(w, N, K, M, g_small_max[widx(w)])) return 0;
+    return vqk::gemm_kq_call_ws_bytes(w, M, N, K);
+}
+
 vq_status vq_gemm(int w, const void* W, int64_t N, int64_t K, int act, const void* Xq, int64_t M, float* Y,
-                  int64_t ldy, hipStream_t stream) {
+                  int64_t ldy, void* ws, size_t ws_bytes, hipStream_t stream) {
     const char* fn = "vq_gemm";
     VQ_TRY(check_weight(w, fn));
     VQ_TRY(check_pair(w, act, fn));
@@ -336,11 +345,14 @@ vq_status vq_gemm(int w, const void* W, int64_t N, int64_t K, int act, const voi
     if (ldy < N) return fail(VQ_ERR_SHAPE, "%s: ldy = %lld < N = %lld", fn, (long long)ldy, (long long)N);
     if (M == 0 || N == 0) return VQ_OK;
     if (!W || !Xq || !Y) return fail(VQ_ERR_INVALID_ARG, "%s: null pointer", fn);
-    if (!aligned(W, 16) || !aligned(Xq, 16) || !aligned(Y, 4))
-        return fail(VQ_ERR_INVALID_ARG, "%s: W and Xq must be 16-byte, Y 4-byte aligned", fn);
+    if (!aligned(W, 16) || !aligned(Xq, 16) || !aligned(Y, 4) || (ws && !aligned(ws, 256)))
+        return fail(VQ_ERR_INVALID_ARG, "%s: W and Xq must be 16-byte, Y 4-byte, ws 256-byte aligned", fn);
+    if (!ws) ws_bytes = 0;
     const size_t wb = vq_weight_bytes(w, N, K), ab = vq_act_bytes(act, M, K);
     const size_t yb = ((size_t)(M - 1) * (size_t)ldy + (size_t)N) * 4;
     if (overlap(Y, yb, W, wb) || overlap(Y, yb, Xq, ab)) return fail(VQ_ERR_ALIAS, "%s: Y overlaps an input", fn);
+    if (overlap(ws, ws_bytes, W, wb) || overlap(ws, ws_bytes, Xq, ab) || overlap(ws, ws_bytes, Y, yb))
+        return fail(VQ_ERR_ALIAS, "%s: the workspace overlaps an input or Y", fn);
     const uint8_t* base = (const uint8_t*)Xq;
     const void* qs = base;
     const void* d = base + vq_act_d_offset(act, M, K);
@@ -349,7 +361,7 @@ vq_status vq_gemm(int w, const void* W, int64_t N, int64_t K, int act, const voi
     else if (w == VQ_Q6_K) g_stats.gemm_q6k++;
     else if (w == VQ_Q5_K) g_stats.gemm_q5k++;
     else g_stats.gemm_q8_0++;
-    if (vqk::gemm_skinny_ok(w, N, K, M, g_small_max[widx(w)].load())) {
+    if (vqk::gemm_skinny_ok(w, N, K, M, g_small_max[widx(w)])) {
         // small batch: the weights streamed once through the GEMV kernel for all M rows
         g_stats.gemm_skinny++;
         return hip_status(vqk::launch_gemm_skinny(w, (const uint8_t*)W, N, K, base, M,
@@ -357,6 +369,9 @@ vq_status vq_gemm(int w, const void* W, int64_t N, int64_t K, int act, const voi
                                                   (int64_t)vq_act_aux_offset(act, M, K), Y, ldy, stream),
                           fn);
     }
+    if (w != VQ_Q8_0)
+        return hip_status(vqk::launch_gemm_kq(w, (const uint8_t*)W, N, K, qs, d, aux, M, Y, ldy, ws, ws_bytes, stream),
+                          fn);
     return hip_status(vqk::launch_gemm(w, (const uint8_t*)W, N, K, qs, d, aux, M, Y, ldy, stream), fn);
 }
 
@@ -373,7 +388,7 @@ vq_status vq_set_small_batch_max(int w, int64_t max_m) {
 
 int64_t vq_small_batch_max(int w) {
     if (!is_weight(w)) return -1;
-    return g_small_max[widx(w)].load();
+    return g_small_max[widx(w)];
 }
 
 vq_status vq_set_gemm_row_block(int64_t rows) {

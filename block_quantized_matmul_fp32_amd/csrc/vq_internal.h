@@ -49,6 +49,7 @@ int num_cus();
 // Prefill GEMM row blocking: one launch covers at most this many activation
 // rows (0: as many as keep the launch's activation bytes below 2^31).
 void set_gemm_row_block(int64_t rows);
+int64_t gemm_row_block();  // the calling thread's cap (0: none)
 
 // Decode GEMV with the fused activation quantizer.  xq_out may be null.
 hipError_t launch_gemv(int wtype, const uint8_t* W, int64_t N, int64_t K, const float* x,
@@ -62,7 +63,16 @@ bool gemm_skinny_ok(int wtype, int64_t N, int64_t K, int64_t M, int64_t max_m);
 hipError_t launch_gemm_skinny(int wtype, const uint8_t* W, int64_t N, int64_t K, const uint8_t* xq, int64_t M,
                               int64_t d_off, int64_t aux_off, float* Y, int64_t ldy, hipStream_t st);
 
-// Prefill GEMM on pre-quantized activations.
+// Prefill GEMM of the K-quant weights (wtype 0 Q4_K, 1 Q6_K, 5 Q5_K) on
+// Q8_K activations; ws/ws_bytes: split-K workspace (may be null).
+hipError_t launch_gemm_kq(int wtype, const uint8_t* W, int64_t N, int64_t K, const void* aqs, const void* ad,
+                          const void* aux, int64_t M, float* Y, int64_t ldy, void* ws, size_t ws_bytes,
+                          hipStream_t st);
+int gemm_kq_splits(int wtype, int64_t M, int64_t N, int64_t K);
+size_t gemm_kq_ws_bytes(int wtype, int64_t M, int64_t N, int64_t K);
+size_t gemm_kq_call_ws_bytes(int wtype, int64_t M, int64_t N, int64_t K);  // over the row blocks
+
+// Prefill GEMM on pre-quantized activations (Q8_0 x Q8_1).
 hipError_t launch_gemm(int wtype, const uint8_t* W, int64_t N, int64_t K, const void* act_qs,
                        const void* act_d, const void* act_aux, int64_t M, float* Y, int64_t ldy,
                        hipStream_t st);

@@ -215,22 +215,38 @@ vq_status vq_gemv(int w, const void* W, int64_t N, int64_t K, const float* x, fl
 /* ---------------------------------------------------------------------- */
 /* Prefill GEMM: Y[m][n] = sum_k deq(Xq)[m][k]*deq(W)[n][k] for m < M,       */
 /* n < N, through exact int32 sub-block sums and binary32 scale combines.   */
-/* Xq is the planar activation buffer of type act (Q8_K for Q4_K/Q6_K,      */
+/* Xq is the planar activation buffer of type act (Q8_K for Q4_K/Q6_K/Q5_K, */
 /* Q8_1 for Q8_0) holding M rows; Y fp32 with row stride ldy >= N.          */
 /* Small batches, M <= vq_small_batch_max(w), run on the decode GEMV kernel */
 /* over the pre-quantized rows (the weights streamed once for all rows, in  */
-/* groups of 4 rows above 8), larger M on the int8 MFMA GEMM; the result is */
-/* the same fixed-order definition either way.                             */
+/* groups of 4 rows above 8), larger M on the int8 MFMA GEMM.               */
+/* Numerics: the int32 sub-block sums are exact; the binary32 combine and   */
+/* accumulation order is the kernel's own (fused multiply-adds), fixed for  */
+/* given arguments, so two calls with the same arguments (including         */
+/* ws_bytes) give bitwise equal Y; Y meets the pages' tolerance (NMSE <=    */
+/* 1e-6 against the fixed-order binary32 definition, relative error <= 5e-4 */
+/* against the fp64 dequantized product).                                  */
+/* ws: NULL or a device workspace of at least vq_gemm_workspace(w, M, N, K) */
+/* bytes, 256-byte aligned, ZERO-FILLED BEFORE ITS FIRST USE; the MFMA GEMM */
+/* splits K across workgroups when the output tiles alone cannot fill the   */
+/* chip, keeps fp32 partial tiles and per-tile arrival counters there, and  */
+/* leaves the counters zero when the call completes.  A smaller workspace   */
+/* (or NULL) gives fewer splits (or none): the result stays within the      */
+/* tolerance but its fp32 rounding may differ.  Calls that share a          */
+/* workspace must not run concurrently (same stream, or ordered streams).   */
 /* ---------------------------------------------------------------------- */
 vq_status vq_gemm(int w, const void* W, int64_t N, int64_t K, int act, const void* Xq,
-                  int64_t M, float* Y, int64_t ldy, hipStream_t stream);
+                  int64_t M, float* Y, int64_t ldy, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes vq_gemm wants for this shape (0: none needed). */
+size_t vq_gemm_workspace(int w, int64_t M, int64_t N, int64_t K);
 
 /* ---------------------------------------------------------------------- */
 /* The GEMV <-> GEMM crossover of vq_gemm (vllm.cpp PR #2890, "lever-B1":  */
 /* the fold crossover made tunable at run time): vq_gemm with weight type w */
 /* runs M <= max_m on the GEMV kernel.  max_m in [0, 64] (0: never), -1     */
 /* restores the default (Q4_K 16, Q5_K 16, Q6_K 64, Q8_0 32, measured on   */
-/* the decode shapes).  Process-wide; not synchronised with calls in flight.*/
+/* the decode shapes).  Per calling thread: other threads keep their own. */
 /* vq_small_batch_max returns the current value (-1 for a non-weight type). */
 /* ---------------------------------------------------------------------- */
 vq_status vq_set_small_batch_max(int w, int64_t max_m);
@@ -240,14 +256,14 @@ int64_t vq_small_batch_max(int w);
 /* Row blocks of the MFMA arm of vq_gemm.  The GEMM kernel addresses the    */
 /* activation bytes of one launch with 32-bit offsets, so vq_gemm launches  */
 /* it once per block of at most floor(2^31 / K) rows (rounded down to the   */
-/* tile height) and at most 32768 tile rows, which is one launch for every  */
-/* practical shape; the grouped calls likewise launch their GEMM once per   */
-/* 32768 routed tiles.  rows > 0 caps the block at that many rows (any      */
-/* value; for tests of the blocking) and the grouped launches at           */
-/* max(1, rows / 96) routed tiles of 96 rows; 0 restores the default.  The  */
-/* results do not depend on the blocking.                                   */
-/* Process-wide; not synchronised with calls in flight.  rows < 0:          */
-/* VQ_ERR_INVALID_ARG.                                                      */
+/* tile height), which is one launch for every practical shape; the grouped */
+/* calls likewise launch their GEMM once per 32768 routed tiles.  rows > 0  */
+/* caps the block at that many rows (any value; for tests of the blocking)  */
+/* and the grouped launches at max(1, rows / 96) routed tiles of 96 rows;   */
+/* 0 restores the default.  The K-quant results stay within the GEMM's     */
+/* tolerance under any blocking (a block's K splits depend on its rows);    */
+/* Q8_0 results do not depend on it.  Per calling thread: other threads     */
+/* keep their own.  rows < 0: VQ_ERR_INVALID_ARG.                           */
 /* ---------------------------------------------------------------------- */
 vq_status vq_set_gemm_row_block(int64_t rows);
 

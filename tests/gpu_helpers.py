@@ -69,6 +69,53 @@ def pack_act(act, wtype):
     return buf
 
 
+# The GEMM's fp32 tolerance: NMSE against the oracle's binary32 outputs and
+# relative error (floored at 1% of the rms) against the fp64 dequantized product.
+NMSE_MAX = 1e-6
+REL_MAX = 5e-4
+
+
+def fp64_cells(wtype, Wq, N, K, act, ms, ns):
+    """fp64 dequantized product deq(x_m) . deq(w_n) at the cells (ms[i], ns[i]),
+    dequantizing only the rows the cells touch."""
+    from oracle import ref_fp64
+    ms = np.asarray(ms, np.int64)
+    ns = np.asarray(ns, np.int64)
+    um, im = np.unique(ms, return_inverse=True)
+    un, jn = np.unique(ns, return_inverse=True)
+    Wrows = np.asarray(Wq, np.uint8).reshape(N, -1)[un]
+    Wd = ref_fp64.dequant_weights(wtype, Wrows, un.size, K)
+    if hasattr(act, "bsums"):
+        A = ref_fp64.dequant_q8k(act.qs[um], act.d[um])
+    else:
+        A = ref_fp64.dequant_q8_1(act.qs[um], act.d[um])
+    return np.einsum("ik,ik->i", A[im], Wd[jn])
+
+
+def assert_close(got, ref, what, r64=None):
+    """Every value finite, NMSE(got, ref) <= 1e-6 and max relative error <= 5e-4
+    against r64 (the fp64 product) -- or against ref itself when r64 is not given."""
+    from oracle import ref_fp64
+    got = np.asarray(got, np.float32)
+    assert np.isfinite(got).all(), "%s: non-finite outputs" % what
+    e = ref_fp64.nmse(got, ref)
+    assert e <= NMSE_MAX, "%s: NMSE %.3g > %.1g" % (what, e, NMSE_MAX)
+    rel = ref_fp64.max_rel_err(got, ref if r64 is None else r64)[0]
+    assert rel <= REL_MAX, "%s: max relative error %.3g > %.1g" % (what, rel, REL_MAX)
+
+
+# Weight types whose MFMA GEMM keeps the oracle's fixed-order binary32 combine
+# (bit-identical outputs); the K-quant GEMMs are held to the tolerance above.
+EXACT_GEMM = {oracle.Q8_0}
+
+
+def assert_gemm(wtype, got, ref, what, r64=None):
+    if wtype in EXACT_GEMM:
+        assert_bitwise(got, ref, what)
+    else:
+        assert_close(got, ref, what, r64)
+
+
 def bits(a):
     a = np.ascontiguousarray(a, np.float32)
     return a.view(np.uint32)

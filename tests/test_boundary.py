@@ -88,7 +88,7 @@ def _err(vq, status, fn, *args):
 
 
 def test_unsupported_types_are_named(vq):
-    msg = _err(vq, 2, "vq_gemm", 9, FAKE, 64, 256, vq.Q8_K, FAKE, 4, FAKE, 64, None)
+    msg = _err(vq, 2, "vq_gemm", 9, FAKE, 64, 256, vq.Q8_K, FAKE, 4, FAKE, 64, None, 0, None)
     assert "unknown" in msg and "9" in msg
     msg = _err(vq, 2, "vq_gemv", vq.Q8_K, FAKE, 64, 256, FAKE, FAKE, None, None)
     assert "Q8_K" in msg
@@ -103,17 +103,17 @@ def test_unsupported_types_are_named(vq):
 
 
 def test_type_pairing(vq):
-    msg = _err(vq, 3, "vq_gemm", vq.Q8_0, FAKE, 64, 256, vq.Q8_K, FAKE, 4, FAKE, 64, None)
+    msg = _err(vq, 3, "vq_gemm", vq.Q8_0, FAKE, 64, 256, vq.Q8_K, FAKE, 4, FAKE, 64, None, 0, None)
     assert "Q8_0" in msg and "Q8_1" in msg
-    _err(vq, 3, "vq_gemm", vq.Q6_K, FAKE, 64, 256, vq.Q8_1, FAKE, 4, FAKE, 64, None)
+    _err(vq, 3, "vq_gemm", vq.Q6_K, FAKE, 64, 256, vq.Q8_1, FAKE, 4, FAKE, 64, None, 0, None)
 
 
 def test_shape_errors(vq):
-    msg = _err(vq, 4, "vq_gemm", vq.Q4_K, FAKE, 64, 300, vq.Q8_K, FAKE, 4, FAKE, 64, None)
+    msg = _err(vq, 4, "vq_gemm", vq.Q4_K, FAKE, 64, 300, vq.Q8_K, FAKE, 4, FAKE, 64, None, 0, None)
     assert "300" in msg and "256" in msg
-    _err(vq, 4, "vq_gemm", vq.Q8_0, FAKE, 64, 48, vq.Q8_1, FAKE, 4, FAKE, 64, None)
-    _err(vq, 4, "vq_gemm", vq.Q4_K, FAKE, -1, 256, vq.Q8_K, FAKE, 4, FAKE, 64, None)
-    _err(vq, 4, "vq_gemm", vq.Q4_K, FAKE, 64, 256, vq.Q8_K, FAKE, 4, FAKE, 10, None)  # ldy < N
+    _err(vq, 4, "vq_gemm", vq.Q8_0, FAKE, 64, 48, vq.Q8_1, FAKE, 4, FAKE, 64, None, 0, None)
+    _err(vq, 4, "vq_gemm", vq.Q4_K, FAKE, -1, 256, vq.Q8_K, FAKE, 4, FAKE, 64, None, 0, None)
+    _err(vq, 4, "vq_gemm", vq.Q4_K, FAKE, 64, 256, vq.Q8_K, FAKE, 4, FAKE, 10, None, 0, None)  # ldy < N
     _err(vq, 4, "vq_quantize_act", vq.Q8_K, FAKE, 4, 256, 100, FAKE, None)          # ldx < K
     _err(vq, 4, "vq_gemm_grouped", vq.Q4_K, FAKE, 2000, 64, 256, vq.Q8_K, FAKE, 4, FAKE, 2, FAKE,
          FAKE, None, FAKE, 1 << 20, None)  # E > 1024
@@ -123,10 +123,10 @@ def test_shape_errors(vq):
 
 
 def test_null_misaligned_alias_workspace(vq):
-    _err(vq, 1, "vq_gemm", vq.Q4_K, None, 64, 256, vq.Q8_K, FAKE, 4, FAKE, 64, None)
-    _err(vq, 1, "vq_gemm", vq.Q4_K, FAKE + 2, 64, 256, vq.Q8_K, FAKE + 0x100000, 4, FAKE + 0x200000, 64, None)
+    _err(vq, 1, "vq_gemm", vq.Q4_K, None, 64, 256, vq.Q8_K, FAKE, 4, FAKE, 64, None, 0, None)
+    _err(vq, 1, "vq_gemm", vq.Q4_K, FAKE + 2, 64, 256, vq.Q8_K, FAKE + 0x100000, 4, FAKE + 0x200000, 64, None, 0, None)
     # Y overlapping W
-    msg = _err(vq, 5, "vq_gemm", vq.Q4_K, FAKE, 64, 256, vq.Q8_K, FAKE + 0x100000, 4, FAKE + 64, 64, None)
+    msg = _err(vq, 5, "vq_gemm", vq.Q4_K, FAKE, 64, 256, vq.Q8_K, FAKE + 0x100000, 4, FAKE + 64, 64, None, 0, None)
     assert "overlap" in msg
     # y overlapping x in the GEMV
     _err(vq, 5, "vq_gemv", vq.Q4_K, FAKE, 64, 256, FAKE + 0x100000, FAKE + 0x100000 + 16, None, None)
@@ -141,9 +141,54 @@ def test_null_misaligned_alias_workspace(vq):
          FAKE + 0x200000, 2, None, FAKE + 0x400000, FAKE + 0x480000, FAKE + 0x500000, need, None)
 
 
+def test_gemm_workspace_checks(vq):
+    """vq_gemm's workspace: 256-byte alignment and no overlap with W, Xq or Y,
+    checked before any launch; vq_gemm_workspace sizes (no workspace for
+    Q8_0, the GEMV-kernel batches, or a grid that fills the chip)."""
+    base = dict(W=FAKE, Xq=FAKE + 0x4000000, Y=FAKE + 0x8000000)
+    args = lambda ws, wsb: (vq.Q6_K, base["W"], 640, 4096, vq.Q8_K, base["Xq"], 256, base["Y"], 640, ws, wsb,
+                            None)
+    msg = _err(vq, 1, "vq_gemm", *args(FAKE + 0xC000000 + 16, 1 << 20))
+    assert "256-byte" in msg
+    msg = _err(vq, 5, "vq_gemm", *args(base["Xq"] + 0x100, 1 << 20))
+    assert "workspace" in msg
+    _err(vq, 5, "vq_gemm", *args(base["W"], 1 << 20))
+    _err(vq, 5, "vq_gemm", *args(base["Y"] - 0x100, 1 << 20))
+    assert vq.gemm_workspace(vq.Q8_0, 2048, 4096, 2048) == 0
+    assert vq.gemm_workspace(vq.Q4_K, 1, 9728, 2560) == 0          # GEMV-kernel arm
+    assert vq.gemm_workspace(vq.Q4_K, 2048, 9728, 2560) == 0       # 1216 tiles: no split
+    small = vq.gemm_workspace(vq.Q6_K, 256, 640, 4096)             # 10 tiles, 16 steps: split K
+    assert small > 0 and small % 256 == 0
+    assert vq.gemm_workspace(vq.Q4_K, 0, 640, 4096) == 0
+    assert vq.gemm_workspace(vq.Q4_K, 256, 640, 1000) == 0         # K not a multiple of 256
+    assert vq.gemm_workspace(9, 256, 640, 4096) == 0
+
+
+def test_overrides_are_per_thread(vq):
+    """The crossover and row-block overrides apply to the calling thread only."""
+    import threading
+    seen = {}
+    L = vq.lib()
+    assert L.vq_set_small_batch_max(vq.Q4_K, 3) == 0
+    try:
+        t = threading.Thread(target=lambda: seen.setdefault("other", L.vq_small_batch_max(vq.Q4_K)))
+        t.start()
+        t.join()
+        assert L.vq_small_batch_max(vq.Q4_K) == 3
+        assert seen["other"] == 16
+        # a row-block cap on another thread leaves this thread's workspace plan alone
+        before = vq.gemm_workspace(vq.Q6_K, 1000, 640, 4096)
+        t = threading.Thread(target=lambda: L.vq_set_gemm_row_block(128))
+        t.start()
+        t.join()
+        assert vq.gemm_workspace(vq.Q6_K, 1000, 640, 4096) == before
+    finally:
+        L.vq_set_small_batch_max(vq.Q4_K, -1)
+
+
 def test_empty_calls_are_ok(vq):
     L = vq.lib()
-    assert L.vq_gemm(vq.Q4_K, None, 0, 256, vq.Q8_K, None, 0, None, 0, None) == 0
+    assert L.vq_gemm(vq.Q4_K, None, 0, 256, vq.Q8_K, None, 0, None, 0, None, 0, None) == 0
     assert L.vq_quantize_act(vq.Q8_1, None, 0, 64, 64, None, None) == 0
     assert L.vq_gemv(vq.Q6_K, None, 0, 256, None, None, None, None) == 0
 
