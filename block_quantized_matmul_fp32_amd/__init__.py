@@ -25,7 +25,7 @@ EXPORTS = [
     "vq_status_string", "vq_last_error", "vq_type_name", "vq_is_supported", "vq_block_values",
     "vq_block_bytes", "vq_weight_bytes", "vq_act_bytes", "vq_act_d_offset", "vq_act_aux_offset",
     "vq_quantize_act", "vq_quantize_weights", "vq_gemv", "vq_gemm", "vq_grouped_workspace_bytes",
-    "vq_gemm_grouped", "vq_gemm_grouped_rows", "vq_weighted_sum", "vq_get_stats", "vq_reset_stats",
+    "vq_gemm_grouped", "vq_gemm_grouped_rows", "vq_gemm_grouped_noalloc", "vq_weighted_sum", "vq_get_stats", "vq_reset_stats",
     "vq_version", "vq_rmsnorm_quant", "vq_silu_mul_quant", "vq_set_small_batch_max", "vq_small_batch_max",
     "vq_set_gemm_row_block", "vq_gemm_workspace",
 ]
@@ -82,6 +82,7 @@ def lib():
         L.vq_grouped_workspace_bytes.restype = Z
         L.vq_gemm_grouped.argtypes = [I, P, I64, I64, I64, I, P, I64, P, I64, P, P, P, P, Z, P]
         L.vq_gemm_grouped_rows.argtypes = [I, P, I64, I64, I64, I, P, I64, P, I64, P, P, P, P, Z, P]
+        L.vq_gemm_grouped_noalloc.argtypes = [I, P, I64, I64, I64, I, P, I64, P, I64, P, P, P, P]
         L.vq_weighted_sum.argtypes = [P, P, I64, I64, I64, P, P]
         L.vq_set_small_batch_max.argtypes = [I, I64]
         L.vq_set_small_batch_max.restype = I
@@ -94,7 +95,7 @@ def lib():
         L.vq_get_stats.argtypes = [ctypes.POINTER(VQStats)]
         L.vq_version.restype = ctypes.c_char_p
         for f in ("vq_quantize_act", "vq_quantize_weights", "vq_gemv", "vq_gemm", "vq_gemm_grouped",
-                  "vq_gemm_grouped_rows", "vq_weighted_sum", "vq_rmsnorm_quant", "vq_silu_mul_quant"):
+                  "vq_gemm_grouped_rows", "vq_gemm_grouped_noalloc", "vq_weighted_sum", "vq_rmsnorm_quant", "vq_silu_mul_quant"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -368,6 +369,24 @@ def gemm_grouped(w: int, W, E: int, N: int, K: int, act: int, Xq, T: int, ids, t
               _dev(Ysum, "Ysum", 4 * T * N, f32), _dev(ws, "ws", need), ws.numel() * ws.element_size() if hasattr(ws, "numel") else need,
               _stream(stream)))
     return Y, Ysum, ws
+
+
+GROUPED_NOALLOC_SCRATCH_BYTES = 4 << 20  # VQ_GROUPED_NOALLOC_SCRATCH_BYTES
+
+
+def gemm_grouped_noalloc(w: int, W, E: int, N: int, K: int, act: int, Xq, T: int, ids, top_k: int,
+                         route_w, Y, Ysum=None, stream=None):
+    """vq_gemm_grouped_noalloc: the broadcast arm with its routing workspace in
+    the library's static per-GPU scratch array.  Y (and Ysum, if wanted) are
+    the caller's: this wrapper allocates nothing either."""
+    torch = _torch()
+    f32 = torch.float32
+    pairs = T * top_k
+    _check(lib().vq_gemm_grouped_noalloc(
+        w, _dev(W, "W", weight_bytes(w, E * N, K)), E, N, K, act, _dev(Xq, "Xq", act_bytes(act, T, K)), T,
+        _dev(ids, "ids", 4 * pairs, torch.int32), top_k, _dev(route_w, "route_w", 4 * pairs, f32),
+        _dev(Y, "Y", 4 * pairs * N, f32), _dev(Ysum, "Ysum", 4 * T * N, f32), _stream(stream)))
+    return Y, Ysum
 
 
 def weighted_sum(Y, route_w, T: int, top_k: int, N: int, Ysum=None, stream=None):

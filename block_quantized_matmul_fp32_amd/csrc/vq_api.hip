@@ -11,6 +11,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/vq.h"
@@ -403,12 +404,43 @@ size_t vq_grouped_workspace_bytes(int64_t E, int64_t T, int64_t top_k) {
     return vqk::route_ws_layout(E, T, top_k, nullptr, nullptr);
 }
 
+// Routing workspace of vq_gemm_grouped_noalloc, for callers that cannot
+// allocate: a static device array, one copy per GPU, held until the process
+// ends.  Host code never passes the array's name to a kernel (on the host it
+// is only a stand-in for the symbol); it uses the device address that
+// hipGetSymbolAddress returns, looked up once per device with that device
+// current and kept in g_scratch_ptr.
+constexpr size_t kScratchBytes = VQ_GROUPED_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[vqk::kMaxDevices] = {};
+
+// The current device's scratch address (looked up on the first call there).
+static vq_status scratch_ptr(const char* fn, void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, fn);
+    if (dev < 0 || dev >= vqk::kMaxDevices)
+        return fail(VQ_ERR_INVALID_ARG, "%s: device %d outside [0, %d)", fn, dev, vqk::kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e, "vq_gemm_grouped_noalloc: hipGetSymbolAddress(scratch)");
+        if (!p) return fail(VQ_ERR_HIP, "%s: hipGetSymbolAddress(scratch) returned NULL", fn);
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return VQ_OK;
+}
+
 // Both arms of the routed-expert GEMM: the broadcast arm reads activation row
-// t for pair (t, s); the per-row arm reads row t*top_k + s.
+// t for pair (t, s); the per-row arm reads row t*top_k + s.  static_ws: take
+// the routing workspace from the static scratch array instead of ws.
 static vq_status gemm_grouped_impl(const char* fn, int per_row, int w, const void* W, int64_t E, int64_t N,
                                    int64_t K, int act, const void* Xq, int64_t T, const int32_t* ids, int64_t top_k,
                                    const float* route_w, float* Y, float* Ysum, void* ws, size_t ws_bytes,
-                                   hipStream_t stream) {
+                                   hipStream_t stream, bool static_ws = false) {
     VQ_TRY(check_weight(w, fn));
     VQ_TRY(check_pair(w, act, fn));
     VQ_TRY(check_k(w, K, fn));
@@ -423,6 +455,15 @@ static vq_status gemm_grouped_impl(const char* fn, int per_row, int w, const voi
     if (!W || !Xq || !ids || !Y) return fail(VQ_ERR_INVALID_ARG, "%s: null pointer", fn);
     if (Ysum && !route_w) return fail(VQ_ERR_INVALID_ARG, "%s: Ysum requested without route_w", fn);
     const size_t need = vq_grouped_workspace_bytes(E, T, top_k);
+    if (static_ws) {
+        if (need > kScratchBytes)
+            return fail(VQ_ERR_WORKSPACE,
+                        "%s: routing workspace of %zu bytes (E = %lld, T*top_k = %lld) exceeds the static %zu-byte "
+                        "scratch array; use vq_gemm_grouped with a workspace",
+                        fn, need, (long long)E, (long long)(T * top_k), kScratchBytes);
+        VQ_TRY(scratch_ptr(fn, &ws));
+        ws_bytes = kScratchBytes;
+    }
     if (!ws || ws_bytes < need)
         return fail(VQ_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws ? ws_bytes : 0);
     if (!aligned(W, 16) || !aligned(Xq, 16) || !aligned(ids, 4) || !aligned(Y, 16) || !aligned(ws, 256) ||
@@ -471,6 +512,13 @@ vq_status vq_gemm_grouped(int w, const void* W, int64_t E, int64_t N, int64_t K,
                           float* Ysum, void* ws, size_t ws_bytes, hipStream_t stream) {
     return gemm_grouped_impl("vq_gemm_grouped", 0, w, W, E, N, K, act, Xq, T, ids, top_k, route_w, Y, Ysum, ws,
                              ws_bytes, stream);
+}
+
+vq_status vq_gemm_grouped_noalloc(int w, const void* W, int64_t E, int64_t N, int64_t K, int act, const void* Xq,
+                                  int64_t T, const int32_t* ids, int64_t top_k, const float* route_w, float* Y,
+                                  float* Ysum, hipStream_t stream) {
+    return gemm_grouped_impl("vq_gemm_grouped_noalloc", 0, w, W, E, N, K, act, Xq, T, ids, top_k, route_w, Y, Ysum,
+                             nullptr, 0, stream, true);
 }
 
 vq_status vq_gemm_grouped_rows(int w, const void* W, int64_t E, int64_t N, int64_t K, int act, const void* Xq,

@@ -306,6 +306,24 @@ vq_status vq_gemm_grouped_rows(int w, const void* W, int64_t E, int64_t N, int64
                                const float* route_w, float* Y, float* Ysum, void* ws,
                                size_t ws_bytes, hipStream_t stream);
 
+/* vq_gemm_grouped without the ws argument, for callers that cannot allocate */
+/* device memory (code under HIP graph capture, tight serving loops,        */
+/* harnesses that forbid hipMalloc).  The routing workspace comes from a    */
+/* static device array of VQ_GROUPED_NOALLOC_SCRATCH_BYTES bytes, one per   */
+/* GPU, held until the process ends; the call itself allocates nothing.    */
+/* The caller still passes every input and output.  Outputs, limits and     */
+/* errors are those of vq_gemm_grouped; a call whose routing workspace,     */
+/* vq_grouped_workspace_bytes(E, T, top_k), exceeds the array (T*top_k of   */
+/* about 410k pairs at E = 256) fails with VQ_ERR_WORKSPACE before any      */
+/* launch.  Every call on one GPU uses that GPU's one array: calls that     */
+/* overlap on one GPU (different streams, or threads without ordering)      */
+/* race and must not be issued; calls ordered on one stream are fine.  The  */
+/* current device must be the one the stream belongs to.                    */
+#define VQ_GROUPED_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+vq_status vq_gemm_grouped_noalloc(int w, const void* W, int64_t E, int64_t N, int64_t K, int act,
+                                  const void* Xq, int64_t T, const int32_t* ids, int64_t top_k,
+                                  const float* route_w, float* Y, float* Ysum, hipStream_t stream);
+
 /* Weighted expert sum alone (same definition as in vq_gemm_grouped):
  * Y fp32 [T][top_k][N], route_w fp32 [T][top_k], Ysum fp32 [T][N]; N % 4 == 0. */
 vq_status vq_weighted_sum(const float* Y, const float* route_w, int64_t T, int64_t top_k,

@@ -186,6 +186,15 @@ def test_overrides_are_per_thread(vq):
         L.vq_set_small_batch_max(vq.Q4_K, -1)
 
 
+def test_grouped_noalloc_rejects_oversized_routing(vq):
+    """The static-scratch grouped call rejects a routing workspace larger than
+    its array before any launch (and before it looks up the array)."""
+    assert vq.grouped_workspace_bytes(256, 1 << 17, 8) > vq.GROUPED_NOALLOC_SCRATCH_BYTES
+    msg = _err(vq, 6, "vq_gemm_grouped_noalloc", vq.Q4_K, FAKE, 256, 64, 256, vq.Q8_K, FAKE + 0x100000, 1 << 17,
+               FAKE + 0x200000, 8, None, FAKE + 0x300000, None, None)
+    assert "static" in msg and str(vq.GROUPED_NOALLOC_SCRATCH_BYTES) in msg
+
+
 def test_empty_calls_are_ok(vq):
     L = vq.lib()
     assert L.vq_gemm(vq.Q4_K, None, 0, 256, vq.Q8_K, None, 0, None, 0, None, 0, None) == 0
