@@ -777,13 +777,11 @@ static hipError_t launch_gemm_grouped_t(const uint8_t* W, int64_t E, int64_t N, 
 
 hipError_t launch_gemm_grouped(int wtype, const uint8_t* W, int64_t E, int64_t N, int64_t K, const void* act_qs,
                                const void* act_d, const void* act_aux, int64_t T, int64_t top_k, int per_row,
-                               RouteWs ws, float* Y, hipStream_t st) {
-    if (wtype == 0)
-        return launch_gemm_grouped_t<0>(W, E, N, K, act_qs, act_d, act_aux, T, top_k, per_row, ws, Y, st);
-    if (wtype == 1)
-        return launch_gemm_grouped_t<1>(W, E, N, K, act_qs, act_d, act_aux, T, top_k, per_row, ws, Y, st);
-    if (wtype == 5)
-        return launch_gemm_grouped_t<3>(W, E, N, K, act_qs, act_d, act_aux, T, top_k, per_row, ws, Y, st);
+                               int tile_rows, RouteWs ws, float* Y, hipStream_t st) {
+    if (wtype != 2)
+        return launch_gemm_kq_grouped(wtype, W, E, N, K, act_qs, act_d, act_aux, T, top_k, per_row, tile_rows, ws, Y,
+                                      st);
+    if (tile_rows != kGroupBM) return hipErrorInvalidValue;
     return launch_gemm_grouped_t<2>(W, E, N, K, act_qs, act_d, act_aux, T, top_k, per_row, ws, Y, st);
 }
 

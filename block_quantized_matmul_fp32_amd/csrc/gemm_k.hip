@@ -15,29 +15,29 @@
 //  * Y tile = activations (MFMA A, rows m) x weights (MFMA B, columns n) on
 //    v_mfma_i32_32x32x32_i8.  A lane's output column is its own weight row,
 //    so the weight scales d, dmin are per-lane scalars in the epilogue.
-//  * A workgroup is G groups of four waves.  Wave w of a group owns weight
-//    rows 32w..32w+31 of the 128-row tile; lane (n, h) owns half h of each
-//    super-block (elements 128h..128h+127), i.e. one 16-value piece of one
-//    sub-block per 32-wide MFMA K chunk.  Each group owns MT 32-row
-//    activation tiles; all groups share the weight rows.
+//  * A workgroup is four waves over a 128-row weight tile: wave w owns
+//    weight rows 32w..32w+31, lane (n, h) half h of each 32-wide K chunk's
+//    sub-block piece.  Every wave runs all MT 32-row activation tiles
+//    (BM = 32 MT activation rows per workgroup).
 //  * Per 256-wide K step: the activation tile (int8 Q8_K bytes, XOR-swizzled
 //    rows) and its scales are copied HBM -> LDS by the LDS-DMA path
-//    (global_load_lds), the raw weight blocks are loaded into registers one
-//    step ahead and stored 16-byte aligned into LDS, double-buffered, one
-//    barrier per step.
-//  * The per-sub-block integer scales are folded into the int8 weight
-//    operand ("planes"), so a super-block is P int32 MFMA accumulations per
-//    tile with no per-sub-block ALU work:
-//      Q4_K: sc (6 bit) = 8*hi + lo; planes q*lo, q*hi (<= 105); S = 8*R1 + R0.
-//      Q5_K: q <= 31; base-4 digits of sc; planes q*digit (<= 93);
-//            S = 16*R2 + 4*R1 + R0.
-//      Q6_K: int8 sc = 64*d2 + 8*d1 + d0, digits in [-3, 4]; planes
-//            (q-32)*digit; S = 64*R2 + 8*R1 + R0.
+//    (global_load_lds) into one of two distinct buffers, and each lane's raw
+//    weight block bytes are loaded straight into its registers by buffer
+//    loads, both one step ahead; one barrier per step.
+//  * The per-sub-block integer scales are folded into two int8 weight
+//    operands ("planes"), unpacked once per step and reused by all MT tiles,
+//    so a super-block is two int32 MFMA accumulations per tile:
+//      Q4_K: sc (6 bit) = 8 hi + lo; planes q lo, q hi (<= 105); S = 8 R1 + R0.
+//      Q5_K: planes of the centred q - 16 times the two 3-bit scale digits;
+//            S = 8 R1 + R0 + 16 sum_j sc_j bsum32_j, the last term on a
+//            second binary16 MFMA.
+//      Q6_K: P = sc (q - 32) in 16-bit lanes, planes P >> 6 in [-64, 64] and
+//            P & 63; S = 64 R1 + R0.
 //    The integer sums are exact.  The Q4_K/Q5_K min term
-//    Mn = sum_j m_j * (bsum_2j + bsum_2j+1) runs on one
+//    Mn = sum_j m_j (bsum_2j + bsum_2j+1) runs on one
 //    v_mfma_f32_32x32x16_f16 per tile (m_j <= 63 and |bsum| <= 2032 are exact
 //    in binary16, the products and the sum of 16 are exact in binary32).
-//  * Epilogue per output and super-block: y += da * (d * S - dmin * Mn) in
+//  * Epilogue per output and super-block: y += da (d S - dmin Mn) in
 //    binary32 with fused multiply-adds; the fp32 order is the kernel's own
 //    and fixed, so two runs are bitwise equal.
 //  * Split K (deterministic): a grid with too few tiles to fill the chip
@@ -49,6 +49,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <atomic>
 #include <type_traits>
 
@@ -68,17 +69,6 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kBN = 128;  // weight rows per workgroup (four waves of 32)
 constexpr int kKS = 256;  // K per step (one super-block)
-
-template <int WT>
-struct KT;
-// P planes; BB bytes per block; RB bytes per block row in LDS (16-aligned);
-// PC 16-byte pieces loaded per row (the last may be short); kMin: scales and mins.
-template <>
-struct KT<0> { static constexpr int P = 2, BB = 144, RB = 144, PC = 9; static constexpr bool kMin = true; };
-template <>
-struct KT<1> { static constexpr int P = 3, BB = 210, RB = 224, PC = 14; static constexpr bool kMin = false; };
-template <>
-struct KT<3> { static constexpr int P = 3, BB = 176, RB = 176, PC = 11; static constexpr bool kMin = true; };
 
 // The four bytes of v times f, when every byte product lies in [0, 255]: one
 // packed 16-bit multiply (the low byte of a 16-bit lane cannot carry into the
@@ -158,7 +148,6 @@ struct GroupArgs {
     int top_k;
     int per_row;            // 1: pair p reads activation row p; 0: row p / top_k
     int64_t expert_stride;  // bytes of one expert's [N][K/256] blocks
-    int tile_base;          // routed tile of workgroup row 0
 };
 
 struct Args {
@@ -370,8 +359,11 @@ struct KQ2 {
 // shared by the four waves).  Per step: unpack the planes of the whole
 // super-block once, then each activation tile in turn: 16 MFMAs (two planes
 // x eight 32-wide chunks), the binary16 min/centring MFMAs and the epilogue.
-template <int WT, int MT, bool kGrouped>
+// kMode: 0 dense; 1 routed rows with 32-bit activation offsets (rows * K
+// below 2^31, checked by the host); 2 routed rows with 64-bit offsets.
+template <int WT, int MT, int kMode>
 __global__ __launch_bounds__(256, 2) void gemm_kq2_kernel(Args a, GroupArgs ga) {
+    constexpr bool kGrouped = kMode != 0;
     using U = Unpack<WT>;
     using T = KQ2<WT>;
     constexpr int NT = 256;
@@ -385,8 +377,9 @@ __global__ __launch_bounds__(256, 2) void gemm_kq2_kernel(Args a, GroupArgs ga) 
 
     __shared__ __attribute__((aligned(16))) int8_t sA0[BM * kKS];
     __shared__ __attribute__((aligned(16))) int8_t sA1[BM * kKS];
-    __shared__ __attribute__((aligned(16))) float sD0[BM < 64 ? 64 : BM];
-    __shared__ __attribute__((aligned(16))) float sD1[BM < 64 ? 64 : BM];
+    // the d DMA writes 64 floats per instruction: NDI * 64 >= BM (96-row tiles: 128)
+    __shared__ __attribute__((aligned(16))) float sD0[64 * NDI];
+    __shared__ __attribute__((aligned(16))) float sD1[64 * NDI];
     __shared__ __attribute__((aligned(16))) _Float16 sB0[kB16 ? BM * 16 : 8];
     __shared__ __attribute__((aligned(16))) _Float16 sB1[kB16 ? BM * 16 : 8];
     __shared__ int sRow[BM];
@@ -397,14 +390,13 @@ __global__ __launch_bounds__(256, 2) void gemm_kq2_kernel(Args a, GroupArgs ga) 
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, h = lane >> 5;
+    // activation byte offsets: 32-bit while the host keeps rows * K below
+    // 2^31 (one launch of the dense GEMM, most routed calls), else 64-bit
+    using AOff = typename std::conditional<kMode == 2, uint64_t, uint32_t>::type;
 
-    const int nwg = a.nblk_n * a.nblk_m * a.splits;
-    int g = blockIdx.x;
-    if ((nwg & 7) == 0) g = (g & 7) * (nwg >> 3) + (g >> 3);
-    const int nb = g % a.nblk_n;
-    const int rest = g / a.nblk_n;
-    const int mb = rest % a.nblk_m;
-    const int sp = rest / a.nblk_m;
+    // One output unit: weight-row block nb, activation-row block (or routed
+    // tile) mb, K part sp.
+    auto run_unit = [&](const int nb, const int mb, const int sp) __attribute__((always_inline)) {
     const int n0 = nb * kBN;
     const int nsteps_all = a.K / kKS;
     const int s_begin = (int)(((int64_t)nsteps_all * sp) / a.splits);
@@ -413,8 +405,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kq2_kernel(Args a, GroupArgs ga) 
 
     const uint8_t* W = a.W;
     if (kGrouped) {
-        const int tix = ga.tile_base + mb;
-        if (tix >= *ga.ntiles) return;  // uniform: the whole workgroup leaves
+        const int tix = mb;
         const int e = ga.tiles[4 * tix + 0];
         const int first = ga.tiles[4 * tix + 1];
         const int rows = ga.tiles[4 * tix + 2];
@@ -451,28 +442,28 @@ __global__ __launch_bounds__(256, 2) void gemm_kq2_kernel(Args a, GroupArgs ga) 
     // lane -> row 4 gi + lane/16, physical chunk lane%16 holding logical chunk
     // (lane%16) ^ (row & 15); 32-bit offsets from the activation base (the host
     // keeps rows * K below 2^31)
-    uint32_t aoff[AIPW];
+    AOff aoff[AIPW];
 #pragma unroll
     for (int j = 0; j < AIPW; ++j) {
         const int gi = wave + 4 * j;
         const int r = 4 * gi + (lane >> 4);
         int ar = (gi < NAI) ? sRow[r] : -1;
         ar = ar >= 0 ? ar : 0;  // rows past the tile read row 0 (never stored)
-        aoff[j] = (uint32_t)ar * (uint32_t)a.K + 16u * (uint32_t)((lane & 15) ^ (r & 15));
+        aoff[j] = (AOff)ar * (AOff)a.K + (AOff)(16u * (uint32_t)((lane & 15) ^ (r & 15)));
     }
-    uint32_t doff;
+    AOff doff;
     {
         const int r = 64 * wave + lane;
         int ar = (r < BM) ? sRow[r] : -1;
         ar = ar >= 0 ? ar : 0;
-        doff = (uint32_t)ar * (uint32_t)nbk;
+        doff = (AOff)ar * (AOff)nbk;
     }
-    uint32_t boff = 0;
+    AOff boff = 0;
     if (kB16) {
         const int r = tid >> 1;
         int ar = (tid < BSI) ? sRow[r] : -1;
         ar = ar >= 0 ? ar : 0;
-        boff = (uint32_t)ar * (uint32_t)(a.K / 16) + 8u * (uint32_t)(tid & 1);
+        boff = (AOff)ar * (AOff)(a.K / 16) + (AOff)(8u * (uint32_t)(tid & 1));
     }
 
     u4v raw[8];
@@ -668,6 +659,26 @@ __global__ __launch_bounds__(256, 2) void gemm_kq2_kernel(Args a, GroupArgs ga) 
             }
         }
     }
+    };  // run_unit
+
+    if constexpr (kGrouped) {
+        // Routed tiles: the grid is sized to the chip, not to the worst-case
+        // tile count; each workgroup takes units blockIdx.x, + gridDim.x, ...
+        // (column block fastest) up to the routing's device tile count.
+        const int units = __builtin_amdgcn_readfirstlane(*ga.ntiles) * a.nblk_n;
+        for (int u = blockIdx.x; u < units; u += gridDim.x) {
+            run_unit(u % a.nblk_n, u / a.nblk_n, 0);
+            __syncthreads();  // the unit's LDS reads are done before the next unit's writes
+        }
+    } else {
+        // Dense: one unit per workgroup, consecutive units on one XCD
+        // (workgroups are dealt to the eight XCDs round-robin).
+        const int nwg = a.nblk_n * a.nblk_m * a.splits;
+        int g = blockIdx.x;
+        if ((nwg & 7) == 0) g = (g & 7) * (nwg >> 3) + (g >> 3);
+        const int rest = g / a.nblk_n;
+        run_unit(g % a.nblk_n, rest % a.nblk_m, rest / a.nblk_m);
+    }
 }
 
 }  // namespace kq
@@ -758,7 +769,7 @@ static hipError_t launch_kq_dense(const uint8_t* W, int64_t N, int64_t K, const 
     const int64_t nwg = tiles * s;
     if (nwg > INT32_MAX) return hipErrorInvalidValue;
     kq::GroupArgs ga = {};
-    kq::gemm_kq2_kernel<WT, kDenseMT, false><<<dim3((unsigned)nwg), kDenseNT, 0, st>>>(a, ga);
+    kq::gemm_kq2_kernel<WT, kDenseMT, 0><<<dim3((unsigned)nwg), kDenseNT, 0, st>>>(a, ga);
     return hipGetLastError();
 }
 
@@ -803,6 +814,94 @@ hipError_t launch_gemm_kq(int wtype, const uint8_t* W, int64_t N, int64_t K, con
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+// Routed tile height of a grouped call (the routed-compact "J rule" of
+// strix-llama.cpp PR #18, restated for 32-row MFMA tiles): tiles are sized
+// from the rows each expert receives, not from the total pair count.  The
+// weights dominate the grouped call's traffic, so the height is the smallest
+// multiple of 32 (at most 128) that holds the mean rows per expert
+// r = T top_k / E plus three standard deviations of a uniform routing
+// (sqrt r): nearly every expert is then one tile and its weights are read
+// once.  r = 16 -> 32 rows, 32 -> 64, 64 -> 96, 128 -> 128 (two tiles).
+// Q8_0 keeps its GEMM's 96-row tiles.  A call whose activation rows take
+// 2^31 bytes or more runs the 64-bit-offset kernel, capped at 64-row tiles.
+int grouped_tile_rows(int wtype, int64_t E, int64_t T, int64_t top_k, int64_t K, int per_row) {
+    if (wtype == 2) return kGroupTileRows;
+    if (E <= 0 || T <= 0) return kGroupMinTileRows;
+    const double r = (double)T * (double)top_k / (double)E;
+    const int mt = (int)std::ceil((r + 3.0 * std::sqrt(r)) / 32.0);
+    int rows = 32 * std::min(4, std::max(1, mt));
+    const int64_t arows = per_row ? T * top_k : T;
+    if (arows * K >= ((int64_t)1 << 31)) rows = std::min(rows, 64);
+    return rows;
+}
+
+template <int WT, int MT, int kMode>
+static hipError_t launch_kq_grouped_t(const uint8_t* W, int64_t E, int64_t N, int64_t K, const void* aqs,
+                                      const void* ad, const void* aux, int64_t T, int64_t top_k, int per_row,
+                                      const RouteWs& ws, float* Y, hipStream_t st) {
+    const int64_t nbk = K / 256;
+    kq::Args a = {};
+    a.W = W;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.aqs = (const int8_t*)aqs;
+    a.ad = (const float*)ad;
+    a.abs = (const int16_t*)aux;
+    a.M = (int)(per_row ? T * top_k : T);
+    a.Y = Y;
+    a.ldy = N;
+    a.splits = 1;
+    a.nblk_n = (int)((N + kq::kBN - 1) / kq::kBN);
+    // the tile table holds at most ceil(pairs / rows) + E tiles
+    const int64_t max_tiles = (T * top_k + 32 * MT - 1) / (32 * MT) + E;
+    a.nblk_m = (int)max_tiles;
+    kq::GroupArgs ga = {};
+    ga.tiles = ws.tiles;
+    ga.ntiles = ws.ntiles;
+    ga.list = ws.list;
+    ga.top_k = (int)top_k;
+    ga.per_row = per_row;
+    ga.expert_stride = N * nbk * kq::KQ2<WT>::BB;
+    const int64_t units = max_tiles * a.nblk_n;
+    const int64_t grid = std::min<int64_t>(units, (int64_t)num_cus() * kResident);
+    if (grid <= 0) return hipSuccess;
+    kq::gemm_kq2_kernel<WT, MT, kMode><<<dim3((unsigned)grid), kDenseNT, 0, st>>>(a, ga);
+    return hipGetLastError();
+}
+
+template <int WT>
+static hipError_t launch_kq_grouped_w(int tile_rows, const uint8_t* W, int64_t E, int64_t N, int64_t K,
+                                      const void* aqs, const void* ad, const void* aux, int64_t T, int64_t top_k,
+                                      int per_row, const RouteWs& ws, float* Y, hipStream_t st) {
+    const int64_t arows = per_row ? T * top_k : T;
+    if (arows * K >= ((int64_t)1 << 31)) {
+        // 64-bit activation offsets (more registers): at most 64-row tiles
+        if (tile_rows == 32)
+            return launch_kq_grouped_t<WT, 1, 2>(W, E, N, K, aqs, ad, aux, T, top_k, per_row, ws, Y, st);
+        if (tile_rows == 64)
+            return launch_kq_grouped_t<WT, 2, 2>(W, E, N, K, aqs, ad, aux, T, top_k, per_row, ws, Y, st);
+        return hipErrorInvalidValue;  // grouped_tile_rows never gives more here
+    }
+    switch (tile_rows) {
+        case 32: return launch_kq_grouped_t<WT, 1, 1>(W, E, N, K, aqs, ad, aux, T, top_k, per_row, ws, Y, st);
+        case 64: return launch_kq_grouped_t<WT, 2, 1>(W, E, N, K, aqs, ad, aux, T, top_k, per_row, ws, Y, st);
+        case 96: return launch_kq_grouped_t<WT, 3, 1>(W, E, N, K, aqs, ad, aux, T, top_k, per_row, ws, Y, st);
+        case 128: return launch_kq_grouped_t<WT, 4, 1>(W, E, N, K, aqs, ad, aux, T, top_k, per_row, ws, Y, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_gemm_kq_grouped(int wtype, const uint8_t* W, int64_t E, int64_t N, int64_t K, const void* aqs,
+                                  const void* ad, const void* aux, int64_t T, int64_t top_k, int per_row,
+                                  int tile_rows, RouteWs ws, float* Y, hipStream_t st) {
+    if (T == 0 || N == 0) return hipSuccess;
+    if (wtype == 0)
+        return launch_kq_grouped_w<0>(tile_rows, W, E, N, K, aqs, ad, aux, T, top_k, per_row, ws, Y, st);
+    if (wtype == 1)
+        return launch_kq_grouped_w<1>(tile_rows, W, E, N, K, aqs, ad, aux, T, top_k, per_row, ws, Y, st);
+    return launch_kq_grouped_w<3>(tile_rows, W, E, N, K, aqs, ad, aux, T, top_k, per_row, ws, Y, st);
 }
 
 }  // namespace vqk

@@ -33,11 +33,10 @@
 namespace vqk {
 
 constexpr int kRouteChunk = 64;   // tokens per routing chunk
-constexpr int kTileRows = kGroupTileRows;
 
 size_t route_ws_layout(int64_t E, int64_t T, int64_t top_k, RouteWs* ws, uint8_t* base) {
     const int64_t nchunks = (T + kRouteChunk - 1) / kRouteChunk;
-    const int64_t max_tiles = (T * top_k + kTileRows - 1) / kTileRows + E;
+    const int64_t max_tiles = (T * top_k + kGroupMinTileRows - 1) / kGroupMinTileRows + E;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t o = off;
@@ -119,7 +118,8 @@ __global__ __launch_bounds__(64) void route_count_kernel(const int32_t* __restri
 // slot, rows).  kScanThreads / E threads share one expert's chunks.
 constexpr int kScanThreads = 1024;
 constexpr int64_t kScanStageCells = 12288;  // chunk-table cells staged in LDS (48 KiB)
-__global__ __launch_bounds__(kScanThreads) void route_scan_kernel(int nchunks, int E, int32_t* __restrict__ chunk,
+__global__ __launch_bounds__(kScanThreads) void route_scan_kernel(int nchunks, int E, int tile_rows,
+                                                                  int32_t* __restrict__ chunk,
                                                                   int32_t* __restrict__ counts,
                                                                   int32_t* __restrict__ offsets,
                                                                   int32_t* __restrict__ tiles,
@@ -186,7 +186,7 @@ __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(int nchunks, i
         st[ex] = 0;
     }
     __syncthreads();
-    const int nt = lead ? (total + kTileRows - 1) / kTileRows : 0;
+    const int nt = lead ? (total + tile_rows - 1) / tile_rows : 0;
     if (lead) {
         sc[e] = total;
         st[e] = nt;
@@ -216,8 +216,8 @@ __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(int nchunks, i
         const int tbase = st[e] - nt;
         for (int i = 0; i < nt; ++i) {
             tiles[4 * (tbase + i) + 0] = e;
-            tiles[4 * (tbase + i) + 1] = off + i * kTileRows;
-            tiles[4 * (tbase + i) + 2] = min(kTileRows, total - i * kTileRows);
+            tiles[4 * (tbase + i) + 1] = off + i * tile_rows;
+            tiles[4 * (tbase + i) + 2] = min(tile_rows, total - i * tile_rows);
             tiles[4 * (tbase + i) + 3] = 0;
         }
         if (e == E - 1) ntiles[0] = st[e];
@@ -238,14 +238,15 @@ __global__ __launch_bounds__(256) void route_place_kernel(const int32_t* __restr
     list[offsets[e] + chunk[c * E + e] + rank[p]] = (int32_t)p;
 }
 
-hipError_t launch_route(const int32_t* ids, int64_t T, int64_t top_k, int64_t E, RouteWs ws,
+hipError_t launch_route(const int32_t* ids, int64_t T, int64_t top_k, int64_t E, int tile_rows, RouteWs ws,
                         hipStream_t st) {
+    if (tile_rows < kGroupMinTileRows) return hipErrorInvalidValue;
     const int nchunks = (int)((T + kRouteChunk - 1) / kRouteChunk);
     if (nchunks > 0)
         route_count_kernel<<<nchunks, 64, 0, st>>>(ids, (int)T, (int)top_k, (int)E, ws.chunk, ws.rank);
     const int64_t ncell = (int64_t)nchunks * E;
     const size_t stage = (ncell <= kScanStageCells) ? (size_t)ncell * 4 : 0;
-    route_scan_kernel<<<1, kScanThreads, stage, st>>>(nchunks, (int)E, ws.chunk, ws.counts, ws.offsets, ws.tiles,
+    route_scan_kernel<<<1, kScanThreads, stage, st>>>(nchunks, (int)E, tile_rows, ws.chunk, ws.counts, ws.offsets, ws.tiles,
                                                       ws.ntiles);
     const int64_t npairs = T * top_k;
     if (npairs > 0)

@@ -484,7 +484,8 @@ static vq_status gemm_grouped_impl(const char* fn, int per_row, int w, const voi
     vqk::RouteWs rws;
     vqk::route_ws_layout(E, T, top_k, &rws, (uint8_t*)ws);
     g_stats.route++;
-    vq_status s = hip_status(vqk::launch_route(ids, T, top_k, E, rws, stream), fn);
+    const int tile_rows = vqk::grouped_tile_rows(w, E, T, top_k, K, per_row);
+    vq_status s = hip_status(vqk::launch_route(ids, T, top_k, E, tile_rows, rws, stream), fn);
     if (s != VQ_OK) return s;
     if (w == VQ_Q4_K) g_stats.gemm_grouped_q4k++;
     else if (w == VQ_Q6_K) g_stats.gemm_grouped_q6k++;
@@ -494,11 +495,11 @@ static vq_status gemm_grouped_impl(const char* fn, int per_row, int w, const voi
     hipError_t e;
     if (act == VQ_Q8_K) {
         const vqk::ActQ8K a = act_q8k((void*)Xq, arows, K);
-        e = vqk::launch_gemm_grouped(w, (const uint8_t*)W, E, N, K, a.qs, a.d, a.bsums, T, top_k, per_row, rws, Y,
+        e = vqk::launch_gemm_grouped(w, (const uint8_t*)W, E, N, K, a.qs, a.d, a.bsums, T, top_k, per_row, tile_rows, rws, Y,
                                      stream);
     } else {
         const vqk::ActQ81 a = act_q81((void*)Xq, arows, K);
-        e = vqk::launch_gemm_grouped(w, (const uint8_t*)W, E, N, K, a.qs, a.d, nullptr, T, top_k, per_row, rws, Y,
+        e = vqk::launch_gemm_grouped(w, (const uint8_t*)W, E, N, K, a.qs, a.d, nullptr, T, top_k, per_row, tile_rows, rws, Y,
                                      stream);
     }
     s = hip_status(e, fn);

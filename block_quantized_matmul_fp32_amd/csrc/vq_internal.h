@@ -10,13 +10,14 @@
 
 namespace vqk {
 
-// Rows of one routed-expert GEMM tile; the routing scan writes its tile table
-// in these units and the grouped GEMM consumes it.  96 rows (four waves of
-// 32 weight rows x 48 activation rows): with 64 +- 8 rows per expert (uniform
-// top-8 of 256 over 2048 tokens) nearly every expert takes one tile, where
-// 64-row tiles gave half of them a second, mostly empty tile (measured 7-11%
-// faster; 128-row tiles and six waves of 32 x 32 measured no faster).
+// Routed-expert GEMM tiles: the routing scan writes its tile table in units
+// of a per-call tile height and the grouped GEMM consumes it.  The Q8_0
+// grouped GEMM keeps 96-row tiles (four waves of 32 weight rows x 48
+// activation rows); the K-quant one takes 32, 64, 96 or 128 rows from the
+// rows per expert (grouped_tile_rows).  The tile table is sized for the
+// smallest height.
 constexpr int kGroupTileRows = 96;
+constexpr int kGroupMinTileRows = 32;
 
 // Planar activation buffers (include/vq.h).
 struct ActQ8K {
@@ -88,11 +89,17 @@ struct RouteWs {
     int32_t* ntiles;   // [1]
 };
 size_t route_ws_layout(int64_t E, int64_t T, int64_t top_k, RouteWs* ws, uint8_t* base);
-hipError_t launch_route(const int32_t* ids, int64_t T, int64_t top_k, int64_t E, RouteWs ws,
+// Routed tile height of the grouped GEMM for a call (a multiple of 32).
+int grouped_tile_rows(int wtype, int64_t E, int64_t T, int64_t top_k, int64_t K, int per_row);
+hipError_t launch_route(const int32_t* ids, int64_t T, int64_t top_k, int64_t E, int tile_rows, RouteWs ws,
                         hipStream_t st);
 hipError_t launch_gemm_grouped(int wtype, const uint8_t* W, int64_t E, int64_t N, int64_t K, const void* act_qs,
                                const void* act_d, const void* act_aux, int64_t T, int64_t top_k, int per_row,
-                               RouteWs ws, float* Y, hipStream_t st);
+                               int tile_rows, RouteWs ws, float* Y, hipStream_t st);
+// K-quant routed-expert GEMM on the MFMA core of the dense K-quant GEMM.
+hipError_t launch_gemm_kq_grouped(int wtype, const uint8_t* W, int64_t E, int64_t N, int64_t K, const void* aqs,
+                                  const void* ad, const void* aux, int64_t T, int64_t top_k, int per_row,
+                                  int tile_rows, RouteWs ws, float* Y, hipStream_t st);
 hipError_t launch_weighted_sum(const float* Y, const float* w, int64_t T, int64_t top_k, int64_t N,
                                float* Ysum, hipStream_t st);
 

@@ -256,14 +256,14 @@ int64_t vq_small_batch_max(int w);
 /* Row blocks of the MFMA arm of vq_gemm.  The GEMM kernel addresses the    */
 /* activation bytes of one launch with 32-bit offsets, so vq_gemm launches  */
 /* it once per block of at most floor(2^31 / K) rows (rounded down to the   */
-/* tile height), which is one launch for every practical shape; the grouped */
-/* calls likewise launch their GEMM once per 32768 routed tiles.  rows > 0  */
+/* tile height), which is one launch for every practical shape; the Q8_0   */
+/* grouped GEMM likewise launches once per 32768 routed tiles.  rows > 0    */
 /* caps the block at that many rows (any value; for tests of the blocking)  */
-/* and the grouped launches at max(1, rows / 96) routed tiles of 96 rows;   */
-/* 0 restores the default.  The K-quant results stay within the GEMM's     */
-/* tolerance under any blocking (a block's K splits depend on its rows);    */
-/* Q8_0 results do not depend on it.  Per calling thread: other threads     */
-/* keep their own.  rows < 0: VQ_ERR_INVALID_ARG.                           */
+/* and the Q8_0 grouped launches at max(1, rows / 96) routed tiles of 96    */
+/* rows; 0 restores the default.  The K-quant results stay within the     */
+/* GEMM's tolerance under any blocking (a block's K splits depend on its   */
+/* rows); Q8_0 results do not depend on it.  Per calling thread: other     */
+/* threads keep their own.  rows < 0: VQ_ERR_INVALID_ARG.                  */
 /* ---------------------------------------------------------------------- */
 vq_status vq_set_gemm_row_block(int64_t rows);
 
@@ -286,6 +286,13 @@ vq_status vq_set_gemm_row_block(int64_t rows);
 /* call it holds, at offset 0, int32 counts[E], then int32 offsets[E+1],     */
 /* then int32 list[T*top_k] (pair indices t*top_k+s grouped per expert in   */
 /* ascending order), each section 256-byte aligned.                         */
+/* Tiles: the pairs of each expert are cut into routed tiles whose height   */
+/* comes from the mean rows per expert r = T*top_k/E ([P3] "routed-compact  */
+/* J rule"): the smallest of 32, 64, 96, 128 rows holding r + 3 sqrt(r), so */
+/* nearly every expert is one tile (Q8_0: 96 rows).  Numerics: routing and  */
+/* Ysum (of the Y written) are exact; the K-quant Y meets the tolerance of  */
+/* vq_gemm and two identical calls are bitwise equal; the Q8_0 Y is the     */
+/* fixed-order binary32 definition.                                         */
 /* Limits: E <= 1024, top_k <= 16, N % 16 == 0.                              */
 /* ---------------------------------------------------------------------- */
 size_t vq_grouped_workspace_bytes(int64_t E, int64_t T, int64_t top_k);

@@ -4,9 +4,9 @@ benchmark times (needs an MI355X).
 Weights are encoded on the host by the oracle and uploaded (the GPU encoder's
 bytes are checked equal to them separately), activations are quantized on the
 GPU and checked byte for byte against the oracle's.  The GEMV, Q8_0 GEMM,
-grouped and weighted-sum outputs are compared bit for bit with the oracle's
-fixed-order binary32 definition; the K-quant prefill GEMMs, whose combine and
-split-K order are their own, in full to the tolerance (NMSE <= 1e-6 against
+routing and weighted-sum outputs are compared bit for bit with the oracle's
+fixed-order binary32 definition; the K-quant prefill and grouped GEMMs, whose
+combine and split-K order are their own, to the tolerance (NMSE <= 1e-6 against
 the oracle, max relative error <= 5e-4 against the fp64 dequantized product)
 and two identical calls bitwise equal.  Outputs are compared in full where the
 oracle finishes in seconds, otherwise on sampled outputs (whole first and last
@@ -202,8 +202,8 @@ def test_q8_0_gemm_sampled():
 
 def test_grouped_moe_full_size():
     """256 experts of Q4_K [512, 2048], 2048 tokens, top-8 routing: routing
-    bitwise in full, Y on sampled tokens, Ysum bitwise in full against the
-    oracle's weighted sum of the GPU's Y."""
+    bitwise in full, Y on sampled tokens within the GEMM tolerance, Ysum
+    bitwise in full against the oracle's weighted sum of the GPU's Y."""
     cfg = synth.WORKLOADS["grouped_moe"]
     E, N, K, T, top_k = cfg["E"], cfg["N"], cfg["K"], cfg["T"], cfg["top_k"]
     Wq = np.concatenate([oracle.quantize_weights(oracle.Q4_K, synth.expert_weights(e, N, K))
@@ -229,7 +229,7 @@ def test_grouped_moe_full_size():
     toks = np.unique(np.concatenate([[0, 1, T - 1], np.random.default_rng(7200).integers(0, T, 29)]))
     act_s = oracle.quantize_q8k(X[toks])
     Y_ref = oracle.gemm_grouped(oracle.Q4_K, Wq, E, N, K, act_s, ids[toks], nthreads=THREADS)
-    H.assert_bitwise(Yh[toks], Y_ref, "grouped Y (sampled tokens)")
+    H.assert_close(Yh[toks], Y_ref, "grouped Y (sampled tokens)")
     H.assert_bitwise(H.host(S), oracle.weighted_sum(Yh, rw), "Ysum")
 
 
@@ -255,5 +255,5 @@ def test_grouped_moe_down_per_row_full_size():
     rows = (toks[:, None] * top_k + np.arange(top_k)[None, :]).reshape(-1)
     act_s = oracle.quantize_q8k(X[rows])
     Y_ref = oracle.gemm_grouped(oracle.Q4_K, Wq, E, N, K, act_s, ids[toks], nthreads=THREADS, per_row=True)
-    H.assert_bitwise(Yh[toks], Y_ref, "grouped down Y (sampled tokens)")
+    H.assert_close(Yh[toks], Y_ref, "grouped down Y (sampled tokens)")
     H.assert_bitwise(H.host(S), oracle.weighted_sum(Yh, rw), "Ysum")

@@ -4,7 +4,8 @@ library's static per-GPU scratch array (needs an MI355X).
 Checked through the C ABI against vq_gemm_grouped with a caller workspace:
 Y and Ysum bit-identical, on two calls in a row, the second with fewer tokens
 and a different routing (the array keeps the first call's contents), and both
-against the oracle.  Sizes beyond the array are rejected before any launch.
+against the oracle (Y within the GEMM tolerance, Ysum bitwise).  Sizes beyond
+the array are rejected before any launch.
 """
 import numpy as np
 import pytest
@@ -54,7 +55,7 @@ def test_noalloc_matches_workspace_call():
         H.assert_bitwise(Y2h, Y1h, "no-alloc Y vs workspace call, T=%d" % T)
         H.assert_bitwise(H.host(S2), H.host(S1), "no-alloc Ysum vs workspace call, T=%d" % T)
         Y_ref = oracle.gemm_grouped(oracle.Q4_K, Wq, E, N, K, oracle.quantize_q8k(X), ids, nthreads=8)
-        H.assert_bitwise(Y2h, Y_ref, "no-alloc Y vs oracle, T=%d" % T)
+        H.assert_close(Y2h, Y_ref, "no-alloc Y vs oracle, T=%d" % T)
         H.assert_bitwise(H.host(S2), oracle.weighted_sum(Y2h, rw), "no-alloc Ysum vs oracle, T=%d" % T)
 
 
