@@ -8,10 +8,16 @@ synthetic data.  value = algorithmic bytes of the step (compressed weights,
 fp32 x and y) / time, in GB/s, with the weights rotated through more buffer
 sets than the 256 MB Infinity Cache holds, so every step streams from HBM.
 
+Timing: each timed quantity is a HIP graph of calls over weight copies
+rotated past the Infinity Cache (cold), replayed several times, each replay
+timed with HIP events; the figure is the median over replays of the per-call
+time.
+
 The same line carries:
-  roofline     -- the dominant kernel (the Q6_K GEMV) against 8 TB/s HBM, its
-                  average launch duration from HIP events recorded around
-                  each of its launches in the timed region;
+  roofline     -- the dominant kernel (the Q6_K GEMV) against 8 TB/s HBM,
+                  achieved from its median cold launch duration (the mean
+                  beside it), and its streaming floor: the same weight bytes
+                  in the same launch shape with no compute (vq_stream_probe);
   cpu_baseline -- the CPU oracle running the same decode step on the host's
                   cores (a bounded number of repetitions);
   prefill / q8_0 / grouped / quantizer -- the prefill GEMM (int8 TOPS), the
@@ -93,12 +99,16 @@ def time_launches(fn, iters, warmup=3):
     return sum(a.elapsed_time(b) for a, b in pairs) / iters
 
 
-def time_graph(fn, per_graph, min_calls, warmup=2):
-    """Average duration (ms) of one call of fn, from HIP events around replays
-    of a HIP graph that holds `per_graph` back-to-back calls fn(0..per_graph-1),
-    recorded on the stream the graph replays on.  A host launch costs several
-    microseconds, more than the decode kernels run, so eager back-to-back
-    launches would time the host; the graph times the GPU."""
+def time_graph(fn, per_graph, min_calls, warmup=2, stats=None):
+    """Duration (ms) of one call of fn: a HIP graph holds `per_graph`
+    back-to-back calls fn(0..per_graph-1) (one per rotation set, so each call
+    is cold when the sets outgrow the Infinity Cache); each replay is timed on
+    its own with HIP events recorded on the stream the graph replays on, and
+    the result is the median over replays of the per-call time.  A host launch
+    costs several microseconds, more than the decode kernels run, so eager
+    back-to-back launches would time the host; the graph times the GPU.
+    Returns (median ms, calls timed); `stats`, if given, receives the mean and
+    the spread."""
     import torch
     for i in range(max(warmup, 1)):
         fn(i)
@@ -112,17 +122,65 @@ def time_graph(fn, per_graph, min_calls, warmup=2):
                 fn(i)
     torch.cuda.current_stream().wait_stream(cap)
     torch.cuda.synchronize()
-    reps = max(1, math.ceil(min_calls / per_graph))
+    reps = max(3, math.ceil(min_calls / per_graph))
     for _ in range(warmup):
         g.replay()
     torch.cuda.synchronize()
-    t0, t1 = event_pair()
-    t0.record()
-    for _ in range(reps):
+    pairs = [event_pair() for _ in range(reps)]
+    for a, b in pairs:
+        a.record()
         g.replay()
-    t1.record()
+        b.record()
     torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / (reps * per_graph), reps * per_graph
+    per = sorted(a.elapsed_time(b) / per_graph for a, b in pairs)
+    med = per[len(per) // 2] if len(per) % 2 else 0.5 * (per[len(per) // 2 - 1] + per[len(per) // 2])
+    if stats is not None:
+        stats["mean_ms"] = sum(per) / len(per)
+        stats["min_ms"] = per[0]
+        stats["max_ms"] = per[-1]
+        stats["replays"] = reps
+    return med, reps * per_graph
+
+
+def cpu_threads():
+    """(threads used, cores in the affinity mask, why): every affinity core,
+    unless the environment sets the host's CPU share per GPU in
+    OMP_NUM_THREADS, which then caps it."""
+    cores = len(os.sched_getaffinity(0))
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    if share.isdigit() and 0 < int(share) < cores:
+        return int(share), cores, "OMP_NUM_THREADS=%s: the host's CPU share for this GPU" % share
+    return cores, cores, "every core in the affinity mask"
+
+
+def run_cpu_fp64_reference(reps_max: int = 20, seconds: float = 5.0):
+    """The fp64 dequantize-then-matmul reference (numpy) on the decode step,
+    with its BLAS library's own thread count."""
+    import numpy as np
+    import oracle
+    from oracle import ref_fp64
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        info = [d for d in threadpool_info() if d.get("user_api") == "blas"]
+    except Exception:  # threadpoolctl missing: the count stays unknown
+        info = []
+    blas = {"library": info[0].get("internal_api"), "threads": info[0].get("num_threads")} if info else None
+    Qa = oracle.quantize_weights(oracle.Q4_K, synth.tensor("decode_gemv", "Wa"))
+    Qb = oracle.quantize_weights(oracle.Q6_K, synth.tensor("decode_gemv", "Wb"))
+    aa = oracle.quantize_q8k(synth.tensor("decode_gemv", "xa"))
+    ab = oracle.quantize_q8k(synth.tensor("decode_gemv", "xb"))
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        ref_fp64.gemm_fp64(oracle.Q4_K, Qa, 9728, 2560, aa)
+        ref_fp64.gemm_fp64(oracle.Q6_K, Qb, 2560, 9728, ab)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= reps_max:
+            break
+    return {"ms_per_step": round(1e3 * el / reps, 2), "repetitions": reps, "blas": blas,
+            "what": "numpy fp64 dequantize-then-matmul of the decode step (both GEMVs)"}
 
 
 def run_cpu_baseline(seconds: float):
@@ -132,7 +190,7 @@ def run_cpu_baseline(seconds: float):
     import numpy as np
     import oracle
     import synth
-    threads = min(16, len(os.sched_getaffinity(0)))
+    threads, cores, why = cpu_threads()
     Wa = synth.tensor("decode_gemv", "Wa")
     Wb = synth.tensor("decode_gemv", "Wb")
     xa = synth.tensor("decode_gemv", "xa")
@@ -151,6 +209,7 @@ def run_cpu_baseline(seconds: float):
         if el >= seconds or reps >= 100000:
             break
     return {"value": round(step_bytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "affinity_cores": cores, "threads_reason": why,
             "kind": "oracle", "cpu_model": cpu_model(),
             "sample": "%d repetitions of the full decode step (Q8_K quantization of x plus the Q4_K "
                       "[9728,2560] and Q6_K [2560,9728] GEMVs) in %.1f s with %d threads" % (reps, el, threads),
@@ -199,10 +258,19 @@ def run_decode(args, torch, vq, synth):
     ms, steps_timed = time_graph(step, R, args.steps, warmup=max(2, args.warmup // R))
     # Per-kernel average launch duration: the same, with one kernel per node.
     ka, _ = time_graph(lambda i: vq.gemv(vq.Q4_K, Qa[i % R], 9728, 2560, xa, y=ya[i % R]), R, args.steps)
-    kb, _ = time_graph(lambda i: vq.gemv(vq.Q6_K, Qb[i % R], 2560, 9728, xb, y=yb[i % R]), R, args.steps)
+    kb_stats = {}
+    kb, _ = time_graph(lambda i: vq.gemv(vq.Q6_K, Qb[i % R], 2560, 9728, xb, y=yb[i % R]), R, args.steps,
+                       stats=kb_stats)
     assert torch.isfinite(ya[0]).all() and torch.isfinite(yb[0]).all()
-    return {"ms_per_step": ms, "q4k_ms": ka, "q6k_ms": kb, "rotation_sets": R, "steps_timed": steps_timed,
-            "rotation_mb": round(R * set_bytes / (1 << 20), 1)}
+    # the streaming floor of each GEMV launch: its weight bytes, its launch
+    # shape, the same rotation, no compute
+    sink = torch.zeros(9728, dtype=torch.int32, device=dev)
+    fa, _ = time_graph(lambda i: vq.stream_probe(vq.Q4_K, Qa[i % R], 9728, 2560, sink), R, args.steps)
+    fb, _ = time_graph(lambda i: vq.stream_probe(vq.Q6_K, Qb[i % R], 2560, 9728, sink), R, args.steps)
+    assert int(sink.abs().sum()) == 0
+    return {"ms_per_step": ms, "q4k_ms": ka, "q6k_ms": kb, "q6k_mean_ms": kb_stats["mean_ms"],
+            "q4k_floor_ms": fa, "q6k_floor_ms": fb,
+            "rotation_sets": R, "steps_timed": steps_timed, "rotation_mb": round(R * set_bytes / (1 << 20), 1)}
 
 
 def run_prefill(torch, vq, synth, iters):
@@ -210,9 +278,16 @@ def run_prefill(torch, vq, synth, iters):
     out = {}
     Wg = torch.from_numpy(synth.tensor("prefill_gemm", "Wgate")).to(dev)
     Wd = torch.from_numpy(synth.tensor("prefill_gemm", "Wdown")).to(dev)
-    Qg = vq.quantize_weights(vq.Q4_K, Wg)
-    Qd = vq.quantize_weights(vq.Q6_K, Wd)
+    Qg0 = vq.quantize_weights(vq.Q4_K, Wg)
+    Qd0 = vq.quantize_weights(vq.Q6_K, Wd)
     del Wg, Wd
+    # weight copies rotated past the Infinity Cache: every call reads its
+    # weights from HBM
+    Rg = max(2, math.ceil(640 * (1 << 20) / Qg0.numel()))
+    Rd = max(2, math.ceil(640 * (1 << 20) / Qd0.numel()))
+    Qg = [Qg0] + [Qg0.clone() for _ in range(Rg - 1)]
+    Qd = [Qd0] + [Qd0.clone() for _ in range(Rd - 1)]
+    out["rotation_sets"] = {"q4k": Rg, "q6k": Rd}
     for M in (512, 2048):
         Xh = torch.from_numpy(synth.prefill_activations("Xh", M)).to(dev)
         Xi = torch.from_numpy(synth.prefill_activations("Xi", M)).to(dev)
@@ -220,8 +295,8 @@ def run_prefill(torch, vq, synth, iters):
         qi = vq.quantize_act(vq.Q8_K, Xi)
         Yg = torch.empty((M, 9728), dtype=torch.float32, device=dev)
         Yd = torch.empty((M, 2560), dtype=torch.float32, device=dev)
-        tg, _ = time_graph(lambda i: vq.gemm(vq.Q4_K, Qg, 9728, 2560, vq.Q8_K, qh, M, Y=Yg), 4, iters)
-        td, _ = time_graph(lambda i: vq.gemm(vq.Q6_K, Qd, 2560, 9728, vq.Q8_K, qi, M, Y=Yd), 4, iters)
+        tg, _ = time_graph(lambda i: vq.gemm(vq.Q4_K, Qg[i % Rg], 9728, 2560, vq.Q8_K, qh, M, Y=Yg), Rg, 3 * Rg)
+        td, _ = time_graph(lambda i: vq.gemm(vq.Q6_K, Qd[i % Rd], 2560, 9728, vq.Q8_K, qi, M, Y=Yd), Rd, 3 * Rd)
         tq, _ = time_graph(lambda i: vq.quantize_act(vq.Q8_K, Xh, Xq=qh), 8, iters)
         ops = 2.0 * M * 9728 * 2560
         out["M%d" % M] = {
@@ -243,18 +318,21 @@ def run_q8_0(torch, vq, synth, iters):
     X = torch.from_numpy(synth.tensor("q8_0_gemm", "X")).to(dev)
     Xq = vq.quantize_act(vq.Q8_1, X)
     Y = torch.empty((2048, 4096), dtype=torch.float32, device=dev)
-    t, _ = time_graph(lambda i: vq.gemm(vq.Q8_0, Q, 4096, 2048, vq.Q8_1, Xq, 2048, Y=Y), 4, iters)
-    tq, _ = time_graph(lambda i: vq.quantize_act(vq.Q8_1, X, Xq=Xq), 8, iters)
     R = max(2, math.ceil(640 * (1 << 20) / Q.numel()))
     Qs = [Q] + [Q.clone() for _ in range(R - 1)]
+    t, _ = time_graph(lambda i: vq.gemm(vq.Q8_0, Qs[i % R], 4096, 2048, vq.Q8_1, Xq, 2048, Y=Y), R, 3 * R)
+    tq, _ = time_graph(lambda i: vq.quantize_act(vq.Q8_1, X, Xq=Xq), 8, iters)
     y = torch.empty(4096, dtype=torch.float32, device=dev)
     tv, _ = time_graph(lambda i: vq.gemv(vq.Q8_0, Qs[i % R], 4096, 2048, X[0], y=y), R, 200)
+    sink = torch.zeros(4096, dtype=torch.int32, device=dev)
+    tf, _ = time_graph(lambda i: vq.stream_probe(vq.Q8_0, Qs[i % R], 4096, 2048, sink), R, 200)
     ops = 2.0 * 2048 * 4096 * 2048
     gbytes = Q.numel() + 4 * 2048 + 4 * 4096
     return {"gemm_M2048_us": round(t * 1e3, 2), "gemm_tops": round(ops / (t * 1e-3) / 1e12, 1),
             "gemm_frac": round(ops / (t * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
             "gemv_us": round(tv * 1e3, 2), "gemv_gbs": round(gbytes / (tv * 1e-3) / 1e9, 1),
             "gemv_frac": round(gbytes / (tv * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "gemv_stream_floor_us": round(tf * 1e3, 2),
             "quantize_q8_1_us": round(tq * 1e3, 2),
             "quantize_q8_1_gbs": round(2048 * 2048 * (4 + 1 + 4 / 32) / (tq * 1e-3) / 1e9, 1)}
 
@@ -272,15 +350,18 @@ def run_q5k(torch, vq, synth, iters):
     x = torch.from_numpy(synth.tensor("q5k_decode", "x")).to(dev)
     y = torch.empty(N, dtype=torch.float32, device=dev)
     tv, _ = time_graph(lambda i: vq.gemv(vq.Q5_K, Qs[i % R], N, K, x, y=y), R, max(200, 4 * R))
+    sink = torch.zeros(N, dtype=torch.int32, device=dev)
+    tf, _ = time_graph(lambda i: vq.stream_probe(vq.Q5_K, Qs[i % R], N, K, sink), R, max(200, 4 * R))
     gbytes = Q.numel() + 4 * K + 4 * N
-    del Qs
+    Y = torch.empty((2048, N), dtype=torch.float32, device=dev)
     X = torch.from_numpy(synth.prefill_activations("Xh", 2048)).to(dev)
     Xq = vq.quantize_act(vq.Q8_K, X)
-    Y = torch.empty((2048, N), dtype=torch.float32, device=dev)
-    tg, _ = time_graph(lambda i: vq.gemm(vq.Q5_K, Q, N, K, vq.Q8_K, Xq, 2048, Y=Y), 4, iters)
+    tg, _ = time_graph(lambda i: vq.gemm(vq.Q5_K, Qs[i % R], N, K, vq.Q8_K, Xq, 2048, Y=Y), R, 3 * R)
+    del Qs
     ops = 2.0 * 2048 * N * K
     return {"gemv_us": round(tv * 1e3, 2), "gemv_gbs": round(gbytes / (tv * 1e-3) / 1e9, 1),
             "gemv_frac": round(gbytes / (tv * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "gemv_stream_floor_us": round(tf * 1e3, 2),
             "gemm_M2048_us": round(tg * 1e3, 2), "gemm_tops": round(ops / (tg * 1e-3) / 1e12, 1),
             "gemm_frac": round(ops / (tg * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)}
 
@@ -359,18 +440,44 @@ def run_grouped(torch, vq, synth, iters):
         vq.gemm_grouped(vq.Q4_K, sets[i % len(sets)], E, N, K, vq.Q8_K, Xq, T, ids, top_k, route_w=rw,
                         Y=Y, Ysum=S, ws=ws)
 
-    t_cold, _ = time_graph(lambda i: call(i, Qs), R, iters)
+    t_cold, _ = time_graph(lambda i: call(i, Qs), R, max(iters, 3 * R))
     t_warm, _ = time_graph(lambda i: call(i, [Q0]), 4, iters)
     ops = 2.0 * T * top_k * N * K
     alg = Q0.numel() + Xq.numel() + Y.numel() * 4 + S.numel() * 4 + T * top_k * 8
-    return {"route_gemm_sum_us_cold": round(t_cold * 1e3, 2),
-            "tops_cold": round(ops / (t_cold * 1e-3) / 1e12, 1),
-            "mfma_frac_cold": round(ops / (t_cold * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
-            "hbm_frac_cold": round(alg / (t_cold * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "route_gemm_sum_us_warm": round(t_warm * 1e3, 2),
-            "tops_warm": round(ops / (t_warm * 1e-3) / 1e12, 1),
-            "mfma_frac_warm": round(ops / (t_warm * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
-            "rotation_sets_cold": R, "algorithmic_bytes": int(alg)}
+    out = {"route_gemm_sum_us_cold": round(t_cold * 1e3, 2),
+           "tops_cold": round(ops / (t_cold * 1e-3) / 1e12, 1),
+           "mfma_frac_cold": round(ops / (t_cold * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
+           "hbm_frac_cold": round(alg / (t_cold * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "route_gemm_sum_us_warm": round(t_warm * 1e3, 2),
+           "tops_warm": round(ops / (t_warm * 1e-3) / 1e12, 1),
+           "mfma_frac_warm": round(ops / (t_warm * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
+           "rotation_sets_cold": R, "algorithmic_bytes": int(alg),
+           "rows_per_expert": T * top_k / E, "tile_rows": tile_rows(T * top_k / E)}
+    # 512 tokens (16 rows per expert): the first tokens of the same X and
+    # routing, the same expert weights
+    T2 = 512
+    Xq2 = vq.quantize_act(vq.Q8_K, X[:T2].contiguous())
+    ids2, rw2 = ids[:T2].contiguous(), rw[:T2].contiguous()
+    Y2 = torch.empty((T2, top_k, N), dtype=torch.float32, device=dev)
+    S2 = torch.empty((T2, N), dtype=torch.float32, device=dev)
+    ws2 = torch.empty(vq.grouped_workspace_bytes(E, T2, top_k), dtype=torch.uint8, device=dev)
+    t2, _ = time_graph(lambda i: vq.gemm_grouped(vq.Q4_K, Qs[i % R], E, N, K, vq.Q8_K, Xq2, T2, ids2, top_k,
+                                                 route_w=rw2, Y=Y2, Ysum=S2, ws=ws2), R, max(iters, 3 * R))
+    ops2 = 2.0 * T2 * top_k * N * K
+    alg2 = Q0.numel() + Xq2.numel() + Y2.numel() * 4 + S2.numel() * 4 + T2 * top_k * 8
+    out["n512"] = {"route_gemm_sum_us_cold": round(t2 * 1e3, 2),
+                   "tops_cold": round(ops2 / (t2 * 1e-3) / 1e12, 1),
+                   "mfma_frac_cold": round(ops2 / (t2 * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
+                   "hbm_frac_cold": round(alg2 / (t2 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                   "algorithmic_bytes": int(alg2), "rows_per_expert": T2 * top_k / E,
+                   "tile_rows": tile_rows(T2 * top_k / E)}
+    return out
+
+
+def tile_rows(r):
+    """The routed tile height the library picks at r rows per expert (for the
+    record: the smallest of 32, 64, 96, 128 rows holding r + 3 sqrt(r))."""
+    return 32 * min(4, max(1, math.ceil((r + 3.0 * math.sqrt(r)) / 32.0)))
 
 
 def run_grouped_down(torch, vq, synth, iters):
@@ -400,7 +507,7 @@ def run_grouped_down(torch, vq, synth, iters):
         vq.gemm_grouped(vq.Q4_K, sets[i % len(sets)], E, N, K, vq.Q8_K, Xq, T, ids, top_k, route_w=rw,
                         Y=Y, Ysum=S, ws=ws, per_row=True)
 
-    t_cold, _ = time_graph(lambda i: call(i, Qs), R, iters)
+    t_cold, _ = time_graph(lambda i: call(i, Qs), R, max(iters, 3 * R))
     ops = 2.0 * T * top_k * N * K
     alg = Q0.numel() + Xq.numel() + Y.numel() * 4 + S.numel() * 4 + T * top_k * 8
     return {"shape": "E=256 x Q4_K [2048,512], per-row Q8_K input [16384,512], top-8",
@@ -471,7 +578,9 @@ def main():
                 "frac": round(ach6 / HBM_PEAK_GBS, 4),
                 "traffic": traffic_from_profiles("gemv_q6k_decode", sha, b6),
                 "algorithmic_bytes_per_launch": b6,
-                "avg_launch_us": round(dec["q6k_ms"] * 1e3, 3),
+                "median_launch_us": round(dec["q6k_ms"] * 1e3, 3),
+                "avg_launch_us": round(dec["q6k_mean_ms"] * 1e3, 3),
+                "stream_floor_us": round(dec["q6k_floor_ms"] * 1e3, 3),
                 "source_sha": sha}
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
@@ -487,8 +596,12 @@ def main():
         "roofline": roofline,
         "decode_kernels": {"q4k_us": round(dec["q4k_ms"] * 1e3, 3), "q4k_gbs": round(ach4, 1),
                            "q4k_frac": round(ach4 / HBM_PEAK_GBS, 4),
+                           "q4k_stream_floor_us": round(dec["q4k_floor_ms"] * 1e3, 3),
                            "q6k_us": round(dec["q6k_ms"] * 1e3, 3), "q6k_gbs": round(ach6, 1),
-                           "q6k_frac": round(ach6 / HBM_PEAK_GBS, 4)},
+                           "q6k_frac": round(ach6 / HBM_PEAK_GBS, 4),
+                           "q6k_stream_floor_us": round(dec["q6k_floor_ms"] * 1e3, 3),
+                           "timing": "median over graph replays of rotated (cold) launches",
+                           "stream_floor": "vq_stream_probe: the GEMV's weight bytes and launch shape, no compute"},
     }
     if not args.no_secondary:
         it = args.secondary_iters
@@ -513,6 +626,8 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline (%.0f s)" % args.cpu_seconds)
         line["cpu_baseline"] = run_cpu_baseline(args.cpu_seconds)
+        log("[bench] fp64 reference (numpy)")
+        line["cpu_baseline"]["fp64_reference"] = run_cpu_fp64_reference()
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

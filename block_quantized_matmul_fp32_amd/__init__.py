@@ -25,7 +25,7 @@ EXPORTS = [
     "vq_status_string", "vq_last_error", "vq_type_name", "vq_is_supported", "vq_block_values",
     "vq_block_bytes", "vq_weight_bytes", "vq_act_bytes", "vq_act_d_offset", "vq_act_aux_offset",
     "vq_quantize_act", "vq_quantize_weights", "vq_gemv", "vq_gemm", "vq_grouped_workspace_bytes",
-    "vq_gemm_grouped", "vq_gemm_grouped_rows", "vq_gemm_grouped_noalloc", "vq_weighted_sum", "vq_get_stats", "vq_reset_stats",
+    "vq_gemm_grouped", "vq_gemm_grouped_rows", "vq_gemm_grouped_noalloc", "vq_stream_probe", "vq_weighted_sum", "vq_get_stats", "vq_reset_stats",
     "vq_version", "vq_rmsnorm_quant", "vq_silu_mul_quant", "vq_set_small_batch_max", "vq_small_batch_max",
     "vq_set_gemm_row_block", "vq_gemm_workspace",
 ]
@@ -83,6 +83,7 @@ def lib():
         L.vq_gemm_grouped.argtypes = [I, P, I64, I64, I64, I, P, I64, P, I64, P, P, P, P, Z, P]
         L.vq_gemm_grouped_rows.argtypes = [I, P, I64, I64, I64, I, P, I64, P, I64, P, P, P, P, Z, P]
         L.vq_gemm_grouped_noalloc.argtypes = [I, P, I64, I64, I64, I, P, I64, P, I64, P, P, P, P]
+        L.vq_stream_probe.argtypes = [I, P, I64, I64, P, Z, P]
         L.vq_weighted_sum.argtypes = [P, P, I64, I64, I64, P, P]
         L.vq_set_small_batch_max.argtypes = [I, I64]
         L.vq_set_small_batch_max.restype = I
@@ -95,7 +96,7 @@ def lib():
         L.vq_get_stats.argtypes = [ctypes.POINTER(VQStats)]
         L.vq_version.restype = ctypes.c_char_p
         for f in ("vq_quantize_act", "vq_quantize_weights", "vq_gemv", "vq_gemm", "vq_gemm_grouped",
-                  "vq_gemm_grouped_rows", "vq_gemm_grouped_noalloc", "vq_weighted_sum", "vq_rmsnorm_quant", "vq_silu_mul_quant"):
+                  "vq_gemm_grouped_rows", "vq_gemm_grouped_noalloc", "vq_stream_probe", "vq_weighted_sum", "vq_rmsnorm_quant", "vq_silu_mul_quant"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -369,6 +370,14 @@ def gemm_grouped(w: int, W, E: int, N: int, K: int, act: int, Xq, T: int, ids, t
               _dev(Ysum, "Ysum", 4 * T * N, f32), _dev(ws, "ws", need), ws.numel() * ws.element_size() if hasattr(ws, "numel") else need,
               _stream(stream)))
     return Y, Ysum, ws
+
+
+def stream_probe(w: int, W, N: int, K: int, sink, stream=None):
+    """vq_stream_probe: read the decode GEMV's weight bytes with its launch
+    shape and nothing else (the streaming floor of that launch)."""
+    nb = sink.numel() * sink.element_size()
+    _check(lib().vq_stream_probe(w, _dev(W, "W", weight_bytes(w, N, K)), N, K, _dev(sink, "sink", 4 * N), nb,
+                                 _stream(stream)))
 
 
 GROUPED_NOALLOC_SCRATCH_BYTES = 4 << 20  # VQ_GROUPED_NOALLOC_SCRATCH_BYTES

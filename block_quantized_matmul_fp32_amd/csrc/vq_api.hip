@@ -327,6 +327,27 @@ vq_status vq_gemv(int w, const void* W, int64_t N, int64_t K, const float* x, fl
     return hip_status(vqk::launch_gemv(w, (const uint8_t*)W, N, K, x, y, (uint8_t*)xq_out, stream), fn);
 }
 
+vq_status vq_stream_probe(int w, const void* W, int64_t N, int64_t K, void* sink, size_t sink_bytes,
+                          hipStream_t stream) {
+    const char* fn = "vq_stream_probe";
+    VQ_TRY(check_weight(w, fn));
+    VQ_TRY(check_k(w, K, fn));
+    VQ_TRY(check_dim(N, "N", fn));
+    if (N == 0) return VQ_OK;
+    if (!W || !sink) return fail(VQ_ERR_INVALID_ARG, "%s: null pointer", fn);
+    if (!aligned(W, 16) || !aligned(sink, 4))
+        return fail(VQ_ERR_INVALID_ARG, "%s: W must be 16-byte, sink 4-byte aligned", fn);
+    if (sink_bytes < (size_t)N * 4)
+        return fail(VQ_ERR_WORKSPACE, "%s: sink of %zu bytes, %lld needed", fn, sink_bytes, (long long)(4 * N));
+    if (overlap(sink, sink_bytes, W, vq_weight_bytes(w, N, K)))
+        return fail(VQ_ERR_ALIAS, "%s: sink overlaps W", fn);
+    const hipError_t e = vqk::launch_stream_probe(w, (const uint8_t*)W, N, K, (uint32_t*)sink, nullptr, stream);
+    if (e == hipErrorInvalidValue)
+        return fail(VQ_ERR_SHAPE, "%s: K = %lld exceeds what the decode GEMV takes for %s", fn, (long long)K,
+                    vq_type_name(w));
+    return hip_status(e, fn);
+}
+
 size_t vq_gemm_workspace(int w, int64_t M, int64_t N, int64_t K) {
     if (!is_weight(w) || w == VQ_Q8_0 || M <= 0 || N <= 0 || K <= 0 || K % 256 != 0 || M > kMaxDim ||
         N > kMaxDim || K > kMaxK)

@@ -78,6 +78,10 @@ hipError_t launch_gemm(int wtype, const uint8_t* W, int64_t N, int64_t K, const 
                        const void* act_d, const void* act_aux, int64_t M, float* Y, int64_t ldy,
                        hipStream_t st);
 
+// Streaming floor of the decode GEMV's launch (measurement only).
+hipError_t launch_stream_probe(int wtype, const uint8_t* W, int64_t N, int64_t K, uint32_t* sink, int64_t* grid_out,
+                               hipStream_t st);
+
 // Routed experts.
 struct RouteWs {
     int32_t* counts;   // [E]

@@ -253,6 +253,20 @@ vq_status vq_set_small_batch_max(int w, int64_t max_m);
 int64_t vq_small_batch_max(int w);
 
 /* ---------------------------------------------------------------------- */
+/* Measurement: the streaming floor of a decode GEMV launch.  Reads the     */
+/* weight bytes that vq_gemv(w, W, N, K, ...) reads, with the GEMV's grid    */
+/* and workgroup size, each workgroup its own rows' bytes once, and does    */
+/* nothing else; its time is what this launch shape needs just to stream    */
+/* the weights from memory ([P3] "mul_mat_vec_q_fq": the decode GEMV keeps  */
+/* the weight stream in flight while it computes, so the stream bounds it). */
+/* W: the weights as for vq_gemv (16-byte aligned); sink: device memory of  */
+/* at least 4*N bytes, 4-byte aligned, that the probe may write (it writes  */
+/* nothing in practice).  Shapes and errors as vq_gemv.                    */
+/* ---------------------------------------------------------------------- */
+vq_status vq_stream_probe(int w, const void* W, int64_t N, int64_t K, void* sink, size_t sink_bytes,
+                          hipStream_t stream);
+
+/* ---------------------------------------------------------------------- */
 /* Row blocks of the MFMA arm of vq_gemm.  The GEMM kernel addresses the    */
 /* activation bytes of one launch with 32-bit offsets, so vq_gemm launches  */
 /* it once per block of at most floor(2^31 / K) rows (rounded down to the   */

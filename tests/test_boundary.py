@@ -195,6 +195,17 @@ def test_grouped_noalloc_rejects_oversized_routing(vq):
     assert "static" in msg and str(vq.GROUPED_NOALLOC_SCRATCH_BYTES) in msg
 
 
+def test_stream_probe_checks(vq):
+    """vq_stream_probe validates like vq_gemv, and its sink's size and aliasing."""
+    _err(vq, 2, "vq_stream_probe", 9, FAKE, 64, 256, FAKE + 0x100000, 256, None)
+    _err(vq, 4, "vq_stream_probe", vq.Q4_K, FAKE, 64, 300, FAKE + 0x100000, 256, None)
+    msg = _err(vq, 6, "vq_stream_probe", vq.Q4_K, FAKE, 64, 256, FAKE + 0x100000, 255, None)
+    assert "256" in msg
+    _err(vq, 5, "vq_stream_probe", vq.Q4_K, FAKE, 64, 256, FAKE + 64, 256, None)
+    _err(vq, 1, "vq_stream_probe", vq.Q4_K, FAKE + 4, 64, 256, FAKE + 0x100000, 256, None)
+    assert vq.lib().vq_stream_probe(vq.Q4_K, None, 0, 256, None, 0, None) == 0
+
+
 def test_empty_calls_are_ok(vq):
     L = vq.lib()
     assert L.vq_gemm(vq.Q4_K, None, 0, 256, vq.Q8_K, None, 0, None, 0, None, 0, None) == 0

@@ -150,6 +150,21 @@ def test_gemv_edge_rows(wtype):
         H.assert_bitwise(H.host(y), y_ref, "gemv edge %s N=%d K=%d" % (WNAME[wtype], N, K))
 
 
+@pytest.mark.parametrize("wtype", WTYPES)
+def test_stream_probe_reads_only(wtype):
+    """vq_stream_probe (the GEMV launch's streaming floor) runs on the decode
+    shapes and a ragged one, and leaves its sink untouched."""
+    import torch
+    qk = 32 if wtype == oracle.Q8_0 else 256
+    for N, K in ((2560, 9728 // qk * qk), (9728, 2560), (301, 17 * qk)):
+        W = synth.normal((1190, wtype, N), (N, K), 0.02)
+        Wq = H.to_dev(oracle.quantize_weights(wtype, W))
+        sink = torch.full((N,), 7, dtype=torch.int32, device=H.dev())
+        H.say("stream probe %s N=%d K=%d" % (WNAME[wtype], N, K))
+        vq.stream_probe(wtype, Wq, N, K, sink)
+        assert (H.host(sink) == 7).all()
+
+
 def gemv_max_k(wtype):
     """Largest K the fused GEMV accepts (its weight row and quantized x must
     fit LDS), found from the library's host-side shape check, which rejects
