@@ -19,7 +19,9 @@ TYPE_NAMES = {Q4_K: "Q4_K", Q6_K: "Q6_K", Q8_0: "Q8_0", Q8_K: "Q8_K", Q8_1: "Q8_
 OP_GEMV, OP_GEMM, OP_GEMM_GROUPED = 0, 1, 2
 
 STATUS = {0: "VQ_OK", 1: "VQ_ERR_INVALID_ARG", 2: "VQ_ERR_UNSUPPORTED_TYPE", 3: "VQ_ERR_TYPE_PAIR",
-          4: "VQ_ERR_SHAPE", 5: "VQ_ERR_ALIAS", 6: "VQ_ERR_WORKSPACE", 7: "VQ_ERR_HIP"}
+          4: "VQ_ERR_SHAPE", 5: "VQ_ERR_ALIAS", 6: "VQ_ERR_WORKSPACE", 7: "VQ_ERR_HIP", 8: "VQ_ERR_DEVICE"}
+DEBUG_SYNC = 1
+DEBUG_CHECK_IDS = 2
 
 EXPORTS = [
     "vq_status_string", "vq_last_error", "vq_type_name", "vq_is_supported", "vq_block_values",
@@ -27,7 +29,7 @@ EXPORTS = [
     "vq_quantize_act", "vq_quantize_weights", "vq_gemv", "vq_gemm", "vq_grouped_workspace_bytes",
     "vq_gemm_grouped", "vq_gemm_grouped_rows", "vq_gemm_grouped_noalloc", "vq_stream_probe", "vq_weighted_sum", "vq_get_stats", "vq_reset_stats",
     "vq_version", "vq_rmsnorm_quant", "vq_silu_mul_quant", "vq_set_small_batch_max", "vq_small_batch_max",
-    "vq_set_gemm_row_block", "vq_gemm_workspace",
+    "vq_set_gemm_row_block", "vq_gemm_workspace", "vq_set_debug", "vq_device_status",
 ]
 
 STAT_FIELDS = ["quantize_q8k", "quantize_q8_1", "quantize_weights", "gemv_q4k", "gemv_q6k", "gemv_q8_0",
@@ -84,6 +86,10 @@ def lib():
         L.vq_gemm_grouped_rows.argtypes = [I, P, I64, I64, I64, I, P, I64, P, I64, P, P, P, P, Z, P]
         L.vq_gemm_grouped_noalloc.argtypes = [I, P, I64, I64, I64, I, P, I64, P, I64, P, P, P, P]
         L.vq_stream_probe.argtypes = [I, P, I64, I64, P, Z, P]
+        L.vq_set_debug.argtypes = [I, I64]
+        L.vq_set_debug.restype = I
+        L.vq_device_status.argtypes = [P]
+        L.vq_device_status.restype = I
         L.vq_weighted_sum.argtypes = [P, P, I64, I64, I64, P, P]
         L.vq_set_small_batch_max.argtypes = [I, I64]
         L.vq_set_small_batch_max.restype = I
@@ -370,6 +376,17 @@ def gemm_grouped(w: int, W, E: int, N: int, K: int, act: int, Xq, T: int, ids, t
               _dev(Ysum, "Ysum", 4 * T * N, f32), _dev(ws, "ws", need), ws.numel() * ws.element_size() if hasattr(ws, "numel") else need,
               _stream(stream)))
     return Y, Ysum, ws
+
+
+def set_debug(flags: int = 0, wait_polls: int = 0):
+    """vq_set_debug for the calling thread (DEBUG_SYNC, DEBUG_CHECK_IDS)."""
+    _check(lib().vq_set_debug(flags, wait_polls))
+
+
+def device_status(stream=None):
+    """vq_device_status: raises VQError(VQ_ERR_DEVICE) if a kernel reported a
+    failure since the last check (and clears the report)."""
+    _check(lib().vq_device_status(_stream(stream)))
 
 
 def stream_probe(w: int, W, N: int, K: int, sink, stream=None):

@@ -143,9 +143,10 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
     const uint8_t* __restrict__ W, int N, int K, int64_t wbytes, const float* __restrict__ x,
     float* __restrict__ y, uint8_t* __restrict__ xq_out, int rows_per_wg, int slice_bytes, int x_vec,
     int nq, int h1_tasks, int kh0, int kh1, const uint8_t* __restrict__ xq_in, int M, int64_t ldy,
-    int64_t xq_d_off, int64_t xq_aux_off) {
+    int64_t xq_d_off, int64_t xq_aux_off, int wait_polls, unsigned int* __restrict__ err_word) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     __shared__ int s_loaders_done;  // loader waves whose second part has landed
+    __shared__ int s_bad;           // a loader wave's wait gave up: this workgroup's rows are NaN
     constexpr int BB = WFmt<WT>::kBlk;
     constexpr int QV = WFmt<WT>::kVals;
     constexpr int LPT = (WT == 2) ? 1 : 2;    // lanes per task
@@ -302,7 +303,10 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
         }
     }
     }
-    if (tid == 0) s_loaders_done = 0;  // wave 0 is a quantizer wave; visible after the barrier
+    if (tid == 0) {  // wave 0 is a quantizer wave; visible after the barrier
+        s_loaders_done = 0;
+        s_bad = 0;
+    }
     lds_barrier();  // quantized x and the first half of the slice visible to every wave
 
     const int grp = lane / LPT, sub = lane % LPT;
@@ -493,15 +497,25 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
         }
         // The loaders alone meet here (the quantizer waves may still be on the
         // first part): each signals that its loads (and any patch) are in LDS,
-        // then waits for the others, whose chunks its tasks read.  Bounded, so
-        // the wave always moves on.
+        // then waits for the others, whose chunks its tasks read.  Bounded
+        // (wait_polls polls), so the wave always moves on; if it gives up, the
+        // workgroup's rows are written as NaN and the device error word gets
+        // bit 1, which vq_device_status reports.
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the patch bytes are written
         if (lane == 0) atomicAdd(&s_loaders_done, 1);
-        for (int spin = 0; spin < (1 << 20); ++spin) {
+        bool ok = false;
+        for (int spin = 0; spin < wait_polls; ++spin) {
             const int done = __builtin_amdgcn_readfirstlane(
                 __hip_atomic_load(&s_loaders_done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
-            if (done >= GL) break;
+            if (done >= GL) {
+                ok = true;
+                break;
+            }
             __builtin_amdgcn_s_sleep(1);
+        }
+        if (!ok && lane == 0) {
+            s_bad = 1;
+            __hip_atomic_fetch_or(err_word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 
@@ -509,6 +523,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
     // are read 16 at a time with independent float4 loads before the adds,
     // so a row costs a few LDS round trips, not one per block.
     auto sum_rows = [&](int row0) {
+    const bool bad = s_bad != 0;  // set before the barrier that precedes every call
     for (int idx = tid; idx < MB * rows; idx += nthr) {
         const int m = idx / rows, r = idx - m * rows;
         if (m >= Mg) break;
@@ -538,7 +553,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
             for (int j = 0; j < 16; ++j)
                 if (b + j < nb) acc = acc + t[j];
         }
-        y[(row0 + m) * ldy + n0 + r] = acc;
+        y[(row0 + m) * ldy + n0 + r] = bad ? __builtin_nanf("") : acc;
     }
     };
 
@@ -723,7 +738,7 @@ static hipError_t launch_gemv_t(const uint8_t* W, int64_t N, int64_t K, const fl
     const int x_vec = (x != nullptr && (((uintptr_t)x) & 15) == 0) ? 1 : 0;
     gemv_kernel<WT, MB><<<grid, 64 * (p.nq + p.nl), p.lds, st>>>(
         W, (int)N, (int)K, (int64_t)N * rb, x, y, xq_out, p.rows, p.slice_bytes, x_vec, p.nq, p.h1, p.kh0, p.kh1,
-        xq_in, (int)M, ldy, d_off, aux_off);
+        xq_in, (int)M, ldy, d_off, aux_off, g_dbg.wait_polls, g_dbg.err_word);
     return hipGetLastError();
 }
 

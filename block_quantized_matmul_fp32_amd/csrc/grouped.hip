@@ -238,6 +238,29 @@ __global__ __launch_bounds__(256) void route_place_kernel(const int32_t* __restr
     list[offsets[e] + chunk[c * E + e] + rank[p]] = (int32_t)p;
 }
 
+// One thread per token: its top_k ids in [0, E) and distinct.
+__global__ __launch_bounds__(256) void check_ids_kernel(const int32_t* __restrict__ ids, int64_t T, int top_k,
+                                                        int E, unsigned int* __restrict__ err_word) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= T) return;
+    const int32_t* row = ids + t * top_k;
+    unsigned int bits = 0;
+    for (int i = 0; i < top_k; ++i) {
+        const int e = row[i];
+        if (e < 0 || e >= E) bits |= 2u;
+        for (int j = 0; j < i; ++j)
+            if (row[j] == e) bits |= 4u;
+    }
+    if (bits) __hip_atomic_fetch_or(err_word, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+hipError_t launch_check_ids(const int32_t* ids, int64_t T, int64_t top_k, int64_t E, unsigned int* err_word,
+                            hipStream_t st) {
+    if (T <= 0) return hipSuccess;
+    check_ids_kernel<<<(unsigned)((T + 255) / 256), 256, 0, st>>>(ids, T, (int)top_k, (int)E, err_word);
+    return hipGetLastError();
+}
+
 hipError_t launch_route(const int32_t* ids, int64_t T, int64_t top_k, int64_t E, int tile_rows, RouteWs ws,
                         hipStream_t st) {
     if (tile_rows < kGroupMinTileRows) return hipErrorInvalidValue;

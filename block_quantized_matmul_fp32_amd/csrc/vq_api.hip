@@ -18,6 +18,10 @@
 #include "vq_device.h"
 #include "vq_internal.h"
 
+namespace vqk {
+thread_local DebugCtx g_dbg;
+}  // namespace vqk
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -132,6 +136,85 @@ vqk::ActQ81 act_q81(void* base, int64_t M, int64_t K) {
 
 }  // namespace
 
+// Routing workspace of vq_gemm_grouped_noalloc, for callers that cannot
+// allocate: a static device array, one copy per GPU, held until the process
+// ends.  Host code never passes the array's name to a kernel (on the host it
+// is only a stand-in for the symbol); it uses the device address that
+// hipGetSymbolAddress returns, looked up once per device with that device
+// current and kept in g_scratch_ptr.
+constexpr size_t kScratchBytes = VQ_GROUPED_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+// The device error word: bits that kernels set when a bounded wait gives up
+// (1) or, in debug mode, for invalid expert ids (2: outside [0, E), 4:
+// repeated within a token).  One per GPU; read and cleared by
+// vq_device_status.
+static __device__ __align__(64) unsigned int err_word[1];
+static std::mutex g_sym_mu;
+static std::atomic<void*> g_scratch_ptr[vqk::kMaxDevices] = {};
+static std::atomic<void*> g_err_ptr[vqk::kMaxDevices] = {};
+
+// A device symbol's address on the current device, looked up once per device
+// with that device current (the host-side name is only a stand-in).
+static vq_status symbol_ptr(const char* fn, std::atomic<void*>* cache, const void* symbol, const char* what,
+                            void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, fn);
+    if (dev < 0 || dev >= vqk::kMaxDevices)
+        return fail(VQ_ERR_INVALID_ARG, "%s: device %d outside [0, %d)", fn, dev, vqk::kMaxDevices);
+    void* p = cache[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_sym_mu);
+        p = cache[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, symbol);
+            if (e != hipSuccess) return fail(VQ_ERR_HIP, "%s: hipGetSymbolAddress(%s): HIP error %d (%s)", fn, what,
+                                             (int)e, hipGetErrorString(e));
+            if (!p) return fail(VQ_ERR_HIP, "%s: hipGetSymbolAddress(%s) returned NULL", fn, what);
+            cache[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return VQ_OK;
+}
+
+// The current device's scratch address.
+static vq_status scratch_ptr(const char* fn, void** out) {
+    return symbol_ptr(fn, g_scratch_ptr, HIP_SYMBOL(scratch), "scratch", out);
+}
+
+// Before a call's launches: the kernels' error word for the current device.
+static vq_status prepare_launch(const char* fn) {
+    void* p = nullptr;
+    VQ_TRY(symbol_ptr(fn, g_err_ptr, HIP_SYMBOL(err_word), "err_word", &p));
+    vqk::g_dbg.err_word = (unsigned int*)p;
+    return VQ_OK;
+}
+
+// Per calling thread: debug flags (VQ_DEBUG_*).
+static thread_local int g_debug_flags = 0;
+
+// Reads and clears the current device's error word after `stream` drains.
+static vq_status read_device_status(const char* fn, hipStream_t stream) {
+    void* p = nullptr;
+    VQ_TRY(symbol_ptr(fn, g_err_ptr, HIP_SYMBOL(err_word), "err_word", &p));
+    VQ_TRY(hip_status(hipStreamSynchronize(stream), fn));
+    unsigned int v = 0;
+    VQ_TRY(hip_status(hipMemcpy(&v, p, sizeof(v), hipMemcpyDeviceToHost), fn));
+    if (v == 0) return VQ_OK;
+    const unsigned int zero = 0;
+    VQ_TRY(hip_status(hipMemcpy(p, &zero, sizeof(zero), hipMemcpyHostToDevice), fn));
+    return fail(VQ_ERR_DEVICE, "%s: device error word 0x%x:%s%s%s", fn, v,
+                (v & 1u) ? " a decode GEMV workgroup's loader wait gave up (its rows were written as NaN);" : "",
+                (v & 2u) ? " an expert id outside [0, E);" : "", (v & 4u) ? " an expert id repeated within a token;" : "");
+}
+
+// After a call's launches: in debug mode, wait for them and report the error word.
+static vq_status finish_launch(const char* fn, vq_status s, hipStream_t stream) {
+    if (s != VQ_OK || !(g_debug_flags & VQ_DEBUG_SYNC)) return s;
+    return read_device_status(fn, stream);
+}
+
 extern "C" {
 
 const char* vq_status_string(vq_status s) {
@@ -144,6 +227,7 @@ const char* vq_status_string(vq_status s) {
         case VQ_ERR_ALIAS: return "VQ_ERR_ALIAS";
         case VQ_ERR_WORKSPACE: return "VQ_ERR_WORKSPACE";
         case VQ_ERR_HIP: return "VQ_ERR_HIP";
+        case VQ_ERR_DEVICE: return "VQ_ERR_DEVICE";
     }
     return "VQ_ERR_UNKNOWN";
 }
@@ -324,7 +408,9 @@ vq_status vq_gemv(int w, const void* W, int64_t N, int64_t K, const float* x, fl
     else if (w == VQ_Q6_K) g_stats.gemv_q6k++;
     else if (w == VQ_Q5_K) g_stats.gemv_q5k++;
     else g_stats.gemv_q8_0++;
-    return hip_status(vqk::launch_gemv(w, (const uint8_t*)W, N, K, x, y, (uint8_t*)xq_out, stream), fn);
+    VQ_TRY(prepare_launch(fn));
+    return finish_launch(fn, hip_status(vqk::launch_gemv(w, (const uint8_t*)W, N, K, x, y, (uint8_t*)xq_out, stream), fn),
+                         stream);
 }
 
 vq_status vq_stream_probe(int w, const void* W, int64_t N, int64_t K, void* sink, size_t sink_bytes,
@@ -347,6 +433,18 @@ vq_status vq_stream_probe(int w, const void* W, int64_t N, int64_t K, void* sink
                     vq_type_name(w));
     return hip_status(e, fn);
 }
+
+vq_status vq_set_debug(int flags, int64_t wait_polls) {
+    if (flags & ~(VQ_DEBUG_SYNC | VQ_DEBUG_CHECK_IDS))
+        return fail(VQ_ERR_INVALID_ARG, "vq_set_debug: unknown flags 0x%x", flags);
+    if (wait_polls < 0 || wait_polls > (1 << 30))
+        return fail(VQ_ERR_INVALID_ARG, "vq_set_debug: wait_polls = %lld outside [0, 2^30]", (long long)wait_polls);
+    g_debug_flags = flags;
+    vqk::g_dbg.wait_polls = wait_polls == 0 ? (1 << 20) : (int)wait_polls;
+    return VQ_OK;
+}
+
+vq_status vq_device_status(hipStream_t stream) { return read_device_status("vq_device_status", stream); }
 
 size_t vq_gemm_workspace(int w, int64_t M, int64_t N, int64_t K) {
     if (!is_weight(w) || w == VQ_Q8_0 || M <= 0 || N <= 0 || K <= 0 || K % 256 != 0 || M > kMaxDim ||
@@ -383,18 +481,19 @@ vq_status vq_gemm(int w, const void* W, int64_t N, int64_t K, int act, const voi
     else if (w == VQ_Q6_K) g_stats.gemm_q6k++;
     else if (w == VQ_Q5_K) g_stats.gemm_q5k++;
     else g_stats.gemm_q8_0++;
+    VQ_TRY(prepare_launch(fn));
+    hipError_t e;
     if (vqk::gemm_skinny_ok(w, N, K, M, g_small_max[widx(w)])) {
         // small batch: the weights streamed once through the GEMV kernel for all M rows
         g_stats.gemm_skinny++;
-        return hip_status(vqk::launch_gemm_skinny(w, (const uint8_t*)W, N, K, base, M,
-                                                  (int64_t)vq_act_d_offset(act, M, K),
-                                                  (int64_t)vq_act_aux_offset(act, M, K), Y, ldy, stream),
-                          fn);
+        e = vqk::launch_gemm_skinny(w, (const uint8_t*)W, N, K, base, M, (int64_t)vq_act_d_offset(act, M, K),
+                                    (int64_t)vq_act_aux_offset(act, M, K), Y, ldy, stream);
+    } else if (w != VQ_Q8_0) {
+        e = vqk::launch_gemm_kq(w, (const uint8_t*)W, N, K, qs, d, aux, M, Y, ldy, ws, ws_bytes, stream);
+    } else {
+        e = vqk::launch_gemm(w, (const uint8_t*)W, N, K, qs, d, aux, M, Y, ldy, stream);
     }
-    if (w != VQ_Q8_0)
-        return hip_status(vqk::launch_gemm_kq(w, (const uint8_t*)W, N, K, qs, d, aux, M, Y, ldy, ws, ws_bytes, stream),
-                          fn);
-    return hip_status(vqk::launch_gemm(w, (const uint8_t*)W, N, K, qs, d, aux, M, Y, ldy, stream), fn);
+    return finish_launch(fn, hip_status(e, fn), stream);
 }
 
 vq_status vq_set_small_batch_max(int w, int64_t max_m) {
@@ -423,36 +522,6 @@ vq_status vq_set_gemm_row_block(int64_t rows) {
 size_t vq_grouped_workspace_bytes(int64_t E, int64_t T, int64_t top_k) {
     if (E <= 0 || T < 0 || top_k <= 0) return 0;
     return vqk::route_ws_layout(E, T, top_k, nullptr, nullptr);
-}
-
-// Routing workspace of vq_gemm_grouped_noalloc, for callers that cannot
-// allocate: a static device array, one copy per GPU, held until the process
-// ends.  Host code never passes the array's name to a kernel (on the host it
-// is only a stand-in for the symbol); it uses the device address that
-// hipGetSymbolAddress returns, looked up once per device with that device
-// current and kept in g_scratch_ptr.
-constexpr size_t kScratchBytes = VQ_GROUPED_NOALLOC_SCRATCH_BYTES;
-static __device__ __align__(256) uint8_t scratch[kScratchBytes];
-static std::mutex g_scratch_mu;
-static void* g_scratch_ptr[vqk::kMaxDevices] = {};
-
-// The current device's scratch address (looked up on the first call there).
-static vq_status scratch_ptr(const char* fn, void** out) {
-    int dev = -1;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return hip_status(e, fn);
-    if (dev < 0 || dev >= vqk::kMaxDevices)
-        return fail(VQ_ERR_INVALID_ARG, "%s: device %d outside [0, %d)", fn, dev, vqk::kMaxDevices);
-    std::lock_guard<std::mutex> lock(g_scratch_mu);
-    if (!g_scratch_ptr[dev]) {
-        void* p = nullptr;
-        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
-        if (e != hipSuccess) return hip_status(e, "vq_gemm_grouped_noalloc: hipGetSymbolAddress(scratch)");
-        if (!p) return fail(VQ_ERR_HIP, "%s: hipGetSymbolAddress(scratch) returned NULL", fn);
-        g_scratch_ptr[dev] = p;
-    }
-    *out = g_scratch_ptr[dev];
-    return VQ_OK;
 }
 
 // Both arms of the routed-expert GEMM: the broadcast arm reads activation row
@@ -504,6 +573,9 @@ static vq_status gemm_grouped_impl(const char* fn, int per_row, int w, const voi
         return fail(VQ_ERR_ALIAS, "%s: workspace overlaps an input", fn);
     vqk::RouteWs rws;
     vqk::route_ws_layout(E, T, top_k, &rws, (uint8_t*)ws);
+    VQ_TRY(prepare_launch(fn));
+    if (g_debug_flags & VQ_DEBUG_CHECK_IDS)
+        VQ_TRY(hip_status(vqk::launch_check_ids(ids, T, top_k, E, vqk::g_dbg.err_word, stream), fn));
     g_stats.route++;
     const int tile_rows = vqk::grouped_tile_rows(w, E, T, top_k, K, per_row);
     vq_status s = hip_status(vqk::launch_route(ids, T, top_k, E, tile_rows, rws, stream), fn);
@@ -524,9 +596,10 @@ static vq_status gemm_grouped_impl(const char* fn, int per_row, int w, const voi
                                      stream);
     }
     s = hip_status(e, fn);
-    if (s != VQ_OK || !Ysum) return s;
+    if (s != VQ_OK || !Ysum) return finish_launch(fn, s, stream);
     g_stats.weighted_sum++;
-    return hip_status(vqk::launch_weighted_sum(Y, route_w, T, top_k, N, Ysum, stream), fn);
+    return finish_launch(fn, hip_status(vqk::launch_weighted_sum(Y, route_w, T, top_k, N, Ysum, stream), fn),
+                         stream);
 }
 
 vq_status vq_gemm_grouped(int w, const void* W, int64_t E, int64_t N, int64_t K, int act, const void* Xq,

@@ -10,6 +10,19 @@
 
 namespace vqk {
 
+// Per calling thread: the failure reporting of the kernels launched by the
+// current call (set by the API before its launches).
+struct DebugCtx {
+    int wait_polls = 1 << 20;          // bound of the decode GEMV loaders' wait
+    unsigned int* err_word = nullptr;  // the current device's error word
+};
+extern thread_local DebugCtx g_dbg;
+
+// Debug check of the routed-expert ids: bit 2 of the error word for an id
+// outside [0, E), bit 4 for an id repeated within a token.
+hipError_t launch_check_ids(const int32_t* ids, int64_t T, int64_t top_k, int64_t E, unsigned int* err_word,
+                            hipStream_t st);
+
 // Routed-expert GEMM tiles: the routing scan writes its tile table in units
 // of a per-call tile height and the grouped GEMM consumes it.  The Q8_0
 // grouped GEMM keeps 96-row tiles (four waves of 32 weight rows x 48

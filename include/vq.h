@@ -103,7 +103,8 @@ typedef enum {
     VQ_ERR_SHAPE = 4,            /* K not a multiple of the block length, size limits */
     VQ_ERR_ALIAS = 5,            /* an output overlaps an input */
     VQ_ERR_WORKSPACE = 6,        /* workspace missing or too small */
-    VQ_ERR_HIP = 7               /* a HIP runtime call failed (launch, attribute) */
+    VQ_ERR_HIP = 7,              /* a HIP runtime call failed (launch, attribute) */
+    VQ_ERR_DEVICE = 8            /* a kernel reported a failure (vq_device_status) */
 } vq_status;
 
 /* Operations for vq_is_supported. */
@@ -251,6 +252,27 @@ size_t vq_gemm_workspace(int w, int64_t M, int64_t N, int64_t K);
 /* ---------------------------------------------------------------------- */
 vq_status vq_set_small_batch_max(int w, int64_t max_m);
 int64_t vq_small_batch_max(int w);
+
+/* ---------------------------------------------------------------------- */
+/* Failures seen on the device.  Kernels never fault or hang on purpose:   */
+/* the decode GEMV's loader waves wait for each other a bounded number of  */
+/* polls, and a workgroup whose wait gives up writes its rows as NaN and   */
+/* sets bit 1 of the GPU's device error word.  In debug mode the grouped    */
+/* calls also check the expert ids on the device (bit 2: an id outside      */
+/* [0, E), bit 4: an id repeated within a token; such pairs are skipped or  */
+/* computed as documented above, never read out of bounds).                 */
+/* vq_device_status(stream): waits for `stream`, then returns VQ_OK, or     */
+/* VQ_ERR_DEVICE with the bits named in vq_last_error, and clears the word. */
+/* vq_set_debug(flags, wait_polls), per calling thread: VQ_DEBUG_SYNC makes */
+/* vq_gemv, vq_gemm and the grouped calls wait for their launches and      */
+/* return VQ_ERR_DEVICE themselves; VQ_DEBUG_CHECK_IDS turns on the id      */
+/* check; wait_polls bounds the GEMV loaders' wait (0: the default 2^20;    */
+/* a tiny bound makes the wait give up, for tests of this reporting).       */
+/* ---------------------------------------------------------------------- */
+#define VQ_DEBUG_SYNC 1
+#define VQ_DEBUG_CHECK_IDS 2
+vq_status vq_set_debug(int flags, int64_t wait_polls);
+vq_status vq_device_status(hipStream_t stream);
 
 /* ---------------------------------------------------------------------- */
 /* Measurement: the streaming floor of a decode GEMV launch.  Reads the     */

@@ -206,6 +206,15 @@ def test_stream_probe_checks(vq):
     assert vq.lib().vq_stream_probe(vq.Q4_K, None, 0, 256, None, 0, None) == 0
 
 
+def test_set_debug_checks(vq):
+    """vq_set_debug: unknown flags and out-of-range bounds are rejected (host only)."""
+    _err(vq, 1, "vq_set_debug", 8, 0)
+    _err(vq, 1, "vq_set_debug", 0, -1)
+    assert vq.lib().vq_set_debug(vq.DEBUG_SYNC | vq.DEBUG_CHECK_IDS, 5) == 0
+    assert vq.lib().vq_set_debug(0, 0) == 0
+    assert vq.lib().vq_status_string(8) == b"VQ_ERR_DEVICE"
+
+
 def test_empty_calls_are_ok(vq):
     L = vq.lib()
     assert L.vq_gemm(vq.Q4_K, None, 0, 256, vq.Q8_K, None, 0, None, 0, None, 0, None) == 0
