@@ -1,5 +1,7 @@
-// gemm.hip -- prefill GEMM Y = X * W^T on int8 MFMA for gfx950, and its
-// routed-expert (MUL_MAT_ID) variant.
+// gemm.hip -- the Q8_0 x Q8_1 prefill GEMM Y = X * W^T on int8 MFMA for
+// gfx950, and its routed-expert (MUL_MAT_ID) variant.  (The K-quant weight
+// types run on gemm_k.hip; this kernel template keeps their plane unpacking,
+// which only Q8_0's single plane instantiates.)
 //
 // Pages: vllm.cpp PR #3035 "scope a cooperative activation share for the WMMA
 // kernels" (each warp re-reading the same activation rows is the diagnosed
@@ -686,58 +688,15 @@ static hipError_t launch_gemm_cfg(const uint8_t* W, int64_t N, int64_t K, const 
     return hipSuccess;
 }
 
-// Tile choice (weight rows x activation rows): 64 x 256, 64 x 192 or 64 x 128,
-// whichever gives the least estimated time = workgroup rounds (workgroups /
-// CUs, rounded up: one workgroup per CU) x the relative time of one
-// workgroup of that height.  The relative times, per mille of the 64 x 256
-// workgroup, were measured on the prefill shapes:
-//   Q4_K / Q5_K (eight waves of 32 x 64, 32 x 48, 32 x 32): 1000, 856, 610;
-//   Q6_K (sixteen, twelve, eight waves of 32 x 32):           1000, 905, 850.
-// So a grid that would leave a mostly empty last round takes the shorter
-// tiles: Q4_K at M = 512 (304 workgroups of 64 x 256 on 256 CUs; 64 x 192:
-// 14% faster) and Q6_K at M = 2048 (320 workgroups; 64 x 192: 9% faster).
-// Ties go to the taller tile.  Q8_0, whose per-block epilogue dominates,
-// always takes 64 x 128 tiles (measured faster at every workload shape).
-// Q6_K runs on 32 x 32 waves (four per SIMD at 64 x 256): with three planes
-// its waves wait longest on LDS and MFMA results, and the extra waves cover
-// that; Q4_K and Q5_K measured slower that way (register spills).  (64 x 64
-// tiles for still smaller grids measured no faster: the time of a column
-// tile is its sequence of super-block steps, not the number of tiles.)
-template <int WT>
-static hipError_t launch_gemm_t(const uint8_t* W, int64_t N, int64_t K, const void* aqs, const void* ad,
-                                const void* aux, int64_t M, float* Y, int64_t ldy, hipStream_t st) {
-    if constexpr (WT == 2) {
-        return launch_gemm_cfg<WT, 4, 2>(W, N, K, aqs, ad, aux, M, Y, ldy, st);
-    } else {
-        const int64_t cus = num_cus();
-        const int64_t ncol = (N + kBN - 1) / kBN;
-        auto cost = [&](int64_t bm, int64_t rel) {
-            const int64_t wg = ncol * ((M + bm - 1) / bm);
-            return ((wg + cus - 1) / cus) * rel;
-        };
-        const int64_t t256 = cost(256, 1000);
-        const int64_t t192 = cost(192, WT == 1 ? 905 : 856);
-        const int64_t t128 = cost(128, WT == 1 ? 850 : 610);
-        if (t256 <= t192 && t256 <= t128) {
-            if constexpr (WT == 1) return launch_gemm_cfg<WT, 8, 2>(W, N, K, aqs, ad, aux, M, Y, ldy, st);
-            else return launch_gemm_cfg<WT, 4, 4>(W, N, K, aqs, ad, aux, M, Y, ldy, st);
-        }
-        if (t192 <= t128) {
-            if constexpr (WT == 1) return launch_gemm_cfg<WT, 6, 2>(W, N, K, aqs, ad, aux, M, Y, ldy, st);
-            else return launch_gemm_cfg<WT, 4, 3>(W, N, K, aqs, ad, aux, M, Y, ldy, st);
-        }
-        return launch_gemm_cfg<WT, 4, 2>(W, N, K, aqs, ad, aux, M, Y, ldy, st);
-    }
-}
-
+// Q8_0 x Q8_1 takes 64 x 128 tiles (its per-block epilogue dominates; the
+// other tile heights measured slower at every workload shape).
 hipError_t launch_gemm(int wtype, const uint8_t* W, int64_t N, int64_t K, const void* act_qs,
                        const void* act_d, const void* act_aux, int64_t M, float* Y, int64_t ldy,
                        hipStream_t st) {
+    // the K-quant weight types run on the K-quant GEMM (gemm_k.hip)
+    if (wtype != 2) return hipErrorInvalidValue;
     if (M == 0 || N == 0) return hipSuccess;
-    if (wtype == 0) return launch_gemm_t<0>(W, N, K, act_qs, act_d, act_aux, M, Y, ldy, st);
-    if (wtype == 1) return launch_gemm_t<1>(W, N, K, act_qs, act_d, act_aux, M, Y, ldy, st);
-    if (wtype == 5) return launch_gemm_t<3>(W, N, K, act_qs, act_d, act_aux, M, Y, ldy, st);
-    return launch_gemm_t<2>(W, N, K, act_qs, act_d, act_aux, M, Y, ldy, st);
+    return launch_gemm_cfg<2, 4, 2>(W, N, K, act_qs, act_d, act_aux, M, Y, ldy, st);
 }
 
 // Grouped launch: one 64 x kGroupTileRows tile per (weight-row block, routed
