@@ -31,8 +31,8 @@
 //      Q5_K: planes of the centred q - 16 times the two 3-bit scale digits;
 //            S = 8 R1 + R0 + 16 sum_j sc_j bsum32_j, the last term on a
 //            second binary16 MFMA.
-//      Q6_K: P = sc (q - 32) in 16-bit lanes, planes P >> 6 in [-64, 64] and
-//            P & 63; S = 64 R1 + R0.
+//      Q6_K: P = sc (q - 32) in 16-bit lanes, planes P mod 256 (as int8)
+//            and (P + 128) >> 8 in [-16, 16]; S = 256 R1 + R0.
 //    The integer sums are exact.  The Q4_K/Q5_K min term
 //    Mn = sum_j m_j (bsum_2j + bsum_2j+1) runs on one
 //    v_mfma_f32_32x32x16_f16 per tile (m_j <= 63 and |bsum| <= 2032 are exact
@@ -170,7 +170,8 @@ struct Args {
 // v_perm byte selectors.
 constexpr uint32_t kSelEven = 0x0C020C00u;  // bytes 0, 2 -> low bytes of the two 16-bit lanes
 constexpr uint32_t kSelOdd = 0x0C030C01u;   // bytes 1, 3
-constexpr uint32_t kSelPack = 0x06020400u;  // low bytes of (even lanes, odd lanes) -> 4 bytes in order
+constexpr uint32_t kSelPack = 0x06020400u;    // low bytes of (even lanes, odd lanes) -> 4 bytes in order
+constexpr uint32_t kSelPackHi = 0x07030501u;  // high bytes of (even lanes, odd lanes) -> 4 bytes in order
 
 // Plane bytes of one 16-value piece (four dwords of quants, one per 4 values)
 // for the two planes of each weight type, and the per-lane constants of a
@@ -183,8 +184,10 @@ constexpr uint32_t kSelPack = 0x06020400u;  // low bytes of (even lanes, odd lan
 //         and S = S' + 16 sum_j sc_j bsum32_j, the second term on an exact
 //         binary16 MFMA.
 //   Q6_K: q in [0,63], sub-block (16 values) 8h + c with int8 sc; the
-//         product P = sc (q - 32) in [-4064, 4096] is split P = 64 hi + lo,
-//         hi = P >> 6 in [-64, 64], lo = P & 63 in [0, 63]; S = 64 R1 + R0.
+//         product P = sc (q - 32) in [-4096, 4064] is split P = 256 hi + lo
+//         with lo = P mod 256 read as int8 and hi = (P + 128) >> 8 in
+//         [-16, 16] (the high byte of P + 128, formed in the same 16-bit
+//         multiply-add); S = 256 R1 + R0.
 template <int WT>
 struct Unpack;
 
@@ -299,7 +302,7 @@ __device__ __forceinline__ uint2 gload8_a2(const uint8_t* p) {
 template <>
 struct Unpack<1> {
     static constexpr int RAW = 8;  // ql 4, qh 2, sc and d in one
-    static constexpr int SH = 6;
+    static constexpr int SH = 8;
     static __device__ __forceinline__ void load(WRsrc W, uint32_t off, uint32_t soff, int h, u4v (&raw)[8]) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) raw[k] = bload16(W, off + 64 * h + 16 * k, soff);
@@ -320,7 +323,7 @@ struct Unpack<1> {
             // ql bytes 16(c%4) of the lane's 64, nibble c/4; qh bytes 16(c%2) of its 32, pair c/2
             const int sc = (int)(int8_t)((((c < 4) ? raw[6].x : raw[6].y) >> (8 * (c & 3))) & 0xFF);
             const uint32_t f = pair16((uint32_t)sc);
-            const uint32_t a = pair16((uint32_t)(-32 * sc));
+            const uint32_t a = pair16((uint32_t)(128 - 32 * sc));
             const u4v ql = raw[c & 3];
             const u4v qh = raw[4 + (c & 1)];
             const int pr = c >> 1;
@@ -331,16 +334,15 @@ struct Unpack<1> {
                 const uint32_t q6 = (hs & 0x30303030u) | lo;
                 const uint32_t ev = __builtin_amdgcn_perm(0u, q6, kSelEven);
                 const uint32_t od = __builtin_amdgcn_perm(0u, q6, kSelOdd);
-                // P = sc q - 32 sc in 16-bit lanes (exact: |P| <= 4096)
-                const us2 pe = __builtin_bit_cast(us2, ev) * __builtin_bit_cast(us2, f) + __builtin_bit_cast(us2, a);
-                const us2 po = __builtin_bit_cast(us2, od) * __builtin_bit_cast(us2, f) + __builtin_bit_cast(us2, a);
-                typedef short ss2 __attribute__((ext_vector_type(2)));
-                const uint32_t he = __builtin_bit_cast(uint32_t, __builtin_bit_cast(ss2, pe) >> (ss2){6, 6});
-                const uint32_t ho = __builtin_bit_cast(uint32_t, __builtin_bit_cast(ss2, po) >> (ss2){6, 6});
-                const uint32_t le = __builtin_bit_cast(uint32_t, pe) & 0x003F003Fu;
-                const uint32_t lo2 = __builtin_bit_cast(uint32_t, po) & 0x003F003Fu;
-                pl[c][0][k] = (int)__builtin_amdgcn_perm(lo2, le, kSelPack);
-                pl[c][1][k] = (int)__builtin_amdgcn_perm(ho, he, kSelPack);
+                // P + 128 = sc q - 32 sc + 128 in 16-bit lanes (exact: it
+                // lies in [-3968, 4192]); its low byte xor 0x80 is P mod 256,
+                // its high byte (P + 128) >> 8
+                const uint32_t pe = __builtin_bit_cast(
+                    uint32_t, __builtin_bit_cast(us2, ev) * __builtin_bit_cast(us2, f) + __builtin_bit_cast(us2, a));
+                const uint32_t po = __builtin_bit_cast(
+                    uint32_t, __builtin_bit_cast(us2, od) * __builtin_bit_cast(us2, f) + __builtin_bit_cast(us2, a));
+                pl[c][0][k] = (int)(__builtin_amdgcn_perm(po, pe, kSelPack) ^ 0x80808080u);
+                pl[c][1][k] = (int)__builtin_amdgcn_perm(po, pe, kSelPackHi);
             }
         }
     }
@@ -734,12 +736,14 @@ __global__ __launch_bounds__(256, kPipe ? 1 : 2) void gemm_kq2_kernel(Args a, Gr
         }
     } else {
         // Dense: one unit per workgroup, consecutive units on one XCD
-        // (workgroups are dealt to the eight XCDs round-robin).
+        // (workgroups are dealt to the eight XCDs round-robin); the K parts
+        // of a tile are consecutive, so their partial tiles are written and
+        // read in one XCD's L2 within a short time.
         const int nwg = a.nblk_n * a.nblk_m * a.splits;
         int g = blockIdx.x;
         if ((nwg & 7) == 0) g = (g & 7) * (nwg >> 3) + (g >> 3);
-        const int rest = g / a.nblk_n;
-        run_unit(g % a.nblk_n, rest % a.nblk_m, rest / a.nblk_m);
+        const int rest = g / a.splits;
+        run_unit(rest % a.nblk_n, rest / a.nblk_n, g % a.splits);
     }
 }
 
@@ -760,46 +764,56 @@ constexpr int kPartThreads = 256;
 constexpr int64_t kPartTileBytes = (int64_t)kPartThreads * kDenseMT * 16 * 4;  // one partial tile
 constexpr int kMaxSplits = 8;
 
-// Estimated microseconds of one 256-wide K step of one tile (one workgroup
-// per CU), per weight type: MFMA cycles of the step at 2.4 GHz with the
-// measured overheads folded in.  Only the ratio against the partial-tile
-// traffic matters for the plan.
-double step_us(int wtype) { return wtype == 0 ? 0.9 : 1.3; }
-
 }  // namespace
 
-// Workgroups resident per CU (four waves of up to 256 registers, 75 KB LDS each).
+// Workgroups resident per CU (four waves of up to 256 registers, 66-75 KB LDS each).
 constexpr int kResident = 2;
+// Split-K workspace layout, the same for every shape: arrival counters in
+// the first kCntBytes (one int per tile), then the partial tiles.  A fixed
+// counter region matters because callers reuse one workspace across calls:
+// a region sized per call would let one call's partial tiles lie where a
+// later call with more tiles keeps its counters, which must be zero.
+constexpr int64_t kCntBytes = 65536;
+constexpr int64_t kMaxSplitTiles = kCntBytes / 4;
+// Largest split-K workspace the plan asks for (with at least two parts it
+// keeps the tile count within the counter region).
+constexpr int64_t kMaxPlanWsBytes = (int64_t)1 << 30;
+static_assert(kMaxPlanWsBytes / (2 * kPartTileBytes) <= kMaxSplitTiles, "the counters of a split grid fit");
 
-// Splits of the K range for a dense K-quant GEMM (1 = no split): the S that
-// minimises whole rounds of workgroups (kResident per CU) times the per-part
-// K length, plus the partial tiles' HBM traffic (written once, read once).
+// Splits of the K range for a dense K-quant GEMM (1 = no split), from
+// measured times at the prefill shapes.  Partial tiles are 64 KiB each,
+// written and read back once, and cost about as much as the compute they
+// redistribute once the grid fills the chip (Q4_K at M = 2048: 141 us
+// unsplit, 431 us in eight parts), so only short grids split:
+//  * at most one tile per CU: the largest S that keeps one workgroup per CU
+//    (Q6_K at M = 512, 80 tiles: S = 3, 156 -> 67-70 us; S = 4 puts two
+//    workgroups on some CUs, 75 us);
+//  * up to two tiles per CU with a long K (at least 16 steps): two parts,
+//    so every CU holds two workgroups (Q6_K at M = 2048, 320 tiles: 237 ->
+//    221 us);
+//  * else none.
+// The workspace it needs is capped at kMaxPlanWsBytes.
 int gemm_kq_splits(int wtype, int64_t M, int64_t N, int64_t K) {
-    const int64_t cus = num_cus() * kResident;
+    (void)wtype;
+    const int64_t cus = num_cus();
     const int64_t tiles = ((N + kq::kBN - 1) / kq::kBN) * ((M + kDenseBM - 1) / kDenseBM);
     const int64_t nsteps = K / 256;
     if (tiles <= 0 || nsteps <= 1) return 1;
-    const double t_tile = (double)nsteps * step_us(wtype);
-    int best = 1;
-    double best_t = 1e30;
-    for (int s = 1; s <= kMaxSplits && s <= nsteps; ++s) {
-        const int64_t wg = tiles * s;
-        const double rounds = (double)((wg + cus - 1) / cus);
-        double t = rounds * t_tile / s;
-        if (s > 1) t += (double)(tiles * s * kPartTileBytes) * 2.0 / 5.0e6;  // bytes / (5 TB/s) in us
-        if (t < best_t * 0.97) {
-            best_t = t;
-            best = s;
-        }
-    }
-    return best;
+    int s = 1;
+    if (tiles <= cus)
+        s = (int)std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(kMaxSplits, nsteps), cus / tiles));
+    else if (tiles <= kResident * cus && nsteps >= 16)
+        s = 2;
+    while (s > 1 && tiles * s * kPartTileBytes > kMaxPlanWsBytes) --s;
+    if (tiles > kMaxSplitTiles) s = 1;
+    return s;
 }
 
 size_t gemm_kq_ws_bytes(int wtype, int64_t M, int64_t N, int64_t K) {
     const int s = gemm_kq_splits(wtype, M, N, K);
     if (s <= 1) return 0;
     const int64_t tiles = ((N + kq::kBN - 1) / kq::kBN) * ((M + kDenseBM - 1) / kDenseBM);
-    return align256((size_t)tiles * 4) + (size_t)(tiles * s) * (size_t)kPartTileBytes;
+    return (size_t)kCntBytes + (size_t)(tiles * s) * (size_t)kPartTileBytes;
 }
 
 template <int WT>
@@ -821,12 +835,13 @@ static hipError_t launch_kq_dense(const uint8_t* W, int64_t N, int64_t K, const 
     const int64_t tiles = (int64_t)a.nblk_n * a.nblk_m;
     int s = gemm_kq_splits(WT == 3 ? 5 : WT, M, N, K);
     // a smaller workspace than the plan asks for: the largest split it holds
-    while (s > 1 && (!ws || align256((size_t)tiles * 4) + (size_t)(tiles * s) * (size_t)kPartTileBytes > ws_bytes))
+    while (s > 1 && (!ws || tiles > kMaxSplitTiles ||
+                     (size_t)kCntBytes + (size_t)(tiles * s) * (size_t)kPartTileBytes > ws_bytes))
         --s;
     a.splits = s;
     if (s > 1) {
         a.cnt = (int*)ws;
-        a.part = (float*)((uint8_t*)ws + align256((size_t)tiles * 4));
+        a.part = (float*)((uint8_t*)ws + kCntBytes);
     }
     const int64_t nwg = tiles * s;
     if (nwg > INT32_MAX) return hipErrorInvalidValue;

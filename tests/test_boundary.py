@@ -143,8 +143,8 @@ def test_null_misaligned_alias_workspace(vq):
 
 def test_gemm_workspace_checks(vq):
     """vq_gemm's workspace: 256-byte alignment and no overlap with W, Xq or Y,
-    checked before any launch; vq_gemm_workspace sizes (no workspace for
-    Q8_0, the GEMV-kernel batches, or a grid that fills the chip)."""
+    checked before any launch; vq_gemm_workspace sizes (none for Q8_0 or the
+    GEMV-kernel batches; the split plan's parts per grid size; the cap)."""
     base = dict(W=FAKE, Xq=FAKE + 0x4000000, Y=FAKE + 0x8000000)
     args = lambda ws, wsb: (vq.Q6_K, base["W"], 640, 4096, vq.Q8_K, base["Xq"], 256, base["Y"], 640, ws, wsb,
                             None)
@@ -156,7 +156,10 @@ def test_gemm_workspace_checks(vq):
     _err(vq, 5, "vq_gemm", *args(base["Y"] - 0x100, 1 << 20))
     assert vq.gemm_workspace(vq.Q8_0, 2048, 4096, 2048) == 0
     assert vq.gemm_workspace(vq.Q4_K, 1, 9728, 2560) == 0          # GEMV-kernel arm
-    assert vq.gemm_workspace(vq.Q4_K, 2048, 9728, 2560) == 0       # 1216 tiles: no split
+    assert vq.gemm_workspace(vq.Q4_K, 2048, 9728, 2560) == 0       # 1216 tiles fill the chip: no split
+    assert vq.gemm_workspace(vq.Q6_K, 512, 2560, 9728) == 65536 + 80 * 3 * 128 * 128 * 4   # one per CU
+    assert vq.gemm_workspace(vq.Q6_K, 2048, 2560, 9728) == 65536 + 320 * 2 * 128 * 128 * 4  # two per CU
+    assert vq.gemm_workspace(vq.Q4_K, 512, 9728, 2560) == 0         # 304 tiles, 10 steps: no split
     small = vq.gemm_workspace(vq.Q6_K, 256, 640, 4096)             # 10 tiles, 16 steps: split K
     assert small > 0 and small % 256 == 0
     assert vq.gemm_workspace(vq.Q4_K, 0, 640, 4096) == 0

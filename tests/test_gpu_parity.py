@@ -556,7 +556,7 @@ def test_gemm_split_k_workspace(wtype):
     Wd, Xq = H.to_dev(Wq), H.to_dev(H.pack_act(act, wtype))
     need = vq.gemm_workspace(wtype, M, N, K)
     tiles = ((N + 127) // 128) * ((M + 127) // 128)
-    cnt_bytes = (tiles * 4 + 255) // 256 * 256
+    cnt_bytes = 65536  # the arrival counters' fixed region
     part_tile = 128 * 128 * 4  # one binary32 partial tile of 128 x 128 outputs
     assert need > cnt_bytes + tiles * 2 * part_tile, "the plan takes more than two splits"
     two = cnt_bytes + tiles * 2 * part_tile
@@ -571,11 +571,30 @@ def test_gemm_split_k_workspace(wtype):
             vq.gemm(wtype, Wd, N, K, vq.Q8_K, Xq, M, Y=Yd, ws=ws)
             runs.append(H.host(Yd))
             if ws is not None:
-                assert not H.host(ws[:tiles * 4]).any(), "arrival counters left non-zero"
+                assert not H.host(ws[:cnt_bytes]).any(), "arrival counters left non-zero"
         assert np.array_equal(H.bits(runs[0]), H.bits(runs[1])), "two identical calls differ (%s)" % name
         H.assert_close(runs[0], ref, "split K %s %s" % (WNAME[wtype], name), r64)
         outs[name] = runs[0]
     H.assert_close(outs["planned"], outs["none"], "split vs no split %s" % WNAME[wtype])
+
+
+@pytest.mark.parametrize("wtype", [oracle.Q4_K, oracle.Q6_K])
+def test_gemm_workspace_reused_across_shapes(wtype):
+    """One workspace for a 10-tile call split eight ways, then an 80-tile call
+    split three ways: the second call's counters (80 of them) must not meet
+    the first call's partial tiles, so both outputs meet the tolerance."""
+    import torch
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device=H.dev())
+    for (M, N, K), seed in (((256, 640, 4096), 1680), ((512, 2560, 2048), 1690)):
+        assert vq.gemm_workspace(wtype, M, N, K) > 0
+        W = synth.normal((seed, wtype), (N, K), 0.02)
+        X = synth.normal((seed + 1, wtype), (M, K))
+        Wq = oracle.quantize_weights(wtype, W)
+        act = oracle_act(wtype, X)
+        H.say("gemm reused workspace %s M=%d N=%d K=%d" % (WNAME[wtype], M, N, K))
+        Y = vq.gemm(wtype, H.to_dev(Wq), N, K, vq.Q8_K, H.to_dev(H.pack_act(act, wtype)), M, ws=ws)
+        H.assert_close(H.host(Y), oracle.gemm(wtype, Wq, N, K, act, nthreads=8),
+                       "reused workspace %s M=%d" % (WNAME[wtype], M), ref_fp64.gemm_fp64(wtype, Wq, N, K, act))
 
 
 def test_determinism_and_witness():
