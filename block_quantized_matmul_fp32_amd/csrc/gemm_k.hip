@@ -408,11 +408,13 @@ __global__ __launch_bounds__(256, kPipe ? 1 : 2) void gemm_kq2_kernel(Args a, Gr
     const int nst = s_end - s_begin;
 
     const uint8_t* W = a.W;
+    int rows_here;  // valid activation rows of this tile (uniform)
     if (kGrouped) {
         const int tix = mb;
         const int e = ga.tiles[4 * tix + 0];
         const int first = ga.tiles[4 * tix + 1];
         const int rows = ga.tiles[4 * tix + 2];
+        rows_here = rows;
         W = a.W + (int64_t)e * ga.expert_stride;
         for (int r = tid; r < BM; r += NT) {
             if (r < rows) {
@@ -426,12 +428,17 @@ __global__ __launch_bounds__(256, kPipe ? 1 : 2) void gemm_kq2_kernel(Args a, Gr
         }
     } else {
         const int m0 = mb * BM;
+        rows_here = min(BM, a.M - m0);
         for (int r = tid; r < BM; r += NT) {
             const int m = m0 + r;
             sRow[r] = (m < a.M) ? m : -1;
             sOut[r] = (m < a.M) ? m : -1;
         }
     }
+    rows_here = __builtin_amdgcn_readfirstlane(rows_here);
+    // 32-row activation tiles that hold a valid row (the rest are skipped:
+    // their MFMAs and epilogue would only compute padding)
+    const int mt_live = (rows_here + 31) / 32;
     __syncthreads();
 
     const int nbk = a.K / kKS;
@@ -607,6 +614,7 @@ __global__ __launch_bounds__(256, kPipe ? 1 : 2) void gemm_kq2_kernel(Args a, Gr
         v4i av = *(const v4i*)(abuf + abase[0] + 16 * (0 ^ ax7[0]));
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
+            if (t > 0 && t >= mt_live) break;  // uniform: only padding rows left
             v16i R0 = {}, R1 = {};
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
