@@ -746,12 +746,21 @@ __global__ __launch_bounds__(256, kPipe ? 1 : 2) void gemm_kq2_kernel(Args a, Gr
         // Dense: one unit per workgroup, consecutive units on one XCD
         // (workgroups are dealt to the eight XCDs round-robin); the K parts
         // of a tile are consecutive, so their partial tiles are written and
-        // read in one XCD's L2 within a short time.
+        // read in one XCD's L2 within a short time.  Tiles run in groups of
+        // kGroupN weight-row blocks, activation-row block by block, so the
+        // workgroups resident on one XCD at a time share a few weight and a
+        // few activation blocks instead of each reading its own weight block.
         const int nwg = a.nblk_n * a.nblk_m * a.splits;
         int g = blockIdx.x;
         if ((nwg & 7) == 0) g = (g & 7) * (nwg >> 3) + (g >> 3);
         const int rest = g / a.splits;
-        run_unit(rest % a.nblk_n, rest / a.nblk_n, g % a.splits);
+        constexpr int kGroupN = 8;
+        const int per_group = kGroupN * a.nblk_m;
+        const int grp = rest / per_group;
+        const int first_nb = grp * kGroupN;
+        const int gn = min(kGroupN, a.nblk_n - first_nb);
+        const int within = rest - grp * per_group;
+        run_unit(first_nb + within % gn, within / gn, g % a.splits);
     }
 }
 

@@ -10,8 +10,11 @@
 //
 // Routing is integer bookkeeping with one answer: counts per expert, the
 // exclusive prefix offsets, and the pair indices t*top_k+s listed per expert
-// in ascending (t, s) order.  It is built without atomics in three small
-// launches, so the list is deterministic:
+// in ascending (t, s) order.  It is built without atomics, so the list is
+// deterministic.  A call of up to 8192 pairs is routed by one workgroup in
+// one launch (route_one_kernel below); larger calls take three launches,
+// which spread the ballot work (the bulk of the routing's instructions) over
+// one CU per chunk:
 //  * one wave per chunk of 64 tokens walks the chunk's pairs 64 at a time;
 //    the lanes holding the same expert are found with one ballot per bit of
 //    the expert id, which gives each pair its rank among the chunk's earlier
@@ -224,6 +227,148 @@ __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(int nchunks, i
     }
 }
 
+// One workgroup routes a whole call of up to kOneMaxPairs pairs in a single
+// launch (no chunk table and no second or third launch).  Wave v of the 16
+// takes the contiguous pair range [v L, (v + 1) L), L = 64 rounds:
+//  * count: per round of 64 pairs, the ballot-per-id-bit groups give each
+//    pair its rank among the wave's earlier pairs of its expert (kept in
+//    rank[]) and advance the wave's per-expert count in LDS;
+//  * scan: one thread per expert turns the 16 wave counts into the waves'
+//    exclusive offsets inside the expert (wave order is pair order) and the
+//    expert's total; totals and tile counts are scanned over experts, and the
+//    counts, offsets and tile table are written;
+//  * place: each wave walks its pairs again, list[offset(e) + wave offset(e)
+//    + rank] = pair index.
+// Per-wave counts and offsets stay below 2^16 (at most kOneMaxPairs pairs).
+// Every round costs each wave about 140 instructions, and the 16 waves share
+// one CU's four SIMDs (about 1.3 us per round of 1024 pairs measured), so
+// above kOneMaxPairs the three-launch path, with one CU per chunk, is faster.
+constexpr int kOneThreads = 1024;
+constexpr int kOneWaves = kOneThreads / 64;
+constexpr int64_t kOneMaxPairs = 8192;
+constexpr int kOneIdBatch = 8;  // rounds whose ids are requested together
+__global__ __launch_bounds__(kOneThreads) void route_one_kernel(const int32_t* __restrict__ ids, int npairs, int E,
+                                                                int tile_rows, int32_t* __restrict__ rank,
+                                                                int32_t* __restrict__ counts,
+                                                                int32_t* __restrict__ offsets,
+                                                                int32_t* __restrict__ list,
+                                                                int32_t* __restrict__ tiles,
+                                                                int32_t* __restrict__ ntiles) {
+    __shared__ uint16_t wcnt[kOneWaves * 1024];  // [wave][expert]: count, then the wave's offset
+    __shared__ int32_t eoff[1024];               // exclusive offset of each expert in the list
+    __shared__ int32_t wsc[kOneWaves], wst[kOneWaves];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int v = __builtin_amdgcn_readfirstlane(tid >> 6);
+    for (int i = tid; i < kOneWaves * E; i += kOneThreads) wcnt[i] = 0;
+    __syncthreads();
+    const int rounds = (npairs + kOneThreads - 1) / kOneThreads;
+    const int p0 = v * rounds * 64;
+    uint16_t* cnt = wcnt + v * E;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int idv[kOneIdBatch];
+    for (int r0 = 0; r0 < rounds; r0 += kOneIdBatch) {
+#pragma unroll
+        for (int k = 0; k < kOneIdBatch; ++k) {
+            const int p = p0 + 64 * (r0 + k) + lane;
+            idv[k] = (r0 + k < rounds && p < npairs) ? ids[p] : -1;
+        }
+#pragma unroll
+        for (int k = 0; k < kOneIdBatch; ++k) {
+            if (r0 + k >= rounds) break;  // uniform
+            const int p = p0 + 64 * (r0 + k) + lane;
+            const int e = idv[k];
+            const bool ok = p < npairs && e >= 0 && e < E;
+            const int key = ok ? e : 1024 + lane;  // a pair not routed matches no other lane
+            uint64_t same = ~0ull;
+#pragma unroll
+            for (int b = 0; b < kIdBits; ++b) {
+                const uint64_t set = __ballot((key >> b) & 1);
+                same &= ((key >> b) & 1) ? set : ~set;
+            }
+            // the wave's LDS operations run in order, so this round reads what
+            // the previous round's group leaders wrote
+            const int before = ok ? (int)cnt[e] : 0;
+            if (ok) rank[p] = before + __popcll(same & below);
+            if (ok && (same >> lane) == 1ull) cnt[e] = (uint16_t)(before + __popcll(same));
+        }
+    }
+    __syncthreads();
+    int total = 0;
+    if (tid < E) {
+        int c[kOneWaves];  // all 16 counts read before the first offset is written
+#pragma unroll
+        for (int u = 0; u < kOneWaves; ++u) c[u] = wcnt[u * E + tid];
+#pragma unroll
+        for (int u = 0; u < kOneWaves; ++u) {
+            wcnt[u * E + tid] = (uint16_t)total;
+            total += c[u];
+        }
+        counts[tid] = total;
+    }
+    const int nt = (tid < E) ? (total + tile_rows - 1) / tile_rows : 0;
+    // inclusive scans of the totals and tile counts over experts (index =
+    // tid): within each wave by shuffles, then the earlier waves' sums added
+    int a = total, b = nt;
+    for (int o = 1; o < 64; o <<= 1) {
+        const int ua = __shfl_up(a, o, 64), ub = __shfl_up(b, o, 64);
+        if (lane >= o) {
+            a += ua;
+            b += ub;
+        }
+    }
+    if (lane == 63) {
+        wsc[v] = a;
+        wst[v] = b;
+    }
+    __syncthreads();
+    for (int k = 0; k < v; ++k) {
+        a += wsc[k];
+        b += wst[k];
+    }
+    if (tid < E) {
+        const int off = a - total;
+        eoff[tid] = off;
+        offsets[tid] = off;
+        if (tid == E - 1) {
+            offsets[E] = a;
+            ntiles[0] = b;
+        }
+        const int tbase = b - nt;
+        for (int i = 0; i < nt; ++i) {
+            tiles[4 * (tbase + i) + 0] = tid;
+            tiles[4 * (tbase + i) + 1] = off + i * tile_rows;
+            tiles[4 * (tbase + i) + 2] = min(tile_rows, total - i * tile_rows);
+            tiles[4 * (tbase + i) + 3] = 0;
+        }
+    }
+    __syncthreads();  // expert offsets and wave offsets visible
+    for (int r0 = 0; r0 < rounds; r0 += kOneIdBatch) {
+        // The batch's ids and ranks (this thread's own stores above) are
+        // loaded unconditionally (pair index clamped into the call) and every
+        // slot is computed before the first list store, so the stores do not
+        // wait on each other.
+        int rkv[kOneIdBatch], dst[kOneIdBatch];
+#pragma unroll
+        for (int k = 0; k < kOneIdBatch; ++k) {
+            const int p = min(p0 + 64 * (r0 + k) + lane, npairs - 1);
+            idv[k] = ids[p];
+            rkv[k] = rank[p];
+        }
+#pragma unroll
+        for (int k = 0; k < kOneIdBatch; ++k) {
+            const int p = p0 + 64 * (r0 + k) + lane;
+            const int e = idv[k];
+            const bool ok = r0 + k < rounds && p < npairs && e >= 0 && e < E;
+            const int ec = ok ? e : 0;
+            dst[k] = ok ? eoff[ec] + (int)cnt[ec] + rkv[k] : -1;
+        }
+#pragma unroll
+        for (int k = 0; k < kOneIdBatch; ++k)
+            if (dst[k] >= 0) list[dst[k]] = p0 + 64 * (r0 + k) + lane;
+    }
+}
+
 // One thread per pair: list[offsets[e] + chunk offset + rank] = pair index.
 __global__ __launch_bounds__(256) void route_place_kernel(const int32_t* __restrict__ ids, int64_t npairs,
                                                           int top_k, int E, const int32_t* __restrict__ chunk,
@@ -264,6 +409,12 @@ hipError_t launch_check_ids(const int32_t* ids, int64_t T, int64_t top_k, int64_
 hipError_t launch_route(const int32_t* ids, int64_t T, int64_t top_k, int64_t E, int tile_rows, RouteWs ws,
                         hipStream_t st) {
     if (tile_rows < kGroupMinTileRows) return hipErrorInvalidValue;
+    const int64_t npairs_all = T * top_k;
+    if (npairs_all <= kOneMaxPairs) {
+        route_one_kernel<<<1, kOneThreads, 0, st>>>(ids, (int)npairs_all, (int)E, tile_rows, ws.rank, ws.counts,
+                                                    ws.offsets, ws.list, ws.tiles, ws.ntiles);
+        return hipGetLastError();
+    }
     const int nchunks = (int)((T + kRouteChunk - 1) / kRouteChunk);
     if (nchunks > 0)
         route_count_kernel<<<nchunks, 64, 0, st>>>(ids, (int)T, (int)top_k, (int)E, ws.chunk, ws.rank);

@@ -715,10 +715,9 @@ def test_grouped_types_and_arms(wtype, per_row):
 
 
 def test_grouped_route_unstaged_scan():
-    """Many experts and tokens (1000 x top-4 over 1024 experts): the routing
-    scan's chunk table (16 chunks x 1024 experts) is too large to stage in
-    LDS, so the scan reads and writes it in global memory; routing
-    bit-identical to the oracle, Y within the GEMM tolerance."""
+    """Many experts (1000 tokens x top-4 over 1024 experts, routed by the
+    single-workgroup kernel with its per-wave counts for every expert):
+    routing bit-identical to the oracle, Y within the GEMM tolerance."""
     E, N, K, T, top_k = 1024, 16, 256, 1000, 4
     ids = synth.random_ids(1880, T, E, top_k)
     Wq, act, rw, Y, Ysum, ws = run_grouped(E, N, K, T, top_k, ids, 1890)
@@ -730,6 +729,35 @@ def test_grouped_route_unstaged_scan():
     Y_ref = oracle.gemm_grouped(oracle.Q4_K, Wq, E, N, K, act, ids, nthreads=8)
     Yh = H.host(Y)
     H.assert_gemm(oracle.Q4_K, Yh, Y_ref, "grouped Y (unstaged routing scan)")
+    H.assert_bitwise(H.host(Ysum), oracle.weighted_sum(Yh, rw), "weighted sum of the GPU's Y")
+
+
+@pytest.mark.parametrize("E,T,top_k,skew", [(16, 1100, 8, False), (1024, 1100, 8, False),
+                                             (8, 1024, 8, True), (9, 1025, 8, True)])
+def test_grouped_route_size_paths(E, T, top_k, skew):
+    """Routing on both sides of the single-workgroup limit (8192 pairs):
+    1100 x top-8 takes the three-launch path with its chunk table staged in
+    LDS (16 experts) or read in global memory (1024 experts); 1024 x 8 pairs
+    almost all on one expert (repeated ids) fill the single-workgroup
+    kernel to its limit, and one token more goes to the three-launch path.
+    Counts, offsets and the list bit-identical to the oracle, Y within the
+    GEMM tolerance."""
+    N, K = 16, 256
+    if skew:
+        ids = np.zeros((T, top_k), np.int32)
+        ids[::37, 1] = 1
+        ids[5::41, 2] = E - 1
+    else:
+        ids = synth.random_ids(1940 + E, T, E, top_k)
+    Wq, act, rw, Y, Ysum, ws = run_grouped(E, N, K, T, top_k, ids, 1950)
+    counts, offsets, lst = vq.grouped_ws_views(ws, E, T, top_k)
+    c_ref, o_ref, l_ref = oracle.route(ids, E)
+    assert np.array_equal(H.host(counts), c_ref)
+    assert np.array_equal(H.host(offsets), o_ref)
+    assert np.array_equal(H.host(lst), l_ref)
+    Y_ref = oracle.gemm_grouped(oracle.Q4_K, Wq, E, N, K, act, ids, nthreads=8)
+    Yh = H.host(Y)
+    H.assert_gemm(oracle.Q4_K, Yh, Y_ref, "grouped Y (routing size paths)")
     H.assert_bitwise(H.host(Ysum), oracle.weighted_sum(Yh, rw), "weighted sum of the GPU's Y")
 
 
