@@ -20,11 +20,15 @@ The same line carries:
                   in the same launch shape with no compute (vq_stream_probe);
   cpu_baseline -- the CPU oracle running the same decode step on the host's
                   cores (a bounded number of repetitions);
-  prefill / q8_0 / grouped / quantizer -- the prefill GEMM (int8 TOPS), the
-                  Q8_0 x Q8_1 GEMM and GEMV, the routed-expert grouped GEMM with
-                  the weighted expert sum (broadcast arm, and the per-row arm
-                  at the down-projection shape), and the standalone quantizer,
-                  timed with HIP events in the same run (secondary numbers).
+  prefill / q8_0 / grouped / quantizer -- the prefill GEMM (int8 TOPS; also
+                  end to end with its activation quantizer), the Q8_0 x Q8_1
+                  GEMM and GEMV, the routed-expert grouped GEMM with the
+                  weighted expert sum (broadcast arm, and the per-row arm at
+                  the down-projection shape), and the standalone quantizer,
+                  timed with HIP events in the same run (secondary numbers);
+  ceilings     -- measured references beside the spec peaks: the int8 MFMA
+                  rate of vq_mfma_probe, a 1 GiB device-to-device copy and a
+                  570 MB read-only stream.
 
 Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 20]
 """
@@ -208,7 +212,9 @@ def run_cpu_baseline(seconds: float):
         el = time.perf_counter() - t0
         if el >= seconds or reps >= 100000:
             break
+    step_ops = 2.0 * (9728 * 2560 + 2560 * 9728)
     return {"value": round(step_bytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "gops": round(step_ops * reps / el / 1e9, 3),
             "affinity_cores": cores, "threads_reason": why,
             "kind": "oracle", "cpu_model": cpu_model(),
             "sample": "%d repetitions of the full decode step (Q8_K quantization of x plus the Q4_K "
@@ -298,12 +304,18 @@ def run_prefill(torch, vq, synth, iters):
         tg, _ = time_graph(lambda i: vq.gemm(vq.Q4_K, Qg[i % Rg], 9728, 2560, vq.Q8_K, qh, M, Y=Yg), Rg, 3 * Rg)
         td, _ = time_graph(lambda i: vq.gemm(vq.Q6_K, Qd[i % Rd], 2560, 9728, vq.Q8_K, qi, M, Y=Yd), Rd, 3 * Rd)
         tq, _ = time_graph(lambda i: vq.quantize_act(vq.Q8_K, Xh, Xq=qh), 8, iters)
+        # end to end: the quantizer of the fp32 activations, then the GEMM
+        tgq, _ = time_graph(lambda i: (vq.quantize_act(vq.Q8_K, Xh, Xq=qh),
+                                       vq.gemm(vq.Q4_K, Qg[i % Rg], 9728, 2560, vq.Q8_K, qh, M, Y=Yg)), Rg, 3 * Rg)
+        tdq, _ = time_graph(lambda i: (vq.quantize_act(vq.Q8_K, Xi, Xq=qi),
+                                       vq.gemm(vq.Q6_K, Qd[i % Rd], 2560, 9728, vq.Q8_K, qi, M, Y=Yd)), Rd, 3 * Rd)
         ops = 2.0 * M * 9728 * 2560
         out["M%d" % M] = {
             "q4k_gate_us": round(tg * 1e3, 2), "q4k_tops": round(ops / (tg * 1e-3) / 1e12, 1),
             "q4k_frac": round(ops / (tg * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
             "q6k_down_us": round(td * 1e3, 2), "q6k_tops": round(ops / (td * 1e-3) / 1e12, 1),
             "q6k_frac": round(ops / (td * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
+            "q4k_quant_gemm_us": round(tgq * 1e3, 2), "q6k_quant_gemm_us": round(tdq * 1e3, 2),
             "quantize_q8k_us": round(tq * 1e3, 2),
             "quantize_q8k_gbs": round(M * 2560 * (4 + 1 + 4 / 256 + 2 / 16) / (tq * 1e-3) / 1e9, 1),
         }
@@ -518,6 +530,70 @@ def run_grouped_down(torch, vq, synth, iters):
             "rotation_sets_cold": R, "algorithmic_bytes": int(alg)}
 
 
+def run_ceilings(torch, vq):
+    """Measured ceilings beside the spec peaks: the int8 MFMA rate of
+    vq_mfma_probe (register operands, nothing else, 2 workgroups per CU), a
+    1 GiB device-to-device copy (read + write bytes) by torch, and a 570 MB
+    read-only stream (vq_stream_probe)."""
+    dev = torch.device("cuda:0")
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    iters = 4096
+    for _ in range(5):  # about 5 ms of the same load first: the clocks settle under it
+        vq.mfma_probe(iters, sink)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(9):
+        a, b = event_pair()
+        a.record()
+        ops = vq.mfma_probe(iters, sink)
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    ms = sorted(times)[len(times) // 2]
+    tops = ops / (ms * 1e-3) / 1e12
+    n = 1 << 28  # 1 GiB of fp32
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ct = []
+    for _ in range(5):
+        a, b = event_pair()
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        ct.append(a.elapsed_time(b))
+    cms = sorted(ct)[len(ct) // 2]
+    gbs = 2 * 4 * n / (cms * 1e-3) / 1e9
+    del src, dst
+    # read-only: the streaming probe over a 570 MB Q8_0 buffer (262144 rows of
+    # 2048), each workgroup reading its rows once
+    Nr, Kr = 262144, 2048
+    Wr = torch.zeros(vq.weight_bytes(vq.Q8_0, Nr, Kr), dtype=torch.uint8, device=dev)
+    rsink = torch.zeros(Nr, dtype=torch.int32, device=dev)
+    vq.stream_probe(vq.Q8_0, Wr, Nr, Kr, rsink)
+    torch.cuda.synchronize()
+    rt = []
+    for _ in range(5):
+        a, b = event_pair()
+        a.record()
+        vq.stream_probe(vq.Q8_0, Wr, Nr, Kr, rsink)
+        b.record()
+        torch.cuda.synchronize()
+        rt.append(a.elapsed_time(b))
+    rms = sorted(rt)[len(rt) // 2]
+    rgbs = Wr.numel() / (rms * 1e-3) / 1e9
+    del Wr, rsink
+    return {"int8_mfma_tops": round(tops, 1), "int8_mfma_frac_of_spec": round(tops / INT8_PEAK_TOPS, 4),
+            "int8_mfma_probe": "vq_mfma_probe: %d rounds of 8 v_mfma_i32_32x32x32_i8 chains per wave, "
+                               "2 workgroups of 4 waves per CU, %.1f us" % (iters, ms * 1e3),
+            "hbm_copy_gbs": round(gbs, 1), "hbm_copy_frac_of_spec": round(gbs / HBM_PEAK_GBS, 4),
+            "hbm_copy": "1 GiB device-to-device copy (torch), read + write bytes, %.1f us" % (cms * 1e3),
+            "hbm_read_gbs": round(rgbs, 1), "hbm_read_frac_of_spec": round(rgbs / HBM_PEAK_GBS, 4),
+            "hbm_read": "vq_stream_probe over a 570 MB buffer (Q8_0 [262144, 2048]), %.1f us" % (rms * 1e3)}
+
+
 def calibrate_copy(torch, nbytes):
     """A plain device copy of known size, for scaling rocprofv3 FETCH_SIZE and
     WRITE_SIZE (run under rocprofv3 --pmc)."""
@@ -541,7 +617,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--secondary-iters", type=int, default=20)
-    ap.add_argument("--sections", default="prefill,q8_0,q5k,small_batch,producers,grouped,grouped_down_per_row",
+    ap.add_argument("--sections", default="prefill,q8_0,q5k,small_batch,producers,grouped,grouped_down_per_row,ceilings",
                     help="comma-separated secondary sections to run (all by default)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (rocprofv3 counter scaling)")
@@ -603,6 +679,7 @@ def main():
                            "timing": "median over graph replays of rotated (cold) launches",
                            "stream_floor": "vq_stream_probe: the GEMV's weight bytes and launch shape, no compute"},
     }
+    wanted = set(x for x in args.sections.split(",") if x)
     if not args.no_secondary:
         it = args.secondary_iters
         sections = [
@@ -615,17 +692,20 @@ def main():
             ("grouped_down_per_row", "grouped per-row arm (MoE down projection)",
              lambda: run_grouped_down(torch, vq, synth, max(5, it // 2))),
         ]
-        wanted = set(x for x in args.sections.split(",") if x)
-        unknown = wanted - set(k for k, _, _ in sections)
+        unknown = wanted - set(k for k, _, _ in sections) - {"ceilings"}
         if unknown:
             sys.exit("unknown --sections entries: %s" % ", ".join(sorted(unknown)))
         for key, what, fn in sections:
             if key in wanted:
                 log("[bench] " + what)
                 line[key] = fn()
+    if not args.no_secondary and "ceilings" in wanted:
+        log("[bench] measured ceilings (int8 MFMA probe, 1 GiB copy)")
+        line["ceilings"] = run_ceilings(torch, vq)
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline (%.0f s)" % args.cpu_seconds)
         line["cpu_baseline"] = run_cpu_baseline(args.cpu_seconds)
+        line["cpu_baseline"]["gpu_speedup"] = round(line["cpu_baseline"]["ms_per_step"] / dec["ms_per_step"], 1)
         log("[bench] fp64 reference (numpy)")
         line["cpu_baseline"]["fp64_reference"] = run_cpu_fp64_reference()
     else:

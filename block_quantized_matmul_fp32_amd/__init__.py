@@ -29,7 +29,7 @@ EXPORTS = [
     "vq_quantize_act", "vq_quantize_weights", "vq_gemv", "vq_gemm", "vq_grouped_workspace_bytes",
     "vq_gemm_grouped", "vq_gemm_grouped_rows", "vq_gemm_grouped_noalloc", "vq_stream_probe", "vq_weighted_sum", "vq_get_stats", "vq_reset_stats",
     "vq_version", "vq_rmsnorm_quant", "vq_silu_mul_quant", "vq_set_small_batch_max", "vq_small_batch_max",
-    "vq_set_gemm_row_block", "vq_gemm_workspace", "vq_set_debug", "vq_device_status",
+    "vq_set_gemm_row_block", "vq_gemm_workspace", "vq_set_debug", "vq_device_status", "vq_mfma_probe",
 ]
 
 STAT_FIELDS = ["quantize_q8k", "quantize_q8_1", "quantize_weights", "gemv_q4k", "gemv_q6k", "gemv_q8_0",
@@ -86,6 +86,8 @@ def lib():
         L.vq_gemm_grouped_rows.argtypes = [I, P, I64, I64, I64, I, P, I64, P, I64, P, P, P, P, Z, P]
         L.vq_gemm_grouped_noalloc.argtypes = [I, P, I64, I64, I64, I, P, I64, P, I64, P, P, P, P]
         L.vq_stream_probe.argtypes = [I, P, I64, I64, P, Z, P]
+        L.vq_mfma_probe.argtypes = [I64, P, Z, ctypes.POINTER(ctypes.c_int64), P]
+        L.vq_mfma_probe.restype = I
         L.vq_set_debug.argtypes = [I, I64]
         L.vq_set_debug.restype = I
         L.vq_device_status.argtypes = [P]
@@ -395,6 +397,16 @@ def stream_probe(w: int, W, N: int, K: int, sink, stream=None):
     nb = sink.numel() * sink.element_size()
     _check(lib().vq_stream_probe(w, _dev(W, "W", weight_bytes(w, N, K)), N, K, _dev(sink, "sink", 4 * N), nb,
                                  _stream(stream)))
+
+
+def mfma_probe(iters: int, sink, stream=None) -> int:
+    """vq_mfma_probe: the int8 MFMA ceiling launch (register operands, eight
+    chains per wave, nothing else); returns the int8 operations it performs."""
+    addr = _dev(sink, "sink", 4)
+    ops = ctypes.c_int64(0)
+    _check(lib().vq_mfma_probe(int(iters), addr, sink.numel() * sink.element_size(), ctypes.byref(ops),
+                               _stream(stream)))
+    return ops.value
 
 
 GROUPED_NOALLOC_SCRATCH_BYTES = 4 << 20  # VQ_GROUPED_NOALLOC_SCRATCH_BYTES

@@ -998,4 +998,45 @@ hipError_t launch_gemm_kq_grouped(int wtype, const uint8_t* W, int64_t E, int64_
     return launch_kq_grouped_w<3>(tile_rows, W, E, N, K, aqs, ad, aux, T, top_k, per_row, ws, Y, st);
 }
 
+// The int8 MFMA ceiling: every lane of every wave keeps eight independent
+// v_mfma_i32_32x32x32_i8 accumulator chains busy on register operands for
+// `iters` rounds and does nothing else, two workgroups of four waves per CU
+// (two waves per SIMD), so its rate is what the matrix cores sustain at the
+// clocks this part runs under load.  The accumulators are folded into one
+// word that is stored only if it equals `key` (in practice never), so the
+// MFMAs are kept and nothing is written.
+constexpr int kMfmaProbeChains = 8;
+constexpr int kMfmaProbeThreads = 256;
+constexpr int kMfmaProbeWgsPerCu = 2;
+__global__ __launch_bounds__(kMfmaProbeThreads, kMfmaProbeWgsPerCu) void mfma_probe_kernel(int64_t iters,
+                                                                                       uint32_t key,
+                                                                                       uint32_t* sink) {
+    const int t = (int)threadIdx.x;
+    const kq::v4i a = {t * 0x01010101, t ^ 0x5A5A5A5A, ~t, t * 3};
+    const kq::v4i b = {t + 1, t * 7, t ^ 0x33333333, t << 3};
+    kq::v16i acc[kMfmaProbeChains];
+#pragma unroll
+    for (int c = 0; c < kMfmaProbeChains; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[c][r] = c;
+    for (int64_t i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int c = 0; c < kMfmaProbeChains; ++c) acc[c] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acc[c], 0, 0, 0);
+    }
+    uint32_t x = 0;
+#pragma unroll
+    for (int c = 0; c < kMfmaProbeChains; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x ^= (uint32_t)acc[c][r];
+    if (x == key) sink[0] = x;
+}
+
+hipError_t launch_mfma_probe(int64_t iters, uint32_t* sink, int64_t* ops_out, hipStream_t st) {
+    const int64_t grid = (int64_t)num_cus() * kMfmaProbeWgsPerCu;
+    const int64_t waves = grid * (kMfmaProbeThreads / 64);
+    if (ops_out) *ops_out = waves * iters * kMfmaProbeChains * (2 * 32 * 32 * 32);
+    mfma_probe_kernel<<<(unsigned)grid, kMfmaProbeThreads, 0, st>>>(iters, 0x9E3779B9u, sink);
+    return hipGetLastError();
+}
+
 }  // namespace vqk

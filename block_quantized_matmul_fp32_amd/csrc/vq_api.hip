@@ -434,6 +434,16 @@ vq_status vq_stream_probe(int w, const void* W, int64_t N, int64_t K, void* sink
     return hip_status(e, fn);
 }
 
+vq_status vq_mfma_probe(int64_t iters, void* sink, size_t sink_bytes, int64_t* ops_out, hipStream_t stream) {
+    const char* fn = "vq_mfma_probe";
+    if (iters < 1 || iters > ((int64_t)1 << 24))
+        return fail(VQ_ERR_INVALID_ARG, "%s: iters = %lld outside [1, 2^24]", fn, (long long)iters);
+    if (!sink) return fail(VQ_ERR_INVALID_ARG, "%s: null sink", fn);
+    if (!aligned(sink, 4)) return fail(VQ_ERR_INVALID_ARG, "%s: sink must be 4-byte aligned", fn);
+    if (sink_bytes < 4) return fail(VQ_ERR_WORKSPACE, "%s: sink of %zu bytes, 4 needed", fn, sink_bytes);
+    return hip_status(vqk::launch_mfma_probe(iters, (uint32_t*)sink, ops_out, stream), fn);
+}
+
 vq_status vq_set_debug(int flags, int64_t wait_polls) {
     if (flags & ~(VQ_DEBUG_SYNC | VQ_DEBUG_CHECK_IDS))
         return fail(VQ_ERR_INVALID_ARG, "vq_set_debug: unknown flags 0x%x", flags);

@@ -92,6 +92,8 @@ hipError_t launch_gemm(int wtype, const uint8_t* W, int64_t N, int64_t K, const 
                        hipStream_t st);
 
 // Streaming floor of the decode GEMV's launch (measurement only).
+// int8 MFMA ceiling (one launch of 2 workgroups per CU); ops_out gets its int8 operations.
+hipError_t launch_mfma_probe(int64_t iters, uint32_t* sink, int64_t* ops_out, hipStream_t st);
 hipError_t launch_stream_probe(int wtype, const uint8_t* W, int64_t N, int64_t K, uint32_t* sink, int64_t* grid_out,
                                hipStream_t st);
 

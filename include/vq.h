@@ -293,6 +293,19 @@ vq_status vq_stream_probe(int w, const void* W, int64_t N, int64_t K, void* sink
                           hipStream_t stream);
 
 /* ---------------------------------------------------------------------- */
+/* Measurement: the int8 MFMA ceiling, the secondary reference beside the   */
+/* 5.0 POP/s spec for the GEMMs' fractions.  Two workgroups of four waves   */
+/* per CU, each wave running eight independent chains of                    */
+/* v_mfma_i32_32x32x32_i8 on register operands for `iters` rounds and      */
+/* nothing else: the rate the matrix cores sustain at this part's clocks    */
+/* under load.  iters in [1, 2^24]; sink: device memory of at least 4       */
+/* bytes, 4-byte aligned (stored to only if the accumulators reach a value  */
+/* the probe never produces in practice); ops_out (host, may be NULL): the  */
+/* int8 operations of the launch (2*32*32*32 per MFMA).                     */
+/* ---------------------------------------------------------------------- */
+vq_status vq_mfma_probe(int64_t iters, void* sink, size_t sink_bytes, int64_t* ops_out, hipStream_t stream);
+
+/* ---------------------------------------------------------------------- */
 /* Row blocks of the MFMA arm of vq_gemm.  The GEMM kernel addresses the    */
 /* activation bytes of one launch with 32-bit offsets, so vq_gemm launches  */
 /* it once per block of at most floor(2^31 / K) rows (rounded down to the   */

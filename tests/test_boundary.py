@@ -209,6 +209,16 @@ def test_stream_probe_checks(vq):
     assert vq.lib().vq_stream_probe(vq.Q4_K, None, 0, 256, None, 0, None) == 0
 
 
+def test_mfma_probe_checks(vq):
+    """vq_mfma_probe: the round count's range and the sink (host only)."""
+    _err(vq, 1, "vq_mfma_probe", 0, FAKE, 4, None, None)
+    _err(vq, 1, "vq_mfma_probe", (1 << 24) + 1, FAKE, 4, None, None)
+    _err(vq, 1, "vq_mfma_probe", 16, None, 4, None, None)
+    _err(vq, 1, "vq_mfma_probe", 16, FAKE + 2, 4, None, None)
+    msg = _err(vq, 6, "vq_mfma_probe", 16, FAKE, 3, None, None)
+    assert "4" in msg
+
+
 def test_set_debug_checks(vq):
     """vq_set_debug: unknown flags and out-of-range bounds are rejected (host only)."""
     _err(vq, 1, "vq_set_debug", 8, 0)

@@ -165,6 +165,19 @@ def test_stream_probe_reads_only(wtype):
         assert (H.host(sink) == 7).all()
 
 
+def test_mfma_probe_runs():
+    """vq_mfma_probe (the int8 MFMA ceiling) runs, leaves its sink untouched
+    and reports 2*32*32*32 ops per MFMA: eight chains per wave, four waves
+    per workgroup, two workgroups per CU."""
+    import torch
+    sink = torch.full((4,), 7, dtype=torch.int32, device=H.dev())
+    H.say("mfma probe")
+    ops = vq.mfma_probe(64, sink)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert ops == cus * 2 * 4 * 64 * 8 * 65536
+    assert (H.host(sink) == 7).all()
+
+
 def gemv_max_k(wtype):
     """Largest K the fused GEMV accepts (its weight row and quantized x must
     fit LDS), found from the library's host-side shape check, which rejects
