@@ -223,15 +223,26 @@ def run_cpu_baseline(seconds: float):
 
 
 def cpu_model() -> str:
-    """The host CPU's model name (first entry of /proc/cpuinfo), or "unknown"."""
+    """The host CPU's model name with its family / model / stepping and clock
+    (first processor of /proc/cpuinfo; a virtualised host may show a short
+    name), or "unknown"."""
+    fields = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if not line.strip():
+                    break
+                k, _, v = line.partition(":")
+                fields[k.strip()] = v.strip()
     except OSError:
         pass
-    return "unknown"
+    name = fields.get("model name")
+    if not name:
+        return "unknown"
+    ids = ["%s %s" % (k, fields[k]) for k in ("cpu family", "model", "stepping") if k in fields]
+    if "cpu MHz" in fields:
+        ids.append("%s MHz" % fields["cpu MHz"].split(".")[0])
+    return "%s (%s)" % (name, ", ".join(ids)) if ids else name
 
 
 def decode_step_bytes():
