@@ -357,3 +357,14 @@ def test_product_and_oracle_share_no_code():
         func = bench.rfind("\ndef ", 0, pos)
         name = re.match(r"\ndef (\w+)", bench[func:]).group(1) if func >= 0 else "<module>"
         assert "cpu" in name, "bench.py uses the oracle outside its CPU baseline (in %s)" % name
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus N > 1 exits with status 2 and says so
+    (before anything touches a GPU)."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2, r.stderr
+    assert "one GPU" in r.stderr and r.stdout == ""
