@@ -38,8 +38,12 @@ struct Counters {
 Counters g_stats;
 
 // Largest M that vq_gemm runs on the GEMV kernel, per weight type (Q4_K,
-// Q6_K, Q8_0): the GEMV <-> GEMM crossover.
-constexpr int64_t kSmallMaxDefault[4] = {16, 64, 32, 16};
+// Q6_K, Q8_0, Q5_K): the GEMV <-> GEMM crossover, measured on the decode
+// shapes against the MFMA GEMM with its split K (GEMV / GEMM at M = 16 and
+// 24: Q4_K 19.9 / 21.7 and 27.3 / 21.8 us, Q6_K 28.2 / 34.4 and 40.0 /
+// 34.1, Q5_K 21.6 / 24.2 and 29.6 / 24.3; Q8_0 at 32 and 48: 24.9 / 34.5
+// and 35.1 / 35.0).
+constexpr int64_t kSmallMaxDefault[4] = {16, 16, 32, 16};
 // Per calling thread, so a test's override never reaches another thread's calls.
 thread_local int64_t g_small_max[4] = {kSmallMaxDefault[0], kSmallMaxDefault[1], kSmallMaxDefault[2],
                                        kSmallMaxDefault[3]};

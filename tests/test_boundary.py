@@ -245,14 +245,14 @@ def test_status_strings_and_stats(vq):
 
 def test_small_batch_crossover_setting(vq):
     """vq_set_small_batch_max: defaults, range and type checks (host only)."""
-    defaults = {vq.Q4_K: 16, vq.Q6_K: 64, vq.Q8_0: 32}
+    defaults = {vq.Q4_K: 16, vq.Q6_K: 16, vq.Q8_0: 32, vq.Q5_K: 16}
     for w, d in defaults.items():
         assert vq.small_batch_max(w) == d
     try:
         vq.set_small_batch_max(vq.Q6_K, 3)
         assert vq.small_batch_max(vq.Q6_K) == 3
         vq.set_small_batch_max(vq.Q6_K, -1)
-        assert vq.small_batch_max(vq.Q6_K) == 64
+        assert vq.small_batch_max(vq.Q6_K) == 16
         with pytest.raises(vq.VQError, match="INVALID_ARG"):
             vq.set_small_batch_max(vq.Q4_K, 65)
         with pytest.raises(vq.VQError, match="INVALID_ARG"):
