@@ -390,9 +390,10 @@ def run_q5k(torch, vq, synth, iters):
 
 
 def run_small_batch(torch, vq, synth, iters):
-    """vq_gemm at M = 2, 4, 8, 16 on the decode matrices (the GEMV-kernel arm),
-    weights rotated past the Infinity Cache; rate = weight bytes + activation
-    bytes + output bytes per call."""
+    """vq_gemm at M = 2, 4, 8, 16, 32 on the decode matrices with the default
+    crossover ("arm": the GEMV kernel up to the crossover, the MFMA GEMM with
+    its split K above), weights rotated past the Infinity Cache; rate = weight
+    bytes + activation bytes + output bytes per call."""
     dev = torch.device("cuda:0")
     out = {}
     for name, wt, wn, xn in (("q4k", vq.Q4_K, "Wa", "Xh"), ("q6k", vq.Q6_K, "Wb", "Xi")):
@@ -402,14 +403,15 @@ def run_small_batch(torch, vq, synth, iters):
         del W
         R = max(2, math.ceil(640 * (1 << 20) / Q.numel()))
         Qs = [Q] + [Q.clone() for _ in range(R - 1)]
-        X = torch.from_numpy(synth.prefill_activations(xn, 16)).to(dev)
-        for M in (2, 4, 8, 16):
+        X = torch.from_numpy(synth.prefill_activations(xn, 32)).to(dev)
+        for M in (2, 4, 8, 16, 32):
             Xq = vq.quantize_act(vq.Q8_K, X[:M].contiguous())
             Y = torch.empty((M, N), dtype=torch.float32, device=dev)
             t, _ = time_graph(lambda i: vq.gemm(wt, Qs[i % R], N, K, vq.Q8_K, Xq, M, Y=Y), R, max(iters, 5 * R))
             b = Q.numel() + vq.act_bytes(vq.Q8_K, M, K) + 4 * M * N
             out["%s_M%d" % (name, M)] = {"us": round(t * 1e3, 2), "gbs": round(b / (t * 1e-3) / 1e9, 1),
-                                         "frac": round(b / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+                                         "frac": round(b / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                         "arm": "gemv" if M <= vq.small_batch_max(wt) else "mfma"}
         del Qs, Q
     return out
 

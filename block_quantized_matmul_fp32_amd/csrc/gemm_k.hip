@@ -692,11 +692,15 @@ __global__ __launch_bounds__(256, kPipe ? 1 : 2) void gemm_kq2_kernel(Args a, Gr
     float* pbase = a.part + ((int64_t)tile * a.splits) * (NT * MT * 16);
     {
         float* mine = pbase + (int64_t)sp * (NT * MT * 16);
+        // only the 32-row tiles that hold a valid row: the others are never
+        // read back (a small M leaves most of a 128-row tile as padding)
 #pragma unroll
-        for (int t = 0; t < MT; ++t)
+        for (int t = 0; t < MT; ++t) {
+            if (t > 0 && t >= mt_live) break;  // uniform
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 __hip_atomic_store(mine + (t * 16 + r) * NT + tid, y[t][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -711,7 +715,8 @@ __global__ __launch_bounds__(256, kPipe ? 1 : 2) void gemm_kq2_kernel(Args a, Gr
     for (int z = 0; z < a.splits; ++z) {
         const float* pz = pbase + (int64_t)z * (NT * MT * 16);
 #pragma unroll
-        for (int t = 0; t < MT; ++t)
+        for (int t = 0; t < MT; ++t) {
+            if (t > 0 && t >= mt_live) break;  // uniform: tiles of padding rows were not stored
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const float v = (z == sp) ? y[t][r]
@@ -719,11 +724,13 @@ __global__ __launch_bounds__(256, kPipe ? 1 : 2) void gemm_kq2_kernel(Args a, Gr
                                                               __HIP_MEMORY_SCOPE_AGENT);
                 acc[t][r] = (z == 0) ? v : acc[t][r] + v;
             }
+        }
     }
     if (tid == 0) __hip_atomic_store(a.cnt + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (n < a.N) {
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
+            if (t > 0 && t >= mt_live) break;  // uniform: only padding rows left
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int orow = sOut[32 * t + 8 * (r >> 2) + 4 * h + (r & 3)];

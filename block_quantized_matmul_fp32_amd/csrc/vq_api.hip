@@ -39,11 +39,11 @@ Counters g_stats;
 
 // Largest M that vq_gemm runs on the GEMV kernel, per weight type (Q4_K,
 // Q6_K, Q8_0, Q5_K): the GEMV <-> GEMM crossover, measured on the decode
-// shapes against the MFMA GEMM with its split K (GEMV / GEMM at M = 16 and
-// 24: Q4_K 19.9 / 21.7 and 27.3 / 21.8 us, Q6_K 28.2 / 34.4 and 40.0 /
-// 34.1, Q5_K 21.6 / 24.2 and 29.6 / 24.3; Q8_0 at 32 and 48: 24.9 / 34.5
-// and 35.1 / 35.0).
-constexpr int64_t kSmallMaxDefault[4] = {16, 16, 32, 16};
+// shapes against the MFMA GEMM with its split K (GEMV / GEMM at M = 8 and
+// 12: Q4_K 10.7 / 14.1 and 16.4 / 14.0 us, Q6_K 17.3 / 22.9 and 23.2 /
+// 23.1, Q5_K 10.7 / 16.7 and 17.5 / 16.8; Q8_0 at 32 and 48: 25.0 / 34.6
+// and 35.1 / 35.1).
+constexpr int64_t kSmallMaxDefault[4] = {8, 8, 32, 8};
 // Per calling thread, so a test's override never reaches another thread's calls.
 thread_local int64_t g_small_max[4] = {kSmallMaxDefault[0], kSmallMaxDefault[1], kSmallMaxDefault[2],
                                        kSmallMaxDefault[3]};

@@ -250,7 +250,7 @@ size_t vq_gemm_workspace(int w, int64_t M, int64_t N, int64_t K);
 /* The GEMV <-> GEMM crossover of vq_gemm (vllm.cpp PR #2890, "lever-B1":  */
 /* the fold crossover made tunable at run time): vq_gemm with weight type w */
 /* runs M <= max_m on the GEMV kernel.  max_m in [0, 64] (0: never), -1     */
-/* restores the default (Q4_K 16, Q5_K 16, Q6_K 16, Q8_0 32, measured on   */
+/* restores the default (Q4_K 8, Q5_K 8, Q6_K 8, Q8_0 32, measured on      */
 /* the decode shapes).  Per calling thread: other threads keep their own. */
 /* vq_small_batch_max returns the current value (-1 for a non-weight type). */
 /* ---------------------------------------------------------------------- */

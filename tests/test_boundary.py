@@ -178,7 +178,7 @@ def test_overrides_are_per_thread(vq):
         t.start()
         t.join()
         assert L.vq_small_batch_max(vq.Q4_K) == 3
-        assert seen["other"] == 16
+        assert seen["other"] == 8
         # a row-block cap on another thread leaves this thread's workspace plan alone
         before = vq.gemm_workspace(vq.Q6_K, 1000, 640, 4096)
         t = threading.Thread(target=lambda: L.vq_set_gemm_row_block(128))
@@ -245,14 +245,14 @@ def test_status_strings_and_stats(vq):
 
 def test_small_batch_crossover_setting(vq):
     """vq_set_small_batch_max: defaults, range and type checks (host only)."""
-    defaults = {vq.Q4_K: 16, vq.Q6_K: 16, vq.Q8_0: 32, vq.Q5_K: 16}
+    defaults = {vq.Q4_K: 8, vq.Q6_K: 8, vq.Q8_0: 32, vq.Q5_K: 8}
     for w, d in defaults.items():
         assert vq.small_batch_max(w) == d
     try:
         vq.set_small_batch_max(vq.Q6_K, 3)
         assert vq.small_batch_max(vq.Q6_K) == 3
         vq.set_small_batch_max(vq.Q6_K, -1)
-        assert vq.small_batch_max(vq.Q6_K) == 16
+        assert vq.small_batch_max(vq.Q6_K) == 8
         with pytest.raises(vq.VQError, match="INVALID_ARG"):
             vq.set_small_batch_max(vq.Q4_K, 65)
         with pytest.raises(vq.VQError, match="INVALID_ARG"):

@@ -113,7 +113,11 @@ def test_decode_small_batch_full(which, M):
     Xq = vq.quantize_act(vq.Q8_K, H.to_dev(X))
     act = check_act_bytes(wtype, Xq, X)
     vq.reset_stats()
-    Y = vq.gemm(wtype, H.to_dev(Wq), N, K, vq.Q8_K, Xq, M, Y=H.to_dev(np.full((M, N), np.nan, np.float32)))
+    vq.set_small_batch_max(wtype, 64)   # this arm at every M here, whatever the default crossover
+    try:
+        Y = vq.gemm(wtype, H.to_dev(Wq), N, K, vq.Q8_K, Xq, M, Y=H.to_dev(np.full((M, N), np.nan, np.float32)))
+    finally:
+        vq.set_small_batch_max(wtype, -1)
     assert vq.get_stats()["gemm_skinny"] == 1
     H.assert_bitwise(H.host(Y), oracle.gemm(wtype, Wq, N, K, act, nthreads=THREADS), "small batch " + which)
 
@@ -135,7 +139,13 @@ def test_q5k_decode_full():
     H.assert_bitwise(H.host(y), oracle.gemm(oracle.Q5_K, Wq, N, K, act, nthreads=THREADS)[0], "Q5_K GEMV")
     Xq = vq.quantize_act(vq.Q8_K, H.to_dev(X))
     actX = check_act_bytes(oracle.Q5_K, Xq, X)
-    Y = vq.gemm(vq.Q5_K, Wd, N, K, vq.Q8_K, Xq, X.shape[0])
+    vq.reset_stats()
+    vq.set_small_batch_max(vq.Q5_K, 64)   # the GEMV-kernel arm, whatever the default crossover
+    try:
+        Y = vq.gemm(vq.Q5_K, Wd, N, K, vq.Q8_K, Xq, X.shape[0])
+    finally:
+        vq.set_small_batch_max(vq.Q5_K, -1)
+    assert vq.get_stats()["gemm_skinny"] == 1
     H.assert_bitwise(H.host(Y), oracle.gemm(oracle.Q5_K, Wq, N, K, actX, nthreads=THREADS), "Q5_K batch")
 
 
