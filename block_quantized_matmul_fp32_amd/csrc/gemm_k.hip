@@ -812,9 +812,11 @@ static_assert(kMaxPlanWsBytes / (2 * kPartTileBytes) <= kMaxSplitTiles, "the cou
 //  * at most one tile per CU: the largest S that keeps one workgroup per CU
 //    (Q6_K at M = 512, 80 tiles: S = 3, 156 -> 67-70 us; S = 4 puts two
 //    workgroups on some CUs, 75 us);
-//  * up to two tiles per CU with a long K (at least 16 steps): two parts,
-//    so every CU holds two workgroups (Q6_K at M = 2048, 320 tiles: 237 ->
-//    221 us);
+//  * up to two tiles per CU with a long K (at least 16 steps): two or three
+//    parts, whichever leaves the last round of workgroups (two per CU)
+//    fuller, ties to two (Q6_K at M = 2048, 320 tiles: three parts fill 1.875
+//    rounds, two 1.25; measured 214 / 192 / 181 / 195 us for 1 / 2 / 3 / 4
+//    parts);
 //  * else none.
 // The workspace it needs is capped at kMaxPlanWsBytes.
 int gemm_kq_splits(int wtype, int64_t M, int64_t N, int64_t K) {
@@ -826,8 +828,13 @@ int gemm_kq_splits(int wtype, int64_t M, int64_t N, int64_t K) {
     int s = 1;
     if (tiles <= cus)
         s = (int)std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(kMaxSplits, nsteps), cus / tiles));
-    else if (tiles <= kResident * cus && nsteps >= 16)
-        s = 2;
+    else if (tiles <= kResident * cus && nsteps >= 16) {
+        // fill of the last round: (units / slots) / ceil(units / slots), compared exactly
+        const int64_t slots = kResident * cus;
+        const int64_t u2 = 2 * tiles, u3 = 3 * tiles;
+        const int64_t r2 = (u2 + slots - 1) / slots, r3 = (u3 + slots - 1) / slots;
+        s = (u3 * r2 > u2 * r3 && nsteps >= 24) ? 3 : 2;
+    }
     while (s > 1 && tiles * s * kPartTileBytes > kMaxPlanWsBytes) --s;
     if (tiles > kMaxSplitTiles) s = 1;
     return s;
