@@ -712,7 +712,28 @@ __global__ __launch_bounds__(256, kPipe ? 1 : 2) void gemm_kq2_kernel(Args a, Gr
     if (!sLast) return;
     // last arrival: the parts in order 0..S-1 (its own from registers)
     float acc[MT][16];
-    for (int z = 0; z < a.splits; ++z) {
+    int z = 0;
+    if (mt_live == 1) {
+        // one live 32-row tile (small M): the loads of four parts at a time
+        // are in flight together, then added in part order
+        for (; z + 4 <= a.splits; z += 4) {
+            float v[4][16];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float* pz = pbase + (int64_t)(z + k) * (NT * MT * 16);
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    v[k][r] = (z + k == sp) ? y[0][r]
+                                            : __hip_atomic_load(pz + r * NT + tid, __ATOMIC_RELAXED,
+                                                                __HIP_MEMORY_SCOPE_AGENT);
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[0][r] = (z + k == 0) ? v[k][r] : acc[0][r] + v[k][r];
+        }
+    }
+    for (; z < a.splits; ++z) {
         const float* pz = pbase + (int64_t)z * (NT * MT * 16);
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
