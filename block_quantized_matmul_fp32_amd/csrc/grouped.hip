@@ -12,16 +12,19 @@
 // exclusive prefix offsets, and the pair indices t*top_k+s listed per expert
 // in ascending (t, s) order.  It is built without atomics, so the list is
 // deterministic.  A call of up to 8192 pairs is routed by one workgroup in
-// one launch (route_one_kernel below); larger calls take three launches,
-// which spread the ballot work (the bulk of the routing's instructions) over
-// one CU per chunk:
+// one launch (route_one_kernel below); larger calls take two launches (up to
+// 64 chunks) or three, which spread the ballot work (the bulk of the
+// routing's instructions) over one CU per chunk:
 //  * one wave per chunk of 64 tokens walks the chunk's pairs 64 at a time;
 //    the lanes holding the same expert are found with one ballot per bit of
 //    the expert id, which gives each pair its rank among the chunk's earlier
 //    pairs of that expert and the chunk's per-expert counts;
-//  * one workgroup scans the per-chunk counts over chunks and experts and
-//    writes the tile table;
-//  * one thread per pair writes it to its list slot.
+//  * up to 64 chunks: one workgroup per chunk sums the chunk table, scans
+//    it over experts and places the chunk's pairs (workgroup 0 writes the
+//    counts, offsets and tile table);
+//  * more chunks: one workgroup scans the per-chunk counts over chunks and
+//    experts and writes the tile table, then one thread per pair writes it
+//    to its list slot.
 // The tile table stays on the device, so the grouped GEMM needs no host
 // synchronisation.  Pairs whose id is outside [0, E) are neither counted nor
 // placed.
@@ -369,6 +372,120 @@ __global__ __launch_bounds__(kOneThreads) void route_one_kernel(const int32_t* _
     }
 }
 
+// Calls of more than kOneMaxPairs pairs in at most kFuseMaxChunks chunks:
+// after the count launch, one workgroup per chunk c sums the chunk table over
+// chunks for every expert (the expert's total, and its pairs in the chunks
+// before c), scans the totals over experts and places its own chunk's pairs:
+// list[offset(e) + pairs of e in chunks < c + rank] = pair index.  Workgroup
+// 0 also writes the counts, the offsets and the tile table.  Every workgroup
+// reads the whole table (nchunks x E cells, at most 256 KiB), which takes the
+// place of the single-workgroup scan launch and the separate place launch.
+constexpr int kFuseThreads = 256;
+constexpr int kFuseMaxChunks = 64;
+constexpr int kFuseBatch = 32;  // chunk rows whose loads are in flight together
+__global__ __launch_bounds__(kFuseThreads) void route_scan_place_kernel(
+    const int32_t* __restrict__ ids, int T, int top_k, int E, int tile_rows, const int32_t* __restrict__ chunk,
+    const int32_t* __restrict__ rank, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ list, int32_t* __restrict__ tiles, int32_t* __restrict__ ntiles) {
+    __shared__ int32_t sTot[1024];  // expert totals
+    __shared__ int32_t sOff[1024];  // list offset of expert e, then plus its pairs in chunks before c
+    __shared__ int32_t wsum[kFuseThreads / 64], wnt[kFuseThreads / 64];
+    const int tid = threadIdx.x, c = blockIdx.x, nchunks = gridDim.x;
+    // strided ownership for the sums over chunks: experts tid + 256 j
+    int tot[4] = {0, 0, 0, 0}, pre[4] = {0, 0, 0, 0};
+    for (int c0 = 0; c0 < nchunks; c0 += kFuseBatch) {
+        int v[4][kFuseBatch];
+#pragma unroll
+        for (int k = 0; k < kFuseBatch; ++k)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int e = tid + kFuseThreads * j, cc = c0 + k;
+                v[j][k] = (e < E && cc < nchunks) ? chunk[(int64_t)cc * E + e] : 0;
+            }
+#pragma unroll
+        for (int k = 0; k < kFuseBatch; ++k)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                tot[j] += v[j][k];
+                pre[j] += (c0 + k < c) ? v[j][k] : 0;
+            }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = tid + kFuseThreads * j;
+        if (e < E) sTot[e] = tot[j];
+    }
+    __syncthreads();
+    // contiguous ownership for the scans over experts: experts 4 tid .. 4 tid + 3
+    int a[4], nt[4], sa = 0, snt = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int e = 4 * tid + q;
+        a[q] = (e < E) ? sTot[e] : 0;
+        nt[q] = (a[q] + tile_rows - 1) / tile_rows;
+        sa += a[q];
+        snt += nt[q];
+    }
+    const int lane = tid & 63, w = tid >> 6;
+    int ia = sa, int_ = snt;
+    for (int o = 1; o < 64; o <<= 1) {
+        const int ua = __shfl_up(ia, o, 64), ub = __shfl_up(int_, o, 64);
+        if (lane >= o) {
+            ia += ua;
+            int_ += ub;
+        }
+    }
+    if (lane == 63) {
+        wsum[w] = ia;
+        wnt[w] = int_;
+    }
+    __syncthreads();
+    int ea = ia - sa, en = int_ - snt;  // exclusive prefixes of this thread's first expert
+    int all_a = 0, all_n = 0;
+    for (int k = 0; k < kFuseThreads / 64; ++k) {
+        ea += (k < w) ? wsum[k] : 0;
+        en += (k < w) ? wnt[k] : 0;
+        all_a += wsum[k];
+        all_n += wnt[k];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int e = 4 * tid + q;
+        if (e < E) {
+            sOff[e] = ea;
+            if (c == 0) {
+                counts[e] = a[q];
+                offsets[e] = ea;
+                for (int i = 0; i < nt[q]; ++i) {
+                    tiles[4 * (en + i) + 0] = e;
+                    tiles[4 * (en + i) + 1] = ea + i * tile_rows;
+                    tiles[4 * (en + i) + 2] = min(tile_rows, a[q] - i * tile_rows);
+                    tiles[4 * (en + i) + 3] = 0;
+                }
+            }
+            ea += a[q];
+            en += nt[q];
+        }
+    }
+    if (c == 0 && tid == 0) {
+        offsets[E] = all_a;
+        ntiles[0] = all_n;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = tid + kFuseThreads * j;
+        if (e < E) sOff[e] += pre[j];
+    }
+    __syncthreads();
+    const int64_t p0 = (int64_t)c * kRouteChunk * top_k;
+    const int64_t p1 = (int64_t)min(T, (c + 1) * kRouteChunk) * top_k;
+    for (int64_t p = p0 + tid; p < p1; p += kFuseThreads) {
+        const int e = ids[p];
+        if (e >= 0 && e < E) list[sOff[e] + rank[p]] = (int32_t)p;
+    }
+}
+
 // One thread per pair: list[offsets[e] + chunk offset + rank] = pair index.
 __global__ __launch_bounds__(256) void route_place_kernel(const int32_t* __restrict__ ids, int64_t npairs,
                                                           int top_k, int E, const int32_t* __restrict__ chunk,
@@ -418,6 +535,12 @@ hipError_t launch_route(const int32_t* ids, int64_t T, int64_t top_k, int64_t E,
     const int nchunks = (int)((T + kRouteChunk - 1) / kRouteChunk);
     if (nchunks > 0)
         route_count_kernel<<<nchunks, 64, 0, st>>>(ids, (int)T, (int)top_k, (int)E, ws.chunk, ws.rank);
+    if (nchunks > 0 && nchunks <= kFuseMaxChunks) {
+        route_scan_place_kernel<<<nchunks, kFuseThreads, 0, st>>>(ids, (int)T, (int)top_k, (int)E, tile_rows,
+                                                                 ws.chunk, ws.rank, ws.counts, ws.offsets, ws.list,
+                                                                 ws.tiles, ws.ntiles);
+        return hipGetLastError();
+    }
     const int64_t ncell = (int64_t)nchunks * E;
     const size_t stage = (ncell <= kScanStageCells) ? (size_t)ncell * 4 : 0;
     route_scan_kernel<<<1, kScanThreads, stage, st>>>(nchunks, (int)E, tile_rows, ws.chunk, ws.counts, ws.offsets, ws.tiles,

@@ -746,15 +746,18 @@ def test_grouped_route_unstaged_scan():
 
 
 @pytest.mark.parametrize("E,T,top_k,skew", [(16, 1100, 8, False), (1024, 1100, 8, False),
-                                             (8, 1024, 8, True), (9, 1025, 8, True)])
+                                             (8, 1024, 8, True), (9, 1025, 8, True),
+                                             (16, 4200, 2, False), (1024, 4200, 2, False)])
 def test_grouped_route_size_paths(E, T, top_k, skew):
-    """Routing on both sides of the single-workgroup limit (8192 pairs):
-    1100 x top-8 takes the three-launch path with its chunk table staged in
-    LDS (16 experts) or read in global memory (1024 experts); 1024 x 8 pairs
-    almost all on one expert (repeated ids) fill the single-workgroup
-    kernel to its limit, and one token more goes to the three-launch path.
-    Counts, offsets and the list bit-identical to the oracle, Y within the
-    GEMM tolerance."""
+    """Routing on every path: 1100 x top-8 (18 chunks of 64 tokens) takes the
+    two-launch path (count, then one workgroup per chunk scanning and
+    placing) with 16 or 1024 experts; 1024 x 8 pairs almost all on one
+    expert (repeated ids) fill the single-workgroup kernel to its limit of
+    8192 pairs, and one token more goes to the two-launch path; 4200 x top-2
+    (66 chunks) takes the three-launch path with its chunk table staged in
+    LDS (16 experts) or read in global memory (1024 experts).  Counts,
+    offsets and the list bit-identical to the oracle, Y within the GEMM
+    tolerance."""
     N, K = 16, 256
     if skew:
         ids = np.zeros((T, top_k), np.int32)
