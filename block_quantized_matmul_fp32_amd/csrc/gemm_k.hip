@@ -363,10 +363,9 @@ struct KQ2 {
 // x eight 32-wide chunks), the binary16 min/centring MFMAs and the epilogue.
 // kMode: 0 dense; 1 routed rows with 32-bit activation offsets (rows * K
 // below 2^31, checked by the host); 2 routed rows with 64-bit offsets.
-// kPipe: one workgroup per CU (up to 512 registers per lane) with the tiles
-// of a step software-pipelined inside each wave; else two workgroups per CU.
-template <int WT, int MT, int kMode, bool kPipe = false>
-__global__ __launch_bounds__(256, kPipe ? 1 : 2) void gemm_kq2_kernel(Args a, GroupArgs ga) {
+// Two workgroups per CU.
+template <int WT, int MT, int kMode>
+__global__ __launch_bounds__(256, 2) void gemm_kq2_kernel(Args a, GroupArgs ga) {
     constexpr bool kGrouped = kMode != 0;
     using U = Unpack<WT>;
     using T = KQ2<WT>;
@@ -550,66 +549,6 @@ __global__ __launch_bounds__(256, kPipe ? 1 : 2) void gemm_kq2_kernel(Args a, Gr
         const int8_t* abuf = buf ? sA1 : sA0;
         const _Float16* sBc = buf ? sB1 : sB0;
         const float* sDc = buf ? sD1 : sD0;
-        if constexpr (kPipe) {
-            // Software pipeline over the step's tiles (one wave per SIMD, so
-            // MFMA and VALU work overlap only within the wave): while tile
-            // t's 16 int8 MFMAs run, the next tile's activation fragments are
-            // read and tile t-1 goes through its combine S = (R1 << SH) + R0
-            // as binary32 (chunks 0-1), its binary16 min/centring MFMAs
-            // (chunk 2) and its epilogue (chunks 3-6), issued between the
-            // MFMAs.  Iteration t = MT drains the last tile.
-            v4i af[2][8];
-            v16i R[2][2];
-            v16f sfq = {}, mnq = {};
-#pragma unroll
-            for (int c = 0; c < 8; ++c) af[0][c] = *(const v4i*)(abuf + abase[0] + 16 * (c ^ ax7[0]));
-#pragma unroll
-            for (int t = 0; t <= MT; ++t) {
-                const int p = t & 1;
-                if (t + 1 < MT) {
-#pragma unroll
-                    for (int c = 0; c < 8; ++c)
-                        af[p ^ 1][c] = *(const v4i*)(abuf + abase[t + 1] + 16 * (c ^ ax7[t + 1]));
-                }
-                if (t < MT) {
-                    R[p][0] = (v16i){};
-                    R[p][1] = (v16i){};
-                }
-#pragma unroll
-                for (int c = 0; c < 8; ++c) {
-                    if (t < MT) R[p][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[p][c], pl[c][0], R[p][0], 0, 0, 0);
-                    if (t > 0) {
-                        const int q = p ^ 1;  // tile t-1
-                        const int tb = 32 * (t - 1);
-                        if (c < 2) {
-#pragma unroll
-                            for (int r = 8 * c; r < 8 * c + 8; ++r)
-                                sfq[r] = (float)(int)(((uint32_t)R[q][1][r] << U::SH) + (uint32_t)R[q][0][r]);
-                        } else if (c == 2) {
-                            if (kMin) {
-                                const h8 bsv = *(const h8*)(sBc + 16 * (tb + l32) + 8 * h);
-                                if (T::kSc) sfq = __builtin_amdgcn_mfma_f32_32x32x16_f16(bsv, sco, sfq, 0, 0, 0);
-                                mnq = __builtin_amdgcn_mfma_f32_32x32x16_f16(bsv, mco, (v16f){}, 0, 0, 0);
-                            }
-                        } else if (c < 7) {
-                            // outputs 4 kk .. 4 kk + 3: rows 8 kk + 4 h + q of the tile
-                            const int kk = c - 3;
-                            const float4 da4 = *(const float4*)(sDc + tb + 4 * h + 8 * kk);
-                            const float da[4] = {da4.x, da4.y, da4.z, da4.w};
-#pragma unroll
-                            for (int q4 = 0; q4 < 4; ++q4) {
-                                const int r = 4 * kk + q4;
-                                float u = dw * sfq[r];
-                                if (kMin) u = __builtin_fmaf(-dmn, mnq[r], u);
-                                y[t - 1][r] = __builtin_fmaf(da[q4], u, y[t - 1][r]);
-                            }
-                        }
-                    }
-                    if (t < MT) R[p][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[p][c], pl[c][1], R[p][1], 0, 0, 0);
-                }
-            }
-            return;
-        }
         // Activation fragments are read one chunk ahead of their MFMAs.
         v4i av = *(const v4i*)(abuf + abase[0] + 16 * (0 ^ ax7[0]));
 #pragma unroll
