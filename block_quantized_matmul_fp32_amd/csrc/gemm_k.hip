@@ -112,20 +112,6 @@ __device__ __forceinline__ uint32_t bload2(WRsrc r, uint32_t off, uint32_t soff)
     return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, (int)soff, 0);
 }
 
-// 16 bytes from a 2-byte aligned global address with 4-byte aligned loads
-// (four dwords and, when p is not 4-byte aligned, the halfword at p + 14):
-// every byte read lies in [p, p + 16).
-typedef uint32_t u4a __attribute__((ext_vector_type(4), aligned(4)));  // 16 bytes, 4-byte aligned
-__device__ __forceinline__ u4v gload16_a2(const uint8_t* p) {
-    const uint32_t sh = (uint32_t)((uintptr_t)p & 3);
-    const uint32_t* q = (const uint32_t*)(p - sh);
-    const u4a w = *(const u4a*)q;  // one dwordx4 load (dword alignment suffices)
-    if (sh == 0) return (u4v){w.x, w.y, w.z, w.w};
-    const uint32_t w4 = *(const uint16_t*)(q + 4);
-    return (u4v){__builtin_amdgcn_alignbyte(w.y, w.x, sh), __builtin_amdgcn_alignbyte(w.z, w.y, sh),
-                 __builtin_amdgcn_alignbyte(w.w, w.z, sh), __builtin_amdgcn_alignbyte(w4, w.w, sh)};
-}
-
 // Orders a computation after `dep`: x passes through an empty asm that also
 // reads dep, so nothing that depends on x can be scheduled before dep is
 // complete.  The asm exists in the device pass only (the host pass of this
@@ -288,16 +274,6 @@ struct Unpack<3> {
         }
     }
 };
-
-// 8 bytes from a 2-byte aligned global address (every byte read in [p, p+8)).
-__device__ __forceinline__ uint2 gload8_a2(const uint8_t* p) {
-    const uint32_t sh = (uint32_t)((uintptr_t)p & 3);
-    const uint32_t* q = (const uint32_t*)(p - sh);
-    const uint32_t w0 = q[0], w1 = q[1];
-    if (sh == 0) return make_uint2(w0, w1);
-    const uint32_t w2 = *(const uint16_t*)(q + 2);
-    return make_uint2(__builtin_amdgcn_alignbyte(w1, w0, sh), __builtin_amdgcn_alignbyte(w2, w1, sh));
-}
 
 template <>
 struct Unpack<1> {

@@ -23,12 +23,9 @@ constexpr int kQ6KBytes = 210;
 constexpr int kQ5KBytes = 176;
 constexpr int kQ80Bytes = 34;
 
-__device__ __forceinline__ int lane_id() { return __lane_id(); }
-
 __device__ __forceinline__ int shfl_xor_i(int v, int m) { return __shfl_xor(v, m, 64); }
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
 __device__ __forceinline__ int shfl_i(int v, int src) { return __shfl(v, src, 64); }
-__device__ __forceinline__ float shfl_f(float v, int src) { return __shfl(v, src, 64); }
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
     _Float16 v = __builtin_bit_cast(_Float16, (uint16_t)h);
@@ -41,22 +38,6 @@ __device__ __forceinline__ uint32_t float_to_half_bits(float f) {
 
 __device__ __forceinline__ int sdot4(int a, int b, int c) {
     return __builtin_amdgcn_sdot4(a, b, c, false);
-}
-
-// 16 bytes at a 2-byte aligned LDS address, as four dwords, using only
-// 4-byte aligned reads.
-// The aligned pointer is formed by pointer arithmetic (not an integer round
-// trip) so the compiler keeps the LDS address space and emits ds_read.  The
-// fifth dword is always read (callers keep 4 bytes of slack after the data);
-// v_alignbyte with a zero shift returns its low operand.
-__device__ __forceinline__ void lds_read16_a2(const uint8_t* p, uint32_t out[4]) {
-    const uint32_t sh = (uint32_t)((uintptr_t)p & 3);
-    const uint32_t* q = (const uint32_t*)(p - sh);
-    const uint32_t w0 = q[0], w1 = q[1], w2 = q[2], w3 = q[3], w4 = q[4];
-    out[0] = __builtin_amdgcn_alignbyte(w1, w0, sh);
-    out[1] = __builtin_amdgcn_alignbyte(w2, w1, sh);
-    out[2] = __builtin_amdgcn_alignbyte(w3, w2, sh);
-    out[3] = __builtin_amdgcn_alignbyte(w4, w3, sh);
 }
 
 // ---------------------------------------------------------------------------
@@ -74,14 +55,6 @@ template <int C>
 __device__ __forceinline__ float dppf(float v) {
     return __builtin_bit_cast(float, dppi<C>(__builtin_bit_cast(int, v)));
 }
-// Sum over each group of 8 lanes, left on all 8 lanes (exact for ints).
-__device__ __forceinline__ int sum8(int v) {
-    v += dppi<0xB1>(v);
-    v += dppi<0x4E>(v);
-    v += dppi<0x141>(v);
-    return v;
-}
-__device__ __forceinline__ int readlane_i(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
 __device__ __forceinline__ float readlane_f(float v, int l) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
 }
