@@ -501,8 +501,8 @@ def run_grouped(torch, vq, synth, iters):
 
 def tile_rows(r):
     """The routed tile height the library picks at r rows per expert (for the
-    record: the smallest of 32, 64, 96, 128 rows holding r + 3 sqrt(r))."""
-    return 32 * min(4, max(1, math.ceil((r + 3.0 * math.sqrt(r)) / 32.0)))
+    record: the smallest of 32, 64, 96 rows holding r + 3 sqrt(r), else 96)."""
+    return 32 * min(3, max(1, math.ceil((r + 3.0 * math.sqrt(r)) / 32.0)))
 
 
 def run_grouped_down(torch, vq, synth, iters):

@@ -864,10 +864,14 @@ hipError_t launch_gemm_kq(int wtype, const uint8_t* W, int64_t N, int64_t K, con
 // strix-llama.cpp PR #18, restated for 32-row MFMA tiles): tiles are sized
 // from the rows each expert receives, not from the total pair count.  The
 // weights dominate the grouped call's traffic, so the height is the smallest
-// multiple of 32 (at most 128) that holds the mean rows per expert
-// r = T top_k / E plus three standard deviations of a uniform routing
-// (sqrt r): nearly every expert is then one tile and its weights are read
-// once.  r = 16 -> 32 rows, 32 -> 64, 64 -> 96, 128 -> 128 (two tiles).
+// multiple of 32 that holds the mean rows per expert r = T top_k / E plus
+// three standard deviations of a uniform routing (sqrt r): nearly every
+// expert is then one tile and its weights are read once.  r = 16 -> 32
+// rows, 32 -> 64, 64 and more -> 96.  The height stops at 96: the 128-row
+// routed kernel (its gathered-row offsets on top of the dense kernel's
+// registers) spills, and two or three 96-row tiles per expert measured
+// 5-10 % faster (warm, 96 to 256 rows per expert: 4,096 tokens 206 -> 196 us,
+// 8,192 tokens 349 -> 317 us).
 // Q8_0 keeps its GEMM's 96-row tiles.  A call whose activation rows take
 // 2^31 bytes or more runs the 64-bit-offset kernel, capped at 64-row tiles.
 int grouped_tile_rows(int wtype, int64_t E, int64_t T, int64_t top_k, int64_t K, int per_row) {
@@ -875,7 +879,7 @@ int grouped_tile_rows(int wtype, int64_t E, int64_t T, int64_t top_k, int64_t K,
     if (E <= 0 || T <= 0) return kGroupMinTileRows;
     const double r = (double)T * (double)top_k / (double)E;
     const int mt = (int)std::ceil((r + 3.0 * std::sqrt(r)) / 32.0);
-    int rows = 32 * std::min(4, std::max(1, mt));
+    int rows = 32 * std::min(3, std::max(1, mt));
     const int64_t arows = per_row ? T * top_k : T;
     if (arows * K >= ((int64_t)1 << 31)) rows = std::min(rows, 64);
     return rows;
@@ -932,7 +936,6 @@ static hipError_t launch_kq_grouped_w(int tile_rows, const uint8_t* W, int64_t E
         case 32: return launch_kq_grouped_t<WT, 1, 1>(W, E, N, K, aqs, ad, aux, T, top_k, per_row, ws, Y, st);
         case 64: return launch_kq_grouped_t<WT, 2, 1>(W, E, N, K, aqs, ad, aux, T, top_k, per_row, ws, Y, st);
         case 96: return launch_kq_grouped_t<WT, 3, 1>(W, E, N, K, aqs, ad, aux, T, top_k, per_row, ws, Y, st);
-        case 128: return launch_kq_grouped_t<WT, 4, 1>(W, E, N, K, aqs, ad, aux, T, top_k, per_row, ws, Y, st);
         default: return hipErrorInvalidValue;
     }
 }

@@ -341,11 +341,11 @@ vq_status vq_set_gemm_row_block(int64_t rows);
 /* ascending order), each section 256-byte aligned.                         */
 /* Tiles: the pairs of each expert are cut into routed tiles whose height   */
 /* comes from the mean rows per expert r = T*top_k/E ([P3] "routed-compact  */
-/* J rule"): the smallest of 32, 64, 96, 128 rows holding r + 3 sqrt(r), so */
-/* nearly every expert is one tile (Q8_0: 96 rows).  Numerics: routing and  */
-/* Ysum (of the Y written) are exact; the K-quant Y meets the tolerance of  */
-/* vq_gemm and two identical calls are bitwise equal; the Q8_0 Y is the     */
-/* fixed-order binary32 definition.                                         */
+/* J rule"): the smallest of 32, 64, 96 rows holding r + 3 sqrt(r), and 96 */
+/* above that, so nearly every expert is one tile or a few (Q8_0: 96 rows). */
+/* Numerics: routing and Ysum (of the Y written) are exact; the K-quant Y   */
+/* meets the tolerance of vq_gemm and two identical calls are bitwise      */
+/* equal; the Q8_0 Y is the fixed-order binary32 definition.               */
 /* Limits: E <= 1024, top_k <= 16, N % 16 == 0.                              */
 /* ---------------------------------------------------------------------- */
 size_t vq_grouped_workspace_bytes(int64_t E, int64_t T, int64_t top_k);

@@ -800,7 +800,7 @@ def test_grouped_tile_launches(per_row):
     H.assert_bitwise(outs[1][0], Y_ref, "grouped tile launches vs oracle")
 
 
-# rows per expert r -> routed tile height 32 (r = 4, 16), 64 (32), 96 (64), 128 (128)
+# rows per expert r -> routed tile height 32 (r = 4, 16), 64 (32), 96 (64; 128 in two tiles)
 @pytest.mark.parametrize("wtype", [oracle.Q4_K, oracle.Q6_K, oracle.Q5_K])
 @pytest.mark.parametrize("rows", [4, 16, 32, 64, 128])
 def test_grouped_rows_per_expert(wtype, rows):
