@@ -112,6 +112,32 @@ __device__ __forceinline__ uint32_t bload2(WRsrc r, uint32_t off, uint32_t soff)
     return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, (int)soff, 0);
 }
 
+// Buffer loads of 16 or 4 bytes per lane straight into LDS (lane i's bytes
+// at lds + 16 i or lds + 4 i), at byte offset voff + soff of the resource;
+// reads past the resource's range return zeros.  Device pass only (the host
+// pass of this single-source file sees kernel bodies but compiles none of
+// them).
+__device__ __forceinline__ void bload16_lds(WRsrc r, lds_void* lds, uint32_t voff, uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, (int)voff, (int)soff, 0, 0);
+#else
+    (void)r;
+    (void)lds;
+    (void)voff;
+    (void)soff;
+#endif
+}
+__device__ __forceinline__ void bload4_lds(WRsrc r, lds_void* lds, uint32_t voff, uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 4, (int)voff, (int)soff, 0, 0);
+#else
+    (void)r;
+    (void)lds;
+    (void)voff;
+    (void)soff;
+#endif
+}
+
 // Orders a computation after `dep`: x passes through an empty asm that also
 // reads dep, so nothing that depends on x can be scheduled before dep is
 // complete.  The asm exists in the device pass only (the host pass of this
@@ -362,6 +388,9 @@ __global__ __launch_bounds__(256, 2) void gemm_kq2_kernel(Args a, GroupArgs ga) 
     __shared__ __attribute__((aligned(16))) _Float16 sB0[kB16 ? BM * 16 : 8];
     __shared__ __attribute__((aligned(16))) _Float16 sB1[kB16 ? BM * 16 : 8];
     __shared__ int sRow[BM];
+    // byte offset of each bsum-loading thread's piece (32-bit offsets): read
+    // from LDS every step instead of held in a register across the loop
+    __shared__ uint32_t sBo[(kB16 && kMode != 2) ? 256 : 1];
     __shared__ int sOut[BM];
     __shared__ int sLast;
 
@@ -415,6 +444,14 @@ __global__ __launch_bounds__(256, 2) void gemm_kq2_kernel(Args a, GroupArgs ga) 
     // their MFMAs and epilogue would only compute padding)
     const int mt_live = (rows_here + 31) / 32;
     __syncthreads();
+    if constexpr (kB16 && kMode != 2) {
+        // written and later read by the same thread
+        if (tid < BSI) {
+            int ar = sRow[tid >> 1];
+            ar = ar >= 0 ? ar : 0;
+            sBo[tid] = (uint32_t)ar * (uint32_t)(a.K / 8) + 16u * (uint32_t)(tid & 1);
+        }
+    }
 
     const int nbk = a.K / kKS;
     const int64_t rowbytes = (int64_t)nbk * T::BB;
@@ -428,24 +465,35 @@ __global__ __launch_bounds__(256, 2) void gemm_kq2_kernel(Args a, GroupArgs ga) 
     // lane -> row 4 gi + lane/16, physical chunk lane%16 holding logical chunk
     // (lane%16) ^ (row & 15); 32-bit offsets from the activation base (the host
     // keeps rows * K below 2^31)
-    AOff aoff[AIPW];
+    // Routed tiles gather their rows (an offset per instruction); the dense
+    // tile's rows are consecutive, so its instruction j is the first one
+    // plus 16 j rows, one offset register with the rest in the uniform
+    // offset of a buffer load whose range ends at the launch's last row
+    // (rows past it read zeros, never stored).
+    constexpr int kAOffs = (kMode == 0) ? 1 : AIPW;
+    AOff aoff[kAOffs];
+    if constexpr (kMode == 0) {
+        const int r = 4 * wave + (lane >> 4);
+        aoff[0] = (uint32_t)(mb * BM + r) * (uint32_t)a.K + 16u * (uint32_t)((lane & 15) ^ (r & 15));
+    } else {
 #pragma unroll
-    for (int j = 0; j < AIPW; ++j) {
-        const int gi = wave + 4 * j;
-        const int r = 4 * gi + (lane >> 4);
-        int ar = (gi < NAI) ? sRow[r] : -1;
-        ar = ar >= 0 ? ar : 0;  // rows past the tile read row 0 (never stored)
-        aoff[j] = (AOff)ar * (AOff)a.K + (AOff)(16u * (uint32_t)((lane & 15) ^ (r & 15)));
+        for (int j = 0; j < AIPW; ++j) {
+            const int gi = wave + 4 * j;
+            const int r = 4 * gi + (lane >> 4);
+            int ar = (gi < NAI) ? sRow[r] : -1;
+            ar = ar >= 0 ? ar : 0;  // rows past the tile read row 0 (never stored)
+            aoff[j] = (AOff)ar * (AOff)a.K + (AOff)(16u * (uint32_t)((lane & 15) ^ (r & 15)));
+        }
     }
-    AOff doff;
-    {
+    AOff doff = 0;
+    if constexpr (kMode == 2) {
         const int r = 64 * wave + lane;
         int ar = (r < BM) ? sRow[r] : -1;
         ar = ar >= 0 ? ar : 0;
         doff = (AOff)ar * (AOff)nbk;
     }
     AOff boff = 0;
-    if (kB16) {
+    if (kB16 && kMode == 2) {
         const int r = tid >> 1;
         int ar = (tid < BSI) ? sRow[r] : -1;
         ar = ar >= 0 ? ar : 0;
@@ -454,22 +502,56 @@ __global__ __launch_bounds__(256, 2) void gemm_kq2_kernel(Args a, GroupArgs ga) 
 
     u4v raw[8];
     uint4 rb = make_uint4(0, 0, 0, 0);
+    // the bsums and the scales d of the launch's activation rows (< 2^32
+    // bytes while the offsets are 32-bit)
+    const WRsrc brs = make_wrsrc((const uint8_t*)a.abs, (int64_t)a.M * (a.K / 16) * 2);
+    const WRsrc drs = make_wrsrc((const uint8_t*)a.ad, (int64_t)a.M * nbk * 4);
+    const WRsrc ars = make_wrsrc((const uint8_t*)a.aqs, (int64_t)a.M * a.K);
     // Copies of step s: activations and their scales by LDS-DMA into buffer
     // B, bsums and the weight blocks into registers.
     auto issue_act = [&](int s, auto bufc) __attribute__((always_inline)) {
         constexpr int buf = decltype(bufc)::value;
         int8_t* sAb = buf ? sA1 : sA0;
         float* sDb = buf ? sD1 : sD0;
-        const int8_t* ab = a.aqs + (int64_t)s * kKS;
 #pragma unroll
         for (int j = 0; j < AIPW; ++j) {
             const int gi = wave + 4 * j;
-            if (gi < NAI)
-                __builtin_amdgcn_global_load_lds((const void*)(ab + aoff[j]), (lds_void*)(sAb + 4 * gi * kKS), 16, 0, 0);
+            if constexpr (kMode == 0) {
+                if (gi < NAI)
+                    bload16_lds(ars, (lds_void*)(sAb + 4 * gi * kKS), aoff[0],
+                                (uint32_t)s * kKS + (uint32_t)(16 * j) * (uint32_t)a.K);
+            } else {
+                const int8_t* ab = a.aqs + (int64_t)s * kKS;
+                if (gi < NAI)
+                    __builtin_amdgcn_global_load_lds((const void*)(ab + aoff[j]), (lds_void*)(sAb + 4 * gi * kKS), 16,
+                                                     0, 0);
+            }
         }
-        if (wave < NDI)
-            __builtin_amdgcn_global_load_lds((const void*)(a.ad + s + doff), (lds_void*)(sDb + 64 * wave), 4, 0, 0);
-        if (kB16 && tid < BSI) rb = *(const uint4*)(a.abs + (int64_t)s * 16 + boff);
+        if (wave < NDI) {
+            if constexpr (kMode == 2) {
+                __builtin_amdgcn_global_load_lds((const void*)(a.ad + s + doff), (lds_void*)(sDb + 64 * wave), 4, 0,
+                                                 0);
+            } else {
+                // 32-bit offsets: a buffer load into LDS, its row from LDS each
+                // step (an address kept across the loop is spilled, and its
+                // reload's wait would also wait for the copies just issued)
+                const int r = 64 * wave + lane;
+                int ar = (r < BM) ? sRow[r] : -1;
+                ar = ar >= 0 ? ar : 0;
+                bload4_lds(drs, (lds_void*)(sDb + 64 * wave), (uint32_t)ar * (uint32_t)nbk * 4u, (uint32_t)s * 4u);
+            }
+        }
+        if (kB16 && tid < BSI) {
+            // 32-bit offsets: a buffer load with a uniform resource
+            if constexpr (kMode == 2) {
+                rb = *(const uint4*)(a.abs + (int64_t)s * 16 + boff);
+            } else {
+                // the offset from LDS each step (an offset kept across the
+                // loop is spilled, and its reload's wait would also wait for
+                // the activation copies just issued)
+                rb = __builtin_bit_cast(uint4, bload16(brs, sBo[tid], (uint32_t)s * 32u));
+            }
+        }
     };
     auto issue_w = [&](int s) __attribute__((always_inline)) {
         U::load(wrs, woff, (uint32_t)(s * T::BB), h, raw);
