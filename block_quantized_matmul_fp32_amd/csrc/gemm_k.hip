@@ -467,9 +467,8 @@ __global__ __launch_bounds__(256, 2) void gemm_kq2_kernel(Args a, GroupArgs ga) 
     // keeps rows * K below 2^31)
     // Routed tiles gather their rows (an offset per instruction); the dense
     // tile's rows are consecutive, so its instruction j is the first one
-    // plus 16 j rows, one offset register with the rest in the uniform
-    // offset of a buffer load whose range ends at the launch's last row
-    // (rows past it read zeros, never stored).
+    // plus 16 j rows: one offset register, and buffer loads whose range ends
+    // at the launch's last row (rows past it read zeros, never stored).
     constexpr int kAOffs = (kMode == 0) ? 1 : AIPW;
     AOff aoff[kAOffs];
     if constexpr (kMode == 0) {
@@ -518,8 +517,10 @@ __global__ __launch_bounds__(256, 2) void gemm_kq2_kernel(Args a, GroupArgs ga) 
             const int gi = wave + 4 * j;
             if constexpr (kMode == 0) {
                 if (gi < NAI)
-                    bload16_lds(ars, (lds_void*)(sAb + 4 * gi * kKS), aoff[0],
-                                (uint32_t)s * kKS + (uint32_t)(16 * j) * (uint32_t)a.K);
+                    // the row part in the lane offset, which the range
+                    // check covers; the step offset (< K) in the uniform one
+                    bload16_lds(ars, (lds_void*)(sAb + 4 * gi * kKS), aoff[0] + (uint32_t)(16 * j) * (uint32_t)a.K,
+                                (uint32_t)s * kKS);
             } else {
                 const int8_t* ab = a.aqs + (int64_t)s * kKS;
                 if (gi < NAI)
