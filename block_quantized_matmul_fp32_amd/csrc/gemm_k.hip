@@ -829,8 +829,13 @@ static_assert(kMaxPlanWsBytes / (2 * kPartTileBytes) <= kMaxSplitTiles, "the cou
 // redistribute once the grid fills the chip (Q4_K at M = 2048: 141 us
 // unsplit, 431 us in eight parts), so only short grids split:
 //  * at most one tile per CU: the largest S that keeps one workgroup per CU
-//    (Q6_K at M = 512, 80 tiles: S = 3, 156 -> 67-70 us; S = 4 puts two
-//    workgroups on some CUs, 75 us);
+//    (Q6_K at M = 512, 80 tiles: S = 3, 156 -> 63 us), or the largest that
+//    keeps two per CU when that at least doubles S and leaves every part
+//    three steps or more (Q6_K at M = 512: S = 6, 63 -> 60 us; Q4_K at
+//    M = 200, 152 tiles: S = 3, 35.5 -> 31.3 us; Q5_K at M = 512, 256 tiles:
+//    S = 2, 46 -> 44 us).  Smaller gains in S, or shorter parts, measured
+//    slower (Q6_K at M = 200, 40 tiles: 6 -> 8 parts 46 -> 53 us; Q4_K at
+//    M = 64, 76 tiles: 3 -> 6 parts 17.5 -> 20.7 us);
 //  * up to two tiles per CU with a long K (at least 16 steps): two or three
 //    parts, whichever leaves the last round of workgroups (two per CU)
 //    fuller, ties to two (Q6_K at M = 2048, 320 tiles: three parts fill 1.875
@@ -845,8 +850,12 @@ int gemm_kq_splits(int wtype, int64_t M, int64_t N, int64_t K) {
     const int64_t nsteps = K / 256;
     if (tiles <= 0 || nsteps <= 1) return 1;
     int s = 1;
-    if (tiles <= cus)
-        s = (int)std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(kMaxSplits, nsteps), cus / tiles));
+    if (tiles <= cus) {
+        const int64_t cap = std::min<int64_t>(kMaxSplits, nsteps);
+        const int64_t s1 = std::max<int64_t>(1, std::min<int64_t>(cap, cus / tiles));
+        const int64_t s2 = std::max<int64_t>(1, std::min<int64_t>(cap, kResident * cus / tiles));
+        s = (int)((s2 >= 2 * s1 && nsteps >= 3 * s2) ? s2 : s1);
+    }
     else if (tiles <= kResident * cus && nsteps >= 16) {
         // fill of the last round: (units / slots) / ceil(units / slots), compared exactly
         const int64_t slots = kResident * cus;

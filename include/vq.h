@@ -230,15 +230,15 @@ vq_status vq_gemv(int w, const void* W, int64_t N, int64_t K, const float* x, fl
 /* ws: NULL or a device workspace of at least vq_gemm_workspace(w, M, N, K) */
 /* bytes, 256-byte aligned, ZERO-FILLED BEFORE ITS FIRST USE; the MFMA GEMM */
 /* splits K across workgroups when its tiles cannot fill the chip (a grid  */
-/* of at most one tile per CU into as many parts, up to eight, as keep one  */
-/* workgroup per CU; up to two tiles per CU with K >= 4096 in two), keeps  */
-/* per-tile arrival counters in the first 64 KiB of the workspace (the same */
-/* place for every shape) and the fp32 partial tiles after them, and leaves */
-/* the counters zero when the call completes, so one workspace serves calls */
-/* of any shape.  A smaller workspace (or NULL) gives fewer splits (or      */
-/* none): the result stays within the tolerance but its fp32 rounding may   */
-/* differ.  Calls that share a workspace must not run concurrently (same    */
-/* stream, or ordered streams).                                             */
+/* of at most one tile per CU into up to eight parts, one or two           */
+/* workgroups per CU; up to two tiles per CU with K >= 4096 in two or      */
+/* three), keeps per-tile arrival counters in the first 64 KiB of the      */
+/* workspace (the same place for every shape) and the fp32 partial tiles   */
+/* after them, and leaves the counters zero when the call completes, so    */
+/* one workspace serves calls of any shape.  A smaller workspace (or NULL) */
+/* gives fewer splits (or none): the result stays within the tolerance    */
+/* but its fp32 rounding may differ.  Calls that share a workspace must    */
+/* not run concurrently (same stream, or ordered streams).                 */
 /* ---------------------------------------------------------------------- */
 vq_status vq_gemm(int w, const void* W, int64_t N, int64_t K, int act, const void* Xq,
                   int64_t M, float* Y, int64_t ldy, void* ws, size_t ws_bytes, hipStream_t stream);

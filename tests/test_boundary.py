@@ -157,11 +157,14 @@ def test_gemm_workspace_checks(vq):
     assert vq.gemm_workspace(vq.Q8_0, 2048, 4096, 2048) == 0
     assert vq.gemm_workspace(vq.Q4_K, 1, 9728, 2560) == 0          # GEMV-kernel arm
     assert vq.gemm_workspace(vq.Q4_K, 2048, 9728, 2560) == 0       # 1216 tiles fill the chip: no split
-    assert vq.gemm_workspace(vq.Q6_K, 512, 2560, 9728) == 65536 + 80 * 3 * 128 * 128 * 4   # one per CU
+    assert vq.gemm_workspace(vq.Q6_K, 512, 2560, 9728) == 65536 + 80 * 6 * 128 * 128 * 4   # two per CU
     # 320 tiles: three parts fill 1.875 rounds of two workgroups per CU, two parts 1.25
     assert vq.gemm_workspace(vq.Q6_K, 2048, 2560, 9728) == 65536 + 320 * 3 * 128 * 128 * 4
     assert vq.gemm_workspace(vq.Q6_K, 3200, 2560, 9728) == 65536 + 500 * 2 * 128 * 128 * 4  # ties go to two
     assert vq.gemm_workspace(vq.Q4_K, 512, 9728, 2560) == 0         # 304 tiles, 10 steps: no split
+    assert vq.gemm_workspace(vq.Q4_K, 200, 9728, 2560) == 65536 + 152 * 3 * 128 * 128 * 4  # two per CU
+    assert vq.gemm_workspace(vq.Q4_K, 64, 9728, 2560) == 65536 + 76 * 3 * 128 * 128 * 4   # parts of 3+ steps
+    assert vq.gemm_workspace(vq.Q6_K, 200, 2560, 9728) == 65536 + 40 * 6 * 128 * 128 * 4  # 8 is not twice 6
     small = vq.gemm_workspace(vq.Q6_K, 256, 640, 4096)             # 10 tiles, 16 steps: split K
     assert small > 0 and small % 256 == 0
     assert vq.gemm_workspace(vq.Q4_K, 0, 640, 4096) == 0
