@@ -610,6 +610,38 @@ def test_gemm_workspace_reused_across_shapes(wtype):
                        "reused workspace %s M=%d" % (WNAME[wtype], M), ref_fp64.gemm_fp64(wtype, Wq, N, K, act))
 
 
+@pytest.mark.parametrize("wtype,M,N,K,parts", [(oracle.Q4_K, 200, 9728, 2560, 3), (oracle.Q5_K, 300, 8192, 2560, 2)])
+def test_gemm_split_two_per_cu(wtype, M, N, K, parts):
+    """Grids of at most one tile per CU that the plan splits into two
+    workgroups per CU (152 tiles in three parts, 192 tiles in two), with a
+    ragged last row tile: every output written, sampled outputs (whole first
+    and last rows and columns) within the GEMM tolerance, two calls bitwise
+    equal."""
+    tiles = ((N + 127) // 128) * ((M + 127) // 128)
+    assert vq.gemm_workspace(wtype, M, N, K) == 65536 + tiles * parts * 128 * 128 * 4
+    W = synth.normal((1710, wtype), (N, K), 0.02)
+    X = synth.normal((1711, wtype, M), (M, K))
+    Wq = oracle.quantize_weights(wtype, W)
+    del W
+    act = oracle_act(wtype, X)
+    Wd, Xq = H.to_dev(Wq), H.to_dev(H.pack_act(act, wtype))
+    runs = []
+    for rep in range(2):
+        H.say("gemm two per CU %s M=%d N=%d K=%d run %d" % (WNAME[wtype], M, N, K, rep))
+        Yd = H.to_dev(np.full((M, N), np.nan, np.float32))
+        vq.gemm(wtype, Wd, N, K, vq.Q8_K, Xq, M, Y=Yd)
+        runs.append(H.host(Yd))
+    Yh = runs[0]
+    assert np.isfinite(Yh).all(), "every output written"
+    assert np.array_equal(H.bits(runs[1]), H.bits(Yh)), "two identical calls differ"
+    rng = np.random.default_rng(1712)
+    ms = np.concatenate([np.arange(M), rng.integers(0, M, 3000), np.full(N, M - 1)]).astype(np.int64)
+    ns = np.concatenate([np.full(M, N - 1), rng.integers(0, N, 3000), np.arange(N)]).astype(np.int64)
+    ref = oracle.gemm_sampled(wtype, Wq, N, K, act, ms, ns, nthreads=8)
+    H.assert_gemm(wtype, Yh[ms, ns], ref, "gemm two per CU %s" % WNAME[wtype],
+                  H.fp64_cells(wtype, Wq, N, K, act, ms, ns))
+
+
 def test_determinism_and_witness():
     N, K, M = 256, 2560, 130
     W = synth.normal(1700, (N, K), 0.02)
