@@ -15,10 +15,12 @@
 // one launch (route_one_kernel below); larger calls take two launches (up to
 // 64 chunks) or three, which spread the ballot work (the bulk of the
 // routing's instructions) over one CU per chunk:
-//  * one wave per chunk of 64 tokens walks the chunk's pairs 64 at a time;
-//    the lanes holding the same expert are found with one ballot per bit of
-//    the expert id, which gives each pair its rank among the chunk's earlier
-//    pairs of that expert and the chunk's per-expert counts;
+//  * four waves per chunk of 64 tokens, each walking a quarter of the
+//    chunk's pairs 64 at a time; the lanes holding the same expert are found
+//    with one ballot per bit of the expert id, which gives each pair its rank
+//    among the quarter's earlier pairs of that expert and the quarter's
+//    per-expert counts, and the quarters' counts then give the ranks in the
+//    chunk and the chunk's per-expert counts;
 //  * up to 64 chunks: one workgroup per chunk sums the chunk table, scans
 //    it over experts and places the chunk's pairs (workgroup 0 writes the
 //    counts, offsets and tile table);
@@ -70,53 +72,86 @@ size_t route_ws_layout(int64_t E, int64_t T, int64_t top_k, RouteWs* ws, uint8_t
 
 constexpr int kIdBits = 11;  // expert ids < 1024, plus 64 distinct keys for pairs not routed
 
-// One wave per chunk of kRouteChunk tokens: rank[p] = number of earlier pairs
-// of the chunk with the same expert, chunk[c][e] = the chunk's pairs of e.
-__global__ __launch_bounds__(64) void route_count_kernel(const int32_t* __restrict__ ids, int T, int top_k,
-                                                         int E, int32_t* __restrict__ chunk,
-                                                         int32_t* __restrict__ rank) {
-    __shared__ int32_t cnt[1024];
-    const int lane = threadIdx.x;
+// One workgroup of kCountWaves waves per chunk of kRouteChunk tokens:
+// rank[p] = number of earlier pairs of the chunk with the same expert,
+// chunk[c][e] = the chunk's pairs of e.  Wave w takes the contiguous pair
+// range [w L, (w + 1) L) of the chunk (L a multiple of 64) and ranks its
+// pairs among the range's earlier pairs (ballot-per-id-bit groups, as in
+// route_one_kernel), counting per expert in its own LDS row; then the
+// counts are turned into each wave's exclusive offset inside the expert
+// (wave order is pair order), and a pair's rank is its rank in the range
+// plus its wave's offset.  Same ranks and counts as one wave walking the
+// whole chunk, in a quarter of the rounds.  Grouped calls take top_k <= 16,
+// so a chunk holds at most 1024 pairs and a wave at most 4 rounds.
+constexpr int kCountWaves = 4;
+constexpr int kCountThreads = 64 * kCountWaves;
+constexpr int kCountMaxPairs = kRouteChunk * 16;
+constexpr int kCountMaxRounds = kCountMaxPairs / kCountThreads;
+__global__ __launch_bounds__(kCountThreads) void route_count_kernel(const int32_t* __restrict__ ids, int T,
+                                                                    int top_k, int E, int32_t* __restrict__ chunk,
+                                                                    int32_t* __restrict__ rank) {
+    __shared__ int32_t cnt[kCountWaves * 1024];  // [wave][expert]: count, then the wave's offset
+    __shared__ int32_t lrank[kCountMaxPairs];     // rank inside the wave's range, or -1 (not routed)
+    __shared__ int16_t lexp[kCountMaxPairs];      // the pair's expert
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = blockIdx.x;
     const int64_t p0 = (int64_t)c * kRouteChunk * top_k;
     const int np = min(kRouteChunk, T - c * kRouteChunk) * top_k;
-    for (int e = lane; e < E; e += 64) cnt[e] = 0;
-    // The chunk's ids are requested up front, kIdBatch rounds of 64 at a time,
-    // so the rounds do not wait on one global load each.
-    constexpr int kIdBatch = 8;
-    int idv[kIdBatch];
+    for (int i = tid; i < kCountWaves * E; i += kCountThreads) cnt[i] = 0;
     __syncthreads();
+    const int L = 64 * ((np + kCountThreads - 1) / kCountThreads);
+    const int a = min(w * L, np), b = min(a + L, np);
+    int32_t* cw = cnt + w * E;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int base = 0; base < np; base += 64) {
-        const int j = (base / 64) % kIdBatch;
-        if (j == 0) {
+    // the range's ids are requested up front, so the rounds do not each wait
+    // on a global load
+    int idv[kCountMaxRounds];
 #pragma unroll
-            for (int k = 0; k < kIdBatch; ++k) {
-                const int ik = base + 64 * k + lane;
-                idv[k] = (ik < np) ? ids[p0 + ik] : -1;
-            }
-        }
-        const int i = base + lane;
-        int e = -1;
+    for (int k = 0; k < kCountMaxRounds; ++k) {
+        const int i = a + 64 * k + lane;
+        idv[k] = (i < b) ? ids[p0 + i] : -1;
+    }
 #pragma unroll
-        for (int k = 0; k < kIdBatch; ++k)
-            if (k == j) e = idv[k];
-        const bool ok = (i < np) && e >= 0 && e < E;
+    for (int k = 0; k < kCountMaxRounds; ++k) {
+        if (a + 64 * k >= b) break;  // uniform
+        const int i = a + 64 * k + lane;
+        const int e = idv[k];
+        const bool ok = (i < b) && e >= 0 && e < E;
         const int key = ok ? e : 1024 + lane;  // a pair not routed matches no other lane
         uint64_t same = ~0ull;
 #pragma unroll
-        for (int b = 0; b < kIdBits; ++b) {
-            const uint64_t set = __ballot((key >> b) & 1);
-            same &= ((key >> b) & 1) ? set : ~set;
+        for (int bit = 0; bit < kIdBits; ++bit) {
+            const uint64_t set = __ballot((key >> bit) & 1);
+            same &= ((key >> bit) & 1) ? set : ~set;
         }
-        const int r = __popcll(same & below);
-        const int before = ok ? cnt[e] : 0;
-        if (ok) rank[p0 + i] = before + r;
+        // the wave's LDS operations run in order, so this round reads what
+        // the previous round's group leaders wrote
+        const int before = ok ? cw[e] : 0;
+        if (i < b) {
+            lrank[i] = ok ? before + __popcll(same & below) : -1;
+            lexp[i] = (int16_t)(ok ? e : 0);
+        }
         // the highest lane of each expert's group advances the count
-        if (ok && (same >> lane) == 1ull) cnt[e] = before + __popcll(same);
-        __syncthreads();
+        if (ok && (same >> lane) == 1ull) cw[e] = before + __popcll(same);
     }
-    for (int e = lane; e < E; e += 64) chunk[(int64_t)c * E + e] = cnt[e];
+    __syncthreads();
+    for (int e = tid; e < E; e += kCountThreads) {
+        int run = 0;
+#pragma unroll
+        for (int u = 0; u < kCountWaves; ++u) {
+            const int v = cnt[u * E + e];
+            cnt[u * E + e] = run;
+            run += v;
+        }
+        chunk[(int64_t)c * E + e] = run;
+    }
+    __syncthreads();
+    for (int i = tid; i < np; i += kCountThreads) {
+        const int lr = lrank[i];
+        if (lr >= 0) rank[p0 + i] = lr + cnt[(i / L) * E + lexp[i]];
+    }
 }
 
 // One workgroup: chunk[c][e] becomes the exclusive offset of chunk c inside
@@ -526,6 +561,8 @@ hipError_t launch_check_ids(const int32_t* ids, int64_t T, int64_t top_k, int64_
 hipError_t launch_route(const int32_t* ids, int64_t T, int64_t top_k, int64_t E, int tile_rows, RouteWs ws,
                         hipStream_t st) {
     if (tile_rows < kGroupMinTileRows) return hipErrorInvalidValue;
+    // the count kernel's LDS holds 16 pairs per token and ids below 1024
+    if (top_k < 1 || top_k > 16 || E < 1 || E > 1024) return hipErrorInvalidValue;
     const int64_t npairs_all = T * top_k;
     if (npairs_all <= kOneMaxPairs) {
         route_one_kernel<<<1, kOneThreads, 0, st>>>(ids, (int)npairs_all, (int)E, tile_rows, ws.rank, ws.counts,
@@ -534,7 +571,7 @@ hipError_t launch_route(const int32_t* ids, int64_t T, int64_t top_k, int64_t E,
     }
     const int nchunks = (int)((T + kRouteChunk - 1) / kRouteChunk);
     if (nchunks > 0)
-        route_count_kernel<<<nchunks, 64, 0, st>>>(ids, (int)T, (int)top_k, (int)E, ws.chunk, ws.rank);
+        route_count_kernel<<<nchunks, kCountThreads, 0, st>>>(ids, (int)T, (int)top_k, (int)E, ws.chunk, ws.rank);
     if (nchunks > 0 && nchunks <= kFuseMaxChunks) {
         route_scan_place_kernel<<<nchunks, kFuseThreads, 0, st>>>(ids, (int)T, (int)top_k, (int)E, tile_rows,
                                                                  ws.chunk, ws.rank, ws.counts, ws.offsets, ws.list,
