@@ -779,7 +779,8 @@ def test_grouped_route_unstaged_scan():
 
 @pytest.mark.parametrize("E,T,top_k,skew", [(16, 1100, 8, False), (1024, 1100, 8, False),
                                              (8, 1024, 8, True), (9, 1025, 8, True),
-                                             (16, 4200, 2, False), (1024, 4200, 2, False)])
+                                             (16, 4200, 2, False), (1024, 4200, 2, False),
+                                             (64, 600, 16, False), (1024, 700, 16, True)])
 def test_grouped_route_size_paths(E, T, top_k, skew):
     """Routing on every path: 1100 x top-8 (18 chunks of 64 tokens) takes the
     two-launch path (count, then one workgroup per chunk scanning and
@@ -787,7 +788,9 @@ def test_grouped_route_size_paths(E, T, top_k, skew):
     expert (repeated ids) fill the single-workgroup kernel to its limit of
     8192 pairs, and one token more goes to the two-launch path; 4200 x top-2
     (66 chunks) takes the three-launch path with its chunk table staged in
-    LDS (16 experts) or read in global memory (1024 experts).  Counts,
+    LDS (16 experts) or read in global memory (1024 experts); 600 and 700
+    tokens x top-16 fill each chunk of the count kernel (1024 pairs, four
+    rounds per wave), the second almost all on one expert.  Counts,
     offsets and the list bit-identical to the oracle, Y within the GEMM
     tolerance."""
     N, K = 16, 256
